@@ -1,0 +1,247 @@
+"""Throughput of the block verify pass on one MI355X.
+
+A step is one verify pass plus its commit (every step of the hot path) over
+one batch: the 0.5B-class FP8 target (24 layers, hidden 896, 14/2 heads,
+head_dim 64, SwiGLU 4864, vocab 151936, tied BF16 lm_head), 32 sequences with
+contexts uniform in [512, 4096], 16-token blocks (512 rows per GEMM).  All
+inputs are seeded synthetic data resident in HBM before timing: FP8 weights
+drawn N(0, 0.02^2), BF16 KV caches drawn N(0, (0.02*sqrt(H))^2), drafts
+planted from the pass's own greedy continuation with acceptance lengths
+min(Geometric(0.1), 16).  The timed region replays a captured graph of
+{restore kv_len, verify, commit} K times between two events.
+
+Prints one JSON line (see the keys below).  --gpus N > 1 is refused: this
+build measures one GPU.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense BF16 MFMA
+RIDGE = MFMA_BF16_PEAK / HBM_PEAK
+METRIC = "verify passes/s & accepted tok/s, 0.5B FP8 target, K=16 block; % of HBM peak"
+WORKLOAD = "0.5b-fp8-b32-ctx512to4096"
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def weight_bytes_per_layer(m):
+    H, I, D = m.hidden, m.intermediate, m.head_dim
+    qkv = m.qkv_rows * H + m.qkv_rows * 4
+    o = H * m.n_q_heads * D + H * 4
+    if m.mlp_format == "fp8":
+        gu, dn = 2 * I * H + 2 * I * 4, H * I + H * 4
+    else:
+        gu, dn = 2 * I * H // 2 + 2 * I * H // 32, H * I // 2 + H * I // 32
+    return {"qkv": qkv, "o_proj": o, "gate_up": gu, "down": dn, "norms": 2 * H * 4}
+
+
+def kernel_work(kind, m, lens):
+    """Algorithmic (bytes, flops) of ONE launch of a kernel class."""
+    B = len(lens)
+    M, H, D, I, V = B * 16, m.hidden, m.head_dim, m.intermediate, m.vocab
+    wb = weight_bytes_per_layer(m)
+    HqD = m.n_q_heads * D
+    if kind == "attention":
+        kv = int(np.sum(lens + 16)) * m.n_kv_heads * D * 2 * 2
+        flops = sum(int(np.sum(n + 1 + np.arange(16))) for n in lens) * m.n_q_heads * D * 4
+        return kv + 2 * M * HqD * 2, flops
+    if kind == "qkv":
+        return wb["qkv"] + M * H * 2 + M * (HqD + 2 * m.n_kv_heads * D) * 2, 2 * M * m.qkv_rows * H
+    if kind == "o_proj":
+        return wb["o_proj"] + M * HqD * 2 + 2 * M * H * 4, 2 * M * H * HqD
+    if kind == "gate_up":
+        return wb["gate_up"] + M * H * 2 + M * I * 2, 2 * M * 2 * I * H
+    if kind == "down":
+        return wb["down"] + M * I * 2 + 2 * M * H * 4, 2 * M * H * I
+    if kind == "lm_head":
+        return V * H * 2 + M * H * 2 + (V // 64) * M * 8, 2 * M * V * H
+    if kind == "rmsnorm":
+        return M * H * 4 + M * H * 2 + H * 4, 4 * M * H
+    return 0, 0
+
+
+def pass_bytes(m, lens):
+    """Algorithmic HBM bytes of one verify pass + commit: every weight byte once,
+    the KV read (committed rows plus the block rows), the block's KV write,
+    the embedding gather."""
+    B = len(lens)
+    wb = weight_bytes_per_layer(m)
+    w = m.n_layers * sum(wb.values()) + m.vocab * m.hidden * 2 + m.hidden * 4
+    per_tok = m.n_layers * m.n_kv_heads * m.head_dim * 2 * 2
+    kv_read = int(np.sum(lens + 16)) * per_tok
+    kv_write = B * 16 * per_tok
+    return w + kv_read + kv_write + B * 16 * m.hidden * 2
+
+
+def cpu_baseline(wl, weights, kv_layers, lens, n_seq):
+    """The oracle (float64 numpy) timed on this host for a bounded sample: the
+    verify pass of the first n_seq sequences (random drafts; the oracle's
+    work does not depend on draft values).  Scaled to passes/s of the whole
+    batch by n_seq / B."""
+    import oracle
+    import workload as W
+    from threadpoolctl import threadpool_info
+    m = wl.model
+    om = oracle.OracleModel(m, weights)
+    sl = lens[:n_seq]
+    okv = oracle.OracleKV.from_bf16(m, [k[:n_seq] for k, _ in kv_layers], [v[:n_seq] for _, v in kv_layers], sl)
+    blocks = np.stack([W.draft_rng(wl, b, 1).integers(0, m.vocab, size=16) for b in range(n_seq)])
+    oracle.verify_block(om, okv, blocks[:1, :1], seqs=[0])  # decode weights once (untimed)
+    t0 = time.time()
+    oracle.verify_block(om, okv, blocks)
+    dt = time.time() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": (n_seq / len(lens)) / dt, "unit": "verify passes/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"float64 numpy oracle, verify pass of {n_seq} of {len(lens)} sequences "
+                      f"({dt:.1f} s), scaled by {n_seq}/{len(lens)}; weight decoding untimed"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import workload as W
+    from block_draft_verification_amd import DeviceModel, Verifier
+
+    wl = W.WORKLOADS[args.workload]
+    m = wl.model
+    B = wl.batch
+    log(f"workload {wl.name}: generating weights")
+    weights = W.model_weights(m, wl.seed)
+    lens = W.context_lengths(wl)
+    log("synthetic KV")
+    kv_layers = [W.synthetic_kv_layer(m, wl.seed, l, lens, wl.max_ctx) for l in range(m.n_layers)]
+    log("upload")
+    dev = DeviceModel(m, weights, max_batch=B, max_ctx=wl.max_ctx, kv_layers=kv_layers, kv_len=lens)
+    ver = Verifier(dev)
+    torch.cuda.synchronize()
+
+    # plant drafts from the pass's own greedy continuation: row j-1's argmax
+    # depends only on tokens 0..j-1, so 15 uncommitted passes fill the block
+    L = W.accept_lengths(wl)
+    blocks = np.stack([W.draft_rng(wl, b).integers(0, m.vocab, size=16) for b in range(B)]).astype(np.int32)
+    blocks[:, 0] = W.pending_tokens(wl)
+    tok = torch.from_numpy(blocks).cuda()
+    log("planting drafts (15 passes)")
+    for j in range(1, 16):
+        g = ver.verify(tok)["argmax"].cpu().numpy()
+        for b in range(B):
+            if j < L[b]:
+                blocks[b, j] = g[b, j - 1]
+            elif j == L[b]:
+                redraw = W.draft_rng(wl, b, 2)
+                while blocks[b, j] == g[b, j - 1]:
+                    blocks[b, j] = redraw.integers(0, m.vocab)
+        tok.copy_(torch.from_numpy(blocks))
+    out = ver.verify(tok)
+    tau = out["accept_len"].cpu().numpy()
+    log(f"planted L == tau: {np.array_equal(tau, L)}; sum tau = {tau.sum()}")
+
+    # graph of one step: restore kv_len, verify, commit
+    kv0 = dev.kv_len.clone()
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    bon = torch.empty(B, dtype=torch.int32, device="cuda")
+    amx = torch.empty(B, 16, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            dev.kv_len.copy_(kv0)
+            ver.verify(tok, acc, bon, amx)
+            ver.commit(B)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dev.kv_len.copy_(kv0)
+        ver.verify(tok, acc, bon, amx)
+        ver.commit(B)
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} steps")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    assert np.array_equal(acc.cpu().numpy(), tau)
+    assert ver.device_error() == 0
+
+    # per-kernel-class launch durations (eager passes, events on the stream)
+    kinds = ["qkv", "attention", "o_proj", "gate_up", "down", "lm_head", "rmsnorm", "accept", "embed", "commit"]
+    per_kind = {}
+    reps = max(3, min(20, args.steps // 5))
+    for k in kinds:
+        ver.time_kernel(k)
+        for _ in range(reps):
+            dev.kv_len.copy_(kv0)
+            ver.verify(tok, acc, bon, amx)
+            ver.commit(B)
+        ver.time_kernel(None)
+        tot, n = ver.kernel_time()
+        per_kind[k] = {"ms_per_pass": tot / reps, "us_per_launch": 1000 * tot / max(n, 1),
+                       "launches_per_pass": n // reps}
+    dom = max(per_kind, key=lambda k: per_kind[k]["ms_per_pass"])
+    by, fl = kernel_work(dom, m, lens)
+    t_launch = per_kind[dom]["us_per_launch"] * 1e-6
+    if fl / max(by, 1) > RIDGE:
+        roof = {"bound": "mfma", "achieved": fl / t_launch / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": by / t_launch / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = dom
+    roof["us_per_launch"] = per_kind[dom]["us_per_launch"]
+    roof["algorithmic_bytes_per_launch"] = by
+    roof["algorithmic_flops_per_launch"] = fl
+
+    passes = 1000.0 / ms
+    nbytes = pass_bytes(m, lens)
+    res = {
+        "metric": METRIC, "value": passes, "unit": "verify passes/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "block": 16, "rows": B * 16,
+                   "context": "uniform [512, 4096]", "weights": "fp8-e4m3 per-row, bf16 tied lm_head",
+                   "activations": "bf16 (fp32 accumulate)"},
+        "emitted_tok_per_s": passes * float(tau.sum()),
+        "accepted_draft_tok_per_s": passes * float((tau - 1).sum()),
+        "sum_tau": int(tau.sum()),
+        "hbm_frac_of_peak": nbytes / (ms * 1e-3) / HBM_PEAK,
+        "algorithmic_bytes_per_pass": nbytes,
+        "roofline": roof,
+        "kernels": per_kind,
+    }
+    ver.close()
+    if not args.no_cpu:
+        log(f"cpu baseline: oracle on {args.cpu_seqs} sequences")
+        res["cpu_baseline"] = cpu_baseline(wl, weights, kv_layers, lens, args.cpu_seqs)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,8 @@
+"""Block-draft verify pass for MI355X (gfx950).
+
+The compute lives in libspecverify.so (hand-written HIP, C ABI in
+include/spec_verify.h); this package is its thin Python binding.
+"""
+from ._binding import (  # noqa: F401
+    BLOCK, DERR_CAPACITY, DERR_COMMIT, DERR_TOKEN, EXPORTS, KERNEL_KINDS, LIB_PATH, WFMT_BF16, WFMT_FP8_E4M3_ROW, WFMT_MXFP4,
+    DeviceModel, SpecError, Verifier, debug_attention, debug_linear, load_library)

@@ -1,0 +1,234 @@
+"""ctypes binding of libspecverify.so: argument marshalling only.
+
+Every step of the verify pass runs in the HIP library; this module only
+places caller-owned buffers in device memory (torch tensors), fills the
+descriptor structs of include/spec_verify.h and forwards pointers and the
+current HIP stream.  It fails loudly when the library is missing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+
+SPEC_OK = 0
+WFMT_FP8_E4M3_ROW, WFMT_MXFP4, WFMT_BF16 = 1, 2, 3
+DERR_TOKEN, DERR_CAPACITY, DERR_COMMIT = 1, 2, 4
+BLOCK = 16
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+
+
+class SpecModelDesc(ctypes.Structure):
+    _fields_ = [("n_layers", _I), ("hidden", _I), ("n_q_heads", _I), ("n_kv_heads", _I), ("head_dim", _I),
+                ("intermediate", _I), ("vocab", _I), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
+                ("attn_wfmt", _I), ("mlp_wfmt", _I), ("tied_lm_head", _I)]
+
+
+class SpecLayerWeights(ctypes.Structure):
+    _fields_ = [(n, _P) for n in ("w_qkv", "s_qkv", "w_o", "s_o", "w_gate_up", "s_gate_up", "w_down", "s_down",
+                                  "attn_norm", "mlp_norm")]
+
+
+class SpecWeights(ctypes.Structure):
+    _fields_ = [("layers", ctypes.POINTER(SpecLayerWeights)), ("embed", _P), ("lm_head", _P), ("final_norm", _P)]
+
+
+class SpecKV(ctypes.Structure):
+    _fields_ = [("k_cache", _P), ("v_cache", _P), ("kv_len", _P), ("max_batch", _I), ("max_ctx", _I)]
+
+
+EXPORTS = {
+    "spec_verify_init": (_I, [ctypes.POINTER(SpecModelDesc), ctypes.POINTER(SpecWeights), ctypes.POINTER(SpecKV),
+                              _P, ctypes.POINTER(_P)]),
+    "spec_verify_block": (_I, [_P, _I, _P, _P, _P, _P, _P]),
+    "spec_commit_kv": (_I, [_P, _I, _P, _P]),
+    "spec_verify_destroy": (_I, [_P]),
+    "spec_get_device_error": (_I, [_P, ctypes.POINTER(_I), _P]),
+    "spec_status_str": (ctypes.c_char_p, [_I]),
+    "spec_debug_set_dump": (_I, [_P, _P, _P]),
+    "spec_debug_linear": (_I, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "spec_debug_attention": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P]),
+    "spec_debug_time_kernel": (_I, [_P, _I]),
+    "spec_debug_kernel_time": (_I, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I)]),
+}
+
+KERNEL_KINDS = {"embed": 1, "rmsnorm": 2, "qkv": 3, "attention": 4, "o_proj": 5, "gate_up": 6, "down": 7,
+                "lm_head": 8, "accept": 9, "commit": 10}
+
+_lib = None
+
+
+def load_library():
+    """Load libspecverify.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build the HIP library first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in EXPORTS.items():
+            fn = getattr(lib, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+class SpecError(RuntimeError):
+    pass
+
+
+def _check(rc: int, what: str):
+    if rc != SPEC_OK:
+        raise SpecError(f"{what}: {load_library().spec_status_str(rc).decode()} ({rc})")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dev(a: np.ndarray, device):
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(a).to(device)
+
+
+def _wfmt(name: str) -> int:
+    return {"fp8": WFMT_FP8_E4M3_ROW, "mxfp4": WFMT_MXFP4}[name]
+
+
+class DeviceModel:
+    """Caller-owned device buffers: weights in the boundary's layout, the BF16
+    KV cache [L][max_batch][Hkv][max_ctx][D] for K and V, and kv_len."""
+
+    def __init__(self, shape, weights: dict, max_batch: int, max_ctx: int, kv_layers=None, kv_len=None,
+                 device="cuda"):
+        self.shape, self.max_batch, self.max_ctx, self.device = shape, max_batch, max_ctx, device
+        m = shape
+        self.layers = []
+        for lw in weights["layers"]:
+            self.layers.append({k: _dev(v, device) for k, v in lw.items()})
+        self.embed = _dev(weights["embed"], device)
+        self.lm_head = None if weights.get("lm_head") is None else _dev(weights["lm_head"], device)
+        self.final_norm = _dev(weights["final_norm"], device)
+        cache_shape = (m.n_layers, max_batch, m.n_kv_heads, max_ctx, m.head_dim)
+        self.k_cache = torch.zeros(cache_shape, dtype=torch.int16, device=device)
+        self.v_cache = torch.zeros(cache_shape, dtype=torch.int16, device=device)
+        self.kv_len = torch.zeros(max_batch, dtype=torch.int32, device=device)
+        if kv_layers is not None:
+            for l, (K, V) in enumerate(kv_layers):
+                self.load_kv_layer(l, K, V)
+        if kv_len is not None:
+            self.kv_len[:len(kv_len)] = torch.as_tensor(np.asarray(kv_len, np.int32), device=device)
+
+    def load_kv_layer(self, l, K, V):
+        b = K.shape[0]
+        self.k_cache[l, :b].copy_(_dev(K, "cpu"))
+        self.v_cache[l, :b].copy_(_dev(V, "cpu"))
+
+    def structs(self):
+        m = self.shape
+        desc = SpecModelDesc(m.n_layers, m.hidden, m.n_q_heads, m.n_kv_heads, m.head_dim, m.intermediate, m.vocab,
+                             m.rms_eps, m.rope_theta, WFMT_FP8_E4M3_ROW, _wfmt(m.mlp_format),
+                             1 if m.tied_lm_head else 0)
+        arr = (SpecLayerWeights * m.n_layers)()
+        for i, lw in enumerate(self.layers):
+            for name in SpecLayerWeights._fields_:
+                setattr(arr[i], name[0], lw[name[0]].data_ptr())
+        w = SpecWeights(arr, self.embed.data_ptr(), None if self.lm_head is None else self.lm_head.data_ptr(),
+                        self.final_norm.data_ptr())
+        kv = SpecKV(self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.kv_len.data_ptr(), self.max_batch,
+                    self.max_ctx)
+        return desc, arr, w, kv
+
+
+class Verifier:
+    """One spec_ctx bound to a DeviceModel."""
+
+    def __init__(self, dev: DeviceModel):
+        lib = load_library()
+        self.dev = dev
+        self._desc, self._arr, self._w, self._kv = dev.structs()
+        h = ctypes.c_void_p()
+        _check(lib.spec_verify_init(ctypes.byref(self._desc), ctypes.byref(self._w), ctypes.byref(self._kv),
+                                    _stream(), ctypes.byref(h)), "spec_verify_init")
+        self._h = h
+        self._dump = (None, None)
+
+    def verify(self, tokens: torch.Tensor, accept_len=None, bonus=None, argmax="alloc"):
+        """tokens int32 [B, 16] on the device.  Returns the output tensors."""
+        B = tokens.shape[0]
+        assert tokens.dtype == torch.int32 and tokens.is_contiguous() and tokens.shape[1] == BLOCK
+        d = tokens.device
+        accept_len = torch.empty(B, dtype=torch.int32, device=d) if accept_len is None else accept_len
+        bonus = torch.empty(B, dtype=torch.int32, device=d) if bonus is None else bonus
+        if isinstance(argmax, str):
+            argmax = torch.empty(B, BLOCK, dtype=torch.int32, device=d)
+        _check(load_library().spec_verify_block(self._h, B, _ptr(tokens), _ptr(accept_len), _ptr(bonus),
+                                                _ptr(argmax), _stream()), "spec_verify_block")
+        return {"accept_len": accept_len, "bonus": bonus, "argmax": argmax}
+
+    def commit(self, batch: int, n_commit: torch.Tensor | None = None):
+        _check(load_library().spec_commit_kv(self._h, batch, _ptr(n_commit), _stream()), "spec_commit_kv")
+
+    def device_error(self) -> int:
+        v = ctypes.c_int32()
+        _check(load_library().spec_get_device_error(self._h, ctypes.byref(v), _stream()), "spec_get_device_error")
+        return v.value
+
+    def set_dump(self, hidden=None, logits=None):
+        self._dump = (hidden, logits)
+        _check(load_library().spec_debug_set_dump(self._h, _ptr(hidden), _ptr(logits)), "spec_debug_set_dump")
+
+    def time_kernel(self, kind: str | None):
+        """Start (or stop, with None) event timing of one kernel class."""
+        _check(load_library().spec_debug_time_kernel(self._h, 0 if kind is None else KERNEL_KINDS[kind]),
+               "spec_debug_time_kernel")
+
+    def kernel_time(self):
+        """(total ms, launches) recorded since the last call."""
+        ms, n = ctypes.c_float(), ctypes.c_int32()
+        _check(load_library().spec_debug_kernel_time(self._h, ctypes.byref(ms), ctypes.byref(n)),
+               "spec_debug_kernel_time")
+        return ms.value, n.value
+
+    def close(self):
+        if self._h is not None:
+            _check(load_library().spec_verify_destroy(self._h), "spec_verify_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def debug_linear(x_bf16: torch.Tensor, w: torch.Tensor, scales, wfmt: int, N: int) -> torch.Tensor:
+    """y = x W^T (fp32) through the library's linear kernel."""
+    M, K = x_bf16.shape
+    y = torch.empty(M, N, dtype=torch.float32, device=x_bf16.device)
+    _check(load_library().spec_debug_linear(M, N, K, _ptr(x_bf16), _ptr(w), _ptr(scales), wfmt, _ptr(y),
+                                            _stream()), "spec_debug_linear")
+    return y
+
+
+def debug_attention(q, k_cache, v_cache, kv_len, batch, n_q_heads, n_kv_heads, head_dim, split_len=0):
+    """One layer's block-causal attention through the library's kernel."""
+    max_batch, _, max_ctx, _ = k_cache.shape
+    o = torch.empty_like(q)
+    _check(load_library().spec_debug_attention(batch, n_q_heads, n_kv_heads, head_dim, max_batch, max_ctx,
+                                               _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(o),
+                                               split_len, _stream()), "spec_debug_attention")
+    return o

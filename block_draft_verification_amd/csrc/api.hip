@@ -1,0 +1,369 @@
+// Host side of the C ABI declared in include/spec_verify.h.
+#include <math.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "common.h"
+#include "kernels.h"
+
+struct spec_ctx {
+  spec_model_desc m;
+  std::vector<spec_layer_weights> layers;
+  const uint16_t *embed, *lm_table;
+  const float *final_norm;
+  spec_kv kv;
+  int Mmax, part_units;  // part_units: (sequence, kv head, split) slots for attention partials
+  // workspace (one allocation)
+  void *ws;
+  float *h;
+  uint16_t *x, *q, *ao, *act;
+  float *part_o;
+  float2 *part_ml;
+  int32_t *counters, *last_tau, *err;
+  ArgmaxPart *amax;
+  float2 *rope;
+  float *dump_hidden, *dump_logits;
+  // launch timing of one kernel class (measurement hook)
+  int prof_kind = SPEC_K_NONE;
+  std::vector<hipEvent_t> ev;  // pairs
+  size_t ev_used = 0;
+};
+
+static const size_t kMaxTimedLaunches = 8192;
+
+// Brackets one launch with events when its class is being timed.
+struct Timed {
+  spec_ctx *c;
+  hipStream_t st;
+  bool on;
+  Timed(spec_ctx *c_, int kind, hipStream_t s) : c(c_), st(s), on(false) {
+    if (c->prof_kind != kind || c->ev_used + 2 > c->ev.size()) return;
+    on = hipEventRecord(c->ev[c->ev_used], st) == hipSuccess;
+  }
+  ~Timed() {
+    if (!on) return;
+    if (hipEventRecord(c->ev[c->ev_used + 1], st) == hipSuccess) c->ev_used += 2;
+  }
+};
+
+#define CK(expr)                                  \
+  do {                                            \
+    if ((expr) != hipSuccess) return SPEC_E_HIP;  \
+  } while (0)
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
+static int check_model(const spec_model_desc *m) {
+  if (m->n_layers < 1 || m->hidden < 64 || m->n_q_heads < 1 || m->n_kv_heads < 1 || m->intermediate < 64 ||
+      m->vocab < 64 || !(m->rms_eps > 0.f) || !(m->rope_theta > 0.f))
+    return SPEC_E_SHAPE;
+  if (m->head_dim != 64 && m->head_dim != 128) return SPEC_E_SHAPE;
+  if (m->hidden % 64 || m->intermediate % 64 || m->vocab % 64) return SPEC_E_SHAPE;
+  if (m->n_q_heads % m->n_kv_heads || m->n_q_heads / m->n_kv_heads > 8) return SPEC_E_SHAPE;
+  if ((m->n_q_heads * m->head_dim) % 64) return SPEC_E_SHAPE;
+  if (m->attn_wfmt != SPEC_WFMT_FP8_E4M3_ROW) return SPEC_E_UNSUPPORTED;
+  if (m->mlp_wfmt != SPEC_WFMT_FP8_E4M3_ROW && m->mlp_wfmt != SPEC_WFMT_MXFP4) return SPEC_E_UNSUPPORTED;
+  return SPEC_OK;
+}
+
+static int attn_nsplit(int split_len, int max_ctx) { return (max_ctx + split_len - 1) / split_len; }
+
+extern "C" {
+
+const char *spec_status_str(int s) {
+  switch (s) {
+    case SPEC_OK: return "ok";
+    case SPEC_E_ARG: return "invalid argument";
+    case SPEC_E_SHAPE: return "unsupported model or cache shape";
+    case SPEC_E_UNSUPPORTED: return "unsupported weight format";
+    case SPEC_E_HIP: return "HIP runtime error";
+    case SPEC_E_NOMEM: return "workspace allocation failed";
+  }
+  return "unknown status";
+}
+
+int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec_kv *kv, hipStream_t st,
+                     spec_ctx **out) {
+  if (!m || !w || !kv || !out || !w->layers || !w->embed || !w->final_norm) return SPEC_E_ARG;
+  int rc = check_model(m);
+  if (rc) return rc;
+  if (!kv->k_cache || !kv->v_cache || !kv->kv_len || kv->max_batch < 1 || kv->max_ctx < 16) return SPEC_E_ARG;
+  if (!m->tied_lm_head && !w->lm_head) return SPEC_E_ARG;
+  if (!aligned16(kv->k_cache) || !aligned16(kv->v_cache) || !aligned16(w->embed) ||
+      !aligned16(w->final_norm) || (w->lm_head && !aligned16(w->lm_head)))
+    return SPEC_E_ARG;
+  for (int l = 0; l < m->n_layers; ++l) {
+    const spec_layer_weights &L = w->layers[l];
+    const void *ps[] = {L.w_qkv, L.s_qkv, L.w_o, L.s_o, L.w_gate_up, L.s_gate_up, L.w_down, L.s_down,
+                        L.attn_norm, L.mlp_norm};
+    for (const void *p : ps)
+      if (!p || !aligned16(p)) return SPEC_E_ARG;
+  }
+
+  spec_ctx *c = new (std::nothrow) spec_ctx();
+  if (!c) return SPEC_E_NOMEM;
+  c->m = *m;
+  c->layers.assign(w->layers, w->layers + m->n_layers);
+  c->embed = w->embed;
+  c->lm_table = m->tied_lm_head ? w->embed : w->lm_head;
+  c->final_norm = w->final_norm;
+  c->kv = *kv;
+  const int H = m->hidden, D = m->head_dim, Hq = m->n_q_heads, Hkv = m->n_kv_heads;
+  const int G = Hq / Hkv, I = m->intermediate, V = m->vocab;
+  c->Mmax = kv->max_batch * 16;
+  int units = 0;
+  for (int b = 1; b <= kv->max_batch; ++b) {
+    const int u = b * Hkv * attn_nsplit(attention_split_len(b, Hkv, kv->max_ctx), kv->max_ctx);
+    if (u > units) units = u;
+  }
+  c->part_units = units;
+
+  const size_t Mm = c->Mmax;
+  size_t sizes[] = {Mm * H * 4,                      // h
+                    Mm * H * 2,                      // x
+                    Mm * Hq * D * 2,                 // q
+                    Mm * Hq * D * 2,                 // ao
+                    Mm * I * 2,                      // act
+                    (size_t)units * G * 16 * D * 4,  // part_o
+                    (size_t)units * G * 16 * 8,      // part_ml
+                    (size_t)kv->max_batch * Hkv * 4, // counters
+                    (size_t)kv->max_batch * 4,       // last_tau
+                    4,                               // err
+                    (size_t)lm_parts(V) * Mm * 8,    // amax
+                    (size_t)kv->max_ctx * (D / 2) * 8};  // rope
+  const int NS = sizeof(sizes) / sizeof(sizes[0]);
+  size_t off[NS], total = 0;
+  for (int i = 0; i < NS; ++i) {
+    off[i] = total;
+    total += (sizes[i] + 255) & ~(size_t)255;
+  }
+  if (hipMalloc(&c->ws, total) != hipSuccess) {
+    delete c;
+    return SPEC_E_NOMEM;
+  }
+  char *base = (char *)c->ws;
+  c->h = (float *)(base + off[0]);
+  c->x = (uint16_t *)(base + off[1]);
+  c->q = (uint16_t *)(base + off[2]);
+  c->ao = (uint16_t *)(base + off[3]);
+  c->act = (uint16_t *)(base + off[4]);
+  c->part_o = (float *)(base + off[5]);
+  c->part_ml = (float2 *)(base + off[6]);
+  c->counters = (int32_t *)(base + off[7]);
+  c->last_tau = (int32_t *)(base + off[8]);
+  c->err = (int32_t *)(base + off[9]);
+  c->amax = (ArgmaxPart *)(base + off[10]);
+  c->rope = (float2 *)(base + off[11]);
+  c->dump_hidden = c->dump_logits = nullptr;
+
+  // RoPE table: angle = p * theta^(-2i/D), in double, stored as fp32 (cos, sin)
+  std::vector<float2> rope((size_t)kv->max_ctx * (D / 2));
+  for (int p = 0; p < kv->max_ctx; ++p)
+    for (int i = 0; i < D / 2; ++i) {
+      const double ang = (double)p * pow((double)m->rope_theta, -2.0 * i / D);
+      rope[(size_t)p * (D / 2) + i] = make_float2((float)cos(ang), (float)sin(ang));
+    }
+  if (hipMemcpyAsync(c->rope, rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice, st) !=
+          hipSuccess ||
+      launch_fill_i32(c->counters, kv->max_batch * Hkv, 0, st) != hipSuccess ||
+      launch_fill_i32(c->last_tau, kv->max_batch, 0, st) != hipSuccess ||
+      launch_fill_i32(c->err, 1, 0, st) != hipSuccess || hipStreamSynchronize(st) != hipSuccess) {
+    (void)hipFree(c->ws);
+    delete c;
+    return SPEC_E_HIP;
+  }
+  *out = c;
+  return SPEC_OK;
+}
+
+int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t *accept_len, int32_t *bonus,
+                      int32_t *argmax, hipStream_t st) {
+  if (!c || !tokens || !accept_len || !bonus) return SPEC_E_ARG;
+  if (batch < 1 || batch > c->kv.max_batch) return SPEC_E_ARG;
+  const spec_model_desc &m = c->m;
+  const int M = batch * 16, H = m.hidden, D = m.head_dim, Hq = m.n_q_heads, Hkv = m.n_kv_heads;
+  const int I = m.intermediate, V = m.vocab, max_ctx = c->kv.max_ctx;
+  const size_t lstride = (size_t)c->kv.max_batch * Hkv * max_ctx * D;
+
+  AttnArgs aa{};
+  aa.q = c->q;
+  aa.kv_len = c->kv.kv_len;
+  aa.o = c->ao;
+  aa.part_o = c->part_o;
+  aa.part_ml = c->part_ml;
+  aa.counters = c->counters;
+  aa.batch = batch;
+  aa.Hq = Hq;
+  aa.Hkv = Hkv;
+  aa.max_ctx = max_ctx;
+  aa.split_len = attention_split_len(batch, Hkv, max_ctx);
+  aa.nsplit = attn_nsplit(aa.split_len, max_ctx);
+
+  {
+    Timed t(c, SPEC_K_EMBED, st);
+    CK(launch_embed(tokens, M, H, V, c->embed, c->h, c->kv.kv_len, max_ctx, c->err, st));
+  }
+  for (int l = 0; l < m.n_layers; ++l) {
+    const spec_layer_weights &L = c->layers[l];
+    uint16_t *kc = c->kv.k_cache + l * lstride, *vc = c->kv.v_cache + l * lstride;
+    {
+      Timed t(c, SPEC_K_RMSNORM, st);
+      CK(launch_rmsnorm(c->h, L.attn_norm, M, H, m.rms_eps, c->x, nullptr, st));
+    }
+    QkvOut qo{c->q, kc, vc, c->kv.kv_len, c->rope, Hq, Hkv, max_ctx};
+    {
+      Timed t(c, SPEC_K_QKV, st);
+      CK(launch_qkv(c->x, M, H, D, LinearW{L.w_qkv, L.s_qkv, SPEC_WFMT_FP8_E4M3_ROW}, qo, st));
+    }
+    aa.k_cache = kc;
+    aa.v_cache = vc;
+    {
+      Timed t(c, SPEC_K_ATTENTION, st);
+      CK(launch_attention(aa, D, st));
+    }
+    {
+      Timed t(c, SPEC_K_OPROJ, st);
+      CK(launch_residual(c->ao, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, c->h, st));
+    }
+    {
+      Timed t(c, SPEC_K_RMSNORM, st);
+      CK(launch_rmsnorm(c->h, L.mlp_norm, M, H, m.rms_eps, c->x, nullptr, st));
+    }
+    {
+      Timed t(c, SPEC_K_GATE_UP, st);
+      CK(launch_swiglu(c->x, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, c->act, st));
+    }
+    {
+      Timed t(c, SPEC_K_DOWN, st);
+      CK(launch_residual(c->act, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, c->h, st));
+    }
+  }
+  {
+    Timed t(c, SPEC_K_RMSNORM, st);
+    CK(launch_rmsnorm(c->h, c->final_norm, M, H, m.rms_eps, c->x, c->dump_hidden, st));
+  }
+  {
+    Timed t(c, SPEC_K_LM_HEAD, st);
+    CK(launch_lm_argmax(c->x, M, V, H, c->lm_table, c->amax, c->dump_logits, st));
+  }
+  {
+    Timed t(c, SPEC_K_ACCEPT, st);
+    CK(launch_accept(c->amax, lm_parts(V), M, tokens, batch, accept_len, bonus, argmax, c->last_tau, st));
+  }
+  return SPEC_OK;
+}
+
+int spec_commit_kv(spec_ctx *c, int32_t batch, const int32_t *n_commit, hipStream_t st) {
+  if (!c) return SPEC_E_ARG;
+  if (batch < 1 || batch > c->kv.max_batch) return SPEC_E_ARG;
+  {
+    Timed t(c, SPEC_K_COMMIT, st);
+    CK(launch_commit(batch, n_commit, c->last_tau, c->kv.kv_len, c->kv.max_ctx, c->err, st));
+  }
+  return SPEC_OK;
+}
+
+int spec_verify_destroy(spec_ctx *c) {
+  if (!c) return SPEC_OK;
+  for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  const hipError_t e = hipFree(c->ws);
+  delete c;
+  return e == hipSuccess ? SPEC_OK : SPEC_E_HIP;
+}
+
+int spec_get_device_error(spec_ctx *c, int32_t *code, hipStream_t st) {
+  if (!c || !code) return SPEC_E_ARG;
+  int32_t v = 0;
+  CK(hipMemcpyAsync(&v, c->err, 4, hipMemcpyDeviceToHost, st));
+  CK(hipStreamSynchronize(st));
+  CK(launch_fill_i32(c->err, 1, 0, st));
+  CK(hipStreamSynchronize(st));
+  *code = v;
+  return SPEC_OK;
+}
+
+int spec_debug_time_kernel(spec_ctx *c, int32_t kind) {
+  if (!c || kind < SPEC_K_NONE || kind > SPEC_K_COMMIT) return SPEC_E_ARG;
+  if (kind != SPEC_K_NONE && c->ev.empty()) {
+    c->ev.resize(2 * kMaxTimedLaunches);
+    for (hipEvent_t &e : c->ev)
+      if (hipEventCreate(&e) != hipSuccess) return SPEC_E_HIP;
+  }
+  c->prof_kind = kind;
+  return SPEC_OK;
+}
+
+int spec_debug_kernel_time(spec_ctx *c, float *total_ms, int32_t *launches) {
+  if (!c || !total_ms || !launches) return SPEC_E_ARG;
+  float sum = 0.f;
+  for (size_t i = 0; i + 1 < c->ev_used; i += 2) {
+    float ms = 0.f;
+    CK(hipEventSynchronize(c->ev[i + 1]));
+    CK(hipEventElapsedTime(&ms, c->ev[i], c->ev[i + 1]));
+    sum += ms;
+  }
+  *total_ms = sum;
+  *launches = (int32_t)(c->ev_used / 2);
+  c->ev_used = 0;
+  return SPEC_OK;
+}
+
+int spec_debug_set_dump(spec_ctx *c, float *hidden, float *logits) {
+  if (!c) return SPEC_E_ARG;
+  if ((hidden && !aligned16(hidden)) || (logits && !aligned16(logits))) return SPEC_E_ARG;
+  c->dump_hidden = hidden;
+  c->dump_logits = logits;
+  return SPEC_OK;
+}
+
+int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const void *w, const void *scales,
+                      int32_t wfmt, float *y, hipStream_t st) {
+  if (M < 1 || N < 64 || K < 64 || N % 64 || K % 64 || !x || !w || !y) return SPEC_E_ARG;
+  if (wfmt != SPEC_WFMT_BF16 && !scales) return SPEC_E_ARG;
+  if (wfmt != SPEC_WFMT_BF16 && wfmt != SPEC_WFMT_FP8_E4M3_ROW && wfmt != SPEC_WFMT_MXFP4)
+    return SPEC_E_UNSUPPORTED;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (wfmt == SPEC_WFMT_FP8_E4M3_ROW && !aligned16(scales)))
+    return SPEC_E_ARG;
+  CK(launch_linear_f32(x, M, N, K, LinearW{w, scales, wfmt}, y, st));
+  CK(hipStreamSynchronize(st));
+  return SPEC_OK;
+}
+
+int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_batch, int32_t max_ctx,
+                         const uint16_t *q, const uint16_t *k_cache, const uint16_t *v_cache,
+                         const int32_t *kv_len, uint16_t *o, int32_t split_len, hipStream_t st) {
+  if (!q || !k_cache || !v_cache || !kv_len || !o) return SPEC_E_ARG;
+  if (batch < 1 || batch > max_batch || Hkv < 1 || Hq % Hkv || Hq / Hkv > 8 || max_ctx < 16) return SPEC_E_ARG;
+  if (D != 64 && D != 128) return SPEC_E_SHAPE;
+  if (split_len < 0 || split_len % 64) return SPEC_E_ARG;
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return SPEC_E_ARG;
+  AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.kv_len = kv_len;
+  a.o = o;
+  a.batch = batch;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_ctx = max_ctx;
+  a.split_len = split_len ? split_len : attention_split_len(batch, Hkv, max_ctx);
+  a.nsplit = attn_nsplit(a.split_len, max_ctx);
+  const size_t units = (size_t)batch * Hkv * a.nsplit, R = (size_t)(Hq / Hkv) * 16;
+  void *buf = nullptr;
+  if (hipMalloc(&buf, units * R * D * 4 + units * R * 8 + (size_t)batch * Hkv * 4 + 256) != hipSuccess)
+    return SPEC_E_NOMEM;
+  a.part_o = (float *)buf;
+  a.part_ml = (float2 *)((char *)buf + units * R * D * 4);
+  a.counters = (int32_t *)((char *)a.part_ml + units * R * 8);
+  int rc = SPEC_OK;
+  if (launch_fill_i32(a.counters, batch * Hkv, 0, st) != hipSuccess || launch_attention(a, D, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    rc = SPEC_E_HIP;
+  (void)hipFree(buf);
+  return rc;
+}
+
+}  // extern "C"

@@ -1,0 +1,221 @@
+// Block-causal GQA attention of the 16 block rows over the KV cache (gfx950).
+//
+// Row j of sequence b sits at position n_b + j and sees keys 0 .. n_b + j:
+// the committed prefix plus the block rows up to itself, which the QKV step
+// has already stored at slots n_b .. n_b+15 (HunyuanOCR-1.5 / DFlash write-up,
+// inference loop, step 3: the whole block is verified in one forward).
+// Query head h reads KV head h / G, so the G*16 query rows of one KV head
+// share every K/V tile: the pass is bound by reading the cache once.
+//
+// Work unit = (split, kv head, sequence): one workgroup of 4 waves walks its
+// split's keys in tiles of 64, staged through LDS (K row-major, V transposed).
+// A wave owns 16-row query tiles (one query head each, rows j = 0..15).
+// Scores are computed transposed, S^T = K Q^T, with the MFMA A operand taken
+// from K in LDS and the B operand = Q^T held in registers; in that layout a
+// lane (r, g) holds 16 keys of query r, so softmax statistics need only the
+// xor-16/32 shuffles, and the probabilities are already the B operand of
+// O^T = V^T P^T.  Online softmax in fp32 (base 2), P rounded to BF16.
+//
+// Splits write unnormalised partials (m, l, o); the last workgroup of a
+// (sequence, kv head) to finish -- found with an integer atomic counter --
+// merges them in split order, so the result does not depend on timing.
+#include "common.h"
+#include "kernels.h"
+
+#define KT 64  // keys per LDS tile
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2) {
+  constexpr int DT = D / 16;   // 16-wide d tiles
+  constexpr int DK = D / 32;   // k32 steps over d
+  constexpr int KP = D + 8;    // padded K row (bf16)
+  constexpr int VP = KT + 8;   // padded V^T row (bf16)
+  __shared__ __align__(16) uint16_t Ks[KT * KP];
+  __shared__ __align__(16) uint16_t Vt[D * VP];
+  __shared__ int s_last;
+
+  const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int G = a.Hq / a.Hkv;
+  const int n = a.kv_len[b];
+  const int L = min(max(n, 0) + 16, a.max_ctx);
+  const int nsplit = (L + a.split_len - 1) / a.split_len;
+  if (sp >= nsplit) return;  // whole workgroup
+  const int key_lo = sp * a.split_len, key_hi = min(key_lo + a.split_len, L);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
+  const size_t cache_base = ((size_t)b * a.Hkv + kvh) * a.max_ctx;
+  const size_t unit = (size_t)b * a.Hkv + kvh;
+  const int qstride = a.Hq * D;
+
+  // this wave's query tiles (at most 2: G <= 8)
+  const int nqt = (G - wave + 3) / 4;  // tiles wave, wave+4
+  u32x4_t qf[2][DK];
+  f32x4_t oacc[2][DT];
+  float mrow[2], lrow[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    mrow[u] = -INFINITY;
+    lrow[u] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[u][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (u < nqt) {
+      const int hq = kvh * G + wave + 4 * u;
+      const uint16_t *qp = a.q + (size_t)(b * 16 + r) * qstride + hq * D + 8 * g;
+#pragma unroll
+      for (int kd = 0; kd < DK; ++kd) qf[u][kd] = *reinterpret_cast<const u32x4_t *>(qp + 32 * kd);
+    }
+  }
+
+  for (int kt0 = key_lo; kt0 < key_hi; kt0 += KT) {
+    __syncthreads();
+    // stage K (row-major) and V (transposed) for keys kt0 .. kt0+63; zero past key_hi
+    for (int c = tid; c < KT * D / 8; c += 256) {
+      const int kk = c / (D / 8), d0 = (c % (D / 8)) * 8;
+      const int key = kt0 + kk;
+      u32x4_t kv4 = u32x4_t{0, 0, 0, 0}, vv4 = u32x4_t{0, 0, 0, 0};
+      if (key < key_hi) {
+        kv4 = *reinterpret_cast<const u32x4_t *>(a.k_cache + (cache_base + key) * D + d0);
+        vv4 = *reinterpret_cast<const u32x4_t *>(a.v_cache + (cache_base + key) * D + d0);
+      }
+      *reinterpret_cast<u32x4_t *>(&Ks[kk * KP + d0]) = kv4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        Vt[(d0 + 2 * e) * VP + kk] = (uint16_t)(vv4[e] & 0xffff);
+        Vt[(d0 + 2 * e + 1) * VP + kk] = (uint16_t)(vv4[e] >> 16);
+      }
+    }
+    __syncthreads();
+
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      if (u >= nqt) break;  // wave-uniform
+      // S^T tiles: 4 subtiles of 16 keys; lane holds keys kt0 + 16ks + 4g + i for query r
+      f32x4_t st[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        st[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kd = 0; kd < DK; ++kd) {
+          const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(&Ks[(16 * ks + r) * KP + 32 * kd + 8 * g]);
+          st[ks] = mfma16x16x32(kf, qf[u][kd], st[ks]);
+        }
+      }
+      // mask + scale (log2 domain), tile max
+      const int last_visible = n + r;  // row j = r
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kt0 + 16 * ks + 4 * g + i;
+          const float v = (key <= last_visible && key < key_hi) ? st[ks][i] * scale_log2 : -INFINITY;
+          st[ks][i] = v;
+          tmax = fmaxf(tmax, v);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      const float mnew = fmaxf(mrow[u], tmax);
+      float alpha, psum = 0.f;
+      u32x4_t pb[2];
+      if (mnew == -INFINITY) {  // nothing visible yet for this row
+        alpha = 1.f;
+        pb[0] = pb[1] = u32x4_t{0, 0, 0, 0};
+      } else {
+        alpha = exp2f(mrow[u] - mnew);
+        float p[4][4];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            p[ks][i] = exp2f(st[ks][i] - mnew);
+            psum += p[ks][i];
+          }
+        // B operand for keys 32c + {4g+i} (slots 0-3) and 32c + 16 + {4g+i} (slots 4-7)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+          pb[c] = u32x4_t{pack_bf16x2(p[2 * c][0], p[2 * c][1]), pack_bf16x2(p[2 * c][2], p[2 * c][3]),
+                          pack_bf16x2(p[2 * c + 1][0], p[2 * c + 1][1]),
+                          pack_bf16x2(p[2 * c + 1][2], p[2 * c + 1][3])};
+      }
+      psum += __shfl_xor(psum, 16);
+      psum += __shfl_xor(psum, 32);
+      mrow[u] = mnew;
+      lrow[u] = lrow[u] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[u][dt] = oacc[u][dt] * alpha;
+      // O^T += V^T P^T
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) {
+          const uint16_t *vrow = &Vt[(16 * dt + r) * VP + 32 * c + 4 * g];
+          const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
+          const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 16);
+          oacc[u][dt] = mfma16x16x32(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb[c], oacc[u][dt]);
+        }
+    }
+  }
+
+  // partials: row R = tile*16 + j, o[d] with d = 16dt + 4g + i held by lane (r = j, g)
+  const int R = G * 16;
+  float *po = a.part_o + ((unit * a.nsplit + sp) * R) * D;
+  float2 *pml = a.part_ml + (unit * a.nsplit + sp) * R;
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    if (u >= nqt) break;
+    const int row = (wave + 4 * u) * 16 + r;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4_t *>(po + (size_t)row * D + 16 * dt + 4 * g) = oacc[u][dt];
+    if (g == 0) pml[row] = make_float2(mrow[u], lrow[u]);
+  }
+
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) s_last = atomicAdd(&a.counters[unit], 1) == nsplit - 1;
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+
+  // merge the splits in order: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
+  const float *po0 = a.part_o + (unit * a.nsplit) * R * D;
+  const float2 *pml0 = a.part_ml + (unit * a.nsplit) * R;
+  for (int idx = tid; idx < R * D; idx += 256) {
+    const int row = idx / D, d = idx % D;
+    float M = -INFINITY;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, __builtin_nontemporal_load(&pml0[s * R + row].x));
+    float num = 0.f, den = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = __builtin_nontemporal_load(&pml0[s * R + row].x);
+      if (ms == -INFINITY) continue;
+      const float w = exp2f(ms - M);
+      num += w * __builtin_nontemporal_load(&po0[((size_t)s * R + row) * D + d]);
+      den += w * __builtin_nontemporal_load(&pml0[s * R + row].y);
+    }
+    const int j = row & 15, hq = kvh * G + (row >> 4);
+    a.o[(size_t)(b * 16 + j) * qstride + hq * D + d] = (uint16_t)f32_to_bf16(num / den);
+  }
+  if (tid == 0) a.counters[unit] = 0;
+}
+
+int attention_split_len(int batch, int Hkv, int max_ctx) {
+  // aim for about 512 workgroups across the batch; splits are whole 64-key tiles
+  const long target = 512;
+  long sl = ((long)batch * Hkv * max_ctx + target - 1) / target;
+  sl = ((sl + KT - 1) / KT) * KT;
+  if (sl < KT) sl = KT;
+  return (int)sl;
+}
+
+hipError_t launch_attention(const AttnArgs &a, int D, hipStream_t st) {
+  dim3 grid(a.nsplit, a.Hkv, a.batch);
+  if (D == 64) {
+    hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(256), 0, st, a, (float)(1.4426950408889634 / 8.0));
+  } else if (D == 128) {
+    hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(256), 0, st, a,
+                       (float)(1.4426950408889634 / 11.313708498984761));
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}

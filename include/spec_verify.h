@@ -1,0 +1,213 @@
+/*
+ * spec_verify.h -- C ABI of the block-draft verify pass on MI355X (gfx950).
+ *
+ * What the library computes (HunyuanOCR-1.5 / DFlash write-up, inference
+ * loop, steps 3-5; "The Inference Stack Behind OCRia", speculative decoding
+ * section):
+ *
+ *   A drafter proposes a block; the target model checks the whole block in
+ *   ONE forward pass and keeps the longest prefix whose tokens equal the
+ *   target's own greedy choices, cutting at the first left-to-right
+ *   mismatch.  The pass also yields one more token from the target itself:
+ *   the correction after a rejected draft, or the bonus after a fully
+ *   accepted block ("LLM 推理加速" article, section 3.2, describes both).
+ *
+ * A block is 16 token ids per sequence: t[0] is the pending token (the last
+ * token emitted, not yet in the KV cache) and t[1..15] are drafts.  Row j sits
+ * at position p = kv_len[b] + j and sees cache keys 0 .. p (the committed
+ * prefix plus the block rows up to itself).  g[j] = argmax of the lm_head at
+ * row j (lowest id on ties).  The accepted length is
+ *     tau = min{ j in [1,16) : t[j] != g[j-1] }, or 16 if there is none,
+ * and bonus = g[tau-1].  tau counts block rows kept (pending included), so
+ * the caller emits t[1..tau-1] followed by bonus, and commits tau KV rows.
+ *
+ * Model (pre-norm GQA decoder, no biases): h = E[t];
+ *   per layer: x = RMSNorm(h); q,k,v = x Wqkv^T; RoPE(q,k) (rotate-half,
+ *   inv_freq_i = theta^(-2i/D)); o = softmax(q k^T / sqrt(D)) v under the
+ *   block-causal mask, query head h reading KV head h / (Hq/Hkv);
+ *   h += o Wo^T; x = RMSNorm(h); h += (SiLU(x Wg^T) * (x Wu^T)) Wd^T;
+ *   final x = RMSNorm(h); logits = x E^T (or x Wlm^T for an untied head).
+ *
+ * Numerics of this implementation: weights decoded exactly to BF16; BF16
+ * activations (normed x, q/k/v, the KV cache, attention output, SwiGLU
+ * output, softmax weights); fp32 accumulation, residual stream, softmax
+ * statistics and logits.
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).
+ *   - The caller owns all device memory it passes in (weights, KV caches,
+ *     kv_len, tokens, outputs).  The library owns only the workspace it
+ *     allocates in spec_verify_init and frees in spec_verify_destroy.
+ *   - Work is enqueued on the given stream and returns without waiting;
+ *     nothing is copied device->host except in spec_get_device_error.
+ *   - Return values: SPEC_OK (0) or a negative spec_status.  Argument errors
+ *     are detected on the host before anything is enqueued.  Conditions only
+ *     the device can see (a token id >= vocab, a cache that would overflow)
+ *     set bits in a sticky device error word; affected rows skip their
+ *     writes, so no access ever leaves its buffer.
+ *   - One context per stream; calls on one context must not overlap.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPEC_BLOCK 16
+
+typedef enum {
+  SPEC_OK = 0,
+  SPEC_E_ARG = -1,         /* NULL pointer, batch out of range, bad count   */
+  SPEC_E_SHAPE = -2,       /* model/cache shape the kernels do not support  */
+  SPEC_E_UNSUPPORTED = -3, /* weight format not supported for that matrix   */
+  SPEC_E_HIP = -4,         /* a HIP runtime call failed                     */
+  SPEC_E_NOMEM = -5        /* workspace allocation failed                   */
+} spec_status;
+
+/* Weight formats ("The Inference Stack Behind OCRia", quantization section:
+ * FP8 halves the bytes per weight; per-layer mixes of precisions). */
+typedef enum {
+  SPEC_WFMT_FP8_E4M3_ROW = 1, /* uint8 OCP e4m3fn codes [rows][cols] + fp32
+                                 scale per row: w = e4m3(code) * scale[row] */
+  SPEC_WFMT_MXFP4 = 2,        /* uint8 [rows][cols/2] e2m1 nibbles, low nibble
+                                 = even column, + uint8 e8m0 [rows][cols/32]:
+                                 w = e2m1 * 2^(e8m0 - 127)                    */
+  SPEC_WFMT_BF16 = 3          /* uint16 bf16 bit patterns [rows][cols]       */
+} spec_wfmt;
+
+/* Device error bits (sticky until read by spec_get_device_error). */
+#define SPEC_DERR_TOKEN 1    /* a token id outside [0, vocab): row uses id 0  */
+#define SPEC_DERR_CAPACITY 2 /* kv_len + 16 > max_ctx: the sequence's block
+                                K/V writes are skipped                        */
+#define SPEC_DERR_COMMIT 4   /* a commit count outside [0,16] or past max_ctx:
+                                that sequence's kv_len is left unchanged      */
+
+typedef struct {
+  int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
+  float rms_eps;     /* e.g. 1e-6 */
+  float rope_theta;  /* e.g. 1e4  */
+  int32_t attn_wfmt; /* format of w_qkv and w_o: SPEC_WFMT_FP8_E4M3_ROW       */
+  int32_t mlp_wfmt;  /* format of w_gate_up and w_down: FP8_E4M3_ROW | MXFP4 */
+  int32_t tied_lm_head; /* 1: logits use the embedding table */
+} spec_model_desc;
+
+/* One decoder layer (all device pointers, caller-owned).
+ *   w_qkv  [(Hq+2Hkv)*D][H], rows = q heads, then k heads, then v heads
+ *   w_o    [H][Hq*D]
+ *   w_gate_up [2I][H], rows = gate (I rows) then up (I rows)
+ *   w_down [H][I]
+ * s_* : fp32 [rows] for FP8_E4M3_ROW; uint8 e8m0 [rows][cols/32] for MXFP4.
+ * attn_norm, mlp_norm: fp32 RMSNorm gains [H]. */
+typedef struct {
+  const void *w_qkv, *s_qkv;
+  const void *w_o, *s_o;
+  const void *w_gate_up, *s_gate_up;
+  const void *w_down, *s_down;
+  const float *attn_norm, *mlp_norm;
+} spec_layer_weights;
+
+typedef struct {
+  const spec_layer_weights *layers; /* (host) array of n_layers; copied at init */
+  const uint16_t *embed;            /* bf16 [V][H]                             */
+  const uint16_t *lm_head;          /* bf16 [V][H]; NULL when tied             */
+  const float *final_norm;          /* fp32 [H]                                */
+} spec_weights;
+
+/* KV cache: BF16 [n_layers][max_batch][Hkv][max_ctx][D] for K and for V.
+ * kv_len[b] = committed length of sequence b (int32, device).  A verify
+ * writes the block's K/V to slots kv_len[b] .. kv_len[b]+15 without
+ * changing kv_len; slots >= kv_len are otherwise unspecified. */
+typedef struct {
+  uint16_t *k_cache, *v_cache;
+  int32_t *kv_len;
+  int32_t max_batch, max_ctx;
+} spec_kv;
+
+typedef struct spec_ctx spec_ctx;
+
+/* Validate the model and cache description, copy the pointer tables, and
+ * allocate the library workspace (activations for max_batch*16 rows, split
+ * attention partials, argmax partials, a RoPE cos/sin table for positions
+ * < max_ctx, the device error word).  Supported: head_dim 64 or 128, hidden
+ * and intermediate multiples of 64, vocab a multiple of 64, Hq % Hkv == 0.
+ * Synchronous (allocations and one table upload on `stream`).  *out is set
+ * only on success. */
+int spec_verify_init(const spec_model_desc *model /*host*/, const spec_weights *w /*host*/,
+                     const spec_kv *kv /*host*/, hipStream_t stream, spec_ctx **out /*host*/);
+
+/* One verify pass for sequences 0 .. batch-1.
+ *   tokens     int32 [batch][16], row 0 = pending token
+ *   accept_len int32 [batch] out: tau in [1,16]
+ *   bonus      int32 [batch] out: g[tau-1]
+ *   argmax     int32 [batch][16] out, or NULL: g for every row
+ * Writes the block's K/V to cache slots kv_len[b]+j; never changes kv_len.
+ * Asynchronous on `stream`.  SPEC_E_ARG for batch outside [1, max_batch]
+ * or NULL tokens/accept_len/bonus. */
+int spec_verify_block(spec_ctx *ctx, int32_t batch, const int32_t *tokens, int32_t *accept_len,
+                      int32_t *bonus, int32_t *argmax, hipStream_t stream);
+
+/* Commit: kv_len[b] += n_commit[b] for b < batch, or += the tau of the last
+ * verify when n_commit is NULL (the K/V rows are already in place; this is a
+ * length bump, so a rejected suffix is rolled back by not counting it).
+ * Counts must lie in [0, 16] and keep kv_len <= max_ctx, else that sequence
+ * is left unchanged and SPEC_DERR_COMMIT is set.  Asynchronous. */
+int spec_commit_kv(spec_ctx *ctx, int32_t batch, const int32_t *n_commit, hipStream_t stream);
+
+/* Free the workspace.  The caller's buffers are untouched.  NULL is a no-op. */
+int spec_verify_destroy(spec_ctx *ctx);
+
+/* Read and clear the sticky device error word (a mask of SPEC_DERR_*).
+ * Synchronises `stream`. */
+int spec_get_device_error(spec_ctx *ctx, int32_t *code /*host*/, hipStream_t stream);
+
+/* Static description of a spec_status value. */
+const char *spec_status_str(int status);
+
+/* Test hook: when hidden/logits are non-NULL, later verify passes also write
+ * the final normed hidden state (fp32 [batch*16][H], the BF16 values fed to
+ * the lm_head) and the logits (fp32 [batch*16][V]).  NULL disables. */
+int spec_debug_set_dump(spec_ctx *ctx, float *hidden, float *logits);
+
+/* Test hook: one weight-streaming linear on its own,
+ *   y[m][n] = sum_k x[m][k] * w(n, k)     (fp32 out, [M][N])
+ * x bf16 [M][K]; w in format `wfmt` with scales as in spec_layer_weights
+ * (scales NULL for BF16).  K and N multiples of 64 (MXFP4: K % 64 too).
+ * Synchronous. */
+int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const void *w,
+                      const void *scales, int32_t wfmt, float *y, hipStream_t stream);
+
+/* Test hook: block-causal GQA attention on its own for sequences 0..batch-1:
+ * q bf16 [batch*16][Hq*D] (already rotated), K/V caches of ONE layer
+ * ([max_batch][Hkv][max_ctx][D], block rows already stored at kv_len+j),
+ * o bf16 [batch*16][Hq*D].  split_len = keys per split (multiple of 64), or
+ * 0 for the library's choice.  Synchronous. */
+int spec_debug_attention(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                         int32_t max_batch, int32_t max_ctx, const uint16_t *q,
+                         const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *kv_len,
+                         uint16_t *o, int32_t split_len, hipStream_t stream);
+
+/* Kernel classes for spec_debug_time_kernel. */
+typedef enum {
+  SPEC_K_NONE = 0, SPEC_K_EMBED = 1, SPEC_K_RMSNORM = 2, SPEC_K_QKV = 3, SPEC_K_ATTENTION = 4,
+  SPEC_K_OPROJ = 5, SPEC_K_GATE_UP = 6, SPEC_K_DOWN = 7, SPEC_K_LM_HEAD = 8, SPEC_K_ACCEPT = 9,
+  SPEC_K_COMMIT = 10
+} spec_kernel_kind;
+
+/* Test/measurement hook: while `kind` is set, every launch of that kernel
+ * class by later verify/commit calls is bracketed by a pair of HIP events on
+ * the caller's stream (at most 8192 launches are recorded).  Eager use only:
+ * not under graph capture.  SPEC_K_NONE stops recording. */
+int spec_debug_time_kernel(spec_ctx *ctx, int32_t kind);
+
+/* Synchronises the recorded events, returns the summed duration (ms) and the
+ * number of recorded launches, and clears the record. */
+int spec_debug_kernel_time(spec_ctx *ctx, float *total_ms /*host*/, int32_t *launches /*host*/);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SPEC_VERIFY_H */

@@ -120,35 +120,37 @@ class OracleModel:
 
 
 class OracleKV:
-    """Per-layer K and V, float64 [B, Hkv, capacity, D], plus committed lengths n."""
+    """Per-layer, per-sequence K and V, float64 [Hkv, capacity_b, D], plus
+    committed lengths n.  capacity may be one int or one per sequence."""
 
-    def __init__(self, shape, batch: int, capacity: int):
+    def __init__(self, shape, batch: int, capacity):
         self.m = shape
-        self.cap = capacity
-        self.K = [np.zeros((batch, shape.n_kv_heads, capacity, shape.head_dim)) for _ in range(shape.n_layers)]
-        self.V = [np.zeros_like(k) for k in self.K]
+        caps = np.broadcast_to(np.asarray(capacity, dtype=np.int64), (batch,))
+        self.caps = caps.copy()
+        shp = lambda c: (shape.n_kv_heads, int(c), shape.head_dim)
+        self.K = [[np.zeros(shp(c)) for c in caps] for _ in range(shape.n_layers)]
+        self.V = [[np.zeros(shp(c)) for c in caps] for _ in range(shape.n_layers)]
         self.n = np.zeros(batch, dtype=np.int64)
 
     @classmethod
-    def from_bf16(cls, shape, K_layers, V_layers, lens, capacity=None):
+    def from_bf16(cls, shape, K_layers, V_layers, lens, extra: int = 16):
         """Load BF16 caches ([B, Hkv, cap, D] uint16 per layer); only the
-        committed prefix of each sequence is read."""
-        B = len(lens)
-        cap = capacity or K_layers[0].shape[2]
-        kv = cls(shape, B, cap)
+        committed prefix of each sequence is read; each sequence gets room
+        for ``extra`` more rows."""
+        lens = np.asarray(lens)
+        kv = cls(shape, len(lens), lens + extra)
         for l in range(shape.n_layers):
-            for b in range(B):
-                n = int(lens[b])
-                kv.K[l][b, :, :n] = decode_bf16(K_layers[l][b, :, :n])
-                kv.V[l][b, :, :n] = decode_bf16(V_layers[l][b, :, :n])
+            for b, n in enumerate(lens):
+                kv.K[l][b][:, :n] = decode_bf16(K_layers[l][b, :, :n])
+                kv.V[l][b][:, :n] = decode_bf16(V_layers[l][b, :, :n])
         kv.n[:] = lens
         return kv
 
     def copy(self):
         c = OracleKV.__new__(OracleKV)
-        c.m, c.cap = self.m, self.cap
-        c.K = [k.copy() for k in self.K]
-        c.V = [v.copy() for v in self.V]
+        c.m, c.caps = self.m, self.caps.copy()
+        c.K = [[k.copy() for k in layer] for layer in self.K]
+        c.V = [[v.copy() for v in layer] for layer in self.V]
         c.n = self.n.copy()
         return c
 
@@ -164,7 +166,7 @@ def forward(model: OracleModel, kv: OracleKV, tokens, seqs=None) -> np.ndarray:
     Bp, T = tokens.shape
     seqs = np.arange(Bp) if seqs is None else np.asarray(seqs)
     n = kv.n[seqs]
-    assert np.all(n + T <= kv.cap), "block does not fit the cache"
+    assert np.all(n + T <= kv.caps[seqs]), "block does not fit the cache"
     D, Hq, Hkv = m.head_dim, m.n_q_heads, m.n_kv_heads
     pos = n[:, None] + np.arange(T)[None, :]
     h = model.embed(tokens).reshape(Bp * T, m.hidden)
@@ -177,8 +179,8 @@ def forward(model: OracleModel, kv: OracleKV, tokens, seqs=None) -> np.ndarray:
         o = np.empty((Bp, T, Hq, D))
         for i, b in enumerate(seqs):
             nb = int(n[i])
-            kv.K[l][b, :, nb:nb + T] = k[i].transpose(1, 0, 2)
-            kv.V[l][b, :, nb:nb + T] = v[i].transpose(1, 0, 2)
+            kv.K[l][b][:, nb:nb + T] = k[i].transpose(1, 0, 2)
+            kv.V[l][b][:, nb:nb + T] = v[i].transpose(1, 0, 2)
             o[i] = attention(q[i], kv.K[l][b], kv.V[l][b], nb, m.group)
         h = h + o.reshape(Bp * T, Hq * D) @ w["wo"].T
         x = rms_norm(h, w["mlp_norm"], m.rms_eps)

@@ -1,0 +1,184 @@
+"""Whole verify pass on the GPU against the float64 oracle, through the C ABI
+(spec_verify_init / spec_verify_block / spec_commit_kv), on the synthetic
+workloads; plus the data-movement, error-path, determinism and graph-replay
+properties of the boundary.  The parity rule is documented in gpu_cases."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as W
+from block_draft_verification_amd import DERR_CAPACITY, DERR_COMMIT, DERR_TOKEN, DeviceModel, Verifier
+
+from gpu_cases import build_case, compare, gpu_setup, gpu_verify, log, oracle_verify, row_rel
+
+pytestmark = pytest.mark.gpu
+
+
+def _kv_rows(dev, l, b, lo, hi):
+    K = dev.k_cache[l, b, :, lo:hi].cpu().numpy().view(np.uint16)
+    V = dev.v_cache[l, b, :, lo:hi].cpu().numpy().view(np.uint16)
+    return K, V
+
+
+def _check_block_kv(case, dev, okv, seqs, layers):
+    """Block rows land in slots n..n+15 (within tolerance of the oracle's);
+    committed rows below n are untouched, bit for bit."""
+    for l in layers:
+        for i, b in enumerate(seqs):
+            n = int(case.lens[b])
+            K, V = _kv_rows(dev, l, b, 0, n + 16)
+            K0, V0 = case.kv_layers[l]
+            assert np.array_equal(K[:, :n], K0[b, :, :n]) and np.array_equal(V[:, :n], V0[b, :, :n])
+            kr = okv.K[l][i][:, n:n + 16]
+            vr = okv.V[l][i][:, n:n + 16]
+            assert row_rel(oracle.decode_bf16(K[:, n:]), kr).max() < 2e-2
+            assert row_rel(oracle.decode_bf16(V[:, n:]), vr).max() < 2e-2
+
+
+def _full_case(name, check_layers=(0, -1)):
+    case = build_case(name)
+    ref, okv = oracle_verify(case)
+    dev, ver = gpu_setup(case)
+    got = gpu_verify(ver, case)
+    stats = compare(ref, got, case.blocks)
+    log(f"{name}: {stats}")
+    m = case.wl.model
+    _check_block_kv(case, dev, okv, range(len(case.lens)), [l % m.n_layers for l in check_layers])
+    # commit the accepted rows: a length bump by tau
+    ver.commit(len(case.lens))
+    torch.cuda.synchronize()
+    assert np.array_equal(dev.kv_len.cpu().numpy()[:len(case.lens)], case.lens + got["accept_len"])
+    assert ver.device_error() == 0
+    ver.close()
+    return stats
+
+
+def test_verify_tiny():
+    _full_case("tiny-b1-ctx128")
+
+
+def test_verify_05b_b1_ctx2048():
+    _full_case("0.5b-fp8-b1-ctx2048")
+
+
+def test_verify_05b_b32_ragged():
+    _full_case("0.5b-fp8-b32-ctx512to4096")
+
+
+def test_verify_05b_mxfp4_b16():
+    _full_case("0.5b-mxfp4mlp-b16-ctx3072")
+
+
+def test_verify_8b_sampled():
+    """8B shape at full size: the oracle runs sequence 0 (random drafts, so no
+    15-step greedy planting at this size); every sequence is checked for
+    self-consistency and untouched committed rows."""
+    case = build_case("8b-fp8-b8-ctx4096", seqs_planted=[])
+    ref, okv = oracle_verify(case, seqs=[0])
+    dev, ver = gpu_setup(case)
+    got = gpu_verify(ver, case)
+    stats = compare(ref, got, case.blocks, seqs=[0])
+    log(f"8b: {stats}")
+    _check_block_kv(case, dev, okv, [0], [0, 31])
+    g = got["argmax"].reshape(-1, 16)
+    for b in range(8):
+        t = next((j for j in range(1, 16) if case.blocks[b, j] != g[b, j - 1]), 16)
+        assert got["accept_len"][b] == t
+    ver.close()
+
+
+def test_multi_round_tiny_with_explicit_commits():
+    """Four rounds of verify + commit on the tiny model; each round is planted
+    from the oracle's continuation of the committed history, both sides commit
+    the oracle's tau (explicit counts on the GPU side)."""
+    case = build_case("tiny-b1-ctx128", batch=1, extra=16 * 6)
+    m = case.wl.model
+    dev, ver = gpu_setup(case)
+    okv = case.okv
+    pend = case.pending.copy()
+    for rnd in range(4):
+        cont = oracle.greedy_continuation(case.om, okv, pend)
+        L = int(W.geometric_capped(W.child_rng(5, 200 + rnd), 0.3))
+        case.blocks = W.plant_block(cont[0], L, m.vocab, W.child_rng(5, 300 + rnd))[None].astype(np.int32)
+        ref = oracle.verify_block(case.om, okv, case.blocks)
+        got = gpu_verify(ver, case)
+        compare(ref, got, case.blocks)
+        n_commit = torch.tensor(ref.tau.astype(np.int32), device="cuda")
+        ver.commit(1, n_commit)
+        oracle.commit(okv, ref.tau)
+        pend = ref.bonus
+        torch.cuda.synchronize()
+        assert dev.kv_len[0].item() == okv.n[0]
+    assert ver.device_error() == 0
+    ver.close()
+
+
+def test_determinism_and_graph_replay():
+    """Two eager verifies give identical bits; a captured graph of verify +
+    commit replays to the same outputs, with kv_len restored between replays."""
+    case = build_case("tiny-b1-ctx128", seqs_planted=[])
+    m = case.wl.model
+    dev, ver = gpu_setup(case)
+    a = gpu_verify(ver, case)
+    b = gpu_verify(ver, case)
+    for k in ("hidden", "logits", "argmax", "accept_len", "bonus"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    tokens = torch.from_numpy(case.blocks).cuda()
+    outs = {k: torch.empty(1, dtype=torch.int32, device="cuda") for k in ("tau", "bonus")}
+    amax = torch.empty(1, 16, dtype=torch.int32, device="cuda")
+    kv0 = dev.kv_len.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up on the capture stream
+        ver.verify(tokens, outs["tau"], outs["bonus"], amax)
+        ver.commit(1)
+    torch.cuda.current_stream().wait_stream(s)
+    dev.kv_len.copy_(kv0)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ver.verify(tokens, outs["tau"], outs["bonus"], amax)
+        ver.commit(1)
+    for rep in range(3):
+        dev.kv_len.copy_(kv0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert outs["tau"].item() == a["accept_len"][0] and outs["bonus"].item() == a["bonus"][0]
+        assert np.array_equal(amax.cpu().numpy(), a["argmax"])
+        assert dev.kv_len[0].item() == case.lens[0] + a["accept_len"][0]
+    ver.close()
+
+
+def test_error_paths_are_reported_without_stray_writes():
+    case = build_case("tiny-b1-ctx128", seqs_planted=[])
+    m = case.wl.model
+    cap = case.wl.max_ctx
+    dev, ver = gpu_setup(case)
+    # token id out of range -> DERR_TOKEN, pass still completes
+    bad = case.blocks.copy()
+    bad[0, 3] = m.vocab + 5
+    ver.verify(torch.from_numpy(bad).cuda())
+    assert ver.device_error() & DERR_TOKEN
+    assert ver.device_error() == 0                      # reading clears the word
+    # a commit count past 16 -> DERR_COMMIT, kv_len unchanged
+    before = dev.kv_len[0].item()
+    ver.commit(1, torch.tensor([17], dtype=torch.int32, device="cuda"))
+    assert ver.device_error() & DERR_COMMIT and dev.kv_len[0].item() == before
+    # a cache that cannot take the block -> DERR_CAPACITY and no block K/V writes
+    dev.kv_len[0] = cap - 8
+    snap = [(_kv_rows(dev, l, 0, cap - 8, cap)) for l in range(m.n_layers)]
+    ver.verify(torch.from_numpy(case.blocks).cuda())
+    assert ver.device_error() & DERR_CAPACITY
+    for l in range(m.n_layers):
+        K, V = _kv_rows(dev, l, 0, cap - 8, cap)
+        assert np.array_equal(K, snap[l][0]) and np.array_equal(V, snap[l][1])
+    ver.close()
+
+
+def test_batch_bounds_rejected():
+    case = build_case("tiny-b1-ctx128", seqs_planted=[])
+    dev, ver = gpu_setup(case)
+    with pytest.raises(Exception):
+        ver.verify(torch.zeros(2, 16, dtype=torch.int32, device="cuda"))   # batch > max_batch
+    ver.close()

@@ -99,8 +99,8 @@ def test_oracle_matches_independent_full_forward(fmt, gains):
     # cache slots hold K (rotated at absolute position p = slot) and V of every row
     assert kv.n[0] == 45
     for l in range(m.n_layers):
-        assert np.allclose(kv.K[l][0, :, :61], kc[l], rtol=1e-11, atol=1e-11)
-        assert np.allclose(kv.V[l][0, :, :61], vc[l], rtol=1e-11, atol=1e-11)
+        assert np.allclose(kv.K[l][0][:, :61], kc[l], rtol=1e-11, atol=1e-11)
+        assert np.allclose(kv.V[l][0][:, :61], vc[l], rtol=1e-11, atol=1e-11)
 
 
 def _setup_tiny(seed=0, B=1, capacity=128 + 16 * 40):
@@ -130,8 +130,8 @@ def test_block_rows_equal_autoregressive_rows():
         commit(kv2, [1])
     assert np.allclose(np.stack(ar_hidden), r.hidden[0], rtol=1e-12, atol=1e-12)
     for l in range(m.n_layers):
-        assert np.allclose(kv.K[l][0, :, 128:144], kv2.K[l][0, :, 128:144], rtol=1e-12, atol=1e-12)
-        assert np.allclose(kv.V[l][0, :, 128:144], kv2.V[l][0, :, 128:144], rtol=1e-12, atol=1e-12)
+        assert np.allclose(kv.K[l][0][:, 128:144], kv2.K[l][0][:, 128:144], rtol=1e-12, atol=1e-12)
+        assert np.allclose(kv.V[l][0][:, 128:144], kv2.V[l][0][:, 128:144], rtol=1e-12, atol=1e-12)
 
 
 @pytest.mark.parametrize("kind", ["random", "planted", "all_right", "last_wrong", "first_wrong"])
@@ -173,8 +173,9 @@ def test_spec_equals_autoregressive(kind):
     # committed KV equals the autoregressive cache on the common committed prefix
     n = int(min(kv.n.min(), kv_ar.n.min()))
     for l in range(m.n_layers):
-        assert np.allclose(kv.K[l][:, :, :n], kv_ar.K[l][:, :, :n], rtol=1e-11, atol=1e-11)
-        assert np.allclose(kv.V[l][:, :, :n], kv_ar.V[l][:, :, :n], rtol=1e-11, atol=1e-11)
+        for b in range(2):
+            assert np.allclose(kv.K[l][b][:, :n], kv_ar.K[l][b][:, :n], rtol=1e-11, atol=1e-11)
+            assert np.allclose(kv.V[l][b][:, :n], kv_ar.V[l][b][:, :n], rtol=1e-11, atol=1e-11)
 
 
 @pytest.mark.parametrize("p", [0.1, 0.2])
