@@ -24,6 +24,7 @@ struct spec_ctx {
   int32_t *counters, *last_tau, *err;
   ArgmaxPart *amax;
   float2 *rope;
+  GemmWork wk;
   float *dump_hidden, *dump_logits;
   // launch timing of one kernel class (measurement hook)
   int prof_kind = SPEC_K_NONE;
@@ -119,6 +120,13 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
     if (u > units) units = u;
   }
   c->part_units = units;
+  size_t gemm_floats = 0, gemm_counters = 0;
+  for (int b = 1; b <= kv->max_batch; ++b) {
+    size_t cnt = 0;
+    const size_t f = gemm_part_floats(b * 16, H, I, V, Hq, Hkv, D, &cnt);
+    if (f > gemm_floats) gemm_floats = f;
+    if (cnt > gemm_counters) gemm_counters = cnt;
+  }
 
   const size_t Mm = c->Mmax;
   size_t sizes[] = {Mm * H * 4,                      // h
@@ -132,7 +140,9 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
                     (size_t)kv->max_batch * 4,       // last_tau
                     4,                               // err
                     (size_t)lm_parts(V) * Mm * 8,    // amax
-                    (size_t)kv->max_ctx * (D / 2) * 8};  // rope
+                    (size_t)kv->max_ctx * (D / 2) * 8,  // rope
+                    gemm_floats * 4,                  // split-K partials
+                    gemm_counters * 4};               // split-K counters
   const int NS = sizeof(sizes) / sizeof(sizes[0]);
   size_t off[NS], total = 0;
   for (int i = 0; i < NS; ++i) {
@@ -156,6 +166,9 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   c->err = (int32_t *)(base + off[9]);
   c->amax = (ArgmaxPart *)(base + off[10]);
   c->rope = (float2 *)(base + off[11]);
+  c->wk.part = (float *)(base + off[12]);
+  c->wk.part_floats = gemm_floats;
+  c->wk.counters = (int32_t *)(base + off[13]);
   c->dump_hidden = c->dump_logits = nullptr;
 
   // RoPE table: angle = p * theta^(-2i/D), in double, stored as fp32 (cos, sin)
@@ -169,7 +182,9 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
           hipSuccess ||
       launch_fill_i32(c->counters, kv->max_batch * Hkv, 0, st) != hipSuccess ||
       launch_fill_i32(c->last_tau, kv->max_batch, 0, st) != hipSuccess ||
-      launch_fill_i32(c->err, 1, 0, st) != hipSuccess || hipStreamSynchronize(st) != hipSuccess) {
+      launch_fill_i32(c->err, 1, 0, st) != hipSuccess ||
+      launch_fill_i32(c->wk.counters, (int)gemm_counters + 1, 0, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess) {
     (void)hipFree(c->ws);
     delete c;
     return SPEC_E_HIP;
@@ -210,12 +225,12 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     uint16_t *kc = c->kv.k_cache + l * lstride, *vc = c->kv.v_cache + l * lstride;
     {
       Timed t(c, SPEC_K_RMSNORM, st);
-      CK(launch_rmsnorm(c->h, L.attn_norm, M, H, m.rms_eps, c->x, nullptr, st));
+      CK(launch_rmsnorm(c->h, L.attn_norm, M, H, m.rms_eps, c->x, 0, nullptr, st));
     }
     QkvOut qo{c->q, kc, vc, c->kv.kv_len, c->rope, Hq, Hkv, max_ctx};
     {
       Timed t(c, SPEC_K_QKV, st);
-      CK(launch_qkv(c->x, M, H, D, LinearW{L.w_qkv, L.s_qkv, SPEC_WFMT_FP8_E4M3_ROW}, qo, st));
+      CK(launch_qkv(c->x, M, H, D, LinearW{L.w_qkv, L.s_qkv, SPEC_WFMT_FP8_E4M3_ROW}, qo, c->wk, st));
     }
     aa.k_cache = kc;
     aa.v_cache = vc;
@@ -225,28 +240,28 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     }
     {
       Timed t(c, SPEC_K_OPROJ, st);
-      CK(launch_residual(c->ao, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, c->h, st));
+      CK(launch_residual(c->ao, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, c->h, c->wk, st));
     }
     {
       Timed t(c, SPEC_K_RMSNORM, st);
-      CK(launch_rmsnorm(c->h, L.mlp_norm, M, H, m.rms_eps, c->x, nullptr, st));
+      CK(launch_rmsnorm(c->h, L.mlp_norm, M, H, m.rms_eps, c->x, 0, nullptr, st));
     }
     {
       Timed t(c, SPEC_K_GATE_UP, st);
-      CK(launch_swiglu(c->x, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, c->act, st));
+      CK(launch_swiglu(c->x, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, c->act, c->wk, st));
     }
     {
       Timed t(c, SPEC_K_DOWN, st);
-      CK(launch_residual(c->act, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, c->h, st));
+      CK(launch_residual(c->act, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, c->h, c->wk, st));
     }
   }
   {
     Timed t(c, SPEC_K_RMSNORM, st);
-    CK(launch_rmsnorm(c->h, c->final_norm, M, H, m.rms_eps, c->x, c->dump_hidden, st));
+    CK(launch_rmsnorm(c->h, c->final_norm, M, H, m.rms_eps, c->x, 1, c->dump_hidden, st));
   }
   {
     Timed t(c, SPEC_K_LM_HEAD, st);
-    CK(launch_lm_argmax(c->x, M, V, H, c->lm_table, c->amax, c->dump_logits, st));
+    CK(launch_lm_argmax(c->x, M, V, H, c->lm_table, c->amax, c->dump_logits, c->wk, st));
   }
   {
     Timed t(c, SPEC_K_ACCEPT, st);
@@ -326,9 +341,18 @@ int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const 
     return SPEC_E_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (wfmt == SPEC_WFMT_FP8_E4M3_ROW && !aligned16(scales)))
     return SPEC_E_ARG;
-  CK(launch_linear_f32(x, M, N, K, LinearW{w, scales, wfmt}, y, st));
-  CK(hipStreamSynchronize(st));
-  return SPEC_OK;
+  const GemmPlan p = gemm_plan(M, N / 16, K / 64, 1, 8);
+  void *buf = nullptr;
+  const size_t cnt = (size_t)p.nb * p.mb + 1;
+  if (hipMalloc(&buf, p.part_floats * 4 + cnt * 4 + 256) != hipSuccess) return SPEC_E_NOMEM;
+  GemmWork wk{(float *)buf, p.part_floats, (int32_t *)((char *)buf + ((p.part_floats * 4 + 255) & ~(size_t)255))};
+  int rc = SPEC_OK;
+  if (launch_fill_i32(wk.counters, (int)cnt, 0, st) != hipSuccess ||
+      launch_linear_f32(x, M, N, K, LinearW{w, scales, wfmt}, y, wk, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    rc = SPEC_E_HIP;
+  (void)hipFree(buf);
+  return rc;
 }
 
 int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_batch, int32_t max_ctx,

@@ -8,13 +8,15 @@
 // share every K/V tile: the pass is bound by reading the cache once.
 //
 // Work unit = (split, kv head, sequence): one workgroup of 4 waves walks its
-// split's keys in tiles of 64, staged through LDS (K row-major, V transposed).
-// A wave owns 16-row query tiles (one query head each, rows j = 0..15).
-// Scores are computed transposed, S^T = K Q^T, with the MFMA A operand taken
-// from K in LDS and the B operand = Q^T held in registers; in that layout a
-// lane (r, g) holds 16 keys of query r, so softmax statistics need only the
-// xor-16/32 shuffles, and the probabilities are already the B operand of
-// O^T = V^T P^T.  Online softmax in fp32 (base 2), P rounded to BF16.
+// split's keys in tiles of 64.  Each tile is loaded into registers one tile
+// ahead, converted from the BF16 cache to FP16 and stored in LDS (K
+// row-major, V transposed).  A wave owns 16-row query tiles (one query head
+// each, rows j = 0..15).  Scores are computed transposed, S^T = K Q^T, with
+// the MFMA A operand taken from K in LDS and the B operand = Q^T (FP16) held
+// in registers; in that layout a lane (r, g) holds 16 keys of query r, so
+// softmax statistics need only xor-16/32 shuffles, and the FP16
+// probabilities are already the B operand of O^T = V^T P^T.  Online softmax
+// in fp32, base 2.
 //
 // Splits write unnormalised partials (m, l, o); the last workgroup of a
 // (sequence, kv head) to finish -- found with an integer atomic counter --
@@ -28,10 +30,14 @@ template <int D>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2) {
   constexpr int DT = D / 16;   // 16-wide d tiles
   constexpr int DK = D / 32;   // k32 steps over d
-  constexpr int KP = D + 8;    // padded K row (bf16)
-  constexpr int VP = KT + 8;   // padded V^T row (bf16)
+  constexpr int KP = D + 8;    // K row pitch (16-bit elements)
+  constexpr int VP = KT + 4;   // V^T row pitch (16-bit elements), 8-byte aligned rows
+  constexpr int KCH = KT * D / 8;        // K: 16-byte chunks (one key, 8 d) per tile
+  constexpr int VCH = (KT / 2) * D / 4;  // V: chunks of (2 keys, 4 d)
+  constexpr int KPT = KCH / 256, VPT = VCH / 256;
   __shared__ __align__(16) uint16_t Ks[KT * KP];
   __shared__ __align__(16) uint16_t Vt[D * VP];
+  __shared__ float sM[128], sInv[128];
   __shared__ int s_last;
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -47,8 +53,8 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
   const size_t unit = (size_t)b * a.Hkv + kvh;
   const int qstride = a.Hq * D;
 
-  // this wave's query tiles (at most 2: G <= 8)
-  const int nqt = (G - wave + 3) / 4;  // tiles wave, wave+4
+  // this wave's query tiles: wave, wave+4 (G <= 8)
+  const int nqt = (G - wave + 3) / 4;
   u32x4_t qf[2][DK];
   f32x4_t oacc[2][DT];
   float mrow[2], lrow[2];
@@ -66,25 +72,52 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
     }
   }
 
-  for (int kt0 = key_lo; kt0 < key_hi; kt0 += KT) {
-    __syncthreads();
-    // stage K (row-major) and V (transposed) for keys kt0 .. kt0+63; zero past key_hi
-    for (int c = tid; c < KT * D / 8; c += 256) {
-      const int kk = c / (D / 8), d0 = (c % (D / 8)) * 8;
-      const int key = kt0 + kk;
-      u32x4_t kv4 = u32x4_t{0, 0, 0, 0}, vv4 = u32x4_t{0, 0, 0, 0};
-      if (key < key_hi) {
-        kv4 = *reinterpret_cast<const u32x4_t *>(a.k_cache + (cache_base + key) * D + d0);
-        vv4 = *reinterpret_cast<const u32x4_t *>(a.v_cache + (cache_base + key) * D + d0);
-      }
-      *reinterpret_cast<u32x4_t *>(&Ks[kk * KP + d0]) = kv4;
+  u32x4_t kreg[KPT];
+  u32x2_t vreg[VPT][2];
+  auto load_tile = [&](int kt0) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        Vt[(d0 + 2 * e) * VP + kk] = (uint16_t)(vv4[e] & 0xffff);
-        Vt[(d0 + 2 * e + 1) * VP + kk] = (uint16_t)(vv4[e] >> 16);
-      }
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + 256 * i, kk = c / (D / 8), d0 = (c % (D / 8)) * 8, key = kt0 + kk;
+      kreg[i] = key < key_hi ? *reinterpret_cast<const u32x4_t *>(a.k_cache + (cache_base + key) * D + d0)
+                             : u32x4_t{0, 0, 0, 0};
     }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + 256 * i, kk = 2 * (c / (D / 4)), d0 = (c % (D / 4)) * 4, key = kt0 + kk;
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+        vreg[i][e] = key + e < key_hi
+                         ? *reinterpret_cast<const u32x2_t *>(a.v_cache + (cache_base + key + e) * D + d0)
+                         : u32x2_t{0, 0};
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int c = tid + 256 * i, kk = c / (D / 8), d0 = (c % (D / 8)) * 8;
+      const u32x4_t v = kreg[i];
+      *reinterpret_cast<u32x4_t *>(&Ks[kk * KP + d0]) =
+          u32x4_t{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
+    }
+#pragma unroll
+    for (int i = 0; i < VPT; ++i) {
+      const int c = tid + 256 * i, kk = 2 * (c / (D / 4)), d0 = (c % (D / 4)) * 4;
+      const uint32_t a0 = bf16x2_to_f16x2(vreg[i][0].x), a1 = bf16x2_to_f16x2(vreg[i][0].y);
+      const uint32_t b0 = bf16x2_to_f16x2(vreg[i][1].x), b1 = bf16x2_to_f16x2(vreg[i][1].y);
+      // (key kk, key kk+1) pairs for d0 .. d0+3
+      *reinterpret_cast<uint32_t *>(&Vt[(d0 + 0) * VP + kk]) = (a0 & 0xffff) | (b0 << 16);
+      *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * VP + kk]) = (a0 >> 16) | (b0 & 0xffff0000u);
+      *reinterpret_cast<uint32_t *>(&Vt[(d0 + 2) * VP + kk]) = (a1 & 0xffff) | (b1 << 16);
+      *reinterpret_cast<uint32_t *>(&Vt[(d0 + 3) * VP + kk]) = (a1 >> 16) | (b1 & 0xffff0000u);
+    }
+  };
+
+  load_tile(key_lo);
+  for (int kt0 = key_lo; kt0 < key_hi; kt0 += KT) {
+    __syncthreads();  // previous tile consumed
+    store_tile();
     __syncthreads();
+    if (kt0 + KT < key_hi) load_tile(kt0 + KT);  // in flight during the math below
 
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
@@ -97,10 +130,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
 #pragma unroll
         for (int kd = 0; kd < DK; ++kd) {
           const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(&Ks[(16 * ks + r) * KP + 32 * kd + 8 * g]);
-          st[ks] = mfma16x16x32(kf, qf[u][kd], st[ks]);
+          st[ks] = mfma16x16x32_f16(kf, qf[u][kd], st[ks]);
         }
       }
-      // mask + scale (log2 domain), tile max
       const int last_visible = n + r;  // row j = r
       float tmax = -INFINITY;
 #pragma unroll
@@ -133,9 +165,9 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
         // B operand for keys 32c + {4g+i} (slots 0-3) and 32c + 16 + {4g+i} (slots 4-7)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
-          pb[c] = u32x4_t{pack_bf16x2(p[2 * c][0], p[2 * c][1]), pack_bf16x2(p[2 * c][2], p[2 * c][3]),
-                          pack_bf16x2(p[2 * c + 1][0], p[2 * c + 1][1]),
-                          pack_bf16x2(p[2 * c + 1][2], p[2 * c + 1][3])};
+          pb[c] = u32x4_t{pack_f16x2(p[2 * c][0], p[2 * c][1]), pack_f16x2(p[2 * c][2], p[2 * c][3]),
+                          pack_f16x2(p[2 * c + 1][0], p[2 * c + 1][1]),
+                          pack_f16x2(p[2 * c + 1][2], p[2 * c + 1][3])};
       }
       psum += __shfl_xor(psum, 16);
       psum += __shfl_xor(psum, 32);
@@ -151,7 +183,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
           const uint16_t *vrow = &Vt[(16 * dt + r) * VP + 32 * c + 4 * g];
           const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
           const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 16);
-          oacc[u][dt] = mfma16x16x32(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb[c], oacc[u][dt]);
+          oacc[u][dt] = mfma16x16x32_f16(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb[c], oacc[u][dt]);
         }
     }
   }
@@ -180,27 +212,39 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
   // merge the splits in order: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
   const float *po0 = a.part_o + (unit * a.nsplit) * R * D;
   const float2 *pml0 = a.part_ml + (unit * a.nsplit) * R;
-  for (int idx = tid; idx < R * D; idx += 256) {
-    const int row = idx / D, d = idx % D;
+  if (tid < R) {
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, __builtin_nontemporal_load(&pml0[s * R + row].x));
-    float num = 0.f, den = 0.f;
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, __builtin_nontemporal_load(&pml0[s * R + tid].x));
+    float den = 0.f;
+    for (int s = 0; s < nsplit; ++s) {
+      const float ms = __builtin_nontemporal_load(&pml0[s * R + tid].x);
+      if (ms != -INFINITY) den += exp2f(ms - M) * __builtin_nontemporal_load(&pml0[s * R + tid].y);
+    }
+    sM[tid] = M;
+    sInv[tid] = 1.f / den;
+  }
+  __syncthreads();
+  for (int idx = tid; idx < R * D / 4; idx += 256) {
+    const int row = idx / (D / 4), d = (idx % (D / 4)) * 4;
+    const float M = sM[row];
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < nsplit; ++s) {
       const float ms = __builtin_nontemporal_load(&pml0[s * R + row].x);
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
-      num += w * __builtin_nontemporal_load(&po0[((size_t)s * R + row) * D + d]);
-      den += w * __builtin_nontemporal_load(&pml0[s * R + row].y);
+      const f32x4_t os = __builtin_nontemporal_load(
+          reinterpret_cast<const f32x4_t *>(po0 + ((size_t)s * R + row) * D + d));
+      if (ms != -INFINITY) acc += exp2f(ms - M) * os;
     }
+    acc *= sInv[row];
     const int j = row & 15, hq = kvh * G + (row >> 4);
-    a.o[(size_t)(b * 16 + j) * qstride + hq * D + d] = (uint16_t)f32_to_bf16(num / den);
+    *reinterpret_cast<u32x2_t *>(a.o + (size_t)(b * 16 + j) * qstride + hq * D + d) =
+        u32x2_t{pack_f16x2(acc[0], acc[1]), pack_f16x2(acc[2], acc[3])};
   }
   if (tid == 0) a.counters[unit] = 0;
 }
 
 int attention_split_len(int batch, int Hkv, int max_ctx) {
-  // aim for about 512 workgroups across the batch; splits are whole 64-key tiles
-  const long target = 512;
+  // aim for about 384 workgroups across the batch; splits are whole 64-key tiles
+  const long target = 384;
   long sl = ((long)batch * Hkv * max_ctx + target - 1) / target;
   sl = ((sl + KT - 1) / KT) * KT;
   if (sl < KT) sl = KT;

@@ -7,6 +7,8 @@
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
@@ -24,6 +26,40 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
 
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return f32_to_bf16(lo) | (f32_to_bf16(hi) << 16);
+}
+
+// two fp32 -> two fp16 (round to nearest even), packed low-first
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+  f16x2_t h = {(_Float16)lo, (_Float16)hi};
+  return __builtin_bit_cast(uint32_t, h);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t bits16) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// two bf16 (one dword) -> two fp16; exact for |v| >= 2^-14 and |v| < 65520
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+  return pack_f16x2(__uint_as_float(v << 16), __uint_as_float(v & 0xffff0000u));
+}
+
+// Four fp8 e4m3 codes (one dword) -> four fp16 (two dwords), exact.
+__device__ __forceinline__ u32x2_t fp8x4_to_f16x4(uint32_t codes) {
+  u32x2_t r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, false));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(codes, 1.0f, true));
+  return r;
+}
+
+// Eight e2m1 codes (one dword, low nibble first) times a power-of-two scale
+// -> eight fp16 (four dwords); exact while the scaled values stay fp16-normal.
+__device__ __forceinline__ u32x4_t fp4x8_to_f16x8(uint32_t codes, float scale) {
+  u32x4_t r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 3));
+  return r;
 }
 
 // Four fp8 e4m3 codes (one dword) -> four bf16 (two dwords), exact.
@@ -47,9 +83,15 @@ __device__ __forceinline__ u32x4_t fp4x8_to_bf16x8(uint32_t codes, float scale) 
   return r;
 }
 
+// D += A(16x32) * B(32x16); lane (r = lane%16, g = lane/16) supplies row r of
+// A and column r of B for the 8 k of its group, and receives D[4g..4g+3][r].
 __device__ __forceinline__ f32x4_t mfma16x16x32(u32x4_t a, u32x4_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                  __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4_t mfma16x16x32_f16(u32x4_t a, u32x4_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
 __device__ __forceinline__ void set_error(int32_t *err, int32_t bit) {

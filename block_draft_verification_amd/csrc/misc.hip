@@ -22,7 +22,9 @@ __global__ void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
   for (int c = threadIdx.x; c < H; c += blockDim.x) h[(size_t)m * H + c] = bf16_to_f32(row[c]);
 }
 
-// x = bf16(h / sqrt(mean(h^2) + eps) * gain); one wave per row.
+// x = h / sqrt(mean(h^2) + eps) * gain, rounded to FP16 (decoder layers) or
+// BF16 (lm_head input); one wave per row.
+template <bool BF16>
 __global__ void rmsnorm_kernel(const float *__restrict__ h, const float *__restrict__ gain, int M, int H,
                                float eps, uint16_t *__restrict__ x, float *__restrict__ dump) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -40,12 +42,21 @@ __global__ void rmsnorm_kernel(const float *__restrict__ h, const float *__restr
   for (int c = lane * 4; c < H; c += 256) {
     const f32x4_t v = *reinterpret_cast<const f32x4_t *>(hr + c);
     const f32x4_t gv = *reinterpret_cast<const f32x4_t *>(gain + c);
-    const uint32_t lo = pack_bf16x2(v[0] * rs * gv[0], v[1] * rs * gv[1]);
-    const uint32_t hi = pack_bf16x2(v[2] * rs * gv[2], v[3] * rs * gv[3]);
+    uint32_t lo, hi;
+    if constexpr (BF16) {
+      lo = pack_bf16x2(v[0] * rs * gv[0], v[1] * rs * gv[1]);
+      hi = pack_bf16x2(v[2] * rs * gv[2], v[3] * rs * gv[3]);
+    } else {
+      lo = pack_f16x2(v[0] * rs * gv[0], v[1] * rs * gv[1]);
+      hi = pack_f16x2(v[2] * rs * gv[2], v[3] * rs * gv[3]);
+    }
     *reinterpret_cast<u32x2_t *>(x + (size_t)m * H + c) = u32x2_t{lo, hi};
     if (dump) {
-      f32x4_t o = {bf16_to_f32(lo & 0xffff), bf16_to_f32(lo >> 16), bf16_to_f32(hi & 0xffff),
-                   bf16_to_f32(hi >> 16)};
+      f32x4_t o;
+      if constexpr (BF16)
+        o = f32x4_t{bf16_to_f32(lo & 0xffff), bf16_to_f32(lo >> 16), bf16_to_f32(hi & 0xffff), bf16_to_f32(hi >> 16)};
+      else
+        o = f32x4_t{f16_to_f32(lo & 0xffff), f16_to_f32(lo >> 16), f16_to_f32(hi & 0xffff), f16_to_f32(hi >> 16)};
       *reinterpret_cast<f32x4_t *>(dump + (size_t)m * H + c) = o;
     }
   }
@@ -67,7 +78,7 @@ __global__ void accept_kernel(const ArgmaxPart *__restrict__ part, int nparts, i
     float bv = -INFINITY;
     int32_t bi = 0x7fffffff;
     for (int p = tid; p < nparts; p += 256) {
-      const ArgmaxPart q = part[(size_t)p * M + m];
+      const ArgmaxPart q = part[(size_t)m * nparts + p];
       if (better(q.v, q.i, bv, bi)) {
         bv = q.v;
         bi = q.i;
@@ -129,9 +140,12 @@ hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(const float *h, const float *gain, int M, int H, float eps, uint16_t *x,
+hipError_t launch_rmsnorm(const float *h, const float *gain, int M, int H, float eps, uint16_t *x, int out_bf16,
                           float *dump, hipStream_t st) {
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3((M + 3) / 4), dim3(256), 0, st, h, gain, M, H, eps, x, dump);
+  if (out_bf16)
+    hipLaunchKernelGGL(rmsnorm_kernel<true>, dim3((M + 3) / 4), dim3(256), 0, st, h, gain, M, H, eps, x, dump);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<false>, dim3((M + 3) / 4), dim3(256), 0, st, h, gain, M, H, eps, x, dump);
   return hipGetLastError();
 }
 

@@ -28,10 +28,12 @@
  *   h += o Wo^T; x = RMSNorm(h); h += (SiLU(x Wg^T) * (x Wu^T)) Wd^T;
  *   final x = RMSNorm(h); logits = x E^T (or x Wlm^T for an untied head).
  *
- * Numerics of this implementation: weights decoded exactly to BF16; BF16
- * activations (normed x, q/k/v, the KV cache, attention output, SwiGLU
- * output, softmax weights); fp32 accumulation, residual stream, softmax
- * statistics and logits.
+ * Numerics of this implementation: FP8 / MXFP4 weights decoded exactly to
+ * FP16 and multiplied with FP16 activations (normed x, q, softmax weights,
+ * attention output, SwiGLU output); the KV cache is BF16 (converted exactly
+ * to FP16 inside attention); the lm_head multiplies its BF16 table with the
+ * final normed hidden state rounded to BF16; fp32 accumulation, residual
+ * stream, softmax statistics and logits.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host).
@@ -174,16 +176,17 @@ int spec_debug_set_dump(spec_ctx *ctx, float *hidden, float *logits);
 
 /* Test hook: one weight-streaming linear on its own,
  *   y[m][n] = sum_k x[m][k] * w(n, k)     (fp32 out, [M][N])
- * x bf16 [M][K]; w in format `wfmt` with scales as in spec_layer_weights
- * (scales NULL for BF16).  K and N multiples of 64 (MXFP4: K % 64 too).
+ * x: FP16 bits [M][K] for FP8 / MXFP4 weights, BF16 bits for BF16 weights;
+ * w in format `wfmt` with scales as in spec_layer_weights (scales NULL for
+ * BF16).  K and N multiples of 64.  Allocates its own split scratch.
  * Synchronous. */
 int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const void *w,
                       const void *scales, int32_t wfmt, float *y, hipStream_t stream);
 
 /* Test hook: block-causal GQA attention on its own for sequences 0..batch-1:
- * q bf16 [batch*16][Hq*D] (already rotated), K/V caches of ONE layer
+ * q FP16 [batch*16][Hq*D] (already rotated), BF16 K/V caches of ONE layer
  * ([max_batch][Hkv][max_ctx][D], block rows already stored at kv_len+j),
- * o bf16 [batch*16][Hq*D].  split_len = keys per split (multiple of 64), or
+ * o FP16 [batch*16][Hq*D].  split_len = keys per split (multiple of 64), or
  * 0 for the library's choice.  Synchronous. */
 int spec_debug_attention(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                          int32_t max_batch, int32_t max_ctx, const uint16_t *q,

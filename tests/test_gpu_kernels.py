@@ -13,12 +13,19 @@ from block_draft_verification_amd import WFMT_BF16, WFMT_FP8_E4M3_ROW, WFMT_MXFP
 pytestmark = pytest.mark.gpu
 
 
-def _x(M, K, seed):
-    return W.to_bf16_bits(np.random.default_rng(seed).standard_normal((M, K)).astype(np.float32))
+def _x(M, K, seed, f16=True):
+    """Activations as the linear kernel takes them: FP16 bits (FP8/MXFP4
+    weights) or BF16 bits (BF16 weights)."""
+    a = np.random.default_rng(seed).standard_normal((M, K)).astype(np.float32)
+    return a.astype(np.float16).view(np.uint16) if f16 else W.to_bf16_bits(a)
 
 
-def _check_linear(xb, wdeq, y):
-    x = decode_bf16(xb)
+def _dec(bits, f16=True):
+    return bits.view(np.float16).astype(np.float64) if f16 else decode_bf16(bits)
+
+
+def _check_linear(xb, wdeq, y, f16=True):
+    x = _dec(xb, f16)
     ref = x @ wdeq.T
     bound = np.abs(x) @ np.abs(wdeq).T                 # fp32 accumulation of exact products
     err = np.abs(y.astype(np.float64) - ref)
@@ -50,7 +57,7 @@ def test_linear_fp8_every_code_decodes():
     codes = np.zeros((N, 64), np.uint8)
     codes[:len(finite)] = finite[:, None]
     scales = np.ones(N, np.float32)
-    xb = W.to_bf16_bits(np.ones((16, 64), np.float32))
+    xb = np.ones((16, 64), np.float16).view(np.uint16)
     y = debug_linear(_dev(xb), _dev(codes), _dev(scales), WFMT_FP8_E4M3_ROW, N).cpu().numpy()
     assert np.array_equal(y[0, :len(finite)].astype(np.float64), 64 * decode_e4m3(finite))
 
@@ -68,9 +75,9 @@ def test_linear_mxfp4(M, N, K):
 @pytest.mark.parametrize("M,N,K", [(16, 1024, 896), (512, 640, 4096)])
 def test_linear_bf16(M, N, K):
     w = W.to_bf16_bits((np.random.default_rng(5).standard_normal((N, K)) * 0.02).astype(np.float32))
-    xb = _x(M, K, 3)
+    xb = _x(M, K, 3, f16=False)
     y = debug_linear(_dev(xb), _dev(w), None, WFMT_BF16, N).cpu().numpy()
-    _check_linear(xb, decode_bf16(w), y)
+    _check_linear(xb, decode_bf16(w), y, f16=False)
 
 
 NAN_BF16 = 0x7FC0
@@ -78,7 +85,7 @@ NAN_BF16 = 0x7FC0
 
 def _attn_case(B, Hq, Hkv, D, lens, max_ctx, seed, poison=True):
     rng = np.random.default_rng(seed)
-    q = W.to_bf16_bits(rng.standard_normal((B * 16, Hq * D)).astype(np.float32))
+    q = rng.standard_normal((B * 16, Hq * D)).astype(np.float16).view(np.uint16)
     K = W.to_bf16_bits(rng.standard_normal((B, Hkv, max_ctx, D)).astype(np.float32))
     V = W.to_bf16_bits(rng.standard_normal((B, Hkv, max_ctx, D)).astype(np.float32))
     if poison:  # slots past each block are never read
@@ -91,7 +98,7 @@ def _attn_case(B, Hq, Hkv, D, lens, max_ctx, seed, poison=True):
 def _attn_ref(q, K, V, lens, Hq, Hkv, D):
     out = []
     for b, n in enumerate(lens):
-        qb = decode_bf16(q[b * 16:(b + 1) * 16]).reshape(16, Hq, D)
+        qb = _dec(q[b * 16:(b + 1) * 16]).reshape(16, Hq, D)
         o = oracle.attention(qb, decode_bf16(K[b, :, :n + 16]), decode_bf16(V[b, :, :n + 16]), n, Hq // Hkv)
         out.append(o.reshape(16, Hq * D))
     return np.concatenate(out)
@@ -110,7 +117,7 @@ def test_attention(Hq, Hkv, D, lens, split):
     q, K, V = _attn_case(B, Hq, Hkv, D, lens, max_ctx, seed=sum(lens) + Hq)
     ln = torch.tensor(lens, dtype=torch.int32, device="cuda")
     o = debug_attention(_dev(q), _dev(K), _dev(V), ln, B, Hq, Hkv, D, split).cpu().numpy()
-    got = decode_bf16(o.view(np.uint16))
+    got = _dec(o.view(np.uint16))
     ref = _attn_ref(q, K, V, lens, Hq, Hkv, D)
     for h in range(Hq):
         blk = slice(h * D, (h + 1) * D)
