@@ -2,6 +2,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <algorithm>
 #include <new>
 #include <vector>
 
@@ -21,10 +22,10 @@ struct spec_ctx {
   uint16_t *x, *q, *ao, *act;
   float *part_o;
   float2 *part_ml;
-  int32_t *counters, *last_tau, *err;
+  int32_t *last_tau, *err;
   ArgmaxPart *amax;
   float2 *rope;
-  GemmWork wk;
+  float *rpart;  // split-K partials of the O and down projections [nsplit][Mmax][H]
   float *dump_hidden, *dump_logits;
   // launch timing of one kernel class (measurement hook)
   int prof_kind = SPEC_K_NONE;
@@ -120,12 +121,11 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
     if (u > units) units = u;
   }
   c->part_units = units;
-  size_t gemm_floats = 0, gemm_counters = 0;
+  size_t rfloats = 0;
   for (int b = 1; b <= kv->max_batch; ++b) {
-    size_t cnt = 0;
-    const size_t f = gemm_part_floats(b * 16, H, I, V, Hq, Hkv, D, &cnt);
-    if (f > gemm_floats) gemm_floats = f;
-    if (cnt > gemm_counters) gemm_counters = cnt;
+    const int M = b * 16;
+    const int s = std::max(residual_nsplit(M, H, Hq * D), residual_nsplit(M, H, I));
+    rfloats = std::max(rfloats, (size_t)s * M * H);
   }
 
   const size_t Mm = c->Mmax;
@@ -136,13 +136,12 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
                     Mm * I * 2,                      // act
                     (size_t)units * G * 16 * D * 4,  // part_o
                     (size_t)units * G * 16 * 8,      // part_ml
-                    (size_t)kv->max_batch * Hkv * 4, // counters
+                    256,                             // (unused)
                     (size_t)kv->max_batch * 4,       // last_tau
                     4,                               // err
                     (size_t)lm_parts(V) * Mm * 8,    // amax
                     (size_t)kv->max_ctx * (D / 2) * 8,  // rope
-                    gemm_floats * 4,                  // split-K partials
-                    gemm_counters * 4};               // split-K counters
+                    rfloats * 4};                     // residual split-K partials
   const int NS = sizeof(sizes) / sizeof(sizes[0]);
   size_t off[NS], total = 0;
   for (int i = 0; i < NS; ++i) {
@@ -161,14 +160,11 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   c->act = (uint16_t *)(base + off[4]);
   c->part_o = (float *)(base + off[5]);
   c->part_ml = (float2 *)(base + off[6]);
-  c->counters = (int32_t *)(base + off[7]);
   c->last_tau = (int32_t *)(base + off[8]);
   c->err = (int32_t *)(base + off[9]);
   c->amax = (ArgmaxPart *)(base + off[10]);
   c->rope = (float2 *)(base + off[11]);
-  c->wk.part = (float *)(base + off[12]);
-  c->wk.part_floats = gemm_floats;
-  c->wk.counters = (int32_t *)(base + off[13]);
+  c->rpart = (float *)(base + off[12]);
   c->dump_hidden = c->dump_logits = nullptr;
 
   // RoPE table: angle = p * theta^(-2i/D), in double, stored as fp32 (cos, sin)
@@ -180,10 +176,8 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
     }
   if (hipMemcpyAsync(c->rope, rope.data(), rope.size() * sizeof(float2), hipMemcpyHostToDevice, st) !=
           hipSuccess ||
-      launch_fill_i32(c->counters, kv->max_batch * Hkv, 0, st) != hipSuccess ||
       launch_fill_i32(c->last_tau, kv->max_batch, 0, st) != hipSuccess ||
       launch_fill_i32(c->err, 1, 0, st) != hipSuccess ||
-      launch_fill_i32(c->wk.counters, (int)gemm_counters + 1, 0, st) != hipSuccess ||
       hipStreamSynchronize(st) != hipSuccess) {
     (void)hipFree(c->ws);
     delete c;
@@ -208,7 +202,6 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
   aa.o = c->ao;
   aa.part_o = c->part_o;
   aa.part_ml = c->part_ml;
-  aa.counters = c->counters;
   aa.batch = batch;
   aa.Hq = Hq;
   aa.Hkv = Hkv;
@@ -220,17 +213,19 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     Timed t(c, SPEC_K_EMBED, st);
     CK(launch_embed(tokens, M, H, V, c->embed, c->h, c->kv.kv_len, max_ctx, c->err, st));
   }
+  const int ns_o = residual_nsplit(M, H, Hq * D), ns_d = residual_nsplit(M, H, I);
+  int pending = 0;  // splits of the last residual projection not yet added to h
   for (int l = 0; l < m.n_layers; ++l) {
     const spec_layer_weights &L = c->layers[l];
     uint16_t *kc = c->kv.k_cache + l * lstride, *vc = c->kv.v_cache + l * lstride;
     {
       Timed t(c, SPEC_K_RMSNORM, st);
-      CK(launch_rmsnorm(c->h, L.attn_norm, M, H, m.rms_eps, c->x, 0, nullptr, st));
+      CK(launch_norm(c->h, c->rpart, pending, L.attn_norm, M, H, m.rms_eps, c->x, 0, nullptr, st));
     }
     QkvOut qo{c->q, kc, vc, c->kv.kv_len, c->rope, Hq, Hkv, max_ctx};
     {
       Timed t(c, SPEC_K_QKV, st);
-      CK(launch_qkv(c->x, M, H, D, LinearW{L.w_qkv, L.s_qkv, SPEC_WFMT_FP8_E4M3_ROW}, qo, c->wk, st));
+      CK(launch_qkv(c->x, M, H, D, LinearW{L.w_qkv, L.s_qkv, SPEC_WFMT_FP8_E4M3_ROW}, qo, st));
     }
     aa.k_cache = kc;
     aa.v_cache = vc;
@@ -240,28 +235,30 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     }
     {
       Timed t(c, SPEC_K_OPROJ, st);
-      CK(launch_residual(c->ao, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, c->h, c->wk, st));
+      CK(launch_residual_partial(c->ao, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, c->rpart,
+                                 st));
     }
     {
       Timed t(c, SPEC_K_RMSNORM, st);
-      CK(launch_rmsnorm(c->h, L.mlp_norm, M, H, m.rms_eps, c->x, 0, nullptr, st));
+      CK(launch_norm(c->h, c->rpart, ns_o, L.mlp_norm, M, H, m.rms_eps, c->x, 0, nullptr, st));
     }
     {
       Timed t(c, SPEC_K_GATE_UP, st);
-      CK(launch_swiglu(c->x, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, c->act, c->wk, st));
+      CK(launch_swiglu(c->x, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, c->act, st));
     }
     {
       Timed t(c, SPEC_K_DOWN, st);
-      CK(launch_residual(c->act, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, c->h, c->wk, st));
+      CK(launch_residual_partial(c->act, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, c->rpart, st));
     }
+    pending = ns_d;
   }
   {
     Timed t(c, SPEC_K_RMSNORM, st);
-    CK(launch_rmsnorm(c->h, c->final_norm, M, H, m.rms_eps, c->x, 1, c->dump_hidden, st));
+    CK(launch_norm(c->h, c->rpart, pending, c->final_norm, M, H, m.rms_eps, c->x, 1, c->dump_hidden, st));
   }
   {
     Timed t(c, SPEC_K_LM_HEAD, st);
-    CK(launch_lm_argmax(c->x, M, V, H, c->lm_table, c->amax, c->dump_logits, c->wk, st));
+    CK(launch_lm_argmax(c->x, M, V, H, c->lm_table, c->amax, c->dump_logits, st));
   }
   {
     Timed t(c, SPEC_K_ACCEPT, st);
@@ -341,18 +338,9 @@ int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const 
     return SPEC_E_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (wfmt == SPEC_WFMT_FP8_E4M3_ROW && !aligned16(scales)))
     return SPEC_E_ARG;
-  const GemmPlan p = gemm_plan(M, N / 16, K / 64, 1, 8);
-  void *buf = nullptr;
-  const size_t cnt = (size_t)p.nb * p.mb + 1;
-  if (hipMalloc(&buf, p.part_floats * 4 + cnt * 4 + 256) != hipSuccess) return SPEC_E_NOMEM;
-  GemmWork wk{(float *)buf, p.part_floats, (int32_t *)((char *)buf + ((p.part_floats * 4 + 255) & ~(size_t)255))};
-  int rc = SPEC_OK;
-  if (launch_fill_i32(wk.counters, (int)cnt, 0, st) != hipSuccess ||
-      launch_linear_f32(x, M, N, K, LinearW{w, scales, wfmt}, y, wk, st) != hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess)
-    rc = SPEC_E_HIP;
-  (void)hipFree(buf);
-  return rc;
+  CK(launch_linear_f32(x, M, N, K, LinearW{w, scales, wfmt}, y, st));
+  CK(hipStreamSynchronize(st));
+  return SPEC_OK;
 }
 
 int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_batch, int32_t max_ctx,
@@ -377,15 +365,11 @@ int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int3
   a.nsplit = attn_nsplit(a.split_len, max_ctx);
   const size_t units = (size_t)batch * Hkv * a.nsplit, R = (size_t)(Hq / Hkv) * 16;
   void *buf = nullptr;
-  if (hipMalloc(&buf, units * R * D * 4 + units * R * 8 + (size_t)batch * Hkv * 4 + 256) != hipSuccess)
-    return SPEC_E_NOMEM;
+  if (hipMalloc(&buf, units * R * D * 4 + units * R * 8) != hipSuccess) return SPEC_E_NOMEM;
   a.part_o = (float *)buf;
   a.part_ml = (float2 *)((char *)buf + units * R * D * 4);
-  a.counters = (int32_t *)((char *)a.part_ml + units * R * 8);
   int rc = SPEC_OK;
-  if (launch_fill_i32(a.counters, batch * Hkv, 0, st) != hipSuccess || launch_attention(a, D, st) != hipSuccess ||
-      hipStreamSynchronize(st) != hipSuccess)
-    rc = SPEC_E_HIP;
+  if (launch_attention(a, D, st) != hipSuccess || hipStreamSynchronize(st) != hipSuccess) rc = SPEC_E_HIP;
   (void)hipFree(buf);
   return rc;
 }

@@ -8,7 +8,7 @@
 // share every K/V tile: the pass is bound by reading the cache once.
 //
 // Work unit = (split, kv head, sequence): one workgroup of 4 waves walks its
-// split's keys in tiles of 64.  Each tile is loaded into registers one tile
+// split's keys in tiles of 64.  Each tile is loaded into registers two tiles
 // ahead, converted from the BF16 cache to FP16 and stored in LDS (K
 // row-major, V transposed).  A wave owns 16-row query tiles (one query head
 // each, rows j = 0..15).  Scores are computed transposed, S^T = K Q^T, with
@@ -18,9 +18,10 @@
 // probabilities are already the B operand of O^T = V^T P^T.  Online softmax
 // in fp32, base 2.
 //
-// Splits write unnormalised partials (m, l, o); the last workgroup of a
-// (sequence, kv head) to finish -- found with an integer atomic counter --
-// merges them in split order, so the result does not depend on timing.
+// Splits write unnormalised partials (m, l, o); a second kernel merges them
+// in split order per (query head, sequence), so the result does not depend on
+// timing and no workgroup waits on another (a device-wide fence inside the
+// kernel would flush the XCD's L2).
 #include "common.h"
 #include "kernels.h"
 
@@ -37,8 +38,6 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
   constexpr int KPT = KCH / 256, VPT = VCH / 256;
   __shared__ __align__(16) uint16_t Ks[KT * KP];
   __shared__ __align__(16) uint16_t Vt[D * VP];
-  __shared__ float sM[128], sInv[128];
-  __shared__ int s_last;
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
@@ -72,13 +71,16 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
     }
   }
 
-  u32x4_t kreg[KPT];
-  u32x2_t vreg[VPT][2];
-  auto load_tile = [&](int kt0) {
+  struct TileRegs {
+    u32x4_t k[KPT];
+    u32x2_t v[VPT][2];
+  };
+  TileRegs ra, rb;
+  auto load_tile = [&](TileRegs &tr, int kt0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + 256 * i, kk = c / (D / 8), d0 = (c % (D / 8)) * 8, key = kt0 + kk;
-      kreg[i] = key < key_hi ? *reinterpret_cast<const u32x4_t *>(a.k_cache + (cache_base + key) * D + d0)
+      tr.k[i] = key < key_hi ? *reinterpret_cast<const u32x4_t *>(a.k_cache + (cache_base + key) * D + d0)
                              : u32x4_t{0, 0, 0, 0};
     }
 #pragma unroll
@@ -86,24 +88,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
       const int c = tid + 256 * i, kk = 2 * (c / (D / 4)), d0 = (c % (D / 4)) * 4, key = kt0 + kk;
 #pragma unroll
       for (int e = 0; e < 2; ++e)
-        vreg[i][e] = key + e < key_hi
+        tr.v[i][e] = key + e < key_hi
                          ? *reinterpret_cast<const u32x2_t *>(a.v_cache + (cache_base + key + e) * D + d0)
                          : u32x2_t{0, 0};
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&](const TileRegs &tr) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int c = tid + 256 * i, kk = c / (D / 8), d0 = (c % (D / 8)) * 8;
-      const u32x4_t v = kreg[i];
+      const u32x4_t v = tr.k[i];
       *reinterpret_cast<u32x4_t *>(&Ks[kk * KP + d0]) =
           u32x4_t{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
       const int c = tid + 256 * i, kk = 2 * (c / (D / 4)), d0 = (c % (D / 4)) * 4;
-      const uint32_t a0 = bf16x2_to_f16x2(vreg[i][0].x), a1 = bf16x2_to_f16x2(vreg[i][0].y);
-      const uint32_t b0 = bf16x2_to_f16x2(vreg[i][1].x), b1 = bf16x2_to_f16x2(vreg[i][1].y);
+      const uint32_t a0 = bf16x2_to_f16x2(tr.v[i][0].x), a1 = bf16x2_to_f16x2(tr.v[i][0].y);
+      const uint32_t b0 = bf16x2_to_f16x2(tr.v[i][1].x), b1 = bf16x2_to_f16x2(tr.v[i][1].y);
       // (key kk, key kk+1) pairs for d0 .. d0+3
       *reinterpret_cast<uint32_t *>(&Vt[(d0 + 0) * VP + kk]) = (a0 & 0xffff) | (b0 << 16);
       *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * VP + kk]) = (a0 >> 16) | (b0 & 0xffff0000u);
@@ -112,13 +114,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
     }
   };
 
-  load_tile(key_lo);
-  for (int kt0 = key_lo; kt0 < key_hi; kt0 += KT) {
-    __syncthreads();  // previous tile consumed
-    store_tile();
-    __syncthreads();
-    if (kt0 + KT < key_hi) load_tile(kt0 + KT);  // in flight during the math below
-
+  auto compute = [&](int kt0) {
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       if (u >= nqt) break;  // wave-uniform
@@ -186,6 +182,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
           oacc[u][dt] = mfma16x16x32_f16(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb[c], oacc[u][dt]);
         }
     }
+  };
+
+  load_tile(ra, key_lo);
+  if (key_lo + KT < key_hi) load_tile(rb, key_lo + KT);
+  // barriers only order LDS traffic (lds_barrier): a __syncthreads() here would
+  // also wait for the prefetched tile and serialise the pipeline
+  for (int kt0 = key_lo; kt0 < key_hi; kt0 += 2 * KT) {
+    lds_barrier();  // previous tile consumed
+    store_tile(ra);
+    lds_barrier();
+    if (kt0 + 2 * KT < key_hi) load_tile(ra, kt0 + 2 * KT);  // two tiles in flight during the math
+    compute(kt0);
+    if (kt0 + KT >= key_hi) break;
+    lds_barrier();
+    store_tile(rb);
+    lds_barrier();
+    if (kt0 + 3 * KT < key_hi) load_tile(rb, kt0 + 3 * KT);
+    compute(kt0 + KT);
   }
 
   // partials: row R = tile*16 + j, o[d] with d = 16dt + 4g + i held by lane (r = j, g)
@@ -201,50 +215,52 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
       *reinterpret_cast<f32x4_t *>(po + (size_t)row * D + 16 * dt + 4 * g) = oacc[u][dt];
     if (g == 0) pml[row] = make_float2(mrow[u], lrow[u]);
   }
+}
 
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&a.counters[unit], 1) == nsplit - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-
-  // merge the splits in order: o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s
+// o[b*16+j][hq*D + d] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the
+// splits of sequence b, in split order.  One workgroup per (query head, seq).
+template <int D>
+__global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  __shared__ float sM[16], sInv[16];
+  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int G = a.Hq / a.Hkv, kvh = hq / G, tq = hq % G, R = G * 16;
+  const int n = a.kv_len[b];
+  const int L = min(max(n, 0) + 16, a.max_ctx);
+  const int nsplit = (L + a.split_len - 1) / a.split_len;
+  const size_t unit = (size_t)b * a.Hkv + kvh;
   const float *po0 = a.part_o + (unit * a.nsplit) * R * D;
   const float2 *pml0 = a.part_ml + (unit * a.nsplit) * R;
-  if (tid < R) {
+  if (tid < 16) {
+    const int row = tq * 16 + tid;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, __builtin_nontemporal_load(&pml0[s * R + tid].x));
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pml0[s * R + row].x);
     float den = 0.f;
     for (int s = 0; s < nsplit; ++s) {
-      const float ms = __builtin_nontemporal_load(&pml0[s * R + tid].x);
-      if (ms != -INFINITY) den += exp2f(ms - M) * __builtin_nontemporal_load(&pml0[s * R + tid].y);
+      const float2 ml = pml0[s * R + row];
+      if (ml.x != -INFINITY) den += exp2f(ml.x - M) * ml.y;
     }
     sM[tid] = M;
     sInv[tid] = 1.f / den;
   }
   __syncthreads();
-  for (int idx = tid; idx < R * D / 4; idx += 256) {
-    const int row = idx / (D / 4), d = (idx % (D / 4)) * 4;
-    const float M = sM[row];
+  for (int idx = tid; idx < 16 * D / 4; idx += 256) {
+    const int j = idx / (D / 4), d = (idx % (D / 4)) * 4, row = tq * 16 + j;
+    const float M = sM[j];
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < nsplit; ++s) {
-      const float ms = __builtin_nontemporal_load(&pml0[s * R + row].x);
-      const f32x4_t os = __builtin_nontemporal_load(
-          reinterpret_cast<const f32x4_t *>(po0 + ((size_t)s * R + row) * D + d));
-      if (ms != -INFINITY) acc += exp2f(ms - M) * os;
+      const float ms = pml0[s * R + row].x;
+      if (ms != -INFINITY)
+        acc += exp2f(ms - M) * *reinterpret_cast<const f32x4_t *>(po0 + ((size_t)s * R + row) * D + d);
     }
-    acc *= sInv[row];
-    const int j = row & 15, hq = kvh * G + (row >> 4);
-    *reinterpret_cast<u32x2_t *>(a.o + (size_t)(b * 16 + j) * qstride + hq * D + d) =
+    acc *= sInv[j];
+    *reinterpret_cast<u32x2_t *>(a.o + (size_t)(b * 16 + j) * (a.Hq * D) + hq * D + d) =
         u32x2_t{pack_f16x2(acc[0], acc[1]), pack_f16x2(acc[2], acc[3])};
   }
-  if (tid == 0) a.counters[unit] = 0;
 }
 
 int attention_split_len(int batch, int Hkv, int max_ctx) {
-  // aim for about 384 workgroups across the batch; splits are whole 64-key tiles
-  const long target = 384;
+  // aim for about 768 workgroups across the batch; splits are whole 64-key tiles
+  const long target = 768;
   long sl = ((long)batch * Hkv * max_ctx + target - 1) / target;
   sl = ((sl + KT - 1) / KT) * KT;
   if (sl < KT) sl = KT;
@@ -255,9 +271,11 @@ hipError_t launch_attention(const AttnArgs &a, int D, hipStream_t st) {
   dim3 grid(a.nsplit, a.Hkv, a.batch);
   if (D == 64) {
     hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(256), 0, st, a, (float)(1.4426950408889634 / 8.0));
+    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(a.Hq, a.batch), dim3(256), 0, st, a);
   } else if (D == 128) {
     hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(256), 0, st, a,
                        (float)(1.4426950408889634 / 11.313708498984761));
+    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(a.Hq, a.batch), dim3(256), 0, st, a);
   } else {
     return hipErrorInvalidValue;
   }

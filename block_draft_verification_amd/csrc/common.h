@@ -94,6 +94,15 @@ __device__ __forceinline__ f32x4_t mfma16x16x32_f16(u32x4_t a, u32x4_t b, f32x4_
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+// Workgroup barrier without __syncthreads()'s global-memory fence, which on
+// gfx950 waits for every outstanding global load (vmcnt(0)) and so drains
+// any prefetch in flight.  Callers wait for the loads they need themselves;
+// this waits for the wave's own LDS operations, then meets the other waves.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt not waited on
+  __builtin_amdgcn_s_barrier();
+}
+
 __device__ __forceinline__ void set_error(int32_t *err, int32_t bit) {
   if (err) atomicOr(err, bit);
 }

@@ -37,19 +37,45 @@ template <> struct WRaw<SPEC_WFMT_FP8_E4M3_ROW> { u32x4_t c; };
 template <> struct WRaw<SPEC_WFMT_BF16> { u32x4_t lo, hi; };
 template <> struct WRaw<SPEC_WFMT_MXFP4> { u32x2_t c; uint32_t e; };
 
+// An empty asm that reads the registers: placed after the final wait, it
+// keeps the last (discarded) prefetch's destination registers allocated until
+// the load has landed, so the compiler cannot reuse them while it is in flight.
+__device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_FP8_E4M3_ROW> &r) { asm volatile("" ::"v"(r.c)); }
+__device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_BF16> &r) { asm volatile("" ::"v"(r.lo), "v"(r.hi)); }
+__device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_MXFP4> &r) { asm volatile("" ::"v"(r.c), "v"(r.e)); }
+
+// Weight loads are issued as plain vector loads the compiler does not track:
+// its wait analysis cannot count the LDS-DMA activation loads issued after
+// them and would otherwise wait for every outstanding load before each use.
+// The kernel waits for them explicitly (vmcnt) before touching the registers.
+__device__ __forceinline__ u32x4_t vload16(const void *p) {
+  u32x4_t v;
+  asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ u32x2_t vload8(const void *p) {
+  u32x2_t v;
+  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t vload1(const void *p) {
+  uint32_t v;
+  asm volatile("global_load_ubyte %0, %1, off" : "=v"(v) : "v"(p) : "memory");
+  return v;
+}
+
 template <int FMT>
 __device__ __forceinline__ void load_w(WRaw<FMT> &r, const uint8_t *__restrict__ w,
                                        const uint8_t *__restrict__ s, int row, int K, int k) {
   if constexpr (FMT == SPEC_WFMT_FP8_E4M3_ROW) {
-    r.c = *reinterpret_cast<const u32x4_t *>(w + (size_t)row * K + k);
+    r.c = vload16(w + (size_t)row * K + k);
   } else if constexpr (FMT == SPEC_WFMT_BF16) {
-    const u32x4_t *p = reinterpret_cast<const u32x4_t *>(reinterpret_cast<const uint16_t *>(w) +
-                                                         (size_t)row * K + k);
-    r.lo = p[0];
-    r.hi = p[1];
+    const uint16_t *p = reinterpret_cast<const uint16_t *>(w) + (size_t)row * K + k;
+    r.lo = vload16(p);
+    r.hi = vload16(p + 8);
   } else {
-    r.c = *reinterpret_cast<const u32x2_t *>(w + (size_t)row * (K / 2) + k / 2);
-    r.e = s[(size_t)row * (K / 32) + k / 32];
+    r.c = vload8(w + (size_t)row * (K / 2) + k / 2);
+    r.e = vload1(s + (size_t)row * (K / 32) + k / 32);
   }
 }
 
@@ -93,8 +119,6 @@ struct GemmArgs {
   const uint8_t *w, *s;
   int nb, mb;         // N blocks (4 units each), M blocks
   int spl;            // k steps (of 64) per split; gridDim.z splits
-  float *part;        // split partials
-  int32_t *counters;  // per output tile, zero between launches
 };
 
 // Linear workgroup id -> (N block, M block): the M blocks of one N block are
@@ -106,134 +130,139 @@ __device__ __forceinline__ bool tile_of(int L, int nb, int mb, int &n, int &m) {
   return n < nb;
 }
 
+// VMEM loads issued by one wave for one k step: activation rows straight to
+// LDS (16-byte lanes), then the weight rows of its NT tiles into registers.
+template <int FMT> constexpr int w_loads() { return FMT == SPEC_WFMT_FP8_E4M3_ROW ? 1 : 2; }
+
+// s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] in bits 3:0,
+// vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at "no wait").
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+
+// 16 bytes per lane from global memory straight into LDS: lane i of the wave
+// writes lds + 16 * i.  Kept out of the kernel templates (the host pass drops a
+// template kernel that names this builtin directly).
+__device__ __forceinline__ void lds_load16(const void *g, void *l) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)l, 16, 0, 0);
+}
+
+// Waves per SIMD the register budget is sized for: 2 where the accumulators
+// of a wave fit half the register file, else 1.
+template <int FMT, int NT, int MT> struct GemmOcc {
+  static constexpr int value = (NT * MT <= 32 && NT <= 4 && FMT != 3) ? 2 : 1;
+};
+
 template <bool F16, int FMT, int NT, int MT, class Epi>
-__global__ __launch_bounds__(256) void gemm_kernel(GemmArgs ga, Epi epi) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GemmOcc<FMT, NT, MT>::value, 8))) void
+gemm_kernel(GemmArgs ga, Epi epi) {
   constexpr int ROWS = 16 * MT;
-  constexpr int AP = 64 + 8;              // LDS row pitch in 16-bit elements (144 B)
-  constexpr int ACH = ROWS * 8;           // 16-byte chunks per activation tile
-  constexpr int APT = (ACH + 255) / 256;  // chunks per thread
-  __shared__ __align__(16) uint16_t As[2][ROWS * AP];
-  __shared__ int s_last;
+  constexpr int AJ = MT >= 2 ? MT / 2 : 1;  // 1 KB wave-loads per wave per stage
+  constexpr int SE = 4 * AJ * 512;          // 16-bit elements per stage (MT = 1: half is padding)
+  constexpr int NS = 3;                     // stages in flight
+  // activation tile: 16-byte chunk c of row r stored at chunk slot r*8 + (c ^ (r & 7))
+  __shared__ __align__(16) uint16_t As[NS * SE];
 
   int nblk, mblk;
   if (!tile_of(blockIdx.x, ga.nb, ga.mb, nblk, mblk)) return;  // whole workgroup
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = nblk * 4 + wave;
-  const bool active = unit < epi.units;  // wave-uniform
+  const bool active = unit < epi.units;  // wave-uniform; inactive waves compute on row 0 and store nothing
   const int m0 = mblk * ROWS;
   const int M = ga.M, K = ga.K, ksteps = K / 64;
-  const int z = blockIdx.z, nsplit = gridDim.z;
-  const int ks0 = z * ga.spl, ks1 = min(ks0 + ga.spl, ksteps);
+  const int ks0 = blockIdx.z * ga.spl, nsteps = min(ks0 + ga.spl, ksteps) - ks0;
 
-  u32x4_t areg[APT];
-  auto load_a = [&](int ks) {
+  // every wave issues AJ activation wave-loads and NT weight loads per step,
+  // so the vmcnt waits below are the same compile-time count for all waves
+  const uint16_t *agp[AJ];
 #pragma unroll
-    for (int i = 0; i < APT; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8, m = m0 + row;
-      if (c < ACH)
-        areg[i] = m < M ? *reinterpret_cast<const u32x4_t *>(ga.x + (size_t)m * K + ks * 64 + col)
-                        : u32x4_t{0, 0, 0, 0};
-    }
-  };
-  auto store_a = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < APT; ++i) {
-      const int c = tid + 256 * i, row = c >> 3, col = (c & 7) * 8;
-      if (c < ACH) *reinterpret_cast<u32x4_t *>(&As[buf][row * AP + col]) = areg[i];
-    }
-  };
-
+  for (int i = 0; i < AJ; ++i) {
+    const int P = (wave + 4 * i) * 64 + lane, row = P >> 3, c = (P & 7) ^ (row & 7);
+    const int m = (row < ROWS && m0 + row < M) ? m0 + row : 0;  // padding / rows past M read row 0
+    agp[i] = ga.x + (size_t)m * K + ks0 * 64 + c * 8;
+  }
   int wrow[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) wrow[t] = epi.row(active ? unit : 0, t) + r;
+
   f32x4_t acc[NT][MT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  WRaw<FMT> wc[NT];
-  if (active) {
+  auto compute = [&](int stage, const WRaw<FMT>(&wr)[NT]) {
+    __builtin_amdgcn_sched_barrier(0);  // keep the three unrolled steps from interleaving (register pressure)
+    u32x4_t w0[NT], w1[NT];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) load_w<FMT>(wc[t], ga.w, ga.s, wrow[t], K, ks0 * 64 + 16 * g);
-  }
-  load_a(ks0);
-  store_a(0);
-  __syncthreads();
-
-  for (int ks = ks0; ks < ks1; ++ks) {
-    const int buf = (ks - ks0) & 1;
-    const bool more = ks + 1 < ks1;
-    WRaw<FMT> wn[NT];
-    if (more) {
-      load_a(ks + 1);
-      if (active) {
+    for (int t = 0; t < NT; ++t) cvt_w<F16, FMT>(wr[t], w0[t], w1[t]);
+    const uint16_t *base = As + stage * SE;
+    auto read_a = [&](int mt, u32x4_t &a0, u32x4_t &a1) {
+      const int row = 16 * mt + r;
+      a0 = *reinterpret_cast<const u32x4_t *>(base + (row * 8 + ((2 * g) ^ (row & 7))) * 8);
+      a1 = *reinterpret_cast<const u32x4_t *>(base + (row * 8 + ((2 * g + 1) ^ (row & 7))) * 8);
+    };
+    // activation fragments of tile mt+1 are read while tile mt's MFMAs run
+    u32x4_t a0[2], a1[2];
+    read_a(0, a0[0], a1[0]);
 #pragma unroll
-        for (int t = 0; t < NT; ++t) load_w<FMT>(wn[t], ga.w, ga.s, wrow[t], K, (ks + 1) * 64 + 16 * g);
+    for (int mt = 0; mt < MT; ++mt) {
+      if (mt + 1 < MT) read_a(mt + 1, a0[(mt + 1) & 1], a1[(mt + 1) & 1]);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        acc[t][mt] = mma<F16>(w0[t], a0[mt & 1], acc[t][mt]);
+        acc[t][mt] = mma<F16>(w1[t], a1[mt & 1], acc[t][mt]);
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (active) {
-      u32x4_t w0[NT], w1[NT];
+  };
+  // Per k step s: activations for step s+2 go straight to LDS stage (s+2)%3,
+  // weights for step s+1 into the "next" registers, then step s is computed.
+  auto issue_a_to = [&](int step, int stage) {
 #pragma unroll
-      for (int t = 0; t < NT; ++t) cvt_w<F16, FMT>(wc[t], w0[t], w1[t]);
+    for (int i = 0; i < AJ; ++i) lds_load16(agp[i] + step * 64, As + stage * SE + (wave + 4 * i) * 512);
+  };
+  auto issue_a = [&](int step) { issue_a_to(step, step % NS); };
+  auto issue_w = [&](WRaw<FMT>(&wr)[NT], int step) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const uint16_t *ap = &As[buf][(16 * mt + r) * AP + 16 * g];
-        const u32x4_t a0 = *reinterpret_cast<const u32x4_t *>(ap);
-        const u32x4_t a1 = *reinterpret_cast<const u32x4_t *>(ap + 8);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          acc[t][mt] = mma<F16>(w0[t], a0, acc[t][mt]);
-          acc[t][mt] = mma<F16>(w1[t], a1, acc[t][mt]);
-        }
-      }
-    }
-    if (more) {
-      store_a(buf ^ 1);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) wc[t] = wn[t];
-    }
-    __syncthreads();
+    for (int t = 0; t < NT; ++t) load_w<FMT>(wr[t], ga.w, ga.s, wrow[t], K, (ks0 + step) * 64 + 16 * g);
+  };
+  // VMEM order per step: [W(s+1)] then [A(s+2)].  Loads complete in issue
+  // order, so waiting for the weight registers (at the copy below) never waits
+  // for the younger activation loads, which stay two steps ahead.
+  // Two weight register sets alternate (the loop is unrolled by two) so no
+  // register copy of a load destination is ever needed: a copy would be
+  // placed before the wait that covers the load.  Tail steps re-load the last
+  // step into a stage nobody reads.  Issue order per step: [W(s+1)] [A(s+2)].
+  // At the top of step s the outstanding loads are, oldest first, A(s), W(s),
+  // A(s+1): waiting until at most AJ remain leaves only A(s+1) in flight.
+  WRaw<FMT> wa[NT], wb[NT];
+  issue_w(wa, 0);
+  issue_a(0);
+  issue_a(min(1, nsteps - 1));
+  for (int s = 0; s < nsteps; s += 2) {
+    WAIT_VMCNT(AJ);
+    lds_barrier();  // stage s visible to all waves; stage (s+2)%3 = (s-1)%3 free again
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(wb, min(s + 1, nsteps - 1));
+    issue_a_to(min(s + 2, nsteps - 1), (s + 2) % NS);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(s % NS, wa);
+    WAIT_VMCNT(AJ);
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_w(wa, min(s + 2, nsteps - 1));
+    issue_a_to(min(s + 3, nsteps - 1), (s + 3) % NS);
+    __builtin_amdgcn_sched_barrier(0);
+    if (s + 1 < nsteps) compute((s + 1) % NS, wb);
   }
-
-  if (nsplit == 1) {
-    if (active) epi.template store<NT, MT>(unit, m0, M, r, g, acc);
-    return;
+  WAIT_VMCNT(0);  // nothing may still be landing in LDS or registers past this point
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    hold(wa[t]);
+    hold(wb[t]);
   }
-  // split K: partials in the accumulator layout, then the last arriver reduces
-  constexpr int PER_WAVE = NT * MT * 256;
-  const int tile = nblk * ga.mb + mblk, ntiles = ga.nb * ga.mb;
-  if (active) {
-    float *pw = ga.part + ((size_t)(z * ntiles + tile) * 4 + wave) * PER_WAVE;
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        *reinterpret_cast<f32x4_t *>(pw + (t * MT + mt) * 256 + lane * 4) = acc[t][mt];
-  }
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) s_last = atomicAdd(&ga.counters[tile], 1) == nsplit - 1;
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (active) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    for (int zz = 0; zz < nsplit; ++zz) {
-      const float *pz = ga.part + ((size_t)(zz * ntiles + tile) * 4 + wave) * PER_WAVE;
-#pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-          acc[t][mt] += __builtin_nontemporal_load(
-              reinterpret_cast<const f32x4_t *>(pz + (t * MT + mt) * 256 + lane * 4));
-    }
-    epi.template store<NT, MT>(unit, m0, M, r, g, acc);
-  }
-  if (tid == 0) ga.counters[tile] = 0;
+  if (active) epi.template store<NT, MT>(unit, m0, M, r, g, acc, blockIdx.z);
 }
 
 __device__ __forceinline__ void store_f16x4(uint16_t *p, float a, float b, float c, float d) {
@@ -257,7 +286,7 @@ struct EpiF32 {  // y = acc * scale, fp32 out
   const float *scale;
   __device__ int row(int unit, int t) const { return unit * 16 * NTc + 16 * t; }
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT]) const {
+  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT], int z) const {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -268,23 +297,23 @@ struct EpiF32 {  // y = acc * scale, fp32 out
   }
 };
 
+// Split-K partial of a residual projection: P[z][m][n] = acc * scale.  The
+// next RMSNorm adds the partials of every split to h in split order.
 template <int NTc>
-struct EpiResidual {  // h += acc * scale
+struct EpiPartial {
   int units, N;
-  float *h;
+  float *part;  // [nsplit][M][N]
   const float *scale;
   __device__ int row(int unit, int t) const { return unit * 16 * NTc + 16 * t; }
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT]) const {
+  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT], int z) const {
+    float *pz = part + (size_t)z * M * N;
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int m = m0 + 16 * mt + r, n = row(unit, t) + 4 * g;
-        if (m < M) {
-          f32x4_t *p = reinterpret_cast<f32x4_t *>(h + (size_t)m * N + n);
-          *p = *p + acc[t][mt] * row_scale4(scale, n);
-        }
+        if (m < M) *reinterpret_cast<f32x4_t *>(pz + (size_t)m * N + n) = acc[t][mt] * row_scale4(scale, n);
       }
   }
 };
@@ -299,7 +328,7 @@ struct EpiQkv {
   QkvOut o;
   __device__ int row(int unit, int t) const { return unit * 16 * NTc + 16 * t; }
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT]) const {
+  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT], int z) const {
     constexpr int D = 16 * NT, HALF = D / 2;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -356,7 +385,7 @@ struct EpiSwiglu {
     return t < NTc / 2 ? unit * 8 * NTc + 16 * t : I + unit * 8 * NTc + 16 * (t - NTc / 2);
   }
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT]) const {
+  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT], int z) const {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = m0 + 16 * mt + r;
@@ -383,7 +412,7 @@ struct EpiArgmax {
   float *logits;     // optional [M][V]
   __device__ int row(int unit, int t) const { return unit * 16 * NTc + 16 * t; }
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT]) const {
+  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT], int z) const {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = m0 + 16 * mt + r;
@@ -422,22 +451,33 @@ struct EpiArgmax {
 
 // ---------------------------------------------------------------- planning
 
-GemmPlan gemm_plan(int M, int units, int ksteps, int NT, int maxMT) {
+GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split) {
   GemmPlan p;
-  p.MT = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
-  if (p.MT > maxMT) p.MT = maxMT;
+  p.MT = MT;
   p.nb = (units + 3) / 4;
-  p.mb = (M + 16 * p.MT - 1) / (16 * p.MT);
+  p.mb = (M + 16 * MT - 1) / (16 * MT);
   const int tiles = p.nb * p.mb;
-  // split K until about 512 workgroups, keeping >= 4 k steps per split
-  int s = (512 + tiles - 1) / tiles;
+  // split K (residual projections only) until about 256 workgroups, >= 4 k steps per split
+  int s = allow_split ? (256 + tiles - 1) / tiles : 1;
   if (s > ksteps / 4) s = ksteps / 4;
   if (s < 1) s = 1;
   p.spl = (ksteps + s - 1) / s;
   p.nsplit = (ksteps + p.spl - 1) / p.spl;  // every split non-empty
-  p.part_floats = p.nsplit > 1 ? (size_t)p.nsplit * tiles * 4 * NT * p.MT * 256 : 0;
   p.grid_x = 8 * ((p.nb + 7) / 8) * p.mb;
   return p;
+}
+
+// activation rows per workgroup: enough workgroups first, then wide tiles
+static int pick_mt(int M, int units, int maxMT) {
+  int mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  if (mt > maxMT) mt = maxMT;
+  while (mt > 2 && ((units + 3) / 4) * ((M + 16 * mt - 1) / (16 * mt)) < 128) mt /= 2;
+  return mt;
+}
+
+int residual_nsplit(int M, int N, int K) {
+  const int units = M <= 32 ? N / 16 : N / 64;
+  return gemm_plan(M, units, K / 64, pick_mt(M, units, 8), true).nsplit;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -461,18 +501,22 @@ static hipError_t go_m(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hi
   }
 }
 
-template <int NT, class Epi>
-static hipError_t run(const uint16_t *x, int M, int K, const LinearW &w, Epi epi, const GemmWork &wk,
+// FMTS: bit (1 << format) set for each weight format a call site may pass;
+// only those kernels are instantiated.
+constexpr unsigned kFp8 = 1u << SPEC_WFMT_FP8_E4M3_ROW, kMx4 = 1u << SPEC_WFMT_MXFP4, kBf16 = 1u << SPEC_WFMT_BF16;
+
+template <int NT, unsigned FMTS, class Epi>
+static hipError_t run(const uint16_t *x, int M, int K, const LinearW &w, Epi epi, bool allow_split,
                       hipStream_t st) {
-  const GemmPlan p = gemm_plan(M, epi.units, K / 64, NT, NT > 4 ? 4 : 8);
-  if (p.part_floats > wk.part_floats) return hipErrorInvalidValue;
+  const GemmPlan p = gemm_plan(M, epi.units, K / 64, pick_mt(M, epi.units, NT > 4 ? 4 : 8), allow_split);
   GemmArgs ga{x, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
-              p.nb, p.mb, p.spl, wk.part, wk.counters};
-  switch (w.wfmt) {
-    case SPEC_WFMT_FP8_E4M3_ROW: return go_m<true, SPEC_WFMT_FP8_E4M3_ROW, NT>(p, ga, epi, st);
-    case SPEC_WFMT_MXFP4: return go_m<true, SPEC_WFMT_MXFP4, NT>(p, ga, epi, st);
-    case SPEC_WFMT_BF16: return go_m<false, SPEC_WFMT_BF16, NT>(p, ga, epi, st);
-  }
+              p.nb, p.mb, p.spl};
+  if constexpr ((FMTS & kFp8) != 0)
+    if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW) return go_m<true, SPEC_WFMT_FP8_E4M3_ROW, NT>(p, ga, epi, st);
+  if constexpr ((FMTS & kMx4) != 0)
+    if (w.wfmt == SPEC_WFMT_MXFP4) return go_m<true, SPEC_WFMT_MXFP4, NT>(p, ga, epi, st);
+  if constexpr ((FMTS & kBf16) != 0)
+    if (w.wfmt == SPEC_WFMT_BF16) return go_m<false, SPEC_WFMT_BF16, NT>(p, ga, epi, st);
   return hipErrorInvalidValue;
 }
 
@@ -480,53 +524,30 @@ static const float *fp8_scale(const LinearW &w) {
   return w.wfmt == SPEC_WFMT_FP8_E4M3_ROW ? reinterpret_cast<const float *>(w.s) : nullptr;
 }
 
-hipError_t launch_linear_f32(const uint16_t *x, int M, int N, int K, LinearW w, float *y, const GemmWork &wk,
-                             hipStream_t st) {
-  return run<1>(x, M, K, w, EpiF32<1>{N / 16, N, y, fp8_scale(w)}, wk, st);
+hipError_t launch_linear_f32(const uint16_t *x, int M, int N, int K, LinearW w, float *y, hipStream_t st) {
+  return run<1, kFp8 | kMx4 | kBf16>(x, M, K, w, EpiF32<1>{N / 16, N, y, fp8_scale(w)}, false, st);
 }
 
-hipError_t launch_residual(const uint16_t *x, int M, int N, int K, LinearW w, float *h, const GemmWork &wk,
-                           hipStream_t st) {
-  if (M <= 32) return run<1>(x, M, K, w, EpiResidual<1>{N / 16, N, h, fp8_scale(w)}, wk, st);
-  return run<4>(x, M, K, w, EpiResidual<4>{N / 64, N, h, fp8_scale(w)}, wk, st);
+hipError_t launch_residual_partial(const uint16_t *x, int M, int N, int K, LinearW w, float *part, hipStream_t st) {
+  if (M <= 32) return run<1, kFp8 | kMx4>(x, M, K, w, EpiPartial<1>{N / 16, N, part, fp8_scale(w)}, true, st);
+  return run<4, kFp8 | kMx4>(x, M, K, w, EpiPartial<4>{N / 64, N, part, fp8_scale(w)}, true, st);
 }
 
-hipError_t launch_swiglu(const uint16_t *x, int M, int H, int I, LinearW w, uint16_t *a, const GemmWork &wk,
-                         hipStream_t st) {
-  if (M <= 32) return run<2>(x, M, H, w, EpiSwiglu<2>{I / 16, I, fp8_scale(w), a}, wk, st);
-  return run<4>(x, M, H, w, EpiSwiglu<4>{I / 32, I, fp8_scale(w), a}, wk, st);
+hipError_t launch_swiglu(const uint16_t *x, int M, int H, int I, LinearW w, uint16_t *a, hipStream_t st) {
+  if (M <= 32) return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2>{I / 16, I, fp8_scale(w), a}, false, st);
+  return run<4, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<4>{I / 32, I, fp8_scale(w), a}, false, st);
 }
 
-hipError_t launch_qkv(const uint16_t *x, int M, int H, int D, LinearW w, QkvOut o, const GemmWork &wk,
-                      hipStream_t st) {
+hipError_t launch_qkv(const uint16_t *x, int M, int H, int D, LinearW w, QkvOut o, hipStream_t st) {
   if (w.wfmt != SPEC_WFMT_FP8_E4M3_ROW) return hipErrorInvalidValue;
   const float *s = reinterpret_cast<const float *>(w.s);
-  if (D == 64) return run<4>(x, M, H, w, EpiQkv<4>{o.Hq + 2 * o.Hkv, s, o}, wk, st);
-  if (D == 128) return run<8>(x, M, H, w, EpiQkv<8>{o.Hq + 2 * o.Hkv, s, o}, wk, st);
+  if (D == 64) return run<4, kFp8>(x, M, H, w, EpiQkv<4>{o.Hq + 2 * o.Hkv, s, o}, false, st);
+  if (D == 128) return run<8, kFp8>(x, M, H, w, EpiQkv<8>{o.Hq + 2 * o.Hkv, s, o}, false, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,
-                            float *logits_dump, const GemmWork &wk, hipStream_t st) {
-  return run<4>(x, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16}, EpiArgmax<4>{V / 64, V, part, logits_dump},
-                wk, st);
-}
-
-// Partial-buffer floats and counters the launches above may need for M rows.
-size_t gemm_part_floats(int M, int H, int I, int V, int Hq, int Hkv, int D, size_t *counters) {
-  struct S { int units, ksteps, NT; } shapes[] = {
-      {M <= 32 ? H / 16 : H / 64, (Hq * D) / 64, M <= 32 ? 1 : 4},  // O-proj
-      {M <= 32 ? H / 16 : H / 64, I / 64, M <= 32 ? 1 : 4},          // down
-      {M <= 32 ? I / 16 : I / 32, H / 64, M <= 32 ? 2 : 4},          // gate/up
-      {Hq + 2 * Hkv, H / 64, D / 16},                                // QKV
-      {V / 64, H / 64, 4},                                            // lm_head
-  };
-  size_t mx = 0, cnt = 0;
-  for (const S &s : shapes) {
-    const GemmPlan p = gemm_plan(M, s.units, s.ksteps, s.NT, s.NT > 4 ? 4 : 8);
-    if (p.part_floats > mx) mx = p.part_floats;
-    if ((size_t)p.nb * p.mb > cnt) cnt = (size_t)p.nb * p.mb;
-  }
-  *counters = cnt;
-  return mx;
+                            float *logits_dump, hipStream_t st) {
+  return run<4, kBf16>(x, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16}, EpiArgmax<4>{V / 64, V, part, logits_dump},
+                false, st);
 }

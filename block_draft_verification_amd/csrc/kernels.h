@@ -15,21 +15,13 @@ struct LinearW {
 // workgroup, nb x mb output tiles, K split into nsplit pieces of spl steps.
 struct GemmPlan {
   int MT, nb, mb, spl, nsplit, grid_x;
-  size_t part_floats;
 };
-GemmPlan gemm_plan(int M, int units, int ksteps, int NT, int maxMT);
-
-// split-K scratch: fp32 partials and per-tile counters (zero between launches)
-struct GemmWork {
-  float *part;
-  size_t part_floats;
-  int32_t *counters;
-};
-size_t gemm_part_floats(int M, int H, int I, int V, int Hq, int Hkv, int D, size_t *counters);
+GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split);
+// splits the residual projection [M][K] x [N][K]^T will use (partials to reduce)
+int residual_nsplit(int M, int N, int K);
 
 // y fp32 [M][N] (test hook)
-hipError_t launch_linear_f32(const uint16_t *x, int M, int N, int K, LinearW w, float *y, const GemmWork &wk,
-                             hipStream_t st);
+hipError_t launch_linear_f32(const uint16_t *x, int M, int N, int K, LinearW w, float *y, hipStream_t st);
 
 // QKV projection + RoPE; q -> q_out bf16 [M][Hq*D]; k, v -> caches at slot kv_len[b] + j.
 struct QkvOut {
@@ -40,21 +32,19 @@ struct QkvOut {
   int Hq, Hkv, max_ctx;
 };
 // q (FP16) and k, v (BF16 cache) from FP16 x
-hipError_t launch_qkv(const uint16_t *x, int M, int H, int D, LinearW w, QkvOut o, const GemmWork &wk,
-                      hipStream_t st);
+hipError_t launch_qkv(const uint16_t *x, int M, int H, int D, LinearW w, QkvOut o, hipStream_t st);
 
 // a[m][n] = fp16(SiLU(x Wg^T) * (x Wu^T)), W = [gate; up] with I rows each
-hipError_t launch_swiglu(const uint16_t *x, int M, int H, int I, LinearW w, uint16_t *a, const GemmWork &wk,
-                         hipStream_t st);
+hipError_t launch_swiglu(const uint16_t *x, int M, int H, int I, LinearW w, uint16_t *a, hipStream_t st);
 
-// h[m][n] += (x W^T)[m][n], h fp32 [M][N]
-hipError_t launch_residual(const uint16_t *x, int M, int N, int K, LinearW w, float *h, const GemmWork &wk,
-                           hipStream_t st);
+// part[z][m][n] = split z of (x W^T)[m][n] (fp32); residual_nsplit() splits.
+// The following launch_norm adds them to h.
+hipError_t launch_residual_partial(const uint16_t *x, int M, int N, int K, LinearW w, float *part, hipStream_t st);
 
 // lm_head (BF16 x, BF16 table) + per-wave argmax partials: part[m][p] over vocab slices of 64
 struct ArgmaxPart { float v; int32_t i; };
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,
-                            float *logits_dump, const GemmWork &wk, hipStream_t st);
+                            float *logits_dump, hipStream_t st);
 inline int lm_parts(int V) { return V / 64; }
 
 // ---- attention ----
@@ -65,18 +55,19 @@ struct AttnArgs {
   uint16_t *o;                       // FP16 [M][Hq*D]
   float *part_o;                     // [B][Hkv][nsplit][G*16][D]
   float2 *part_ml;                   // [B][Hkv][nsplit][G*16]
-  int32_t *counters;                 // [B][Hkv], zero between launches
   int batch, Hq, Hkv, max_ctx, split_len, nsplit;
 };
+// split attention (partials) followed by the merge kernel (writes o)
 hipError_t launch_attention(const AttnArgs &a, int D, hipStream_t st);
 int attention_split_len(int batch, int Hkv, int max_ctx);
 
 // ---- small kernels ----
 hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16_t *table, float *h,
                         const int32_t *kv_len, int max_ctx, int32_t *err, hipStream_t st);
+// h += part[0] + ... + part[nsplit-1] (in that order; nsplit may be 0), then
 // x = RMSNorm(h) * gain, written as FP16 (out_bf16 = 0) or BF16 (out_bf16 = 1)
-hipError_t launch_rmsnorm(const float *h, const float *gain, int M, int H, float eps, uint16_t *x, int out_bf16,
-                          float *dump, hipStream_t st);
+hipError_t launch_norm(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
+                       uint16_t *x, int out_bf16, float *dump, hipStream_t st);
 hipError_t launch_accept(const ArgmaxPart *part, int nparts, int M, const int32_t *tokens, int batch,
                          int32_t *accept_len, int32_t *bonus, int32_t *argmax, int32_t *last_tau,
                          hipStream_t st);

@@ -22,33 +22,44 @@ __global__ void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
   for (int c = threadIdx.x; c < H; c += blockDim.x) h[(size_t)m * H + c] = bf16_to_f32(row[c]);
 }
 
-// x = h / sqrt(mean(h^2) + eps) * gain, rounded to FP16 (decoder layers) or
-// BF16 (lm_head input); one wave per row.
+// h += part[0] + ... + part[ns-1] (split-K partials of the projection that
+// just ran, added in split order), then x = h / sqrt(mean(h^2) + eps) * gain
+// rounded to FP16 (decoder layers) or BF16 (lm_head input).  One wave per row.
 template <bool BF16>
-__global__ void rmsnorm_kernel(const float *__restrict__ h, const float *__restrict__ gain, int M, int H,
-                               float eps, uint16_t *__restrict__ x, float *__restrict__ dump) {
+__global__ void norm_kernel(float *__restrict__ h, const float *__restrict__ part, int ns,
+                            const float *__restrict__ gain, int M, int H, float eps, uint16_t *__restrict__ x,
+                            float *__restrict__ dump) {
   const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (m >= M) return;
-  const float *hr = h + (size_t)m * H;
+  float *hr = h + (size_t)m * H;
   float ss = 0.f;
-  for (int c = lane * 4; c < H; c += 256) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t *>(hr + c);
-    ss += v[0] * v[0] + v[1] * v[1] + v[2] * v[2] + v[3] * v[3];
+  const int nc = (H + 255) / 256;
+  for (int i = 0; i < nc; ++i) {
+    const int c = lane * 4 + 256 * i;
+    f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    if (c < H) {
+      t = *reinterpret_cast<const f32x4_t *>(hr + c);
+      for (int s = 0; s < ns; ++s) t += *reinterpret_cast<const f32x4_t *>(part + ((size_t)s * M + m) * H + c);
+      if (ns) *reinterpret_cast<f32x4_t *>(hr + c) = t;
+    }
+    ss += t[0] * t[0] + t[1] * t[1] + t[2] * t[2] + t[3] * t[3];
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   const float rs = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int c = lane * 4; c < H; c += 256) {
-    const f32x4_t v = *reinterpret_cast<const f32x4_t *>(hr + c);
+  for (int i = 0; i < nc; ++i) {
+    const int c = lane * 4 + 256 * i;
+    if (c >= H) continue;
+    const f32x4_t t = *reinterpret_cast<const f32x4_t *>(hr + c);  // written above by this lane
     const f32x4_t gv = *reinterpret_cast<const f32x4_t *>(gain + c);
     uint32_t lo, hi;
     if constexpr (BF16) {
-      lo = pack_bf16x2(v[0] * rs * gv[0], v[1] * rs * gv[1]);
-      hi = pack_bf16x2(v[2] * rs * gv[2], v[3] * rs * gv[3]);
+      lo = pack_bf16x2(t[0] * rs * gv[0], t[1] * rs * gv[1]);
+      hi = pack_bf16x2(t[2] * rs * gv[2], t[3] * rs * gv[3]);
     } else {
-      lo = pack_f16x2(v[0] * rs * gv[0], v[1] * rs * gv[1]);
-      hi = pack_f16x2(v[2] * rs * gv[2], v[3] * rs * gv[3]);
+      lo = pack_f16x2(t[0] * rs * gv[0], t[1] * rs * gv[1]);
+      hi = pack_f16x2(t[2] * rs * gv[2], t[3] * rs * gv[3]);
     }
     *reinterpret_cast<u32x2_t *>(x + (size_t)m * H + c) = u32x2_t{lo, hi};
     if (dump) {
@@ -140,12 +151,14 @@ hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(const float *h, const float *gain, int M, int H, float eps, uint16_t *x, int out_bf16,
-                          float *dump, hipStream_t st) {
+hipError_t launch_norm(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
+                       uint16_t *x, int out_bf16, float *dump, hipStream_t st) {
   if (out_bf16)
-    hipLaunchKernelGGL(rmsnorm_kernel<true>, dim3((M + 3) / 4), dim3(256), 0, st, h, gain, M, H, eps, x, dump);
+    hipLaunchKernelGGL(norm_kernel<true>, dim3((M + 3) / 4), dim3(256), 0, st, h, part, nsplit, gain, M, H, eps, x,
+                       dump);
   else
-    hipLaunchKernelGGL(rmsnorm_kernel<false>, dim3((M + 3) / 4), dim3(256), 0, st, h, gain, M, H, eps, x, dump);
+    hipLaunchKernelGGL(norm_kernel<false>, dim3((M + 3) / 4), dim3(256), 0, st, h, part, nsplit, gain, M, H, eps,
+                       x, dump);
   return hipGetLastError();
 }
 

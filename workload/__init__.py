@@ -183,8 +183,48 @@ def _draw(seed, key, shape, std=0.02):
     return out
 
 
+_CHUNK_ELEMS = 1 << 22  # 16 MB of fp32 per drawn row block
+
+
+def _draw_rows(seed, key, rows, cols, std=0.02):
+    """Yields (r0, block) fp32 row blocks of one [rows, cols] draw; the blocks
+    concatenated equal _draw(seed, key, (rows, cols), std) exactly (one
+    generator, consumed in order).  The block buffer is reused between
+    yields, so large matrices never exist in fp32 in full."""
+    g = child_rng(seed, *key)
+    step = max(1, min(rows, _CHUNK_ELEMS // cols))
+    buf = np.empty((step, cols), dtype=np.float32)
+    for r0 in range(0, rows, step):
+        v = buf[:min(step, rows - r0)]
+        g.standard_normal(out=v, dtype=np.float32)
+        v *= np.float32(std)
+        yield r0, v
+
+
 def _encode(fmt, w):
     return encode_fp8_rows(w) if fmt == "fp8" else encode_mxfp4(w)
+
+
+def _encoded_matrix(fmt, seed, layer, parts, cols, ex):
+    """Rows of several drawn matrices stacked in order ([(name, rows), ...]),
+    encoded block by block into preallocated code / scale arrays."""
+    rows = sum(r for _, r in parts)
+    if fmt == "fp8":
+        codes, scales = np.empty((rows, cols), np.uint8), np.empty(rows, np.float32)
+    else:
+        codes, scales = np.empty((rows, cols // 2), np.uint8), np.empty((rows, cols // 32), np.uint8)
+
+    def one(name, off, r):
+        for r0, v in _draw_rows(seed, (_P_WEIGHTS, layer, _MAT_IDS[name]), r, cols):
+            c, sc = _encode(fmt, v)
+            codes[off + r0:off + r0 + len(v)] = c
+            scales[off + r0:off + r0 + len(v)] = sc
+
+    futs, off = [], 0
+    for name, r in parts:
+        futs.append(ex.submit(one, name, off, r))
+        off += r
+    return codes, scales, futs
 
 
 def layer_weights(m: ModelShape, seed: int, layer: int, gains: str = "ones") -> dict:
@@ -193,17 +233,26 @@ def layer_weights(m: ModelShape, seed: int, layer: int, gains: str = "ones") -> 
     w_qkv rows are [q heads | k heads | v heads], each head_dim rows;
     w_gate_up rows are [gate (I rows) | up (I rows)]."""
     H, D, I = m.hidden, m.head_dim, m.intermediate
-    shapes = {"q": (m.n_q_heads * D, H), "k": (m.n_kv_heads * D, H), "v": (m.n_kv_heads * D, H),
-              "o": (H, m.n_q_heads * D), "gate": (I, H), "up": (I, H), "down": (H, I)}
-    with ThreadPoolExecutor(_threads()) as ex:
-        fl = {k: ex.submit(_draw, seed, (_P_WEIGHTS, layer, _MAT_IDS[k]), s) for k, s in shapes.items()}
-        f = {k: v.result() for k, v in fl.items()}
     out = {}
-    out["w_qkv"], out["s_qkv"] = encode_fp8_rows(np.concatenate([f["q"], f["k"], f["v"]], axis=0))
-    out["w_o"], out["s_o"] = encode_fp8_rows(f["o"])
-    out["w_gate_up"], out["s_gate_up"] = _encode(m.mlp_format, np.concatenate([f["gate"], f["up"]], axis=0))
-    out["w_down"], out["s_down"] = _encode(m.mlp_format, f["down"])
+    with ThreadPoolExecutor(_threads()) as ex:
+        futs = []
+        for wk, sk, fmt, parts, cols in (
+                ("w_qkv", "s_qkv", "fp8", [("q", m.n_q_heads * D), ("k", m.n_kv_heads * D), ("v", m.n_kv_heads * D)], H),
+                ("w_o", "s_o", "fp8", [("o", H)], m.n_q_heads * D),
+                ("w_gate_up", "s_gate_up", m.mlp_format, [("gate", I), ("up", I)], H),
+                ("w_down", "s_down", m.mlp_format, [("down", H)], I)):
+            out[wk], out[sk], f = _encoded_matrix(fmt, seed, layer, parts, cols, ex)
+            futs += f
+        for f in futs:
+            f.result()
     out["attn_norm"], out["mlp_norm"] = norm_gains(m, seed, layer, gains)
+    return out
+
+
+def _bf16_table(seed, key, rows, cols):
+    out = np.empty((rows, cols), np.uint16)
+    for r0, v in _draw_rows(seed, key, rows, cols):
+        out[r0:r0 + len(v)] = to_bf16_bits(v)
     return out
 
 
@@ -217,9 +266,8 @@ def norm_gains(m: ModelShape, seed: int, layer: int, gains: str):
 def embedding_weights(m: ModelShape, seed: int, gains: str = "ones") -> dict:
     """BF16 token embedding [V, H]; untied models also get a BF16 lm_head drawn
     the same way; final_norm gains [H]."""
-    out = {"embed": to_bf16_bits(_draw(seed, (_P_WEIGHTS, 10_000, 0), (m.vocab, m.hidden)))}
-    out["lm_head"] = None if m.tied_lm_head else to_bf16_bits(
-        _draw(seed, (_P_WEIGHTS, 10_000, 1), (m.vocab, m.hidden)))
+    out = {"embed": _bf16_table(seed, (_P_WEIGHTS, 10_000, 0), m.vocab, m.hidden)}
+    out["lm_head"] = None if m.tied_lm_head else _bf16_table(seed, (_P_WEIGHTS, 10_000, 1), m.vocab, m.hidden)
     if gains == "ones":
         out["final_norm"] = np.ones(m.hidden, np.float32)
     else:
