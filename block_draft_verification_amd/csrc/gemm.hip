@@ -11,38 +11,45 @@
 // normed activations small enough for a 24-32 layer stack) and BF16 for the
 // lm_head (whose BF16 table is then used as is).  fp32 accumulation.
 //
-// MFMA mapping (v_mfma_f32_16x16x32_{f16,bf16}): the weight tile is the A
-// operand (16 output rows), the activation tile the B operand (16 block
-// rows); lane (r, g) = (lane%16, lane/16) ends with outputs n = 4g..4g+3 of
-// row r, so every epilogue (scale, RoPE pair, gate/up pair, residual,
-// argmax) runs on registers.  Per 64-wide k step a lane reads 16 consecutive
-// k of one weight row (one 16-byte load for FP8) and the matching 16
-// activations; halves feed two MFMAs so A and B always pair the same k.
+// MFMA mapping (v_mfma_f32_32x32x16_{f16,bf16}, which on gfx950 issues at
+// twice the rate of the 16x16x32 shape): the weight tile is the A operand (32
+// output rows), the activation tile the B operand (32 block rows).  Per
+// 64-wide k step lane (c, h) = (lane%32, lane/32) reads the 32 consecutive k
+// 32h..32h+31 of one weight row (two 16-byte loads for FP8, one for MXFP4,
+// whose scale block is exactly those 32 k) and uses its 8-element slice i as
+// the k operand of the step's i-th MFMA; the activation side reads the same k
+// slices, so A and B always pair the same k and the sum over k is complete.
+// Lane (c, h) ends with the outputs of block row c for the weight rows
+// 8q + 4h + (0..3), q = 0..3 of each tile, so every epilogue (scale, RoPE
+// pair, gate/up pair, residual partial, argmax) runs on registers.
 //
 // Work split: a workgroup = 4 waves side by side along N (wave = one "unit"
-// of NT 16-row weight tiles) sharing one activation tile of 16*MT rows,
-// which is staged through LDS (double buffered, one barrier per k step)
-// while each wave streams its own weight rows straight into registers one k
-// step ahead.  Workgroups that share weight rows (all M blocks of one N
-// block) are placed on one XCD so its L2 serves the re-reads.  Shapes with
-// too few output tiles to fill 256 CUs split K over gridDim.z: each split
-// writes fp32 partials and the last workgroup of a tile (integer atomic
-// counter) adds them in split order and runs the epilogue, so results do not
-// depend on timing.
+// of NT 32-row weight tiles) sharing one activation tile of 32*MT rows.  The
+// activation tile goes straight from global memory to LDS (one barrier per k
+// step); each wave streams its own weight rows into registers.  Both run
+// GEMM_DEPTH k steps ahead of the MFMAs.  Workgroups that share weight rows
+// (all M blocks of one N block) are placed on one XCD so its L2 serves the
+// re-reads.  Residual projections with too few output tiles to fill the chip
+// split K over gridDim.z and write fp32 partials; the next RMSNorm adds them
+// in split order, so results do not depend on timing.
 #include "common.h"
 #include "kernels.h"
 
-template <int FMT> struct WRaw;
-template <> struct WRaw<SPEC_WFMT_FP8_E4M3_ROW> { u32x4_t c; };
-template <> struct WRaw<SPEC_WFMT_BF16> { u32x4_t lo, hi; };
-template <> struct WRaw<SPEC_WFMT_MXFP4> { u32x2_t c; uint32_t e; };
+#ifndef GEMM_DEPTH
+#define GEMM_DEPTH 2
+#endif
+#ifndef GEMM_MIN_TILES
+#define GEMM_MIN_TILES 128
+#endif
 
-// An empty asm that reads the registers: placed after the final wait, it
-// keeps the last (discarded) prefetch's destination registers allocated until
-// the load has landed, so the compiler cannot reuse them while it is in flight.
-__device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_FP8_E4M3_ROW> &r) { asm volatile("" ::"v"(r.c)); }
-__device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_BF16> &r) { asm volatile("" ::"v"(r.lo), "v"(r.hi)); }
-__device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_MXFP4> &r) { asm volatile("" ::"v"(r.c), "v"(r.e)); }
+// Raw weight bytes of one 32-row tile for one lane and one k step.
+template <int FMT> struct WRaw;
+template <> struct WRaw<SPEC_WFMT_FP8_E4M3_ROW> { u32x4_t c[2]; };  // 32 codes
+template <> struct WRaw<SPEC_WFMT_BF16> { u32x4_t c[4]; };          // 32 bf16
+template <> struct WRaw<SPEC_WFMT_MXFP4> { u32x4_t c; uint32_t e; };  // 32 nibbles + e8m0
+
+// VMEM instructions per tile and step
+template <int FMT> constexpr int w_loads() { return FMT == SPEC_WFMT_BF16 ? 4 : 2; }
 
 // Weight loads are issued as plain vector loads the compiler does not track:
 // its wait analysis cannot count the LDS-DMA activation loads issued after
@@ -53,64 +60,71 @@ __device__ __forceinline__ u32x4_t vload16(const void *p) {
   asm volatile("global_load_dwordx4 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
   return v;
 }
-__device__ __forceinline__ u32x2_t vload8(const void *p) {
-  u32x2_t v;
-  asm volatile("global_load_dwordx2 %0, %1, off" : "=v"(v) : "v"(p) : "memory");
-  return v;
-}
 __device__ __forceinline__ uint32_t vload1(const void *p) {
   uint32_t v;
   asm volatile("global_load_ubyte %0, %1, off" : "=v"(v) : "v"(p) : "memory");
   return v;
 }
 
+// An empty asm that reads the registers: placed after the final wait, it
+// keeps the last (discarded) prefetch's destination registers allocated until
+// the load has landed, so the compiler cannot reuse them while it is in flight.
+__device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_FP8_E4M3_ROW> &r) {
+  asm volatile("" ::"v"(r.c[0]), "v"(r.c[1]));
+}
+__device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_BF16> &r) {
+  asm volatile("" ::"v"(r.c[0]), "v"(r.c[1]), "v"(r.c[2]), "v"(r.c[3]));
+}
+__device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_MXFP4> &r) { asm volatile("" ::"v"(r.c), "v"(r.e)); }
+
+// k = first of the lane's 32 k (a multiple of 32)
 template <int FMT>
 __device__ __forceinline__ void load_w(WRaw<FMT> &r, const uint8_t *__restrict__ w,
                                        const uint8_t *__restrict__ s, int row, int K, int k) {
   if constexpr (FMT == SPEC_WFMT_FP8_E4M3_ROW) {
-    r.c = vload16(w + (size_t)row * K + k);
+    const uint8_t *p = w + (size_t)row * K + k;
+    r.c[0] = vload16(p);
+    r.c[1] = vload16(p + 16);
   } else if constexpr (FMT == SPEC_WFMT_BF16) {
     const uint16_t *p = reinterpret_cast<const uint16_t *>(w) + (size_t)row * K + k;
-    r.lo = vload16(p);
-    r.hi = vload16(p + 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r.c[i] = vload16(p + 8 * i);
   } else {
-    r.c = vload8(w + (size_t)row * (K / 2) + k / 2);
+    r.c = vload16(w + (size_t)row * (K / 2) + k / 2);
     r.e = vload1(s + (size_t)row * (K / 32) + k / 32);
   }
 }
 
-// 16 weights -> two 8-element MFMA operands in the activation type
+// 32 weights -> four 8-element MFMA operands in the activation type
 template <bool F16, int FMT>
-__device__ __forceinline__ void cvt_w(const WRaw<FMT> &r, u32x4_t &op0, u32x4_t &op1) {
+__device__ __forceinline__ void cvt_w(const WRaw<FMT> &r, u32x4_t (&op)[4]) {
   if constexpr (FMT == SPEC_WFMT_FP8_E4M3_ROW) {
-    u32x2_t a, b, c, d;
-    if constexpr (F16) {
-      a = fp8x4_to_f16x4(r.c.x), b = fp8x4_to_f16x4(r.c.y), c = fp8x4_to_f16x4(r.c.z), d = fp8x4_to_f16x4(r.c.w);
-    } else {
-      a = fp8x4_to_bf16x4(r.c.x), b = fp8x4_to_bf16x4(r.c.y), c = fp8x4_to_bf16x4(r.c.z), d = fp8x4_to_bf16x4(r.c.w);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = r.c[i >> 1][(i & 1) * 2], hi = r.c[i >> 1][(i & 1) * 2 + 1];
+      u32x2_t a, b;
+      if constexpr (F16) {
+        a = fp8x4_to_f16x4(lo), b = fp8x4_to_f16x4(hi);
+      } else {
+        a = fp8x4_to_bf16x4(lo), b = fp8x4_to_bf16x4(hi);
+      }
+      op[i] = u32x4_t{a.x, a.y, b.x, b.y};
     }
-    op0 = u32x4_t{a.x, a.y, b.x, b.y};
-    op1 = u32x4_t{c.x, c.y, d.x, d.y};
   } else if constexpr (FMT == SPEC_WFMT_BF16) {
     static_assert(!F16, "BF16 weights pair with BF16 activations");
-    op0 = r.lo;
-    op1 = r.hi;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op[i] = r.c[i];
   } else {
     const float sc = __uint_as_float(r.e << 23);  // 2^(e-127); e = 0 only on all-zero blocks
-    if constexpr (F16) {
-      op0 = fp4x8_to_f16x8(r.c.x, sc);
-      op1 = fp4x8_to_f16x8(r.c.y, sc);
-    } else {
-      op0 = fp4x8_to_bf16x8(r.c.x, sc);
-      op1 = fp4x8_to_bf16x8(r.c.y, sc);
-    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) op[i] = F16 ? fp4x8_to_f16x8(r.c[i], sc) : fp4x8_to_bf16x8(r.c[i], sc);
   }
 }
 
 template <bool F16>
-__device__ __forceinline__ f32x4_t mma(u32x4_t a, u32x4_t b, f32x4_t c) {
-  if constexpr (F16) return mfma16x16x32_f16(a, b, c);
-  else return mfma16x16x32(a, b, c);
+__device__ __forceinline__ f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
+  if constexpr (F16) return mfma32x32x16_f16(a, b, c);
+  else return mfma32x32x16(a, b, c);
 }
 
 struct GemmArgs {
@@ -130,10 +144,6 @@ __device__ __forceinline__ bool tile_of(int L, int nb, int mb, int &n, int &m) {
   return n < nb;
 }
 
-// VMEM loads issued by one wave for one k step: activation rows straight to
-// LDS (16-byte lanes), then the weight rows of its NT tiles into registers.
-template <int FMT> constexpr int w_loads() { return FMT == SPEC_WFMT_FP8_E4M3_ROW ? 1 : 2; }
-
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] in bits 3:0,
 // vmcnt[5:4] in bits 15:14; expcnt and lgkmcnt left at "no wait").
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
@@ -145,124 +155,159 @@ __device__ __forceinline__ void lds_load16(const void *g, void *l) {
   __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void *)l, 16, 0, 0);
 }
 
-// Waves per SIMD the register budget is sized for: 2 where the accumulators
-// of a wave fit half the register file, else 1.
+// Activation tile in LDS: 16-byte chunk c of row r sits at chunk slot
+// r*8 + (c ^ swz(r)).  A fragment read has the 16 lanes of one LDS phase on 16
+// consecutive rows at one logical chunk; swz sends them to 16 distinct 16-byte
+// bank groups of a 256-byte window (and rows r..r+7 to distinct groups of a
+// 128-byte window), so the reads are free of bank conflicts.
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+// Waves per SIMD the register budget is sized for.
 template <int FMT, int NT, int MT> struct GemmOcc {
-  static constexpr int value = (NT * MT <= 32 && NT <= 4 && FMT != 3) ? 2 : 1;
+  static constexpr int value = (NT * MT <= 4 && FMT != SPEC_WFMT_BF16) ? 2 : 1;
 };
 
 template <bool F16, int FMT, int NT, int MT, class Epi>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GemmOcc<FMT, NT, MT>::value, 8))) void
 gemm_kernel(GemmArgs ga, Epi epi) {
-  constexpr int ROWS = 16 * MT;
-  constexpr int AJ = MT >= 2 ? MT / 2 : 1;  // 1 KB wave-loads per wave per stage
-  constexpr int SE = 4 * AJ * 512;          // 16-bit elements per stage (MT = 1: half is padding)
-  constexpr int NS = 3;                     // stages in flight
-  // activation tile: 16-byte chunk c of row r stored at chunk slot r*8 + (c ^ (r & 7))
-  __shared__ __align__(16) uint16_t As[NS * SE];
+  constexpr int ROWS = 32 * MT;             // activation rows per workgroup
+  constexpr int AJ = MT;                    // LDS-DMA instructions per wave per stage (ROWS*8 chunks / 256 lanes)
+  constexpr int SE = ROWS * 64;             // 16-bit elements per stage
+  constexpr int DIST = GEMM_DEPTH;          // k steps loaded ahead of the one computed
+  constexpr int NS = DIST + 1;              // LDS stages = weight register sets
+  // staged epilogue: per wave a [32][LD] fp32 tile of block rows x output columns
+  constexpr int COLS = Epi::template cols<NT>(), LD = COLS + 4;
+  constexpr int STAGE_BYTES = Epi::kStaged ? 4 * 32 * LD * 4 : 0;
+  constexpr int LDS_BYTES = NS * SE * 2 > STAGE_BYTES ? NS * SE * 2 : STAGE_BYTES;
+  __shared__ __align__(16) uint16_t As[LDS_BYTES / 2];
 
   int nblk, mblk;
   if (!tile_of(blockIdx.x, ga.nb, ga.mb, nblk, mblk)) return;  // whole workgroup
-  const int tid = threadIdx.x, lane = tid & 63, r = lane & 15, g = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = nblk * 4 + wave;
-  const bool active = unit < epi.units;  // wave-uniform; inactive waves compute on row 0 and store nothing
+  const bool active = unit < epi.units;  // wave-uniform; inactive waves compute on unit 0 and store nothing
   const int m0 = mblk * ROWS;
   const int M = ga.M, K = ga.K, ksteps = K / 64;
   const int ks0 = blockIdx.z * ga.spl, nsteps = min(ks0 + ga.spl, ksteps) - ks0;
 
-  // every wave issues AJ activation wave-loads and NT weight loads per step,
-  // so the vmcnt waits below are the same compile-time count for all waves
+  // Every wave issues AJ activation loads and NT*w_loads weight loads per
+  // step, so the vmcnt waits below are one compile-time count for all waves.
   const uint16_t *agp[AJ];
 #pragma unroll
   for (int i = 0; i < AJ; ++i) {
-    const int P = (wave + 4 * i) * 64 + lane, row = P >> 3, c = (P & 7) ^ (row & 7);
-    const int m = (row < ROWS && m0 + row < M) ? m0 + row : 0;  // padding / rows past M read row 0
-    agp[i] = ga.x + (size_t)m * K + ks0 * 64 + c * 8;
+    const int P = (wave + 4 * i) * 64 + lane, row = P >> 3, ch = (P & 7) ^ swz(row);
+    const int m = m0 + row < M ? m0 + row : 0;  // rows past M read row 0 and are never stored
+    agp[i] = ga.x + (size_t)m * K + ks0 * 64 + ch * 8;
   }
   int wrow[NT];
 #pragma unroll
-  for (int t = 0; t < NT; ++t) wrow[t] = epi.row(active ? unit : 0, t) + r;
+  for (int t = 0; t < NT; ++t) wrow[t] = epi.row(active ? unit : 0, t) + c;
 
-  f32x4_t acc[NT][MT];
+  f32x16_t acc[NT][MT];
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[t][mt][v] = 0.f;
 
   auto compute = [&](int stage, const WRaw<FMT>(&wr)[NT]) {
-    __builtin_amdgcn_sched_barrier(0);  // keep the three unrolled steps from interleaving (register pressure)
-    u32x4_t w0[NT], w1[NT];
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4_t wop[NT][4];
 #pragma unroll
-    for (int t = 0; t < NT; ++t) cvt_w<F16, FMT>(wr[t], w0[t], w1[t]);
+    for (int t = 0; t < NT; ++t) cvt_w<F16, FMT>(wr[t], wop[t]);
     const uint16_t *base = As + stage * SE;
-    auto read_a = [&](int mt, u32x4_t &a0, u32x4_t &a1) {
-      const int row = 16 * mt + r;
-      a0 = *reinterpret_cast<const u32x4_t *>(base + (row * 8 + ((2 * g) ^ (row & 7))) * 8);
-      a1 = *reinterpret_cast<const u32x4_t *>(base + (row * 8 + ((2 * g + 1) ^ (row & 7))) * 8);
-    };
-    // activation fragments of tile mt+1 are read while tile mt's MFMAs run
-    u32x4_t a0[2], a1[2];
-    read_a(0, a0[0], a1[0]);
+    // slice i of block row 32*mt + c: logical chunk 4h + i
+    auto read_a = [&](int i, u32x4_t (&af)[MT]) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      if (mt + 1 < MT) read_a(mt + 1, a0[(mt + 1) & 1], a1[(mt + 1) & 1]);
-#pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        acc[t][mt] = mma<F16>(w0[t], a0[mt & 1], acc[t][mt]);
-        acc[t][mt] = mma<F16>(w1[t], a1[mt & 1], acc[t][mt]);
+      for (int mt = 0; mt < MT; ++mt) {
+        const int row = 32 * mt + c;
+        af[mt] = *reinterpret_cast<const u32x4_t *>(base + (row * 8 + ((4 * h + i) ^ swz(row))) * 8);
       }
+    };
+    // the fragments of slice i+1 are read while slice i's MFMAs run
+    u32x4_t af[2][MT];
+    read_a(0, af[0]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (i + 1 < 4) read_a(i + 1, af[(i + 1) & 1]);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) acc[t][mt] = mma<F16>(wop[t][i], af[i & 1][mt], acc[t][mt]);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Per k step s: activations for step s+2 go straight to LDS stage (s+2)%3,
-  // weights for step s+1 into the "next" registers, then step s is computed.
-  auto issue_a_to = [&](int step, int stage) {
+  auto issue_a = [&](int step, int stage) {
 #pragma unroll
     for (int i = 0; i < AJ; ++i) lds_load16(agp[i] + step * 64, As + stage * SE + (wave + 4 * i) * 512);
   };
-  auto issue_a = [&](int step) { issue_a_to(step, step % NS); };
   auto issue_w = [&](WRaw<FMT>(&wr)[NT], int step) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) load_w<FMT>(wr[t], ga.w, ga.s, wrow[t], K, (ks0 + step) * 64 + 16 * g);
+    for (int t = 0; t < NT; ++t) load_w<FMT>(wr[t], ga.w, ga.s, wrow[t], K, (ks0 + step) * 64 + 32 * h);
   };
-  // VMEM order per step: [W(s+1)] then [A(s+2)].  Loads complete in issue
-  // order, so waiting for the weight registers (at the copy below) never waits
-  // for the younger activation loads, which stay two steps ahead.
-  // Two weight register sets alternate (the loop is unrolled by two) so no
-  // register copy of a load destination is ever needed: a copy would be
-  // placed before the wait that covers the load.  Tail steps re-load the last
-  // step into a stage nobody reads.  Issue order per step: [W(s+1)] [A(s+2)].
-  // At the top of step s the outstanding loads are, oldest first, A(s), W(s),
-  // A(s+1): waiting until at most AJ remain leaves only A(s+1) in flight.
-  WRaw<FMT> wa[NT], wb[NT];
-  issue_w(wa, 0);
-  issue_a(0);
-  issue_a(min(1, nsteps - 1));
-  for (int s = 0; s < nsteps; s += 2) {
-    WAIT_VMCNT(AJ);
-    lds_barrier();  // stage s visible to all waves; stage (s+2)%3 = (s-1)%3 free again
-    __builtin_amdgcn_sched_barrier(0);
-    issue_w(wb, min(s + 1, nsteps - 1));
-    issue_a_to(min(s + 2, nsteps - 1), (s + 2) % NS);
-    __builtin_amdgcn_sched_barrier(0);
-    compute(s % NS, wa);
-    WAIT_VMCNT(AJ);
-    lds_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_w(wa, min(s + 2, nsteps - 1));
-    issue_a_to(min(s + 3, nsteps - 1), (s + 3) % NS);
-    __builtin_amdgcn_sched_barrier(0);
-    if (s + 1 < nsteps) compute((s + 1) % NS, wb);
+  // Software pipeline, DIST k steps deep.  At step s the wave issues step
+  // s+DIST (weights into register set (s+DIST)%NS, then activations straight to
+  // LDS stage (s+DIST)%NS) and computes step s from set / stage s%NS.  The loop
+  // is unrolled NS times so every register set has a fixed name: a register
+  // copy of a load destination would be placed before the wait that covers it.
+  // Steps past the end re-load the last step into a set / stage nobody reads.
+  // Loads complete in issue order, so "step s landed" is "at most the loads of
+  // steps s+1 .. s+DIST-1 outstanding".
+  constexpr int PER_STEP = NT * w_loads<FMT>() + AJ;
+  static_assert((DIST - 1) * PER_STEP < 64, "vmcnt holds 6 bits");
+  WRaw<FMT> wr[NS][NT];
+#pragma unroll
+  for (int i = 0; i < DIST; ++i) {
+    issue_w(wr[i], min(i, nsteps - 1));
+    issue_a(min(i, nsteps - 1), i);
+  }
+  for (int s0 = 0; s0 < nsteps; s0 += NS) {
+#pragma unroll
+    for (int ph = 0; ph < NS; ++ph) {
+      const int s = s0 + ph;
+      WAIT_VMCNT((DIST - 1) * PER_STEP);
+      lds_barrier();  // stage s visible to all waves; every wave is done with step s-1's stage
+      __builtin_amdgcn_sched_barrier(0);
+      issue_w(wr[(ph + DIST) % NS], min(s + DIST, nsteps - 1));
+      issue_a(min(s + DIST, nsteps - 1), (ph + DIST) % NS);
+      __builtin_amdgcn_sched_barrier(0);
+      if (ph == 0 || s < nsteps) compute(ph, wr[ph]);
+    }
   }
   WAIT_VMCNT(0);  // nothing may still be landing in LDS or registers past this point
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    hold(wa[t]);
-    hold(wb[t]);
+  for (int i = 0; i < NS; ++i)
+#pragma unroll
+    for (int t = 0; t < NT; ++t) hold(wr[i][t]);
+  if constexpr (Epi::kStaged) {
+    // Each wave writes its finished outputs (scaled, RoPE / SwiGLU applied) as
+    // fp32 into its own LDS tile, then reads it back along rows so that every
+    // global store covers consecutive columns of one row.  The tile is wave
+    // private and a wave's LDS operations run in order, so only the barrier
+    // that retires the activation stages is needed.
+    constexpr int LPR = COLS / 4, RPP = 64 / LPR;  // lanes per row, rows per pass
+    static_assert(COLS % 4 == 0 && 64 % LPR == 0 && LPR <= 64, "staged tile shape");
+    lds_barrier();  // every wave is done reading the activation stages
+    float *st = reinterpret_cast<float *>(As) + wave * 32 * LD;
+    if (active) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        if (m0 + 32 * mt >= M) break;
+        epi.template emit<NT, MT>(unit, mt, m0, M, c, h, acc, st, LD);
+#pragma unroll
+        for (int r0 = 0; r0 < 32; r0 += RPP) {
+          const int row = r0 + lane / LPR, col = 4 * (lane % LPR), m = m0 + 32 * mt + row;
+          const f32x4_t v = *reinterpret_cast<const f32x4_t *>(st + row * LD + col);
+          if (m < M) epi.put(unit, m, col, v, blockIdx.z);
+        }
+      }
+    }
+  } else {
+    if (active) epi.template store<NT, MT>(unit, m0, M, c, h, acc, blockIdx.z);
   }
-  if (active) epi.template store<NT, MT>(unit, m0, M, r, g, acc, blockIdx.z);
 }
 
 __device__ __forceinline__ void store_f16x4(uint16_t *p, float a, float b, float c, float d) {
@@ -277,23 +322,39 @@ __device__ __forceinline__ f32x4_t row_scale4(const float *s, int n) {
   return *reinterpret_cast<const f32x4_t *>(s + n);
 }
 
+// Outputs of lane (c, h) for weight rows 8q + 4h + (0..3) of a tile.
+__device__ __forceinline__ f32x4_t quad(const f32x16_t &a, int q) {
+  return f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
+}
+
 // ---------------------------------------------------------------- epilogues
+// Each epilogue maps (unit, tile t) to the first of the tile's 32 weight rows
+// (row()).  Lane (c, h) holds block row m0 + 32*mt + c and weight rows
+// row(unit, t) + 8q + 4h + (0..3).  Staged epilogues emit() a wave's finished
+// values for one 32-row block into the LDS tile st[block row][output column]
+// (cols() columns) and put() stores 4 consecutive output columns of one row.
 
 template <int NTc>
 struct EpiF32 {  // y = acc * scale, fp32 out
+  static constexpr bool kStaged = true;
   int units, N;
   float *y;
   const float *scale;
-  __device__ int row(int unit, int t) const { return unit * 16 * NTc + 16 * t; }
+  __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
+  template <int NT> static constexpr int cols() { return 32 * NT; }
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT], int z) const {
+  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT], float *st,
+                       int ld) const {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = m0 + 16 * mt + r, n = row(unit, t) + 4 * g;
-        if (m < M) *reinterpret_cast<f32x4_t *>(y + (size_t)m * N + n) = acc[t][mt] * row_scale4(scale, n);
+      for (int q = 0; q < 4; ++q) {
+        const int col = 32 * t + 8 * q + 4 * h;
+        *reinterpret_cast<f32x4_t *>(st + c * ld + col) = quad(acc[t][mt], q) * row_scale4(scale, row(unit, 0) + col);
       }
+  }
+  __device__ void put(int unit, int m, int col, f32x4_t v, int z) const {
+    *reinterpret_cast<f32x4_t *>(y + (size_t)m * N + row(unit, 0) + col) = v;
   }
 };
 
@@ -301,148 +362,169 @@ struct EpiF32 {  // y = acc * scale, fp32 out
 // next RMSNorm adds the partials of every split to h in split order.
 template <int NTc>
 struct EpiPartial {
-  int units, N;
+  static constexpr bool kStaged = true;
+  int units, N, M;
   float *part;  // [nsplit][M][N]
   const float *scale;
-  __device__ int row(int unit, int t) const { return unit * 16 * NTc + 16 * t; }
+  __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
+  template <int NT> static constexpr int cols() { return 32 * NT; }
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT], int z) const {
-    float *pz = part + (size_t)z * M * N;
+  __device__ void emit(int unit, int mt, int m0, int Mr, int c, int h, const f32x16_t (&acc)[NT][MT], float *st,
+                       int ld) const {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const int m = m0 + 16 * mt + r, n = row(unit, t) + 4 * g;
-        if (m < M) *reinterpret_cast<f32x4_t *>(pz + (size_t)m * N + n) = acc[t][mt] * row_scale4(scale, n);
+      for (int q = 0; q < 4; ++q) {
+        const int col = 32 * t + 8 * q + 4 * h;
+        *reinterpret_cast<f32x4_t *>(st + c * ld + col) = quad(acc[t][mt], q) * row_scale4(scale, row(unit, 0) + col);
       }
+  }
+  __device__ void put(int unit, int m, int col, f32x4_t v, int z) const {
+    *reinterpret_cast<f32x4_t *>(part + ((size_t)z * M + m) * N + row(unit, 0) + col) = v;
   }
 };
 
-// One unit = one head of D = 16*NT rows: q heads, then k heads, then v heads.
+// One unit = one head of D = 32*NT rows: q heads, then k heads, then v heads.
 // Rotate-half RoPE pairs d and d + D/2, which are tiles t and t + NT/2 in the
-// same lane and register slot.  q goes out as FP16, k and v into the BF16 cache.
+// same lane and register slot.  q goes out as FP16, k and v into the BF16 cache
+// at slot kv_len[b] + j of block row m = 16b + j.
 template <int NTc>
 struct EpiQkv {
+  static constexpr bool kStaged = true;
   int units;
   const float *scale;
   QkvOut o;
-  __device__ int row(int unit, int t) const { return unit * 16 * NTc + 16 * t; }
+  __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
+  template <int NT> static constexpr int cols() { return 32 * NT; }
+  __device__ bool slot_ok(int n0) const { return n0 >= 0 && n0 + 16 <= o.max_ctx; }  // else flagged by embed
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT], int z) const {
-    constexpr int D = 16 * NT, HALF = D / 2;
+  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT], float *st,
+                       int ld) const {
+    constexpr int HALF = 16 * NT;
+    const int m = m0 + 32 * mt + c;
+    if (m >= M) return;
+    const int n0 = o.kv_len[m >> 4], pos = n0 + (m & 15);
+    if (!slot_ok(n0)) return;
+    if (unit < o.Hq + o.Hkv) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = m0 + 16 * mt + r;
-      if (m >= M) continue;
-      const int b = m >> 4, j = m & 15;
-      const int n0 = o.kv_len[b];
-      const int pos = n0 + j;
-      if (n0 < 0 || n0 + 16 > o.max_ctx) continue;  // flagged by the embed step
-      if (unit < o.Hq + o.Hkv) {
-        const bool isq = unit < o.Hq;
-        uint16_t *dst = isq ? o.q_out + (size_t)m * (o.Hq * D) + unit * D
-                            : o.k_cache + (((size_t)b * o.Hkv + (unit - o.Hq)) * o.max_ctx + pos) * D;
+      for (int t = 0; t < NT / 2; ++t)
 #pragma unroll
-        for (int t = 0; t < NT / 2; ++t) {
-          const int d = 16 * t + 4 * g;
-          const f32x4_t y1 = acc[t][mt] * row_scale4(scale, row(unit, t) + 4 * g);
-          const f32x4_t y2 = acc[t + NT / 2][mt] * row_scale4(scale, row(unit, t + NT / 2) + 4 * g);
-          float o1[4], o2[4];
+        for (int q = 0; q < 4; ++q) {
+          const int d = 32 * t + 8 * q + 4 * h;
+          const f32x4_t y1 = quad(acc[t][mt], q) * row_scale4(scale, row(unit, 0) + d);
+          const f32x4_t y2 = quad(acc[t + NT / 2][mt], q) * row_scale4(scale, row(unit, 0) + d + HALF);
+          const f32x4_t cs01 = *reinterpret_cast<const f32x4_t *>(o.rope + (size_t)pos * HALF + d);
+          const f32x4_t cs23 = *reinterpret_cast<const f32x4_t *>(o.rope + (size_t)pos * HALF + d + 2);
+          const float cs[4] = {cs01[0], cs01[2], cs23[0], cs23[2]}, sn[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
+          f32x4_t o1, o2;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float2 cs = o.rope[(size_t)pos * HALF + d + i];
-            o1[i] = y1[i] * cs.x - y2[i] * cs.y;
-            o2[i] = y2[i] * cs.x + y1[i] * cs.y;
+            o1[i] = y1[i] * cs[i] - y2[i] * sn[i];
+            o2[i] = y2[i] * cs[i] + y1[i] * sn[i];
           }
-          if (isq) {
-            store_f16x4(dst + d, o1[0], o1[1], o1[2], o1[3]);
-            store_f16x4(dst + d + HALF, o2[0], o2[1], o2[2], o2[3]);
-          } else {
-            store_bf16x4(dst + d, o1[0], o1[1], o1[2], o1[3]);
-            store_bf16x4(dst + d + HALF, o2[0], o2[1], o2[2], o2[3]);
-          }
+          *reinterpret_cast<f32x4_t *>(st + c * ld + d) = o1;
+          *reinterpret_cast<f32x4_t *>(st + c * ld + d + HALF) = o2;
         }
-      } else {
-        uint16_t *dst = o.v_cache + (((size_t)b * o.Hkv + (unit - o.Hq - o.Hkv)) * o.max_ctx + pos) * D;
+    } else {
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-          const f32x4_t y = acc[t][mt] * row_scale4(scale, row(unit, t) + 4 * g);
-          store_bf16x4(dst + 16 * t + 4 * g, y[0], y[1], y[2], y[3]);
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int d = 32 * t + 8 * q + 4 * h;
+          *reinterpret_cast<f32x4_t *>(st + c * ld + d) = quad(acc[t][mt], q) * row_scale4(scale, row(unit, 0) + d);
         }
-      }
+    }
+  }
+  __device__ void put(int unit, int m, int col, f32x4_t v, int z) const {
+    constexpr int D = 32 * NTc;
+    const int b = m >> 4, n0 = o.kv_len[b];
+    if (!slot_ok(n0)) return;
+    const int pos = n0 + (m & 15);
+    if (unit < o.Hq) {
+      store_f16x4(o.q_out + (size_t)m * (o.Hq * D) + unit * D + col, v[0], v[1], v[2], v[3]);
+    } else {
+      const bool isk = unit < o.Hq + o.Hkv;
+      const int kvh = isk ? unit - o.Hq : unit - o.Hq - o.Hkv;
+      uint16_t *cache = isk ? o.k_cache : o.v_cache;
+      store_bf16x4(cache + (((size_t)b * o.Hkv + kvh) * o.max_ctx + pos) * D + col, v[0], v[1], v[2], v[3]);
     }
   }
 };
 
 // Tiles [0, NT/2) read gate rows, tiles [NT/2, NT) the matching up rows;
-// a = SiLU(gate) * up goes out as FP16.
+// a = SiLU(gate) * up goes out as FP16.  A unit covers 16*NT outputs.
 template <int NTc>
 struct EpiSwiglu {
+  static constexpr bool kStaged = true;
   int units, I;
   const float *scale;  // per-row FP8 scales [2I], NULL when decoded with the scale
   uint16_t *a;
   __device__ int row(int unit, int t) const {
-    return t < NTc / 2 ? unit * 8 * NTc + 16 * t : I + unit * 8 * NTc + 16 * (t - NTc / 2);
+    return t < NTc / 2 ? unit * 16 * NTc + 32 * t : I + unit * 16 * NTc + 32 * (t - NTc / 2);
   }
+  template <int NT> static constexpr int cols() { return 16 * NT; }
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT], int z) const {
+  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT], float *st,
+                       int ld) const {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int m = m0 + 16 * mt + r;
-      if (m >= M) continue;
+    for (int t = 0; t < NT / 2; ++t)
 #pragma unroll
-      for (int t = 0; t < NT / 2; ++t) {
-        const int n = unit * 8 * NT + 16 * t + 4 * g;
-        const f32x4_t gv = acc[t][mt] * row_scale4(scale, n);
-        const f32x4_t uv = acc[t + NT / 2][mt] * row_scale4(scale ? scale + I : nullptr, n);
-        float v[4];
+      for (int q = 0; q < 4; ++q) {
+        const int col = 32 * t + 8 * q + 4 * h, n = unit * 16 * NT + col;
+        const f32x4_t gv = quad(acc[t][mt], q) * row_scale4(scale, n);
+        const f32x4_t uv = quad(acc[t + NT / 2][mt], q) * row_scale4(scale ? scale + I : nullptr, n);
+        f32x4_t v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = gv[i] / (1.f + __expf(-gv[i])) * uv[i];
-        store_f16x4(a + (size_t)m * I + n, v[0], v[1], v[2], v[3]);
+        *reinterpret_cast<f32x4_t *>(st + c * ld + col) = v;
       }
-    }
+  }
+  __device__ void put(int unit, int m, int col, f32x4_t v, int z) const {
+    store_f16x4(a + (size_t)m * I + unit * 16 * NTc + col, v[0], v[1], v[2], v[3]);
   }
 };
 
 // lm_head tile -> per (row, unit) argmax partial, lowest index on ties.
 template <int NTc>
 struct EpiArgmax {
+  static constexpr bool kStaged = false;
+  template <int NT> static constexpr int cols() { return 4; }
   int units, V;
   ArgmaxPart *part;  // [M][units]
   float *logits;     // optional [M][V]
-  __device__ int row(int unit, int t) const { return unit * 16 * NTc + 16 * t; }
+  __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int r, int g, const f32x4_t (&acc)[NT][MT], int z) const {
+  __device__ void store(int unit, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT], int z) const {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      const int m = m0 + 16 * mt + r;
+      const int m = m0 + 32 * mt + c;
       float bv = -INFINITY;
       int32_t bi = 0x7fffffff;
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int n = row(unit, t) + 4 * g + i;
-          if (better(acc[t][mt][i], n, bv, bi)) {
-            bv = acc[t][mt][i];
+        for (int v = 0; v < 16; ++v) {
+          const int n = row(unit, t) + 8 * (v >> 2) + 4 * h + (v & 3);
+          if (better(acc[t][mt][v], n, bv, bi)) {
+            bv = acc[t][mt][v];
             bi = n;
           }
         }
-#pragma unroll
-      for (int off = 16; off < 64; off <<= 1) {
-        const float ov = __shfl_xor(bv, off);
-        const int32_t oi = __shfl_xor(bi, off);
-        if (better(ov, oi, bv, bi)) {
-          bv = ov;
-          bi = oi;
-        }
+      const float ov = __shfl_xor(bv, 32);  // the other half holds the other rows of the same block row
+      const int32_t oi = __shfl_xor(bi, 32);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
       }
       if (m < M) {
-        if (g == 0) part[(size_t)m * units + unit] = ArgmaxPart{bv, bi};
+        if (h == 0) part[(size_t)m * units + unit] = ArgmaxPart{bv, bi};
         if (logits) {
 #pragma unroll
           for (int t = 0; t < NT; ++t)
-            *reinterpret_cast<f32x4_t *>(logits + (size_t)m * V + row(unit, t) + 4 * g) = acc[t][mt];
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<f32x4_t *>(logits + (size_t)m * V + row(unit, t) + 8 * q + 4 * h) =
+                  quad(acc[t][mt], q);
         }
       }
     }
@@ -455,7 +537,7 @@ GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split) {
   GemmPlan p;
   p.MT = MT;
   p.nb = (units + 3) / 4;
-  p.mb = (M + 16 * MT - 1) / (16 * MT);
+  p.mb = (M + 32 * MT - 1) / (32 * MT);
   const int tiles = p.nb * p.mb;
   // split K (residual projections only) until about 256 workgroups, >= 4 k steps per split
   int s = allow_split ? (256 + tiles - 1) / tiles : 1;
@@ -467,17 +549,19 @@ GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split) {
   return p;
 }
 
-// activation rows per workgroup: enough workgroups first, then wide tiles
+// 32-row activation tiles per workgroup: wide tiles unless that leaves fewer
+// than 128 workgroups
 static int pick_mt(int M, int units, int maxMT) {
-  int mt = M <= 16 ? 1 : M <= 32 ? 2 : M <= 64 ? 4 : 8;
+  int mt = M <= 32 ? 1 : M <= 64 ? 2 : 4;
   if (mt > maxMT) mt = maxMT;
-  while (mt > 2 && ((units + 3) / 4) * ((M + 16 * mt - 1) / (16 * mt)) < 128) mt /= 2;
+  while (mt > 1 && ((units + 3) / 4) * ((M + 32 * mt - 1) / (32 * mt)) < GEMM_MIN_TILES) mt /= 2;
   return mt;
 }
 
+// Residual projections run NT = 2 (64 weight rows per wave).
 int residual_nsplit(int M, int N, int K) {
-  const int units = M <= 32 ? N / 16 : N / 64;
-  return gemm_plan(M, units, K / 64, pick_mt(M, units, 8), true).nsplit;
+  const int units = N / 64;
+  return gemm_plan(M, units, K / 64, pick_mt(M, units, 4), true).nsplit;
 }
 
 // ---------------------------------------------------------------- launchers
@@ -494,10 +578,9 @@ static hipError_t go_m(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hi
   switch (p.MT) {
     case 1: return go<F16, FMT, NT, 1>(p, ga, epi, st);
     case 2: return go<F16, FMT, NT, 2>(p, ga, epi, st);
-    case 4: return go<F16, FMT, NT, 4>(p, ga, epi, st);
     default:
-      if constexpr (NT <= 4) return go<F16, FMT, NT, 8>(p, ga, epi, st);
-      else return go<F16, FMT, NT, 4>(p, ga, epi, st);
+      if constexpr (NT <= 2) return go<F16, FMT, NT, 4>(p, ga, epi, st);
+      else return go<F16, FMT, NT, 2>(p, ga, epi, st);
   }
 }
 
@@ -508,7 +591,7 @@ constexpr unsigned kFp8 = 1u << SPEC_WFMT_FP8_E4M3_ROW, kMx4 = 1u << SPEC_WFMT_M
 template <int NT, unsigned FMTS, class Epi>
 static hipError_t run(const uint16_t *x, int M, int K, const LinearW &w, Epi epi, bool allow_split,
                       hipStream_t st) {
-  const GemmPlan p = gemm_plan(M, epi.units, K / 64, pick_mt(M, epi.units, NT > 4 ? 4 : 8), allow_split);
+  const GemmPlan p = gemm_plan(M, epi.units, K / 64, pick_mt(M, epi.units, NT > 2 ? 2 : 4), allow_split);
   GemmArgs ga{x, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
               p.nb, p.mb, p.spl};
   if constexpr ((FMTS & kFp8) != 0)
@@ -525,29 +608,27 @@ static const float *fp8_scale(const LinearW &w) {
 }
 
 hipError_t launch_linear_f32(const uint16_t *x, int M, int N, int K, LinearW w, float *y, hipStream_t st) {
-  return run<1, kFp8 | kMx4 | kBf16>(x, M, K, w, EpiF32<1>{N / 16, N, y, fp8_scale(w)}, false, st);
+  return run<1, kFp8 | kMx4 | kBf16>(x, M, K, w, EpiF32<1>{N / 32, N, y, fp8_scale(w)}, false, st);
 }
 
 hipError_t launch_residual_partial(const uint16_t *x, int M, int N, int K, LinearW w, float *part, hipStream_t st) {
-  if (M <= 32) return run<1, kFp8 | kMx4>(x, M, K, w, EpiPartial<1>{N / 16, N, part, fp8_scale(w)}, true, st);
-  return run<4, kFp8 | kMx4>(x, M, K, w, EpiPartial<4>{N / 64, N, part, fp8_scale(w)}, true, st);
+  return run<2, kFp8 | kMx4>(x, M, K, w, EpiPartial<2>{N / 64, N, M, part, fp8_scale(w)}, true, st);
 }
 
 hipError_t launch_swiglu(const uint16_t *x, int M, int H, int I, LinearW w, uint16_t *a, hipStream_t st) {
-  if (M <= 32) return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2>{I / 16, I, fp8_scale(w), a}, false, st);
-  return run<4, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<4>{I / 32, I, fp8_scale(w), a}, false, st);
+  return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2>{I / 32, I, fp8_scale(w), a}, false, st);
 }
 
 hipError_t launch_qkv(const uint16_t *x, int M, int H, int D, LinearW w, QkvOut o, hipStream_t st) {
   if (w.wfmt != SPEC_WFMT_FP8_E4M3_ROW) return hipErrorInvalidValue;
   const float *s = reinterpret_cast<const float *>(w.s);
-  if (D == 64) return run<4, kFp8>(x, M, H, w, EpiQkv<4>{o.Hq + 2 * o.Hkv, s, o}, false, st);
-  if (D == 128) return run<8, kFp8>(x, M, H, w, EpiQkv<8>{o.Hq + 2 * o.Hkv, s, o}, false, st);
+  if (D == 64) return run<2, kFp8>(x, M, H, w, EpiQkv<2>{o.Hq + 2 * o.Hkv, s, o}, false, st);
+  if (D == 128) return run<4, kFp8>(x, M, H, w, EpiQkv<4>{o.Hq + 2 * o.Hkv, s, o}, false, st);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,
                             float *logits_dump, hipStream_t st) {
-  return run<4, kBf16>(x, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16}, EpiArgmax<4>{V / 64, V, part, logits_dump},
-                false, st);
+  return run<2, kBf16>(x, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16}, EpiArgmax<2>{V / 64, V, part, logits_dump},
+                       false, st);
 }
