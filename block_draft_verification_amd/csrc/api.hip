@@ -363,6 +363,7 @@ int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int3
   a.max_ctx = max_ctx;
   a.split_len = split_len ? split_len : attention_split_len(batch, Hkv, max_ctx);
   a.nsplit = attn_nsplit(a.split_len, max_ctx);
+  if (a.nsplit > 64) return SPEC_E_ARG;  // the merge step holds at most 64 splits per sequence
   const size_t units = (size_t)batch * Hkv * a.nsplit, R = (size_t)(Hq / Hkv) * 16;
   void *buf = nullptr;
   if (hipMalloc(&buf, units * R * D * 4 + units * R * 8) != hipSuccess) return SPEC_E_NOMEM;

@@ -76,21 +76,24 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
     u32x2_t v[VPT][2];
   };
   TileRegs ra, rb;
+  // Loads are unconditional (indices clamped to the split's last key) so the
+  // wave does not branch around them.
   auto load_tile = [&](TileRegs &tr, int kt0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int c = tid + 256 * i, kk = c / (D / 8), d0 = (c % (D / 8)) * 8, key = kt0 + kk;
-      tr.k[i] = key < key_hi ? *reinterpret_cast<const u32x4_t *>(a.k_cache + (cache_base + key) * D + d0)
-                             : u32x4_t{0, 0, 0, 0};
+      const int c = tid + 256 * i, kk = c / (D / 8), d0 = (c % (D / 8)) * 8, key = min(kt0 + kk, key_hi - 1);
+      tr.k[i] = *reinterpret_cast<const u32x4_t *>(a.k_cache + (cache_base + key) * D + d0);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int c = tid + 256 * i, kk = 2 * (c / (D / 4)), d0 = (c % (D / 4)) * 4, key = kt0 + kk;
+      const int c = tid + 256 * i, kk = 2 * (c / (D / 4)), d0 = (c % (D / 4)) * 4;
 #pragma unroll
-      for (int e = 0; e < 2; ++e)
-        tr.v[i][e] = key + e < key_hi
-                         ? *reinterpret_cast<const u32x2_t *>(a.v_cache + (cache_base + key + e) * D + d0)
-                         : u32x2_t{0, 0};
+      for (int e = 0; e < 2; ++e) {
+        // keys past the split end repeat its last key: their scores are masked to -inf, so
+        // p = 0 and the (finite) values never reach the output
+        const int key = min(kt0 + kk + e, key_hi - 1);
+        tr.v[i][e] = *reinterpret_cast<const u32x2_t *>(a.v_cache + (cache_base + key) * D + d0);
+      }
     }
   };
   auto store_tile = [&](const TileRegs &tr) {
@@ -131,15 +134,25 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
       }
       const int last_visible = n + r;  // row j = r
       float tmax = -INFINITY;
+      if (kt0 + KT <= n && kt0 + KT <= key_hi) {  // whole tile in the committed prefix: nothing to mask
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
+        for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = kt0 + 16 * ks + 4 * g + i;
-          const float v = (key <= last_visible && key < key_hi) ? st[ks][i] * scale_log2 : -INFINITY;
-          st[ks][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
+          for (int i = 0; i < 4; ++i) {
+            st[ks][i] *= scale_log2;
+            tmax = fmaxf(tmax, st[ks][i]);
+          }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int key = kt0 + 16 * ks + 4 * g + i;
+            const float v = (key <= last_visible && key < key_hi) ? st[ks][i] * scale_log2 : -INFINITY;
+            st[ks][i] = v;
+            tmax = fmaxf(tmax, v);
+          }
+      }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       const float mnew = fmaxf(mrow[u], tmax);
@@ -149,13 +162,13 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
         alpha = 1.f;
         pb[0] = pb[1] = u32x4_t{0, 0, 0, 0};
       } else {
-        alpha = exp2f(mrow[u] - mnew);
+        alpha = __builtin_amdgcn_exp2f(mrow[u] - mnew);
         float p[4][4];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            p[ks][i] = exp2f(st[ks][i] - mnew);
+            p[ks][i] = __builtin_amdgcn_exp2f(st[ks][i] - mnew);
             psum += p[ks][i];
           }
         // B operand for keys 32c + {4g+i} (slots 0-3) and 32c + 16 + {4g+i} (slots 4-7)
@@ -218,10 +231,17 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
 }
 
 // o[b*16+j][hq*D + d] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the
-// splits of sequence b, in split order.  One workgroup per (query head, seq).
+// splits of sequence b, in split order.  One workgroup per (query head, seq):
+// the split statistics are loaded in parallel into LDS, each row's weights
+// w_s = 2^(m_s - M) / den are formed once, then every thread sums its 4
+// columns over the splits with independent loads.  A split that saw no key of
+// a row has m_s = -inf and weight 0 (its partial is 0, never NaN).
+#define MAX_SPLITS 64
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  __shared__ float sM[16], sInv[16];
+  __shared__ float2 sML[MAX_SPLITS][16];
+  __shared__ float sW[MAX_SPLITS][16];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int G = a.Hq / a.Hkv, kvh = hq / G, tq = hq % G, R = G * 16;
   const int n = a.kv_len[b];
@@ -230,38 +250,40 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const size_t unit = (size_t)b * a.Hkv + kvh;
   const float *po0 = a.part_o + (unit * a.nsplit) * R * D;
   const float2 *pml0 = a.part_ml + (unit * a.nsplit) * R;
+  for (int i = tid; i < nsplit * 16; i += 256) sML[i >> 4][i & 15] = pml0[(i >> 4) * R + tq * 16 + (i & 15)];
+  __syncthreads();
   if (tid < 16) {
-    const int row = tq * 16 + tid;
     float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pml0[s * R + row].x);
+    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, sML[s][tid].x);
     float den = 0.f;
     for (int s = 0; s < nsplit; ++s) {
-      const float2 ml = pml0[s * R + row];
-      if (ml.x != -INFINITY) den += exp2f(ml.x - M) * ml.y;
+      const float2 ml = sML[s][tid];
+      const float e = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
+      sW[s][tid] = e;
+      den += e * ml.y;
     }
-    sM[tid] = M;
-    sInv[tid] = 1.f / den;
+    const float inv = 1.f / den;
+    for (int s = 0; s < nsplit; ++s) sW[s][tid] *= inv;
   }
   __syncthreads();
   for (int idx = tid; idx < 16 * D / 4; idx += 256) {
     const int j = idx / (D / 4), d = (idx % (D / 4)) * 4, row = tq * 16 + j;
-    const float M = sM[j];
+    const float *p = po0 + (size_t)row * D + d;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int s = 0; s < nsplit; ++s) {
-      const float ms = pml0[s * R + row].x;
-      if (ms != -INFINITY)
-        acc += exp2f(ms - M) * *reinterpret_cast<const f32x4_t *>(po0 + ((size_t)s * R + row) * D + d);
-    }
-    acc *= sInv[j];
+#pragma unroll 4
+    for (int s = 0; s < nsplit; ++s) acc += sW[s][j] * *reinterpret_cast<const f32x4_t *>(p + (size_t)s * R * D);
     *reinterpret_cast<u32x2_t *>(a.o + (size_t)(b * 16 + j) * (a.Hq * D) + hq * D + d) =
         u32x2_t{pack_f16x2(acc[0], acc[1]), pack_f16x2(acc[2], acc[3])};
   }
 }
 
 int attention_split_len(int batch, int Hkv, int max_ctx) {
-  // aim for about 768 workgroups across the batch; splits are whole 64-key tiles
+  // aim for about 768 workgroups across the batch; splits are whole 64-key
+  // tiles and a sequence has at most MAX_SPLITS of them
   const long target = 768;
   long sl = ((long)batch * Hkv * max_ctx + target - 1) / target;
+  const long min_sl = (max_ctx + MAX_SPLITS - 1) / MAX_SPLITS;
+  if (sl < min_sl) sl = min_sl;
   sl = ((sl + KT - 1) / KT) * KT;
   if (sl < KT) sl = KT;
   return (int)sl;

@@ -178,7 +178,7 @@ int spec_debug_set_dump(spec_ctx *ctx, float *hidden, float *logits);
  *   y[m][n] = sum_k x[m][k] * w(n, k)     (fp32 out, [M][N])
  * x: FP16 bits [M][K] for FP8 / MXFP4 weights, BF16 bits for BF16 weights;
  * w in format `wfmt` with scales as in spec_layer_weights (scales NULL for
- * BF16).  K and N multiples of 64.  Allocates its own split scratch.
+ * BF16).  K and N multiples of 64.
  * Synchronous. */
 int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const void *w,
                       const void *scales, int32_t wfmt, float *y, hipStream_t stream);
@@ -187,7 +187,8 @@ int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const 
  * q FP16 [batch*16][Hq*D] (already rotated), BF16 K/V caches of ONE layer
  * ([max_batch][Hkv][max_ctx][D], block rows already stored at kv_len+j),
  * o FP16 [batch*16][Hq*D].  split_len = keys per split (multiple of 64), or
- * 0 for the library's choice.  Synchronous. */
+ * 0 for the library's choice; a split length that gives more than 64 splits
+ * of max_ctx is rejected (SPEC_E_ARG).  Synchronous. */
 int spec_debug_attention(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
                          int32_t max_batch, int32_t max_ctx, const uint16_t *q,
                          const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *kv_len,
