@@ -63,6 +63,7 @@ static int check_model(const spec_model_desc *m) {
     return SPEC_E_SHAPE;
   if (m->head_dim != 64 && m->head_dim != 128) return SPEC_E_SHAPE;
   if (m->hidden % 64 || m->intermediate % 64 || m->vocab % 64) return SPEC_E_SHAPE;
+  if (m->hidden > 4096) return SPEC_E_SHAPE;  // the RMSNorm step keeps a whole row in one wave's registers
   if (m->n_q_heads % m->n_kv_heads || m->n_q_heads / m->n_kv_heads > 8) return SPEC_E_SHAPE;
   if ((m->n_q_heads * m->head_dim) % 64) return SPEC_E_SHAPE;
   if (m->attn_wfmt != SPEC_WFMT_FP8_E4M3_ROW) return SPEC_E_UNSUPPORTED;

@@ -24,42 +24,55 @@ __global__ void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
 
 // h += part[0] + ... + part[ns-1] (split-K partials of the projection that
 // just ran, added in split order), then x = h / sqrt(mean(h^2) + eps) * gain
-// rounded to FP16 (decoder layers) or BF16 (lm_head input).  One wave per row.
+// rounded to FP16 (decoder layers) or BF16 (lm_head input).  One 64-lane
+// workgroup per row; a lane owns the 4-column chunks c = 4*lane + 256*i, and all
+// of a chunk's partial loads are issued before they are added (in order).
 template <bool BF16>
-__global__ void norm_kernel(float *__restrict__ h, const float *__restrict__ part, int ns,
-                            const float *__restrict__ gain, int M, int H, float eps, uint16_t *__restrict__ x,
-                            float *__restrict__ dump) {
-  const int m = blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (m >= M) return;
+__global__ __launch_bounds__(64) void norm_kernel(float *__restrict__ h, const float *__restrict__ part, int ns,
+                                                  const float *__restrict__ gain, int M, int H, float eps,
+                                                  uint16_t *__restrict__ x, float *__restrict__ dump) {
+  constexpr int MAXC = 16;  // H <= 4096
+  const int m = blockIdx.x, lane = threadIdx.x;
   float *hr = h + (size_t)m * H;
+  const size_t pstride = (size_t)M * H;
+  f32x4_t t[MAXC];
   float ss = 0.f;
-  const int nc = (H + 255) / 256;
-  for (int i = 0; i < nc; ++i) {
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
     const int c = lane * 4 + 256 * i;
-    f32x4_t t = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (c < H) {
-      t = *reinterpret_cast<const f32x4_t *>(hr + c);
-      for (int s = 0; s < ns; ++s) t += *reinterpret_cast<const f32x4_t *>(part + ((size_t)s * M + m) * H + c);
-      if (ns) *reinterpret_cast<f32x4_t *>(hr + c) = t;
+    if (c >= H) break;
+    t[i] = *reinterpret_cast<const f32x4_t *>(hr + c);
+    const float *pp = part + (size_t)m * H + c;
+    int s = 0;
+    for (; s + 4 <= ns; s += 4) {
+      const f32x4_t p0 = *reinterpret_cast<const f32x4_t *>(pp + (s + 0) * pstride);
+      const f32x4_t p1 = *reinterpret_cast<const f32x4_t *>(pp + (s + 1) * pstride);
+      const f32x4_t p2 = *reinterpret_cast<const f32x4_t *>(pp + (s + 2) * pstride);
+      const f32x4_t p3 = *reinterpret_cast<const f32x4_t *>(pp + (s + 3) * pstride);
+      t[i] += p0;
+      t[i] += p1;
+      t[i] += p2;
+      t[i] += p3;
     }
-    ss += t[0] * t[0] + t[1] * t[1] + t[2] * t[2] + t[3] * t[3];
+    for (; s < ns; ++s) t[i] += *reinterpret_cast<const f32x4_t *>(pp + s * pstride);
+    if (ns) *reinterpret_cast<f32x4_t *>(hr + c) = t[i];
+    ss += t[i][0] * t[i][0] + t[i][1] * t[i][1] + t[i][2] * t[i][2] + t[i][3] * t[i][3];
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
   const float rs = 1.0f / sqrtf(ss / (float)H + eps);
-  for (int i = 0; i < nc; ++i) {
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
     const int c = lane * 4 + 256 * i;
-    if (c >= H) continue;
-    const f32x4_t t = *reinterpret_cast<const f32x4_t *>(hr + c);  // written above by this lane
+    if (c >= H) break;
     const f32x4_t gv = *reinterpret_cast<const f32x4_t *>(gain + c);
     uint32_t lo, hi;
     if constexpr (BF16) {
-      lo = pack_bf16x2(t[0] * rs * gv[0], t[1] * rs * gv[1]);
-      hi = pack_bf16x2(t[2] * rs * gv[2], t[3] * rs * gv[3]);
+      lo = pack_bf16x2(t[i][0] * rs * gv[0], t[i][1] * rs * gv[1]);
+      hi = pack_bf16x2(t[i][2] * rs * gv[2], t[i][3] * rs * gv[3]);
     } else {
-      lo = pack_f16x2(t[0] * rs * gv[0], t[1] * rs * gv[1]);
-      hi = pack_f16x2(t[2] * rs * gv[2], t[3] * rs * gv[3]);
+      lo = pack_f16x2(t[i][0] * rs * gv[0], t[i][1] * rs * gv[1]);
+      hi = pack_f16x2(t[i][2] * rs * gv[2], t[i][3] * rs * gv[3]);
     }
     *reinterpret_cast<u32x2_t *>(x + (size_t)m * H + c) = u32x2_t{lo, hi};
     if (dump) {
@@ -73,53 +86,51 @@ __global__ void norm_kernel(float *__restrict__ h, const float *__restrict__ par
   }
 }
 
-// One workgroup per sequence: g[j] = argmax over the vocab partials of row
-// b*16+j (lowest id on ties), then tau = first j >= 1 with t[j] != g[j-1]
-// (16 if none) and bonus = g[tau-1] (HunyuanOCR-1.5 / DFlash write-up,
-// inference loop, step 4).
-__global__ void accept_kernel(const ArgmaxPart *__restrict__ part, int nparts, int M,
-                              const int32_t *__restrict__ tokens, int32_t *accept_len, int32_t *bonus,
-                              int32_t *argmax, int32_t *last_tau) {
-  __shared__ float sv[256];
-  __shared__ int32_t si[256];
+// One workgroup of 16 waves per sequence, wave j = block row b*16+j:
+// g[j] = argmax over the vocab partials of the row (lowest id on ties; lanes
+// read the partials with independent loads, then a shuffle tree), then
+// tau = first j >= 1 with t[j] != g[j-1] (16 if none) and bonus = g[tau-1]
+// (HunyuanOCR-1.5 / DFlash write-up, inference loop, step 4).
+__global__ __launch_bounds__(1024) void accept_kernel(const ArgmaxPart *__restrict__ part, int nparts, int M,
+                                                      const int32_t *__restrict__ tokens, int32_t *accept_len,
+                                                      int32_t *bonus, int32_t *argmax, int32_t *last_tau) {
   __shared__ int32_t gsh[16];
-  const int b = blockIdx.x, tid = threadIdx.x;
-  for (int j = 0; j < 16; ++j) {
-    const int m = b * 16 + j;
-    float bv = -INFINITY;
-    int32_t bi = 0x7fffffff;
-    for (int p = tid; p < nparts; p += 256) {
-      const ArgmaxPart q = part[(size_t)m * nparts + p];
-      if (better(q.v, q.i, bv, bi)) {
-        bv = q.v;
-        bi = q.i;
-      }
-    }
-    sv[tid] = bv;
-    si[tid] = bi;
-    __syncthreads();
-    for (int s = 128; s > 0; s >>= 1) {
-      if (tid < s && better(sv[tid + s], si[tid + s], sv[tid], si[tid])) {
-        sv[tid] = sv[tid + s];
-        si[tid] = si[tid + s];
-      }
-      __syncthreads();
-    }
-    if (tid == 0) gsh[j] = si[0] == 0x7fffffff ? 0 : si[0];
-    __syncthreads();
+  const int b = blockIdx.x, j = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const ArgmaxPart *pr = part + (size_t)(b * 16 + j) * nparts;
+  float bv = -INFINITY;
+  int32_t bi = 0x7fffffff;
+  int p = lane;
+  for (; p + 192 < nparts; p += 256) {
+    const ArgmaxPart q0 = pr[p], q1 = pr[p + 64], q2 = pr[p + 128], q3 = pr[p + 192];
+    if (better(q0.v, q0.i, bv, bi)) bv = q0.v, bi = q0.i;
+    if (better(q1.v, q1.i, bv, bi)) bv = q1.v, bi = q1.i;
+    if (better(q2.v, q2.i, bv, bi)) bv = q2.v, bi = q2.i;
+    if (better(q3.v, q3.i, bv, bi)) bv = q3.v, bi = q3.i;
   }
-  if (tid == 0) {
+  for (; p < nparts; p += 64) {
+    const ArgmaxPart q = pr[p];
+    if (better(q.v, q.i, bv, bi)) bv = q.v, bi = q.i;
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    const float ov = __shfl_xor(bv, off);
+    const int32_t oi = __shfl_xor(bi, off);
+    if (better(ov, oi, bv, bi)) bv = ov, bi = oi;
+  }
+  if (lane == 0) gsh[j] = bi == 0x7fffffff ? 0 : bi;
+  __syncthreads();
+  if (threadIdx.x == 0) {
     int tau = 16;
-    for (int j = 1; j < 16; ++j)
-      if (tokens[b * 16 + j] != gsh[j - 1]) {
-        tau = j;
+    for (int k = 1; k < 16; ++k)
+      if (tokens[b * 16 + k] != gsh[k - 1]) {
+        tau = k;
         break;
       }
     accept_len[b] = tau;
     bonus[b] = gsh[tau - 1];
     last_tau[b] = tau;
   }
-  if (argmax && tid < 16) argmax[b * 16 + tid] = gsh[tid];
+  if (argmax && threadIdx.x < 16) argmax[b * 16 + threadIdx.x] = gsh[threadIdx.x];
 }
 
 // kv_len[b] += n (n = n_commit[b], or the last verify's tau).  The block's
@@ -153,19 +164,18 @@ hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16
 
 hipError_t launch_norm(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
                        uint16_t *x, int out_bf16, float *dump, hipStream_t st) {
+  if (H > 4096 || H % 4) return hipErrorInvalidValue;
   if (out_bf16)
-    hipLaunchKernelGGL(norm_kernel<true>, dim3((M + 3) / 4), dim3(256), 0, st, h, part, nsplit, gain, M, H, eps, x,
-                       dump);
+    hipLaunchKernelGGL(norm_kernel<true>, dim3(M), dim3(64), 0, st, h, part, nsplit, gain, M, H, eps, x, dump);
   else
-    hipLaunchKernelGGL(norm_kernel<false>, dim3((M + 3) / 4), dim3(256), 0, st, h, part, nsplit, gain, M, H, eps,
-                       x, dump);
+    hipLaunchKernelGGL(norm_kernel<false>, dim3(M), dim3(64), 0, st, h, part, nsplit, gain, M, H, eps, x, dump);
   return hipGetLastError();
 }
 
 hipError_t launch_accept(const ArgmaxPart *part, int nparts, int M, const int32_t *tokens, int batch,
                          int32_t *accept_len, int32_t *bonus, int32_t *argmax, int32_t *last_tau,
                          hipStream_t st) {
-  hipLaunchKernelGGL(accept_kernel, dim3(batch), dim3(256), 0, st, part, nparts, M, tokens, accept_len,
+  hipLaunchKernelGGL(accept_kernel, dim3(batch), dim3(1024), 0, st, part, nparts, M, tokens, accept_len,
                      bonus, argmax, last_tau);
   return hipGetLastError();
 }

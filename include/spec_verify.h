@@ -135,7 +135,8 @@ typedef struct spec_ctx spec_ctx;
  * allocate the library workspace (activations for max_batch*16 rows, split
  * attention partials, argmax partials, a RoPE cos/sin table for positions
  * < max_ctx, the device error word).  Supported: head_dim 64 or 128, hidden
- * and intermediate multiples of 64, vocab a multiple of 64, Hq % Hkv == 0.
+ * and intermediate multiples of 64 with hidden <= 4096, vocab a multiple of
+ * 64, Hq % Hkv == 0 with Hq / Hkv <= 8.
  * Synchronous (allocations and one table upload on `stream`).  *out is set
  * only on success. */
 int spec_verify_init(const spec_model_desc *model /*host*/, const spec_weights *w /*host*/,
