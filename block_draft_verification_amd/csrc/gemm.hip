@@ -132,16 +132,20 @@ struct GemmArgs {
   int M, K;
   const uint8_t *w, *s;
   int nb, mb;         // N blocks (4 units each), M blocks
+  int per_xcd;        // tiles per XCD (gridDim.x = 8 * per_xcd)
   int spl;            // k steps (of 64) per split; gridDim.z splits
 };
 
-// Linear workgroup id -> (N block, M block): the M blocks of one N block are
-// consecutive workgroups of one XCD (XCD = id % 8).
-__device__ __forceinline__ bool tile_of(int L, int nb, int mb, int &n, int &m) {
-  const int xcd = L & 7, k = L >> 3;
-  n = xcd + 8 * (k / mb);
-  m = k % mb;
-  return n < nb;
+// Linear workgroup id -> (N block, M block).  Workgroup L runs on XCD L % 8;
+// the nb*mb tiles, in N-major order, are cut into 8 contiguous ranges of
+// per_xcd tiles, one per XCD, so the M blocks that share an N block's weight
+// rows sit on one XCD (one L2) as far as possible and every XCD gets work even
+// when there are fewer than 8 N blocks.
+__device__ __forceinline__ bool tile_of(int L, int nb, int mb, int per_xcd, int &n, int &m) {
+  const int t = (L & 7) * per_xcd + (L >> 3);
+  n = t / mb;
+  m = t % mb;
+  return t < nb * mb;
 }
 
 // s_waitcnt with only vmcnt constrained (gfx9 encoding: vmcnt[3:0] in bits 3:0,
@@ -182,7 +186,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
   __shared__ __align__(16) uint16_t As[LDS_BYTES / 2];
 
   int nblk, mblk;
-  if (!tile_of(blockIdx.x, ga.nb, ga.mb, nblk, mblk)) return;  // whole workgroup
+  if (!tile_of(blockIdx.x, ga.nb, ga.mb, ga.per_xcd, nblk, mblk)) return;  // whole workgroup
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int unit = nblk * 4 + wave;
@@ -545,7 +549,7 @@ GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split) {
   if (s < 1) s = 1;
   p.spl = (ksteps + s - 1) / s;
   p.nsplit = (ksteps + p.spl - 1) / p.spl;  // every split non-empty
-  p.grid_x = 8 * ((p.nb + 7) / 8) * p.mb;
+  p.grid_x = 8 * ((tiles + 7) / 8);
   return p;
 }
 
@@ -593,7 +597,7 @@ static hipError_t run(const uint16_t *x, int M, int K, const LinearW &w, Epi epi
                       hipStream_t st) {
   const GemmPlan p = gemm_plan(M, epi.units, K / 64, pick_mt(M, epi.units, NT > 2 ? 2 : 4), allow_split);
   GemmArgs ga{x, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
-              p.nb, p.mb, p.spl};
+              p.nb, p.mb, p.grid_x / 8, p.spl};
   if constexpr ((FMTS & kFp8) != 0)
     if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW) return go_m<true, SPEC_WFMT_FP8_E4M3_ROW, NT>(p, ga, epi, st);
   if constexpr ((FMTS & kMx4) != 0)
