@@ -192,7 +192,8 @@ def main():
     assert ver.device_error() == 0
 
     # per-kernel-class launch durations (eager passes, events on the stream)
-    kinds = ["qkv", "attention", "o_proj", "gate_up", "down", "lm_head", "rmsnorm", "accept", "embed", "commit"]
+    kinds = ["qkv", "attention", "attn_merge", "o_proj", "gate_up", "down", "lm_head", "rmsnorm", "accept", "embed",
+             "commit"]
     per_kind = {}
     reps = max(3, min(20, args.steps // 5))
     for k in kinds:

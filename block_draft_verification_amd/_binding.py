@@ -60,7 +60,7 @@ EXPORTS = {
 }
 
 KERNEL_KINDS = {"embed": 1, "rmsnorm": 2, "qkv": 3, "attention": 4, "o_proj": 5, "gate_up": 6, "down": 7,
-                "lm_head": 8, "accept": 9, "commit": 10}
+                "lm_head": 8, "accept": 9, "commit": 10, "attn_merge": 11}
 
 _lib = None
 

@@ -232,7 +232,11 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     aa.v_cache = vc;
     {
       Timed t(c, SPEC_K_ATTENTION, st);
-      CK(launch_attention(aa, D, st));
+      CK(launch_attention_splits(aa, D, st));
+    }
+    {
+      Timed t(c, SPEC_K_ATTN_MERGE, st);
+      CK(launch_attention_merge(aa, D, st));
     }
     {
       Timed t(c, SPEC_K_OPROJ, st);
@@ -298,7 +302,7 @@ int spec_get_device_error(spec_ctx *c, int32_t *code, hipStream_t st) {
 }
 
 int spec_debug_time_kernel(spec_ctx *c, int32_t kind) {
-  if (!c || kind < SPEC_K_NONE || kind > SPEC_K_COMMIT) return SPEC_E_ARG;
+  if (!c || kind < SPEC_K_NONE || kind > SPEC_K_ATTN_MERGE) return SPEC_E_ARG;
   if (kind != SPEC_K_NONE && c->ev.empty()) {
     c->ev.resize(2 * kMaxTimedLaunches);
     for (hipEvent_t &e : c->ev)

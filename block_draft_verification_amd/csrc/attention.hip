@@ -289,17 +289,29 @@ int attention_split_len(int batch, int Hkv, int max_ctx) {
   return (int)sl;
 }
 
-hipError_t launch_attention(const AttnArgs &a, int D, hipStream_t st) {
+hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st) {
   dim3 grid(a.nsplit, a.Hkv, a.batch);
-  if (D == 64) {
+  if (D == 64)
     hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(256), 0, st, a, (float)(1.4426950408889634 / 8.0));
-    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(a.Hq, a.batch), dim3(256), 0, st, a);
-  } else if (D == 128) {
+  else if (D == 128)
     hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(256), 0, st, a,
                        (float)(1.4426950408889634 / 11.313708498984761));
-    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(a.Hq, a.batch), dim3(256), 0, st, a);
-  } else {
+  else
     return hipErrorInvalidValue;
-  }
   return hipGetLastError();
+}
+
+hipError_t launch_attention_merge(const AttnArgs &a, int D, hipStream_t st) {
+  if (D == 64)
+    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(a.Hq, a.batch), dim3(256), 0, st, a);
+  else if (D == 128)
+    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(a.Hq, a.batch), dim3(256), 0, st, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_attention(const AttnArgs &a, int D, hipStream_t st) {
+  const hipError_t e = launch_attention_splits(a, D, st);
+  return e != hipSuccess ? e : launch_attention_merge(a, D, st);
 }

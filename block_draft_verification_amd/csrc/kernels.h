@@ -58,7 +58,9 @@ struct AttnArgs {
   int batch, Hq, Hkv, max_ctx, split_len, nsplit;
 };
 // split attention (partials) followed by the merge kernel (writes o)
-hipError_t launch_attention(const AttnArgs &a, int D, hipStream_t st);
+hipError_t launch_attention(const AttnArgs &a, int D, hipStream_t st);  // splits, then merge
+hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st);
+hipError_t launch_attention_merge(const AttnArgs &a, int D, hipStream_t st);
 int attention_split_len(int batch, int Hkv, int max_ctx);
 
 // ---- small kernels ----

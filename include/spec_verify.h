@@ -195,11 +195,12 @@ int spec_debug_attention(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, i
                          const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *kv_len,
                          uint16_t *o, int32_t split_len, hipStream_t stream);
 
-/* Kernel classes for spec_debug_time_kernel. */
+/* Kernel classes for spec_debug_time_kernel.  SPEC_K_ATTENTION is the split
+ * attention kernel alone; SPEC_K_ATTN_MERGE the kernel that merges its splits. */
 typedef enum {
   SPEC_K_NONE = 0, SPEC_K_EMBED = 1, SPEC_K_RMSNORM = 2, SPEC_K_QKV = 3, SPEC_K_ATTENTION = 4,
   SPEC_K_OPROJ = 5, SPEC_K_GATE_UP = 6, SPEC_K_DOWN = 7, SPEC_K_LM_HEAD = 8, SPEC_K_ACCEPT = 9,
-  SPEC_K_COMMIT = 10
+  SPEC_K_COMMIT = 10, SPEC_K_ATTN_MERGE = 11
 } spec_kernel_kind;
 
 /* Test/measurement hook: while `kind` is set, every launch of that kernel
