@@ -7,16 +7,22 @@
 // Query head h reads KV head h / G, so the G*16 query rows of one KV head
 // share every K/V tile: the pass is bound by reading the cache once.
 //
-// Work unit = (split, kv head, sequence): one workgroup of 4 waves walks its
-// split's keys in tiles of 64.  Each tile is loaded into registers two tiles
-// ahead, converted from the BF16 cache to FP16 and stored in LDS (K
-// row-major, V transposed).  A wave owns 16-row query tiles (one query head
-// each, rows j = 0..15).  Scores are computed transposed, S^T = K Q^T, with
-// the MFMA A operand taken from K in LDS and the B operand = Q^T (FP16) held
-// in registers; in that layout a lane (r, g) holds 16 keys of query r, so
-// softmax statistics need only xor-16/32 shuffles, and the FP16
-// probabilities are already the B operand of O^T = V^T P^T.  Online softmax
-// in fp32, base 2.
+// Work unit = (key split, kv head, sequence): one workgroup of ceil(G/2)
+// waves; wave w owns the 32 query rows of heads 2w, 2w+1 (rows of a head past
+// G are padding and never stored).  The split's keys are walked in tiles of
+// 64: the next tile's K/V is loaded into registers while the current one is
+// computed, converted from the BF16 cache to FP16 and stored in LDS (K
+// row-major, V transposed; two LDS buffers, one barrier per tile).
+//
+// MFMA v_mfma_f32_32x32x16_f16.  Scores are computed transposed, S^T = K Q^T,
+// 32 keys x 32 queries per block: lane (c, h) supplies key c (A) and query c
+// (B) at the d slice (D/2)h + 8i of MFMA i (the same permutation of d on both
+// sides), and ends with query c's scores for keys 8q + 4h + (0..3).  Softmax
+// statistics therefore need one xor-32 shuffle, and the FP16 probabilities
+// are already the B operand of O^T = V^T P^T, whose 16-key slices use the
+// keys 16s + 4h + (0..3) and 16s + 8 + 4h + (0..3) of lane half h.  Online
+// softmax in fp32, base 2; rows that have seen no visible key yet use 0 as
+// their running maximum, so exp2(-inf) = 0 and nothing becomes NaN.
 //
 // Splits write unnormalised partials (m, l, o); a second kernel merges them
 // in split order per (query head, sequence), so the result does not depend on
@@ -27,17 +33,16 @@
 
 #define KT 64  // keys per LDS tile
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2) {
-  constexpr int DT = D / 16;   // 16-wide d tiles
-  constexpr int DK = D / 32;   // k32 steps over d
-  constexpr int KP = D + 8;    // K row pitch (16-bit elements)
-  constexpr int VP = KT + 4;   // V^T row pitch (16-bit elements), 8-byte aligned rows
-  constexpr int KCH = KT * D / 8;        // K: 16-byte chunks (one key, 8 d) per tile
-  constexpr int VCH = (KT / 2) * D / 4;  // V: chunks of (2 keys, 4 d)
-  constexpr int KPT = KCH / 256, VPT = VCH / 256;
-  __shared__ __align__(16) uint16_t Ks[KT * KP];
-  __shared__ __align__(16) uint16_t Vt[D * VP];
+template <int D, int NW>  // NW = waves = ceil(G/2)
+__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_log2) {
+  constexpr int DS = D / 16;           // S MFMAs per 32-key block (k = 16 each)
+  constexpr int DT = D / 32;           // 32-wide d tiles of O^T
+  constexpr int KP = D + 8;            // K row pitch (16-bit elements): rows land on distinct bank groups
+  constexpr int VP = KT + 4;           // V^T row pitch (16-bit elements), rows 8-byte aligned
+  constexpr int KCH = KT * D / 8;      // K: 16-byte chunks (one key, 8 d) per tile
+  constexpr int VCH = KT * D / 8;      // V: chunks of (2 keys, 4 d)
+  __shared__ __align__(16) uint16_t Ks[2][KT * KP];
+  __shared__ __align__(16) uint16_t Vt[2][D * VP];
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
@@ -47,186 +52,179 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a, float scale_log2)
   if (sp >= nsplit) return;  // whole workgroup
   const int key_lo = sp * a.split_len, key_hi = min(key_lo + a.split_len, L);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, r = lane & 15, g = lane >> 4;
+  constexpr int T = 64 * NW;
+  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, h = lane >> 5;
+  const int wave = tid >> 6;
   const size_t cache_base = ((size_t)b * a.Hkv + kvh) * a.max_ctx;
   const size_t unit = (size_t)b * a.Hkv + kvh;
-  const int qstride = a.Hq * D;
 
-  // this wave's query tiles: wave, wave+4 (G <= 8)
-  const int nqt = (G - wave + 3) / 4;
-  u32x4_t qf[2][DK];
-  f32x4_t oacc[2][DT];
-  float mrow[2], lrow[2];
+  // this wave's queries: lane (c, h) -> head 2*wave + c/16 of the group, block row c%16
+  const int hg = 2 * wave + (c >> 4), j = c & 15;
+  const bool qvalid = hg < G;
+  u32x4_t qf[DS];
+  {
+    const uint16_t *qp = a.q + (size_t)(b * 16 + j) * (a.Hq * D) + (kvh * G + (qvalid ? hg : 0)) * D + (D / 2) * h;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    mrow[u] = -INFINITY;
-    lrow[u] = 0.f;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[u][dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    if (u < nqt) {
-      const int hq = kvh * G + wave + 4 * u;
-      const uint16_t *qp = a.q + (size_t)(b * 16 + r) * qstride + hq * D + 8 * g;
-#pragma unroll
-      for (int kd = 0; kd < DK; ++kd) qf[u][kd] = *reinterpret_cast<const u32x4_t *>(qp + 32 * kd);
-    }
+    for (int i = 0; i < DS; ++i)
+      qf[i] = qvalid ? *reinterpret_cast<const u32x4_t *>(qp + 8 * i) : u32x4_t{0, 0, 0, 0};
   }
+  f32x16_t oacc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) oacc[dt][v] = 0.f;
+  float mrow = -INFINITY, lrow = 0.f;
 
+  // Tile loads are unconditional (key indices clamped to the split's last key,
+  // whose finite values are masked out) so the wave never branches around them.
+  constexpr int KPT = (KCH + T - 1) / T, VPT = (VCH + T - 1) / T;  // chunks per thread (last one partial for NW = 3)
   struct TileRegs {
     u32x4_t k[KPT];
     u32x2_t v[VPT][2];
   };
   TileRegs ra, rb;
-  // Loads are unconditional (indices clamped to the split's last key) so the
-  // wave does not branch around them.
   auto load_tile = [&](TileRegs &tr, int kt0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int c = tid + 256 * i, kk = c / (D / 8), d0 = (c % (D / 8)) * 8, key = min(kt0 + kk, key_hi - 1);
+      const int ch = min(tid + T * i, KCH - 1), kk = ch / (D / 8), d0 = (ch % (D / 8)) * 8,
+                key = min(kt0 + kk, key_hi - 1);
       tr.k[i] = *reinterpret_cast<const u32x4_t *>(a.k_cache + (cache_base + key) * D + d0);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int c = tid + 256 * i, kk = 2 * (c / (D / 4)), d0 = (c % (D / 4)) * 4;
+      const int ch = min(tid + T * i, VCH - 1), kk = 2 * (ch / (D / 4)), d0 = (ch % (D / 4)) * 4;
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
-        // keys past the split end repeat its last key: their scores are masked to -inf, so
-        // p = 0 and the (finite) values never reach the output
         const int key = min(kt0 + kk + e, key_hi - 1);
         tr.v[i][e] = *reinterpret_cast<const u32x2_t *>(a.v_cache + (cache_base + key) * D + d0);
       }
     }
   };
-  auto store_tile = [&](const TileRegs &tr) {
+  auto store_tile = [&](const TileRegs &tr, int buf) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const int c = tid + 256 * i, kk = c / (D / 8), d0 = (c % (D / 8)) * 8;
+      const int ch = tid + T * i, kk = ch / (D / 8), d0 = (ch % (D / 8)) * 8;
+      if (KCH % T != 0 && ch >= KCH) break;  // NW = 3: the last round is partial
       const u32x4_t v = tr.k[i];
-      *reinterpret_cast<u32x4_t *>(&Ks[kk * KP + d0]) =
+      *reinterpret_cast<u32x4_t *>(&Ks[buf][kk * KP + d0]) =
           u32x4_t{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
-      const int c = tid + 256 * i, kk = 2 * (c / (D / 4)), d0 = (c % (D / 4)) * 4;
+      const int ch = tid + T * i, kk = 2 * (ch / (D / 4)), d0 = (ch % (D / 4)) * 4;
+      if (VCH % T != 0 && ch >= VCH) break;
       const uint32_t a0 = bf16x2_to_f16x2(tr.v[i][0].x), a1 = bf16x2_to_f16x2(tr.v[i][0].y);
       const uint32_t b0 = bf16x2_to_f16x2(tr.v[i][1].x), b1 = bf16x2_to_f16x2(tr.v[i][1].y);
       // (key kk, key kk+1) pairs for d0 .. d0+3
-      *reinterpret_cast<uint32_t *>(&Vt[(d0 + 0) * VP + kk]) = (a0 & 0xffff) | (b0 << 16);
-      *reinterpret_cast<uint32_t *>(&Vt[(d0 + 1) * VP + kk]) = (a0 >> 16) | (b0 & 0xffff0000u);
-      *reinterpret_cast<uint32_t *>(&Vt[(d0 + 2) * VP + kk]) = (a1 & 0xffff) | (b1 << 16);
-      *reinterpret_cast<uint32_t *>(&Vt[(d0 + 3) * VP + kk]) = (a1 >> 16) | (b1 & 0xffff0000u);
+      uint16_t *vt = &Vt[buf][0];
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 0) * VP + kk]) = (a0 & 0xffff) | (b0 << 16);
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 1) * VP + kk]) = (a0 >> 16) | (b0 & 0xffff0000u);
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 2) * VP + kk]) = (a1 & 0xffff) | (b1 << 16);
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 3) * VP + kk]) = (a1 >> 16) | (b1 & 0xffff0000u);
     }
   };
 
-  auto compute = [&](int kt0) {
+  auto compute = [&](int kt0, int buf) {
+    const uint16_t *ks = &Ks[buf][0];
+    const uint16_t *vt = &Vt[buf][0];
+    // S^T for the tile's two 32-key blocks
+    f32x16_t st[2];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      if (u >= nqt) break;  // wave-uniform
-      // S^T tiles: 4 subtiles of 16 keys; lane holds keys kt0 + 16ks + 4g + i for query r
-      f32x4_t st[4];
+    for (int blk = 0; blk < 2; ++blk) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        st[ks] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int v = 0; v < 16; ++v) st[blk][v] = 0.f;
+      const uint16_t *krow = ks + (32 * blk + c) * KP + (D / 2) * h;
 #pragma unroll
-        for (int kd = 0; kd < DK; ++kd) {
-          const u32x4_t kf = *reinterpret_cast<const u32x4_t *>(&Ks[(16 * ks + r) * KP + 32 * kd + 8 * g]);
-          st[ks] = mfma16x16x32_f16(kf, qf[u][kd], st[ks]);
+      for (int i = 0; i < DS; ++i)
+        st[blk] = mfma32x32x16_f16(*reinterpret_cast<const u32x4_t *>(krow + 8 * i), qf[i], st[blk]);
+    }
+    float tmax = -INFINITY;
+    if (kt0 + KT <= n && kt0 + KT <= key_hi) {  // whole tile in the committed prefix: nothing to mask
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          st[blk][v] *= scale_log2;
+          tmax = fmaxf(tmax, st[blk][v]);
         }
-      }
-      const int last_visible = n + r;  // row j = r
-      float tmax = -INFINITY;
-      if (kt0 + KT <= n && kt0 + KT <= key_hi) {  // whole tile in the committed prefix: nothing to mask
+    } else {
+      const int last_visible = min(n + j, key_hi - 1);
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
+      for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            st[ks][i] *= scale_log2;
-            tmax = fmaxf(tmax, st[ks][i]);
-          }
-      } else {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kt0 + 16 * ks + 4 * g + i;
-            const float v = (key <= last_visible && key < key_hi) ? st[ks][i] * scale_log2 : -INFINITY;
-            st[ks][i] = v;
-            tmax = fmaxf(tmax, v);
-          }
-      }
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      const float mnew = fmaxf(mrow[u], tmax);
-      float alpha, psum = 0.f;
-      u32x4_t pb[2];
-      if (mnew == -INFINITY) {  // nothing visible yet for this row
-        alpha = 1.f;
-        pb[0] = pb[1] = u32x4_t{0, 0, 0, 0};
-      } else {
-        alpha = __builtin_amdgcn_exp2f(mrow[u] - mnew);
-        float p[4][4];
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            p[ks][i] = __builtin_amdgcn_exp2f(st[ks][i] - mnew);
-            psum += p[ks][i];
-          }
-        // B operand for keys 32c + {4g+i} (slots 0-3) and 32c + 16 + {4g+i} (slots 4-7)
-#pragma unroll
-        for (int c = 0; c < 2; ++c)
-          pb[c] = u32x4_t{pack_f16x2(p[2 * c][0], p[2 * c][1]), pack_f16x2(p[2 * c][2], p[2 * c][3]),
-                          pack_f16x2(p[2 * c + 1][0], p[2 * c + 1][1]),
-                          pack_f16x2(p[2 * c + 1][2], p[2 * c + 1][3])};
-      }
-      psum += __shfl_xor(psum, 16);
-      psum += __shfl_xor(psum, 32);
-      mrow[u] = mnew;
-      lrow[u] = lrow[u] * alpha + psum;
-#pragma unroll
-      for (int dt = 0; dt < DT; ++dt) oacc[u][dt] = oacc[u][dt] * alpha;
-      // O^T += V^T P^T
-#pragma unroll
-      for (int c = 0; c < 2; ++c)
-#pragma unroll
-        for (int dt = 0; dt < DT; ++dt) {
-          const uint16_t *vrow = &Vt[(16 * dt + r) * VP + 32 * c + 4 * g];
-          const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
-          const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 16);
-          oacc[u][dt] = mfma16x16x32_f16(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb[c], oacc[u][dt]);
+        for (int v = 0; v < 16; ++v) {
+          const int key = kt0 + 32 * blk + 8 * (v >> 2) + 4 * h + (v & 3);
+          const float x = key <= last_visible ? st[blk][v] * scale_log2 : -INFINITY;
+          st[blk][v] = x;
+          tmax = fmaxf(tmax, x);
         }
+    }
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+    const float mnew = fmaxf(mrow, tmax);
+    const float mref = mnew == -INFINITY ? 0.f : mnew;
+    const float alpha = __builtin_amdgcn_exp2f(mrow - mref);
+    float psum = 0.f;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        st[blk][v] = __builtin_amdgcn_exp2f(st[blk][v] - mref);
+        psum += st[blk][v];
+      }
+    psum += __shfl_xor(psum, 32);
+    mrow = mnew;
+    lrow = lrow * alpha + psum;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    // O^T += V^T P^T over 4 slices of 16 keys
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
+      const int blk = sl >> 1, q0 = 2 * (sl & 1);
+      const u32x4_t pb = u32x4_t{pack_f16x2(st[blk][4 * q0 + 0], st[blk][4 * q0 + 1]),
+                                 pack_f16x2(st[blk][4 * q0 + 2], st[blk][4 * q0 + 3]),
+                                 pack_f16x2(st[blk][4 * q0 + 4], st[blk][4 * q0 + 5]),
+                                 pack_f16x2(st[blk][4 * q0 + 6], st[blk][4 * q0 + 7])};
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) {
+        const uint16_t *vrow = vt + (32 * dt + c) * VP + 16 * sl + 4 * h;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 8);
+        oacc[dt] = mfma32x32x16_f16(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb, oacc[dt]);
+      }
     }
   };
 
+  // Tile t is computed from LDS buffer t&1 while tiles t+1 and t+2 are in
+  // flight in two register sets (the loop is unrolled by two so the sets have
+  // fixed names).  The barrier at each step makes tile t visible and frees
+  // buffer (t+1)&1.  Loads and stores past the split end are unconditional
+  // (clamped keys into a buffer nobody reads) so the body does not branch.
   load_tile(ra, key_lo);
-  if (key_lo + KT < key_hi) load_tile(rb, key_lo + KT);
-  // barriers only order LDS traffic (lds_barrier): a __syncthreads() here would
-  // also wait for the prefetched tile and serialise the pipeline
+  load_tile(rb, key_lo + KT);
+  store_tile(ra, 0);
+  load_tile(ra, key_lo + 2 * KT);
   for (int kt0 = key_lo; kt0 < key_hi; kt0 += 2 * KT) {
-    lds_barrier();  // previous tile consumed
-    store_tile(ra);
     lds_barrier();
-    if (kt0 + 2 * KT < key_hi) load_tile(ra, kt0 + 2 * KT);  // two tiles in flight during the math
-    compute(kt0);
-    if (kt0 + KT >= key_hi) break;
+    store_tile(rb, 1);
+    load_tile(rb, kt0 + 3 * KT);
+    compute(kt0, 0);
     lds_barrier();
-    store_tile(rb);
-    lds_barrier();
-    if (kt0 + 3 * KT < key_hi) load_tile(rb, kt0 + 3 * KT);
-    compute(kt0 + KT);
+    store_tile(ra, 0);
+    load_tile(ra, kt0 + 4 * KT);
+    if (kt0 + KT < key_hi) compute(kt0 + KT, 1);
   }
 
-  // partials: row R = tile*16 + j, o[d] with d = 16dt + 4g + i held by lane (r = j, g)
-  const int R = G * 16;
-  float *po = a.part_o + ((unit * a.nsplit + sp) * R) * D;
-  float2 *pml = a.part_ml + (unit * a.nsplit + sp) * R;
-#pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    if (u >= nqt) break;
-    const int row = (wave + 4 * u) * 16 + r;
+  // partials: group row R = head*16 + j = 32*wave + c; lane (c, h) holds d = 32dt + 8q + 4h + (0..3)
+  if (qvalid) {
+    const int R = G * 16, row = 32 * wave + c;
+    float *po = a.part_o + ((unit * a.nsplit + sp) * R + row) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<f32x4_t *>(po + (size_t)row * D + 16 * dt + 4 * g) = oacc[u][dt];
-    if (g == 0) pml[row] = make_float2(mrow[u], lrow[u]);
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t *>(po + 32 * dt + 8 * q + 4 * h) =
+            f32x4_t{oacc[dt][4 * q], oacc[dt][4 * q + 1], oacc[dt][4 * q + 2], oacc[dt][4 * q + 3]};
+    if (h == 0) a.part_ml[(unit * a.nsplit + sp) * R + row] = make_float2(mrow, lrow);
   }
 }
 
@@ -290,14 +288,29 @@ int attention_split_len(int batch, int Hkv, int max_ctx) {
 }
 
 hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st) {
-  dim3 grid(a.nsplit, a.Hkv, a.batch);
-  if (D == 64)
-    hipLaunchKernelGGL(attn_kernel<64>, grid, dim3(256), 0, st, a, (float)(1.4426950408889634 / 8.0));
-  else if (D == 128)
-    hipLaunchKernelGGL(attn_kernel<128>, grid, dim3(256), 0, st, a,
-                       (float)(1.4426950408889634 / 11.313708498984761));
-  else
+  const int G = a.Hq / a.Hkv;
+  if (G < 1 || G > 8) return hipErrorInvalidValue;
+  const int nw = (G + 1) / 2;
+  dim3 grid(a.nsplit, a.Hkv, a.batch), block(64 * nw);
+  if (D == 64) {
+    const float sc = (float)(1.4426950408889634 / 8.0);
+    switch (nw) {
+      case 1: hipLaunchKernelGGL((attn_kernel<64, 1>), grid, block, 0, st, a, sc); break;
+      case 2: hipLaunchKernelGGL((attn_kernel<64, 2>), grid, block, 0, st, a, sc); break;
+      case 3: hipLaunchKernelGGL((attn_kernel<64, 3>), grid, block, 0, st, a, sc); break;
+      default: hipLaunchKernelGGL((attn_kernel<64, 4>), grid, block, 0, st, a, sc); break;
+    }
+  } else if (D == 128) {
+    const float sc = (float)(1.4426950408889634 / 11.313708498984761);
+    switch (nw) {
+      case 1: hipLaunchKernelGGL((attn_kernel<128, 1>), grid, block, 0, st, a, sc); break;
+      case 2: hipLaunchKernelGGL((attn_kernel<128, 2>), grid, block, 0, st, a, sc); break;
+      case 3: hipLaunchKernelGGL((attn_kernel<128, 3>), grid, block, 0, st, a, sc); break;
+      default: hipLaunchKernelGGL((attn_kernel<128, 4>), grid, block, 0, st, a, sc); break;
+    }
+  } else {
     return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

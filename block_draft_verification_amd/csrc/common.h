@@ -123,5 +123,5 @@ __device__ __forceinline__ void set_error(int32_t *err, int32_t bit) {
 
 // argmax pair ordering: larger value wins, lower index on equal values.
 __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi) {
-  return v > bv || (v == bv && i < bi);
+  return (v > bv) | ((v == bv) & (i < bi));  // bitwise: no short-circuit branches
 }

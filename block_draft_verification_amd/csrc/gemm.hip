@@ -38,6 +38,12 @@
 #ifndef GEMM_DEPTH
 #define GEMM_DEPTH 2
 #endif
+#ifndef GEMM_BF16_OCC2
+#define GEMM_BF16_OCC2 0
+#endif
+#ifndef GEMM_LM_MAXMT
+#define GEMM_LM_MAXMT 4
+#endif
 #ifndef GEMM_MIN_TILES
 #define GEMM_MIN_TILES 128
 #endif
@@ -168,7 +174,7 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 
 // Waves per SIMD the register budget is sized for.
 template <int FMT, int NT, int MT> struct GemmOcc {
-  static constexpr int value = (NT * MT <= 4 && FMT != SPEC_WFMT_BF16) ? 2 : 1;
+  static constexpr int value = (NT * MT <= 4 && (FMT != SPEC_WFMT_BF16 || GEMM_BF16_OCC2)) ? 2 : 1;
 };
 
 template <bool F16, int FMT, int NT, int MT, class Epi>
@@ -502,6 +508,8 @@ struct EpiArgmax {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = m0 + 32 * mt + c;
+      // a lane visits its candidates in increasing vocab index, so a strict
+      // ">" keeps the lowest index among equal maxima; selects, not branches
       float bv = -INFINITY;
       int32_t bi = 0x7fffffff;
 #pragma unroll
@@ -509,17 +517,15 @@ struct EpiArgmax {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int n = row(unit, t) + 8 * (v >> 2) + 4 * h + (v & 3);
-          if (better(acc[t][mt][v], n, bv, bi)) {
-            bv = acc[t][mt][v];
-            bi = n;
-          }
+          const bool gt = acc[t][mt][v] > bv;
+          bv = gt ? acc[t][mt][v] : bv;
+          bi = gt ? n : bi;
         }
       const float ov = __shfl_xor(bv, 32);  // the other half holds the other rows of the same block row
       const int32_t oi = __shfl_xor(bi, 32);
-      if (better(ov, oi, bv, bi)) {
-        bv = ov;
-        bi = oi;
-      }
+      const bool take = better(ov, oi, bv, bi);
+      bv = take ? ov : bv;
+      bi = take ? oi : bi;
       if (m < M) {
         if (h == 0) part[(size_t)m * units + unit] = ArgmaxPart{bv, bi};
         if (logits) {
@@ -592,10 +598,10 @@ static hipError_t go_m(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hi
 // only those kernels are instantiated.
 constexpr unsigned kFp8 = 1u << SPEC_WFMT_FP8_E4M3_ROW, kMx4 = 1u << SPEC_WFMT_MXFP4, kBf16 = 1u << SPEC_WFMT_BF16;
 
-template <int NT, unsigned FMTS, class Epi>
+template <int NT, unsigned FMTS, class Epi, int MAXMT = (NT > 2 ? 2 : 4)>
 static hipError_t run(const uint16_t *x, int M, int K, const LinearW &w, Epi epi, bool allow_split,
                       hipStream_t st) {
-  const GemmPlan p = gemm_plan(M, epi.units, K / 64, pick_mt(M, epi.units, NT > 2 ? 2 : 4), allow_split);
+  const GemmPlan p = gemm_plan(M, epi.units, K / 64, pick_mt(M, epi.units, MAXMT), allow_split);
   GemmArgs ga{x, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
               p.nb, p.mb, p.grid_x / 8, p.spl};
   if constexpr ((FMTS & kFp8) != 0)
@@ -633,6 +639,6 @@ hipError_t launch_qkv(const uint16_t *x, int M, int H, int D, LinearW w, QkvOut 
 
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,
                             float *logits_dump, hipStream_t st) {
-  return run<2, kBf16>(x, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16}, EpiArgmax<2>{V / 64, V, part, logits_dump},
-                       false, st);
+  return run<2, kBf16, EpiArgmax<2>, GEMM_LM_MAXMT>(x, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16},
+                                                   EpiArgmax<2>{V / 64, V, part, logits_dump}, false, st);
 }
