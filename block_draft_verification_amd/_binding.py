@@ -49,6 +49,8 @@ EXPORTS = {
                               _P, ctypes.POINTER(_P)]),
     "spec_verify_block": (_I, [_P, _I, _P, _P, _P, _P, _P]),
     "spec_commit_kv": (_I, [_P, _I, _P, _P]),
+    "spec_prefill": (_I, [_P, _I, _P, _I, _P, _P, _P, _P]),
+    "spec_export_hidden": (_I, [_P, _I, _P, _P]),
     "spec_verify_destroy": (_I, [_P]),
     "spec_get_device_error": (_I, [_P, ctypes.POINTER(_I), _P]),
     "spec_status_str": (ctypes.c_char_p, [_I]),
@@ -181,6 +183,24 @@ class Verifier:
 
     def commit(self, batch: int, n_commit: torch.Tensor | None = None):
         _check(load_library().spec_commit_kv(self._h, batch, _ptr(n_commit), _stream()), "spec_commit_kv")
+
+    def prefill(self, prompt: torch.Tensor, lengths: torch.Tensor, anchor_hidden: torch.Tensor | None = None,
+                pending: torch.Tensor | None = None):
+        """prompt int32 [B, T], lengths int32 [B] on the device; appends each
+        prompt to its cache.  Returns the pending tokens (int32 [B])."""
+        B, T = prompt.shape
+        assert prompt.dtype == torch.int32 and prompt.is_contiguous() and lengths.dtype == torch.int32
+        pending = torch.empty(B, dtype=torch.int32, device=prompt.device) if pending is None else pending
+        _check(load_library().spec_prefill(self._h, B, _ptr(prompt), T, _ptr(lengths), _ptr(pending),
+                                           _ptr(anchor_hidden), _stream()), "spec_prefill")
+        return pending
+
+    def export_hidden(self, batch: int, out: torch.Tensor | None = None) -> torch.Tensor:
+        """BF16 [batch, hidden] final normed hidden state of row tau-1 of the last pass."""
+        if out is None:
+            out = torch.empty(batch, self.dev.shape.hidden, dtype=torch.bfloat16, device="cuda")
+        _check(load_library().spec_export_hidden(self._h, batch, _ptr(out), _stream()), "spec_export_hidden")
+        return out
 
     def device_error(self) -> int:
         v = ctypes.c_int32()

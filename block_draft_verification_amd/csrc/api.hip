@@ -26,6 +26,8 @@ struct spec_ctx {
   ArgmaxPart *amax;
   float2 *rope;
   float *rpart;  // split-K partials of the O and down projections [nsplit][Mmax][H]
+  // prefill scratch: chunk tokens [Mmax], argmax [Mmax], commit counts, tau, bonus [max_batch]
+  int32_t *pf_tokens, *pf_argmax, *pf_ncommit, *pf_acc, *pf_bonus;
   float *dump_hidden, *dump_logits;
   // launch timing of one kernel class (measurement hook)
   int prof_kind = SPEC_K_NONE;
@@ -137,7 +139,7 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
                     Mm * I * 2,                      // act
                     (size_t)units * G * 16 * D * 4,  // part_o
                     (size_t)units * G * 16 * 8,      // part_ml
-                    256,                             // (unused)
+                    (2 * Mm + 3 * (size_t)kv->max_batch) * 4,  // prefill scratch
                     (size_t)kv->max_batch * 4,       // last_tau
                     4,                               // err
                     (size_t)lm_parts(V) * Mm * 8,    // amax
@@ -161,6 +163,11 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   c->act = (uint16_t *)(base + off[4]);
   c->part_o = (float *)(base + off[5]);
   c->part_ml = (float2 *)(base + off[6]);
+  c->pf_tokens = (int32_t *)(base + off[7]);
+  c->pf_argmax = c->pf_tokens + Mm;
+  c->pf_ncommit = c->pf_argmax + Mm;
+  c->pf_acc = c->pf_ncommit + kv->max_batch;
+  c->pf_bonus = c->pf_acc + kv->max_batch;
   c->last_tau = (int32_t *)(base + off[8]);
   c->err = (int32_t *)(base + off[9]);
   c->amax = (ArgmaxPart *)(base + off[10]);
@@ -269,6 +276,30 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     Timed t(c, SPEC_K_ACCEPT, st);
     CK(launch_accept(c->amax, lm_parts(V), M, tokens, batch, accept_len, bonus, argmax, c->last_tau, st));
   }
+  return SPEC_OK;
+}
+
+int spec_prefill(spec_ctx *c, int32_t batch, const int32_t *prompt, int32_t T, const int32_t *lengths,
+                 int32_t *pending, uint16_t *anchor_hidden, hipStream_t st) {
+  if (!c || !prompt || !lengths || !pending) return SPEC_E_ARG;
+  if (batch < 1 || batch > c->kv.max_batch || T < 1) return SPEC_E_ARG;
+  if (anchor_hidden && !aligned16(anchor_hidden)) return SPEC_E_ARG;
+  const int H = c->m.hidden;
+  for (int ch = 0; ch * 16 < T; ++ch) {
+    CK(launch_prefill_gather(prompt, T, lengths, ch, batch, c->pf_tokens, c->err, st));
+    const int rc = spec_verify_block(c, batch, c->pf_tokens, c->pf_acc, c->pf_bonus, c->pf_argmax, st);
+    if (rc != SPEC_OK) return rc;
+    CK(launch_prefill_finish(lengths, T, ch, batch, c->pf_argmax, c->x, H, c->pf_ncommit, pending, c->last_tau,
+                             anchor_hidden, st));
+    CK(launch_commit(batch, c->pf_ncommit, c->last_tau, c->kv.kv_len, c->kv.max_ctx, c->err, st));
+  }
+  return SPEC_OK;
+}
+
+int spec_export_hidden(spec_ctx *c, int32_t batch, uint16_t *out, hipStream_t st) {
+  if (!c || !out || !aligned16(out)) return SPEC_E_ARG;
+  if (batch < 1 || batch > c->kv.max_batch) return SPEC_E_ARG;
+  CK(launch_export_hidden(batch, c->last_tau, c->x, c->m.hidden, out, st));
   return SPEC_OK;
 }
 

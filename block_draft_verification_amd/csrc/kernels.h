@@ -76,3 +76,10 @@ hipError_t launch_accept(const ArgmaxPart *part, int nparts, int M, const int32_
 hipError_t launch_commit(int batch, const int32_t *n_commit, const int32_t *last_tau, int32_t *kv_len,
                          int max_ctx, int32_t *err, hipStream_t st);
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t st);
+hipError_t launch_prefill_gather(const int32_t *prompt, int T, const int32_t *lens, int chunk, int batch,
+                                 int32_t *tokens, int32_t *err, hipStream_t st);
+hipError_t launch_prefill_finish(const int32_t *lens, int T, int chunk, int batch, const int32_t *argmax,
+                                 const uint16_t *x, int H, int32_t *n_commit, int32_t *pending, int32_t *last_tau,
+                                 uint16_t *anchor, hipStream_t st);
+hipError_t launch_export_hidden(int batch, const int32_t *last_tau, const uint16_t *x, int H, uint16_t *out,
+                                hipStream_t st);

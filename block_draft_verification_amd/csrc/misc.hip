@@ -151,6 +151,56 @@ __global__ void commit_kernel(int batch, const int32_t *__restrict__ n_commit,
   kv_len[b] = cur + n;
 }
 
+// Prefill through the verify pass: chunk c of every prompt goes through the
+// pass as a 16-row block (rows past the prompt's end carry token 0), then all
+// of the chunk's real rows are committed ("HunyuanOCR-1.5 / DFlash" write-up,
+// inference loop, step 1: the target prefills the prompt before drafting).
+__global__ void prefill_gather_kernel(const int32_t *__restrict__ prompt, int T, const int32_t *__restrict__ lens,
+                                      int chunk, int32_t *tokens, int32_t *err) {
+  const int b = blockIdx.x, j = threadIdx.x;
+  const int len = lens[b];
+  const bool ok = len >= 1 && len <= T;
+  if (!ok && j == 0 && chunk == 0) set_error(err, SPEC_DERR_LENGTH);
+  const int p = 16 * chunk + j;
+  tokens[b * 16 + j] = ok && p < len ? prompt[(size_t)b * T + p] : 0;
+}
+
+// After chunk c: commit min(max(len - 16c, 0), 16) rows.  The chunk that holds
+// a prompt's last token (r = len - 16c rows of it) also yields the pending token
+// (the argmax at row r-1: the greedy next token after the prompt) and, when
+// asked, that row's final normed hidden state (BF16), the feature a block
+// drafter is conditioned on.  last_tau = r, so the anchor row is last_tau - 1
+// as after a verify pass.
+__global__ void prefill_finish_kernel(const int32_t *__restrict__ lens, int T, int chunk,
+                                      const int32_t *__restrict__ argmax, const uint16_t *__restrict__ x, int H,
+                                      int32_t *n_commit, int32_t *pending, int32_t *last_tau, uint16_t *anchor) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int len = lens[b];
+  const int rem = (len >= 1 && len <= T) ? len - 16 * chunk : 0;
+  if (tid == 0) n_commit[b] = min(max(rem, 0), 16);
+  if (rem < 1 || rem > 16) return;
+  if (tid == 0) {
+    pending[b] = argmax[b * 16 + rem - 1];
+    last_tau[b] = rem;
+  }
+  if (anchor) {
+    const uint16_t *src = x + (size_t)(b * 16 + rem - 1) * H;
+    for (int i = tid * 8; i < H; i += 8 * blockDim.x)
+      *reinterpret_cast<u32x4_t *>(anchor + (size_t)b * H + i) = *reinterpret_cast<const u32x4_t *>(src + i);
+  }
+}
+
+// out[b] = final normed hidden state (BF16) of row last_tau[b] - 1 of the last
+// pass: the position whose argmax gave the bonus token.
+__global__ void export_hidden_kernel(const int32_t *__restrict__ last_tau, const uint16_t *__restrict__ x, int H,
+                                     uint16_t *out) {
+  const int b = blockIdx.x;
+  const int r = min(max(last_tau[b], 1), 16);
+  const uint16_t *src = x + (size_t)(b * 16 + r - 1) * H;
+  for (int i = threadIdx.x * 8; i < H; i += 8 * blockDim.x)
+    *reinterpret_cast<u32x4_t *>(out + (size_t)b * H + i) = *reinterpret_cast<const u32x4_t *>(src + i);
+}
+
 __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
@@ -184,6 +234,26 @@ hipError_t launch_commit(int batch, const int32_t *n_commit, const int32_t *last
                          int max_ctx, int32_t *err, hipStream_t st) {
   hipLaunchKernelGGL(commit_kernel, dim3((batch + 255) / 256), dim3(256), 0, st, batch, n_commit, last_tau,
                      kv_len, max_ctx, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_gather(const int32_t *prompt, int T, const int32_t *lens, int chunk, int batch,
+                                 int32_t *tokens, int32_t *err, hipStream_t st) {
+  hipLaunchKernelGGL(prefill_gather_kernel, dim3(batch), dim3(16), 0, st, prompt, T, lens, chunk, tokens, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_finish(const int32_t *lens, int T, int chunk, int batch, const int32_t *argmax,
+                                 const uint16_t *x, int H, int32_t *n_commit, int32_t *pending, int32_t *last_tau,
+                                 uint16_t *anchor, hipStream_t st) {
+  hipLaunchKernelGGL(prefill_finish_kernel, dim3(batch), dim3(128), 0, st, lens, T, chunk, argmax, x, H, n_commit,
+                     pending, last_tau, anchor);
+  return hipGetLastError();
+}
+
+hipError_t launch_export_hidden(int batch, const int32_t *last_tau, const uint16_t *x, int H, uint16_t *out,
+                                hipStream_t st) {
+  hipLaunchKernelGGL(export_hidden_kernel, dim3(batch), dim3(128), 0, st, last_tau, x, H, out);
   return hipGetLastError();
 }
 

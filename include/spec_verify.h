@@ -87,6 +87,8 @@ typedef enum {
                                 K/V writes are skipped                        */
 #define SPEC_DERR_COMMIT 4   /* a commit count outside [0,16] or past max_ctx:
                                 that sequence's kv_len is left unchanged      */
+#define SPEC_DERR_LENGTH 8   /* spec_prefill: a prompt length outside [1, T]:
+                                that sequence is not advanced                 */
 
 typedef struct {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
@@ -159,6 +161,33 @@ int spec_verify_block(spec_ctx *ctx, int32_t batch, const int32_t *tokens, int32
  * Counts must lie in [0, 16] and keep kv_len <= max_ctx, else that sequence
  * is left unchanged and SPEC_DERR_COMMIT is set.  Asynchronous. */
 int spec_commit_kv(spec_ctx *ctx, int32_t batch, const int32_t *n_commit, hipStream_t stream);
+
+/* Chunked prefill through the verify pass ("HunyuanOCR-1.5 / DFlash"
+ * write-up, inference loop, step 1: the target processes the prompt before
+ * the first draft).  For b < batch the prompt prompt[b][0 .. lengths[b])
+ * (int32 [batch][T], row-major, device; lengths int32 [batch], device, each
+ * in [1, T]) is appended to the cache at kv_len[b], 16 rows per pass:
+ * chunk c runs rows 16c .. 16c+15 (token 0 past the prompt's end) and
+ * commits the real ones.  On completion kv_len[b] += lengths[b];
+ * pending[b] (int32, device) = the greedy next token after the prompt (the
+ * argmax at its last row), which is row 0 of the first verify block; and,
+ * when anchor_hidden is not NULL (BF16 [batch][hidden], 16-byte aligned,
+ * device), the final normed hidden state of the prompt's last row.  Every
+ * pass writes 16 K/V slots, so kv_len[b] + 16 * ceil(T/16) <= max_ctx is
+ * needed (else SPEC_DERR_CAPACITY, as for a verify).  Lengths outside
+ * [1, T] set SPEC_DERR_LENGTH and leave that sequence unchanged.  Runs
+ * ceil(T/16) verify passes; asynchronous, no host synchronisation. */
+int spec_prefill(spec_ctx *ctx, int32_t batch, const int32_t *prompt, int32_t T, const int32_t *lengths,
+                 int32_t *pending, uint16_t *anchor_hidden, hipStream_t stream);
+
+/* After spec_verify_block (or spec_prefill): out[b] (BF16 [batch][hidden],
+ * 16-byte aligned, device) = the final normed hidden state of block row
+ * tau_b - 1 of the last pass, i.e. the position whose argmax produced the
+ * bonus (the pending token of the next block) -- the target feature a block
+ * drafter is conditioned on ("HunyuanOCR-1.5 / DFlash" write-up, section 一:
+ * the draft model reads the target's hidden states).  Must run before the
+ * next pass overwrites them.  Asynchronous. */
+int spec_export_hidden(spec_ctx *ctx, int32_t batch, uint16_t *out, hipStream_t stream);
 
 /* Free the workspace.  The caller's buffers are untouched.  NULL is a no-op. */
 int spec_verify_destroy(spec_ctx *ctx);

@@ -240,18 +240,23 @@ def verify_block(model, kv, tokens, seqs=None) -> VerifyResult:
     return VerifyResult(g, margin, tau, bonus, x, lg)
 
 
-def prefill(model, kv, prompts, chunk: int = 256):
+def prefill(model, kv, prompts, chunk: int = 256, return_hidden: bool = False):
     """Run each prompt through the model in chunks, committing every row.
-    Returns the pending token per sequence: the argmax at its last prompt row."""
+    Returns the pending token per sequence: the argmax at its last prompt row;
+    with return_hidden, also that row's final normed hidden state [B, H] and
+    the top-2 logit margin there."""
     pend = np.empty(len(prompts), dtype=np.int64)
+    hid = np.empty((len(prompts), model.m.hidden))
+    margin = np.empty(len(prompts))
     for b, p in enumerate(prompts):
         p = np.asarray(p)
         for c0 in range(0, len(p), chunk):
             rows = p[c0:c0 + chunk][None, :]
             x = forward(model, kv, rows, seqs=[b])
             commit(kv, [rows.shape[1]], seqs=[b])
-        pend[b] = greedy(model.logits(x[0, -1:]))[0][0]
-    return pend
+        g, mg = greedy(model.logits(x[0, -1:]))
+        pend[b], margin[b], hid[b] = g[0], mg[0], x[0, -1]
+    return (pend, hid, margin) if return_hidden else pend
 
 
 def greedy_continuation(model, kv, pending, steps: int = BLOCK - 1):

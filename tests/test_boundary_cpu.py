@@ -54,6 +54,13 @@ def test_host_side_argument_checks():
     v = ctypes.c_int32()
     assert lib.spec_get_device_error(None, ctypes.byref(v), None) == -1
     assert lib.spec_debug_set_dump(None, None, None) == -1
+    assert lib.spec_prefill(None, 1, 16, 16, 16, 16, None, None) == -1
+    assert lib.spec_export_hidden(None, 1, 16, None) == -1
+    m0 = B.SpecModelDesc(2, 4096 + 64, 4, 2, 64, 704, 1024, 1e-6, 1e4, 1, 1, 1)  # hidden > 4096
+    w0 = B.SpecWeights((B.SpecLayerWeights * 2)(), 16, None, 16)
+    kv0 = B.SpecKV(16, 16, 16, 1, 128)
+    h0 = ctypes.c_void_p()
+    assert lib.spec_verify_init(ctypes.byref(m0), ctypes.byref(w0), ctypes.byref(kv0), None, ctypes.byref(h0)) == -2
     # shapes the kernels do not support are refused at init
     m = B.SpecModelDesc(2, 256, 4, 2, 96, 704, 1024, 1e-6, 1e4, 1, 1, 1)       # head_dim 96
     arr = (B.SpecLayerWeights * 2)()
