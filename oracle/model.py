@@ -275,17 +275,20 @@ def greedy_continuation(model, kv, pending, steps: int = BLOCK - 1):
     return np.stack(cont, axis=1)
 
 
-def ar_decode(model, kv, pending, n_tokens: int):
+def ar_decode(model, kv, pending, n_tokens: int, return_margin: bool = False):
     """Plain autoregressive greedy decoding: feed the pending token, emit the
-    argmax, commit one row, repeat.  Returns [B, n_tokens] emitted tokens."""
+    argmax, commit one row, repeat.  Returns [B, n_tokens] emitted tokens
+    (and, with return_margin, the top-2 logit margin of each step)."""
     cur = np.asarray(pending, dtype=np.int64)
-    out = []
+    out, margins = [], []
     for _ in range(n_tokens):
         x = forward(model, kv, cur[:, None])
-        cur = greedy(model.logits(x[:, 0]))[0]
+        cur, mg = greedy(model.logits(x[:, 0]))
         commit(kv, np.ones_like(cur))
         out.append(cur)
-    return np.stack(out, axis=1)
+        margins.append(mg)
+    toks = np.stack(out, axis=1)
+    return (toks, np.stack(margins, axis=1)) if return_margin else toks
 
 
 def spec_decode(model, kv, pending, n_tokens: int, draft_fn):
