@@ -41,7 +41,8 @@ class SpecWeights(ctypes.Structure):
 
 
 class SpecKV(ctypes.Structure):
-    _fields_ = [("k_cache", _P), ("v_cache", _P), ("kv_len", _P), ("max_batch", _I), ("max_ctx", _I)]
+    _fields_ = [("k_cache", _P), ("v_cache", _P), ("kv_len", _P), ("max_batch", _I), ("max_ctx", _I),
+                ("page_table", _P), ("page_size", _I), ("num_pages", _I)]
 
 
 EXPORTS = {
@@ -112,11 +113,17 @@ def _wfmt(name: str) -> int:
 
 class DeviceModel:
     """Caller-owned device buffers: weights in the boundary's layout, the BF16
-    KV cache [L][max_batch][Hkv][max_ctx][D] for K and V, and kv_len."""
+    KV cache for K and V, and kv_len.  Contiguous cache: [L][max_batch][Hkv]
+    [max_ctx][D].  Paged cache (page_table given, int [max_batch][max_ctx /
+    page_size]): a pool [L][num_pages][Hkv][page_size][D]; kv_layers are then
+    given in the contiguous shape and scattered into the pages."""
 
     def __init__(self, shape, weights: dict, max_batch: int, max_ctx: int, kv_layers=None, kv_len=None,
-                 device="cuda"):
+                 device="cuda", page_table=None, page_size: int = 0, num_pages: int = 0):
         self.shape, self.max_batch, self.max_ctx, self.device = shape, max_batch, max_ctx, device
+        self.page_size, self.num_pages = page_size, num_pages
+        self.page_table = None if page_table is None else torch.as_tensor(
+            np.asarray(page_table, np.int32), device=device).contiguous()
         m = shape
         self.layers = []
         for lw in weights["layers"]:
@@ -124,7 +131,10 @@ class DeviceModel:
         self.embed = _dev(weights["embed"], device)
         self.lm_head = None if weights.get("lm_head") is None else _dev(weights["lm_head"], device)
         self.final_norm = _dev(weights["final_norm"], device)
-        cache_shape = (m.n_layers, max_batch, m.n_kv_heads, max_ctx, m.head_dim)
+        if self.page_table is None:
+            cache_shape = (m.n_layers, max_batch, m.n_kv_heads, max_ctx, m.head_dim)
+        else:
+            cache_shape = (m.n_layers, num_pages, m.n_kv_heads, page_size, m.head_dim)
         self.k_cache = torch.zeros(cache_shape, dtype=torch.int16, device=device)
         self.v_cache = torch.zeros(cache_shape, dtype=torch.int16, device=device)
         self.kv_len = torch.zeros(max_batch, dtype=torch.int32, device=device)
@@ -135,9 +145,27 @@ class DeviceModel:
             self.kv_len[:len(kv_len)] = torch.as_tensor(np.asarray(kv_len, np.int32), device=device)
 
     def load_kv_layer(self, l, K, V):
+        """K, V: uint16 [b, Hkv, max_ctx, D] for sequences 0 .. b-1."""
         b = K.shape[0]
-        self.k_cache[l, :b].copy_(_dev(K, "cpu"))
-        self.v_cache[l, :b].copy_(_dev(V, "cpu"))
+        if self.page_table is None:
+            self.k_cache[l, :b].copy_(_dev(K, "cpu"))
+            self.v_cache[l, :b].copy_(_dev(V, "cpu"))
+            return
+        ps, pt = self.page_size, self.page_table.cpu().numpy()
+        for s in range(b):
+            for j in range(self.max_ctx // ps):
+                pg = int(pt[s, j])
+                self.k_cache[l, pg].copy_(_dev(np.ascontiguousarray(K[s, :, j * ps:(j + 1) * ps]), "cpu"))
+                self.v_cache[l, pg].copy_(_dev(np.ascontiguousarray(V[s, :, j * ps:(j + 1) * ps]), "cpu"))
+
+    def cache_rows(self, l: int, b: int, n: int, which: str = "k") -> torch.Tensor:
+        """Positions 0 .. n-1 of sequence b in layer l, [Hkv, n, D] int16, in either layout."""
+        cache = self.k_cache if which == "k" else self.v_cache
+        if self.page_table is None:
+            return cache[l, b, :, :n]
+        ps = self.page_size
+        pages = self.page_table[b, :(n + ps - 1) // ps].long()
+        return cache[l, pages].permute(1, 0, 2, 3).reshape(self.shape.n_kv_heads, -1, self.shape.head_dim)[:, :n]
 
     def structs(self):
         m = self.shape
@@ -150,8 +178,9 @@ class DeviceModel:
                 setattr(arr[i], name[0], lw[name[0]].data_ptr())
         w = SpecWeights(arr, self.embed.data_ptr(), None if self.lm_head is None else self.lm_head.data_ptr(),
                         self.final_norm.data_ptr())
+        pt = None if self.page_table is None else self.page_table.data_ptr()
         kv = SpecKV(self.k_cache.data_ptr(), self.v_cache.data_ptr(), self.kv_len.data_ptr(), self.max_batch,
-                    self.max_ctx)
+                    self.max_ctx, pt, self.page_size, self.num_pages)
         return desc, arr, w, kv
 
 

@@ -59,6 +59,11 @@ struct Timed {
 
 static bool aligned16(const void *p) { return ((uintptr_t)p & 15) == 0; }
 
+static KvLayout kv_layout(const spec_kv &kv) {
+  if (!kv.page_table) return KvLayout{nullptr, 0, 0, 0};
+  return KvLayout{kv.page_table, kv.page_size, kv.max_ctx / kv.page_size, kv.num_pages};
+}
+
 static int check_model(const spec_model_desc *m) {
   if (m->n_layers < 1 || m->hidden < 64 || m->n_q_heads < 1 || m->n_kv_heads < 1 || m->intermediate < 64 ||
       m->vocab < 64 || !(m->rms_eps > 0.f) || !(m->rope_theta > 0.f))
@@ -95,6 +100,9 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   int rc = check_model(m);
   if (rc) return rc;
   if (!kv->k_cache || !kv->v_cache || !kv->kv_len || kv->max_batch < 1 || kv->max_ctx < 16) return SPEC_E_ARG;
+  if (kv->page_table && (kv->page_size < 64 || kv->page_size % 64 || kv->max_ctx % kv->page_size ||
+                         kv->num_pages < 1))
+    return SPEC_E_ARG;
   if (!m->tied_lm_head && !w->lm_head) return SPEC_E_ARG;
   if (!aligned16(kv->k_cache) || !aligned16(kv->v_cache) || !aligned16(w->embed) ||
       !aligned16(w->final_norm) || (w->lm_head && !aligned16(w->lm_head)))
@@ -202,7 +210,9 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
   const spec_model_desc &m = c->m;
   const int M = batch * 16, H = m.hidden, D = m.head_dim, Hq = m.n_q_heads, Hkv = m.n_kv_heads;
   const int I = m.intermediate, V = m.vocab, max_ctx = c->kv.max_ctx;
-  const size_t lstride = (size_t)c->kv.max_batch * Hkv * max_ctx * D;
+  const KvLayout kvl = kv_layout(c->kv);
+  const size_t lstride = (kvl.pages ? (size_t)c->kv.num_pages * kvl.page_size : (size_t)c->kv.max_batch * max_ctx) *
+                         Hkv * D;
 
   AttnArgs aa{};
   aa.q = c->q;
@@ -214,12 +224,13 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
   aa.Hq = Hq;
   aa.Hkv = Hkv;
   aa.max_ctx = max_ctx;
+  aa.kvl = kvl;
   aa.split_len = attention_split_len(batch, Hkv, max_ctx);
   aa.nsplit = attn_nsplit(aa.split_len, max_ctx);
 
   {
     Timed t(c, SPEC_K_EMBED, st);
-    CK(launch_embed(tokens, M, H, V, c->embed, c->h, c->kv.kv_len, max_ctx, c->err, st));
+    CK(launch_embed(tokens, M, H, V, c->embed, c->h, c->kv.kv_len, max_ctx, kvl, c->err, st));
   }
   const int ns_o = residual_nsplit(M, H, Hq * D), ns_d = residual_nsplit(M, H, I);
   int pending = 0;  // splits of the last residual projection not yet added to h
@@ -230,7 +241,7 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
       Timed t(c, SPEC_K_RMSNORM, st);
       CK(launch_norm(c->h, c->rpart, pending, L.attn_norm, M, H, m.rms_eps, c->x, 0, nullptr, st));
     }
-    QkvOut qo{c->q, kc, vc, c->kv.kv_len, c->rope, Hq, Hkv, max_ctx};
+    QkvOut qo{c->q, kc, vc, c->kv.kv_len, c->rope, Hq, Hkv, max_ctx, kvl};
     {
       Timed t(c, SPEC_K_QKV, st);
       CK(launch_qkv(c->x, M, H, D, LinearW{L.w_qkv, L.s_qkv, SPEC_WFMT_FP8_E4M3_ROW}, qo, st));

@@ -55,7 +55,6 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
   constexpr int T = 64 * NW;
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, h = lane >> 5;
   const int wave = tid >> 6;
-  const size_t cache_base = ((size_t)b * a.Hkv + kvh) * a.max_ctx;
   const size_t unit = (size_t)b * a.Hkv + kvh;
 
   // this wave's queries: lane (c, h) -> head 2*wave + c/16 of the group, block row c%16
@@ -77,6 +76,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
 
   // Tile loads are unconditional (key indices clamped to the split's last key,
   // whose finite values are masked out) so the wave never branches around them.
+  // A tile's 64 keys share one cache page (pages hold a multiple of 64 rows), so
+  // one row lookup per tile serves both layouts; tb = 64-aligned start of the
+  // tile that holds the (clamped) keys.
   constexpr int KPT = (KCH + T - 1) / T, VPT = (VCH + T - 1) / T;  // chunks per thread (last one partial for NW = 3)
   struct TileRegs {
     u32x4_t k[KPT];
@@ -84,11 +86,14 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
   };
   TileRegs ra, rb;
   auto load_tile = [&](TileRegs &tr, int kt0) {
+    const int tb = min(kt0, (key_hi - 1) & ~(KT - 1));
+    bool ok;
+    const size_t trow = a.kvl.row(b, kvh, a.Hkv, a.max_ctx, tb, ok);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int ch = min(tid + T * i, KCH - 1), kk = ch / (D / 8), d0 = (ch % (D / 8)) * 8,
                 key = min(kt0 + kk, key_hi - 1);
-      tr.k[i] = *reinterpret_cast<const u32x4_t *>(a.k_cache + (cache_base + key) * D + d0);
+      tr.k[i] = *reinterpret_cast<const u32x4_t *>(a.k_cache + (trow + key - tb) * D + d0);
     }
 #pragma unroll
     for (int i = 0; i < VPT; ++i) {
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int key = min(kt0 + kk + e, key_hi - 1);
-        tr.v[i][e] = *reinterpret_cast<const u32x2_t *>(a.v_cache + (cache_base + key) * D + d0);
+        tr.v[i][e] = *reinterpret_cast<const u32x2_t *>(a.v_cache + (trow + key - tb) * D + d0);
       }
     }
   };

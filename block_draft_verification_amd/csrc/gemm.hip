@@ -456,7 +456,9 @@ struct EpiQkv {
       const bool isk = unit < o.Hq + o.Hkv;
       const int kvh = isk ? unit - o.Hq : unit - o.Hq - o.Hkv;
       uint16_t *cache = isk ? o.k_cache : o.v_cache;
-      store_bf16x4(cache + (((size_t)b * o.Hkv + kvh) * o.max_ctx + pos) * D + col, v[0], v[1], v[2], v[3]);
+      bool ok;
+      const size_t r = o.kvl.row(b, kvh, o.Hkv, o.max_ctx, pos, ok);
+      if (ok) store_bf16x4(cache + r * D + col, v[0], v[1], v[2], v[3]);
     }
   }
 };

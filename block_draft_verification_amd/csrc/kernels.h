@@ -24,12 +24,33 @@ int residual_nsplit(int M, int N, int K);
 hipError_t launch_linear_f32(const uint16_t *x, int M, int N, int K, LinearW w, float *y, hipStream_t st);
 
 // QKV projection + RoPE; q -> q_out bf16 [M][Hq*D]; k, v -> caches at slot kv_len[b] + j.
+// Where cache position `pos` of (sequence b, KV head h) lives, as a row index
+// into one layer's K or V array (rows of D elements): contiguous
+// [max_batch][Hkv][max_ctx], or paged [num_pages][Hkv][page_size] through
+// pages[b][pos / page_size].  ok = false for a page index outside the pool
+// (the row returned is then clamped into it).
+struct KvLayout {
+  const int32_t *pages;  // NULL: contiguous
+  int page_size, max_pages, num_pages;
+  __device__ __forceinline__ size_t row(int b, int h, int Hkv, int max_ctx, int pos, bool &ok) const {
+    if (!pages) {
+      ok = true;
+      return ((size_t)b * Hkv + h) * max_ctx + pos;
+    }
+    int pg = pages[(size_t)b * max_pages + pos / page_size];
+    ok = pg >= 0 && pg < num_pages;
+    pg = pg < 0 ? 0 : (pg >= num_pages ? num_pages - 1 : pg);
+    return ((size_t)pg * Hkv + h) * page_size + pos % page_size;
+  }
+};
+
 struct QkvOut {
   uint16_t *q_out;
-  uint16_t *k_cache, *v_cache;  // layer base, [max_batch][Hkv][max_ctx][D]
+  uint16_t *k_cache, *v_cache;  // layer base (contiguous or page pool)
   const int32_t *kv_len;
   const float2 *rope;           // [max_ctx][D/2] (cos, sin)
   int Hq, Hkv, max_ctx;
+  KvLayout kvl;
 };
 // q (FP16) and k, v (BF16 cache) from FP16 x
 hipError_t launch_qkv(const uint16_t *x, int M, int H, int D, LinearW w, QkvOut o, hipStream_t st);
@@ -50,7 +71,8 @@ inline int lm_parts(int V) { return V / 64; }
 // ---- attention ----
 struct AttnArgs {
   const uint16_t *q;                 // FP16 [M][Hq*D]
-  const uint16_t *k_cache, *v_cache; // BF16, layer base
+  const uint16_t *k_cache, *v_cache; // BF16, layer base (contiguous or page pool)
+  KvLayout kvl;
   const int32_t *kv_len;
   uint16_t *o;                       // FP16 [M][Hq*D]
   float *part_o;                     // [B][Hkv][nsplit][G*16][D]
@@ -65,7 +87,7 @@ int attention_split_len(int batch, int Hkv, int max_ctx);
 
 // ---- small kernels ----
 hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16_t *table, float *h,
-                        const int32_t *kv_len, int max_ctx, int32_t *err, hipStream_t st);
+                        const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, hipStream_t st);
 // h += part[0] + ... + part[nsplit-1] (in that order; nsplit may be 0), then
 // x = RMSNorm(h) * gain, written as FP16 (out_bf16 = 0) or BF16 (out_bf16 = 1)
 hipError_t launch_norm(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,

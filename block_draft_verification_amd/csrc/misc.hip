@@ -7,7 +7,7 @@
 // writes of a sequence that does not.
 __global__ void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
                              const uint16_t *__restrict__ table, float *__restrict__ h,
-                             const int32_t *__restrict__ kv_len, int max_ctx, int32_t *err) {
+                             const int32_t *__restrict__ kv_len, int max_ctx, KvLayout kvl, int32_t *err) {
   const int m = blockIdx.x;
   int t = tokens[m];
   if (t < 0 || t >= V) {
@@ -16,7 +16,14 @@ __global__ void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
   }
   if ((m & 15) == 0 && threadIdx.x == 0) {
     const int n = kv_len[m >> 4];
-    if (n < 0 || n + 16 > max_ctx) set_error(err, SPEC_DERR_CAPACITY);
+    if (n < 0 || n + 16 > max_ctx) {
+      set_error(err, SPEC_DERR_CAPACITY);
+    } else if (kvl.pages) {  // every page the pass reads or writes: positions 0 .. n+15
+      for (int p = 0; p < n + 16; p += kvl.page_size) {
+        const int pg = kvl.pages[(size_t)(m >> 4) * kvl.max_pages + p / kvl.page_size];
+        if (pg < 0 || pg >= kvl.num_pages) set_error(err, SPEC_DERR_PAGE);
+      }
+    }
   }
   const uint16_t *row = table + (size_t)t * H;
   for (int c = threadIdx.x; c < H; c += blockDim.x) h[(size_t)m * H + c] = bf16_to_f32(row[c]);
@@ -207,8 +214,8 @@ __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
 }
 
 hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16_t *table, float *h,
-                        const int32_t *kv_len, int max_ctx, int32_t *err, hipStream_t st) {
-  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, st, tokens, H, V, table, h, kv_len, max_ctx, err);
+                        const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, hipStream_t st) {
+  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, st, tokens, H, V, table, h, kv_len, max_ctx, kvl, err);
   return hipGetLastError();
 }
 

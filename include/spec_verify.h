@@ -89,6 +89,8 @@ typedef enum {
                                 that sequence's kv_len is left unchanged      */
 #define SPEC_DERR_LENGTH 8   /* spec_prefill: a prompt length outside [1, T]:
                                 that sequence is not advanced                 */
+#define SPEC_DERR_PAGE 16    /* paged cache: a page index the pass needs lies
+                                outside [0, num_pages)                        */
 
 typedef struct {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
@@ -121,14 +123,28 @@ typedef struct {
   const float *final_norm;          /* fp32 [H]                                */
 } spec_weights;
 
-/* KV cache: BF16 [n_layers][max_batch][Hkv][max_ctx][D] for K and for V.
- * kv_len[b] = committed length of sequence b (int32, device).  A verify
- * writes the block's K/V to slots kv_len[b] .. kv_len[b]+15 without
- * changing kv_len; slots >= kv_len are otherwise unspecified. */
+/* KV cache, BF16, for K and for V.  kv_len[b] = committed length of
+ * sequence b (int32, device).  A verify writes the block's K/V to positions
+ * kv_len[b] .. kv_len[b]+15 without changing kv_len; positions >= kv_len are
+ * otherwise unspecified.
+ *
+ * Contiguous layout (page_table NULL): [n_layers][max_batch][Hkv][max_ctx][D].
+ *
+ * Paged layout (page_table not NULL; "The Inference Stack Behind OCRia",
+ * KV-cache section): a pool [n_layers][num_pages][Hkv][page_size][D];
+ * position p of sequence b lives in page page_table[b][p / page_size] at row
+ * p % page_size.  page_table is int32 [max_batch][max_ctx / page_size] on the
+ * device, owned and filled by the caller (the pages a pass touches,
+ * positions 0 .. kv_len[b]+15, must be valid; an index outside
+ * [0, num_pages) sets SPEC_DERR_PAGE and that page is neither read nor
+ * written).  page_size is a multiple of 64 and divides max_ctx, the
+ * per-sequence capacity.  Commit and rollback remain length changes. */
 typedef struct {
   uint16_t *k_cache, *v_cache;
   int32_t *kv_len;
   int32_t max_batch, max_ctx;
+  const int32_t *page_table; /* NULL: contiguous layout */
+  int32_t page_size, num_pages;
 } spec_kv;
 
 typedef struct spec_ctx spec_ctx;

@@ -61,7 +61,10 @@ def _bf16_cache_from_oracle(okv, m, B, max_ctx):
     return layers
 
 
-def build_case(name: str, seqs_planted=None, batch=None, gains="ones", extra=16) -> Case:
+def build_case(name: str, seqs_planted=None, batch=None, gains="ones", extra=16, oracle_seqs=None) -> Case:
+    """oracle_seqs: the sequences the oracle will be asked about (default all);
+    the others enter the oracle's cache with length 0, which keeps the
+    float64 copy of a large cache small."""
     wl = W.WORKLOADS[name]
     m = wl.model
     B = batch or wl.batch
@@ -79,7 +82,10 @@ def build_case(name: str, seqs_planted=None, batch=None, gains="ones", extra=16)
         log(f"case {name}: synthetic KV")
         kv_layers = [W.synthetic_kv_layer(m, wl.seed, l, lens, wl.max_ctx) for l in range(m.n_layers)]
         pend = W.pending_tokens(wl)[:B]
-    okv = oracle.OracleKV.from_bf16(m, [k for k, _ in kv_layers], [v for _, v in kv_layers], lens, extra=extra)
+    olens = lens.copy()
+    if oracle_seqs is not None:
+        olens[[b for b in range(B) if b not in set(oracle_seqs)]] = 0
+    okv = oracle.OracleKV.from_bf16(m, [k for k, _ in kv_layers], [v for _, v in kv_layers], olens, extra=extra)
     L = W.accept_lengths(wl)[:B]
     planted = range(B) if seqs_planted is None else seqs_planted
     blocks = np.empty((B, 16), np.int32)

@@ -74,7 +74,7 @@ def test_verify_8b_sampled():
     """8B shape at full size: the oracle runs sequence 0 (random drafts, so no
     15-step greedy planting at this size); every sequence is checked for
     self-consistency and untouched committed rows."""
-    case = build_case("8b-fp8-b8-ctx4096", seqs_planted=[])
+    case = build_case("8b-fp8-b8-ctx4096", seqs_planted=[], oracle_seqs=[0])
     ref, okv = oracle_verify(case, seqs=[0])
     dev, ver = gpu_setup(case)
     got = gpu_verify(ver, case)
