@@ -30,7 +30,7 @@ Parity pins: every function here is checked in ``tests/test_oracle_*.py``
 against something other than itself (library routines in float64, closed
 forms, brute force, the speculative == autoregressive invariant).
 """
-from .codecs import decode_bf16, decode_e2m1, decode_e4m3, decode_e8m0  # noqa: F401
+from .codecs import decode_bf16, decode_e2m1, decode_e4m3, decode_e8m0, mxfp8_roundtrip  # noqa: F401
 from .model import (  # noqa: F401
     OracleKV, OracleModel, VerifyResult, accept, ar_decode, attention, commit, forward,
     greedy, greedy_continuation, prefill, rms_norm, rope, silu, spec_decode, verify_block)

@@ -12,6 +12,14 @@ conversion, so that the tests can pin them against the library ones.
   is subnormal (m * 0.5).  Magnitudes: 0, 0.5, 1, 1.5, 2, 3, 4, 6.
 * e8m0: an unsigned power-of-two exponent, value 2^(b-127); 255 is NaN.
 * bfloat16: the upper 16 bits of an IEEE binary32.
+* MXFP8 (OCP microscaling, used here for activations in the FP8-activation
+  mode): blocks of 32 consecutive elements share a power-of-two scale 2^X,
+  X = floor(log2(amax)) - 8 (8 = the largest exponent of e4m3, so the block
+  maximum lands in [256, 512) before the elements are rounded), stored as
+  e8m0 = X + 127 clamped to [0, 254]; each element is rounded to the nearest
+  e4m3 value (ties to the even code), saturating at +-448.  The rounding
+  decisions are taken on float32 values, the precision the kernels hold the
+  activations in.
 """
 import numpy as np
 
@@ -46,9 +54,15 @@ def decode_bf16(bits) -> np.ndarray:
     return u.view(np.float32).astype(np.float64)
 
 
+# decode_e4m3 / decode_e2m1 evaluated once on every code: applying a format to
+# a large array is then a table lookup with exactly the same values.
+_E4M3_TABLE = decode_e4m3(np.arange(256))
+_E2M1_TABLE = decode_e2m1(np.arange(16))
+
+
 def dequant_fp8_rows(codes, scales) -> np.ndarray:
     """w'[n, k] = e4m3(codes[n, k]) * scales[n], exact in float64."""
-    return decode_e4m3(codes) * np.asarray(scales, dtype=np.float64)[:, None]
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)] * np.asarray(scales, dtype=np.float64)[:, None]
 
 
 def dequant_mxfp4(codes, e8) -> np.ndarray:
@@ -56,7 +70,46 @@ def dequant_mxfp4(codes, e8) -> np.ndarray:
     codes = np.asarray(codes, dtype=np.uint8)
     rows, half = codes.shape
     vals = np.empty((rows, 2 * half), dtype=np.float64)
-    vals[:, 0::2] = decode_e2m1(codes & 0xF)
-    vals[:, 1::2] = decode_e2m1(codes >> 4)
+    vals[:, 0::2] = _E2M1_TABLE[codes & 0xF]
+    vals[:, 1::2] = _E2M1_TABLE[codes >> 4]
     scale = np.repeat(decode_e8m0(e8), 32, axis=1)
     return vals * scale
+
+
+_E4M3_POS = _E4M3_TABLE[:127]  # codes 0 .. 126: 0, then increasing finite positive values up to 448
+
+
+def round_e4m3(v) -> np.ndarray:
+    """Nearest e4m3 value of each element of v (ties to the even code),
+    saturating at +-448.  Exact: |v| is compared with the midpoints of
+    neighbouring codes in float64."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 448.0)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 1, 126)  # first code with value >= a
+    lo = hi - 1
+    d_lo, d_hi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    return np.sign(v) * _E4M3_POS[code]
+
+
+def mxfp8_quantize(x):
+    """x [..., n] (n a multiple of 32) -> (values on the e4m3 grid [..., n],
+    X [..., n/32] int): the block exponent and the elements before scaling."""
+    x32 = np.asarray(x, dtype=np.float32)
+    shp = x32.shape
+    blk = x32.reshape(shp[:-1] + (shp[-1] // 32, 32)).astype(np.float64)
+    amax = np.abs(blk).max(axis=-1)
+    with np.errstate(divide="ignore"):
+        X = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - 8, -127)
+    X = np.clip(X, -127, 127).astype(np.int64)
+    el = round_e4m3(blk * np.ldexp(1.0, -X)[..., None])
+    return el.reshape(shp), X
+
+
+def mxfp8_roundtrip(x) -> np.ndarray:
+    """x as MXFP8 holds it: each element's e4m3 value times its block's 2^X."""
+    el, X = mxfp8_quantize(x)
+    shp = el.shape
+    blk = el.reshape(shp[:-1] + (shp[-1] // 32, 32)) * np.ldexp(1.0, X)[..., None]
+    return blk.reshape(shp)

@@ -19,6 +19,7 @@ from dataclasses import dataclass
 
 import numpy as np
 
+from . import codecs
 from .codecs import decode_bf16, dequant_fp8_rows, dequant_mxfp4
 
 BLOCK = 16
@@ -74,10 +75,15 @@ def attention(q, K, V, n, G):
 class OracleModel:
     """Weights in the boundary's layout, decoded to float64 on first use."""
 
-    def __init__(self, shape, weights: dict, cache: bool = True):
+    def __init__(self, shape, weights: dict, cache: bool = True, act_mx8: bool = False):
+        """act_mx8: the FP8-activation mode -- the normed activations that feed
+        the QKV and gate/up projections and the SwiGLU output that feeds the
+        down projection are held as MXFP8 (codecs.mxfp8_roundtrip); everything
+        else is unchanged."""
         self.m = shape
         self.w = weights
         self.cache = cache
+        self.act = codecs.mxfp8_roundtrip if act_mx8 else (lambda x: x)
         self._layers = {}
         self._embed = None
         self._lm = None
@@ -172,7 +178,7 @@ def forward(model: OracleModel, kv: OracleKV, tokens, seqs=None) -> np.ndarray:
     h = model.embed(tokens).reshape(Bp * T, m.hidden)
     for l in range(m.n_layers):
         w = model.layer(l)
-        x = rms_norm(h, w["attn_norm"], m.rms_eps)
+        x = model.act(rms_norm(h, w["attn_norm"], m.rms_eps))
         q = rope((x @ w["wq"].T).reshape(Bp, T, Hq, D), pos, m.rope_theta)
         k = rope((x @ w["wk"].T).reshape(Bp, T, Hkv, D), pos, m.rope_theta)
         v = (x @ w["wv"].T).reshape(Bp, T, Hkv, D)
@@ -183,8 +189,8 @@ def forward(model: OracleModel, kv: OracleKV, tokens, seqs=None) -> np.ndarray:
             kv.V[l][b][:, nb:nb + T] = v[i].transpose(1, 0, 2)
             o[i] = attention(q[i], kv.K[l][b], kv.V[l][b], nb, m.group)
         h = h + o.reshape(Bp * T, Hq * D) @ w["wo"].T
-        x = rms_norm(h, w["mlp_norm"], m.rms_eps)
-        h = h + (silu(x @ w["wg"].T) * (x @ w["wu"].T)) @ w["wd"].T
+        x = model.act(rms_norm(h, w["mlp_norm"], m.rms_eps))
+        h = h + model.act(silu(x @ w["wg"].T) * (x @ w["wu"].T)) @ w["wd"].T
     x = rms_norm(h, model.w["final_norm"], m.rms_eps)
     return x.reshape(Bp, T, m.hidden)
 

@@ -125,3 +125,63 @@ def test_bf16_encoder_round_to_nearest_even():
     assert got[0] == 1.0 and got[1] == 1.0 and got[2] == 1.0 + 2 ** -6
     assert abs(got[3] - (-2.5e-3)) <= 2.5e-3 * 2 ** -8
     assert np.isfinite(got[4])
+
+
+# ---------------------------------------------------------------- MXFP8 (FP8-activation mode)
+
+def test_round_e4m3_brute_force_with_ties():
+    from oracle.codecs import _E4M3_POS, round_e4m3
+    vals = _E4M3_POS
+    mids = (vals[:-1] + vals[1:]) / 2                      # exact ties
+    rng = np.random.default_rng(1)
+    x = np.concatenate([mids, -mids, rng.uniform(-500, 500, 4000), rng.uniform(-0.02, 0.02, 2000), [0.0, 448, 1e4]])
+    got = round_e4m3(x)
+    # brute force: nearest representable magnitude, ties to the even code, saturate
+    a = np.minimum(np.abs(x), 448.0)
+    d = np.abs(a[:, None] - vals[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    codes = np.array([np.flatnonzero(c)[0] if c.sum() == 1 else [k for k in np.flatnonzero(c) if k % 2 == 0][0]
+                      for c in cand])
+    assert np.array_equal(got, np.sign(x) * vals[codes])
+    # ties went to even codes
+    tie_codes = np.searchsorted(vals, np.abs(round_e4m3(mids)))
+    assert np.all(tie_codes % 2 == 0)
+
+
+def test_round_e4m3_matches_torch_in_range():
+    from oracle.codecs import round_e4m3
+    x = np.random.default_rng(2).standard_normal(50000) * 50
+    x = np.clip(x, -448, 448)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(round_e4m3(x), ref)
+
+
+def test_mxfp8_block_scale_saturation_and_idempotence():
+    from oracle.codecs import mxfp8_quantize, mxfp8_roundtrip
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((7, 96)).astype(np.float32)
+    x[1, :32] = 0.0                              # all-zero block
+    x[2, 5] = 1000.0                             # block max 1000 = 1.95 * 2^9: X = 1, saturates at 448 * 2
+    el, X = mxfp8_quantize(x)
+    amax = np.abs(x.reshape(7, 3, 32)).max(-1).astype(np.float64)
+    nz = amax > 0
+    assert np.array_equal(X[nz], np.floor(np.log2(amax[nz])).astype(np.int64) - 8)
+    assert X[1, 0] == -127 and np.all(el[1, :32] == 0)
+    rt = mxfp8_roundtrip(x)
+    assert rt[2, 5] == 448.0 * 2.0 ** X[2, 0] and X[2, 0] == 1
+    assert np.array_equal(mxfp8_roundtrip(rt), rt)                       # idempotent
+    # per element: within half a step of e4m3 (3 mantissa bits) of the block's scale, or saturated
+    step = np.maximum(2.0 ** (np.floor(np.log2(np.maximum(np.abs(x), 1e-30))) - 3), 2.0 ** (X.repeat(32, 1) - 9))
+    sat = np.abs(x) >= 464 * 2.0 ** X.repeat(32, 1)
+    err = np.abs(rt - x.astype(np.float64))
+    assert np.all((err <= step / 2 * (1 + 1e-12)) | sat)
+
+
+def test_mxfp8_decisions_follow_float32():
+    """Values that round to the same float32 quantise identically: the codes
+    are decided on float32, the precision the kernels hold activations in."""
+    from oracle.codecs import mxfp8_roundtrip
+    x32 = np.random.default_rng(4).standard_normal((3, 64)).astype(np.float32)
+    nudged = x32.astype(np.float64) * (1 + 1e-10)
+    assert np.array_equal(mxfp8_roundtrip(x32), mxfp8_roundtrip(nudged))

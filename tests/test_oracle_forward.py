@@ -233,3 +233,54 @@ def test_spec_equals_autoregressive_05b():
 
     out, taus = spec_decode(model, kv, pend, 64, draft)
     assert np.array_equal(out, ref[:, :64])
+
+
+# ---------------------------------------------------------------- FP8-activation mode
+
+def test_act_mx8_mode_changes_only_the_three_points(monkeypatch):
+    """With the MXFP8 round trip replaced by the identity the mode's forward is
+    the exact forward, bit for bit; the round trip runs at exactly three
+    points per layer (normed x before attention, before the MLP, and the
+    SwiGLU output)."""
+    import oracle.codecs as C
+    m = W.TINY
+    wts = W.model_weights(m, 1, gains="random")
+    calls = []
+    monkeypatch.setattr(C, "mxfp8_roundtrip", lambda x: (calls.append(np.shape(x)), x)[1])
+    exact, mode = OracleModel(m, wts), OracleModel(m, wts, act_mx8=True)
+    toks = W.child_rng(1, 60).integers(0, m.vocab, size=(1, 24))
+    a = forward(exact, OracleKV(m, 1, 64), toks)
+    b = forward(mode, OracleKV(m, 1, 64), toks)
+    assert np.array_equal(a, b)
+    assert calls == [(24, m.hidden), (24, m.hidden), (24, m.intermediate)] * m.n_layers
+
+
+def test_act_mx8_mode_spec_equals_autoregressive():
+    """Block quantisation is row-local, so greedy speculative decoding stays
+    lossless in the FP8-activation mode."""
+    m = W.TINY
+    wts = W.model_weights(m, 2)
+    model = OracleModel(m, wts, act_mx8=True)
+    kv = OracleKV(m, 1, 128 + 16 * 12)
+    pend = prefill(model, kv, [W.child_rng(2, 61).integers(0, m.vocab, size=128)], chunk=64)
+    kv_ar = kv.copy()
+    ref = ar_decode(model, kv_ar, pend, 96 + 16)
+    Lg = W.child_rng(2, 62)
+
+    def draft(b, p, emitted):
+        k = len(emitted)
+        d = np.zeros(15, dtype=np.int64)
+        seg = ref[b, k:k + 15]
+        d[:len(seg)] = seg
+        L = int(W.geometric_capped(Lg, 0.2))
+        if L < 16:
+            d[L - 1] = (d[L - 1] + 1) % m.vocab
+        return d
+
+    out, _ = spec_decode(model, kv, pend, 96, draft)
+    assert np.array_equal(out, ref[:, :96])
+    # and the mode does change the numbers (the quantisation is not a no-op)
+    exact = OracleModel(m, wts)
+    x0 = forward(exact, OracleKV(m, 1, 32), ref[:, :16])
+    x1 = forward(model, OracleKV(m, 1, 32), ref[:, :16])
+    assert not np.array_equal(x0, x1) and np.max(np.abs(x0 - x1)) < 0.5
