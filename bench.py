@@ -150,6 +150,61 @@ def e2e_batch1(ver, dev, m, lens, seed, n_rounds=32):
             "lossless": lossless, "drafts": "planted from the AR stream, acceptance min(Geometric(0.1), 16)"}
 
 
+def time_graph(ver, dev, tok, kv0, steps, warmup):
+    """Capture one step (restore kv_len, verify, commit) in a graph; replay
+    `warmup` times, then time `steps` replays with events on the stream.
+    Returns (ms per step, accept_len of the last step)."""
+    import torch
+    B = tok.shape[0]
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    bon = torch.empty(B, dtype=torch.int32, device="cuda")
+    amx = torch.empty(B, 16, dtype=torch.int32, device="cuda")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for _ in range(2):
+            dev.kv_len.copy_(kv0)
+            ver.verify(tok, acc, bon, amx)
+            ver.commit(B)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        dev.kv_len.copy_(kv0)
+        ver.verify(tok, acc, bon, amx)
+        ver.commit(B)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, acc.cpu().numpy()
+
+
+def kernel_times(ver, dev, tok, kv0, kinds, reps):
+    """Per kernel class: launch durations over `reps` eager passes (events on the stream)."""
+    import torch
+    B = tok.shape[0]
+    acc = torch.empty(B, dtype=torch.int32, device="cuda")
+    bon = torch.empty(B, dtype=torch.int32, device="cuda")
+    per_kind = {}
+    for k in kinds:
+        ver.time_kernel(k)
+        for _ in range(reps):
+            dev.kv_len.copy_(kv0)
+            ver.verify(tok, acc, bon, None)
+            ver.commit(B)
+        ver.time_kernel(None)
+        tot, n = ver.kernel_time()
+        per_kind[k] = {"ms_per_pass": tot / reps, "us_per_launch": 1000 * tot / max(n, 1),
+                       "launches_per_pass": n // reps}
+    dev.kv_len.copy_(kv0)
+    return per_kind
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -203,51 +258,16 @@ def main():
 
     # graph of one step: restore kv_len, verify, commit
     kv0 = dev.kv_len.clone()
-    acc = torch.empty(B, dtype=torch.int32, device="cuda")
-    bon = torch.empty(B, dtype=torch.int32, device="cuda")
-    amx = torch.empty(B, 16, dtype=torch.int32, device="cuda")
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for _ in range(2):
-            dev.kv_len.copy_(kv0)
-            ver.verify(tok, acc, bon, amx)
-            ver.commit(B)
-    torch.cuda.current_stream().wait_stream(s)
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        dev.kv_len.copy_(kv0)
-        ver.verify(tok, acc, bon, amx)
-        ver.commit(B)
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
     log(f"timing {args.steps} steps")
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for _ in range(args.steps):
-        graph.replay()
-    e1.record()
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / args.steps
-    assert np.array_equal(acc.cpu().numpy(), tau)
+    ms, acc = time_graph(ver, dev, tok, kv0, args.steps, args.warmup)
+    assert np.array_equal(acc, tau)
     assert ver.device_error() == 0
 
     # per-kernel-class launch durations (eager passes, events on the stream)
     kinds = ["qkv", "attention", "attn_merge", "o_proj", "gate_up", "down", "lm_head", "rmsnorm", "accept", "embed",
              "commit"]
-    per_kind = {}
     reps = max(3, min(20, args.steps // 5))
-    for k in kinds:
-        ver.time_kernel(k)
-        for _ in range(reps):
-            dev.kv_len.copy_(kv0)
-            ver.verify(tok, acc, bon, amx)
-            ver.commit(B)
-        ver.time_kernel(None)
-        tot, n = ver.kernel_time()
-        per_kind[k] = {"ms_per_pass": tot / reps, "us_per_launch": 1000 * tot / max(n, 1),
-                       "launches_per_pass": n // reps}
+    per_kind = kernel_times(ver, dev, tok, kv0, kinds, reps)
     dom = max(per_kind, key=lambda k: per_kind[k]["ms_per_pass"])
     by, fl = kernel_work(dom, m, lens)
     t_launch = per_kind[dom]["us_per_launch"] * 1e-6
@@ -282,6 +302,22 @@ def main():
     log("end-to-end decoding at batch 1")
     res["e2e"] = e2e_batch1(ver, dev, m, lens, wl.seed)
     ver.close()
+    # the FP8-activation mode on the same cache and blocks (drafts planted from
+    # the FP16 mode's greedy continuation, so tau also shows the mode's drift)
+    log("FP8-activation mode")
+    dev.kv_len.copy_(kv0)
+    ver8 = Verifier(dev, act_fmt="mxfp8")
+    ms8, acc8 = time_graph(ver8, dev, tok, kv0, args.steps, args.warmup)
+    k8 = kernel_times(ver8, dev, tok, kv0, ["qkv", "gate_up", "down", "rmsnorm"], reps)
+    assert ver8.device_error() == 0
+    ver8.close()
+    res["fp8_activations"] = {
+        "value": 1000.0 / ms8, "unit": "verify passes/s", "ms_per_step": ms8,
+        "activations": "MXFP8 (e4m3 + e8m0 per 32) into QKV, gate/up and down on the scaled FP8 MFMA; "
+                       "FP16 into O-proj and attention",
+        "sum_tau": int(acc8.sum()), "tau_rows_equal_fp16_mode": int((acc8 == tau).sum()),
+        "mean_tau_fp16_mode": float(tau.mean()), "mean_tau": float(acc8.mean()),
+        "kernels": k8}
     if not args.no_cpu:
         log(f"cpu baseline: oracle on {args.cpu_seqs} sequences")
         res["cpu_baseline"] = cpu_baseline(wl, weights, kv_layers, lens, args.cpu_seqs)

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 
 SPEC_OK = 0
 WFMT_FP8_E4M3_ROW, WFMT_MXFP4, WFMT_BF16 = 1, 2, 3
+ACT_FMTS = {"fp16": 0, "mxfp8": 1}
 DERR_TOKEN, DERR_CAPACITY, DERR_COMMIT = 1, 2, 4
 BLOCK = 16
 
@@ -28,7 +29,7 @@ _I = ctypes.c_int32
 class SpecModelDesc(ctypes.Structure):
     _fields_ = [("n_layers", _I), ("hidden", _I), ("n_q_heads", _I), ("n_kv_heads", _I), ("head_dim", _I),
                 ("intermediate", _I), ("vocab", _I), ("rms_eps", ctypes.c_float), ("rope_theta", ctypes.c_float),
-                ("attn_wfmt", _I), ("mlp_wfmt", _I), ("tied_lm_head", _I)]
+                ("attn_wfmt", _I), ("mlp_wfmt", _I), ("tied_lm_head", _I), ("act_fmt", _I)]
 
 
 class SpecLayerWeights(ctypes.Structure):
@@ -57,6 +58,10 @@ EXPORTS = {
     "spec_status_str": (ctypes.c_char_p, [_I]),
     "spec_debug_set_dump": (_I, [_P, _P, _P]),
     "spec_debug_linear": (_I, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "spec_debug_quant_mx8": (_I, [_I, _I, _P, _P, _P, _P]),
+    "spec_debug_linear_mx8": (_I, [_I, _I, _I, _P, _P, _P, _P, _I, _P, _P]),
+    "spec_debug_rmsnorm": (_I, [_I, _I, _P, _P, ctypes.c_float, _I, _P, _P, _P]),
+    "spec_debug_swiglu": (_I, [_I, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "spec_debug_attention": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P]),
     "spec_debug_time_kernel": (_I, [_P, _I]),
     "spec_debug_kernel_time": (_I, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I)]),
@@ -185,12 +190,14 @@ class DeviceModel:
 
 
 class Verifier:
-    """One spec_ctx bound to a DeviceModel."""
+    """One spec_ctx bound to a DeviceModel.  act_fmt: "fp16" or "mxfp8" (the
+    activation format of the QKV, gate/up and down projections)."""
 
-    def __init__(self, dev: DeviceModel):
+    def __init__(self, dev: DeviceModel, act_fmt: str = "fp16"):
         lib = load_library()
         self.dev = dev
         self._desc, self._arr, self._w, self._kv = dev.structs()
+        self._desc.act_fmt = ACT_FMTS[act_fmt]
         h = ctypes.c_void_p()
         _check(lib.spec_verify_init(ctypes.byref(self._desc), ctypes.byref(self._w), ctypes.byref(self._kv),
                                     _stream(), ctypes.byref(h)), "spec_verify_init")
@@ -271,6 +278,54 @@ def debug_linear(x_bf16: torch.Tensor, w: torch.Tensor, scales, wfmt: int, N: in
     _check(load_library().spec_debug_linear(M, N, K, _ptr(x_bf16), _ptr(w), _ptr(scales), wfmt, _ptr(y),
                                             _stream()), "spec_debug_linear")
     return y
+
+
+def debug_quant_mx8(x: torch.Tensor):
+    """MXFP8 encoding of fp32 rows x [M, K]: (e4m3 codes uint8 [M, K], e8m0 uint8 [M, K/32])."""
+    M, K = x.shape
+    codes = torch.empty(M, K, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(M, K // 32, dtype=torch.uint8, device=x.device)
+    _check(load_library().spec_debug_quant_mx8(M, K, _ptr(x), _ptr(codes), _ptr(scales), _stream()),
+           "spec_debug_quant_mx8")
+    return codes, scales
+
+
+def debug_linear_mx8(codes: torch.Tensor, scales: torch.Tensor, w: torch.Tensor, wscales, wfmt: int,
+                     N: int) -> torch.Tensor:
+    """y = x W^T (fp32) with MXFP8 activations (codes [M, K], e8m0 [M, K/32])."""
+    M, K = codes.shape
+    y = torch.empty(M, N, dtype=torch.float32, device=codes.device)
+    _check(load_library().spec_debug_linear_mx8(M, N, K, _ptr(codes), _ptr(scales), _ptr(w), _ptr(wscales), wfmt,
+                                                _ptr(y), _stream()), "spec_debug_linear_mx8")
+    return y
+
+
+def debug_rmsnorm(h: torch.Tensor, gain: torch.Tensor, eps: float, act_fmt: str = "fp16"):
+    """The pass's RMSNorm on fp32 rows h [M, H]: FP16 bits (int16 [M, H]) or
+    MXFP8 (codes uint8 [M, H], e8m0 uint8 [M, H/32])."""
+    M, H = h.shape
+    if act_fmt == "fp16":
+        x, xs = torch.empty(M, H, dtype=torch.int16, device=h.device), None
+    else:
+        x = torch.empty(M, H, dtype=torch.uint8, device=h.device)
+        xs = torch.empty(M, H // 32, dtype=torch.uint8, device=h.device)
+    _check(load_library().spec_debug_rmsnorm(M, H, _ptr(h), _ptr(gain), eps, ACT_FMTS[act_fmt], _ptr(x), _ptr(xs),
+                                             _stream()), "spec_debug_rmsnorm")
+    return x if xs is None else (x, xs)
+
+
+def debug_swiglu(x: torch.Tensor, x_scales, w: torch.Tensor, wscales, wfmt: int, I: int, out_fmt: str = "fp16"):
+    """SiLU(x Wg^T) * (x Wu^T) through the gate/up kernel.  x: FP16 bits
+    [M, H] (x_scales None) or MXFP8 codes [M, H] with e8m0 x_scales."""
+    M, H = x.shape
+    if out_fmt == "fp16":
+        a, as_ = torch.empty(M, I, dtype=torch.int16, device=x.device), None
+    else:
+        a = torch.empty(M, I, dtype=torch.uint8, device=x.device)
+        as_ = torch.empty(M, I // 32, dtype=torch.uint8, device=x.device)
+    _check(load_library().spec_debug_swiglu(M, H, I, _ptr(x), _ptr(x_scales), _ptr(w), _ptr(wscales), wfmt,
+                                            ACT_FMTS[out_fmt], _ptr(a), _ptr(as_), _stream()), "spec_debug_swiglu")
+    return a if as_ is None else (a, as_)
 
 
 def debug_attention(q, k_cache, v_cache, kv_len, batch, n_q_heads, n_kv_heads, head_dim, split_len=0):

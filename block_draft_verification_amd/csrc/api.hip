@@ -20,6 +20,7 @@ struct spec_ctx {
   void *ws;
   float *h;
   uint16_t *x, *q, *ao, *act;
+  uint8_t *x8, *xs8, *a8, *as8;  // MXFP8 activations: normed x [Mmax][H] (+ e8m0 [Mmax][H/32]), SwiGLU [Mmax][I]
   float *part_o;
   float2 *part_ml;
   int32_t *last_tau, *err;
@@ -75,6 +76,7 @@ static int check_model(const spec_model_desc *m) {
   if ((m->n_q_heads * m->head_dim) % 64) return SPEC_E_SHAPE;
   if (m->attn_wfmt != SPEC_WFMT_FP8_E4M3_ROW) return SPEC_E_UNSUPPORTED;
   if (m->mlp_wfmt != SPEC_WFMT_FP8_E4M3_ROW && m->mlp_wfmt != SPEC_WFMT_MXFP4) return SPEC_E_UNSUPPORTED;
+  if (m->act_fmt != SPEC_ACT_FP16 && m->act_fmt != SPEC_ACT_MXFP8) return SPEC_E_UNSUPPORTED;
   return SPEC_OK;
 }
 
@@ -152,7 +154,9 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
                     4,                               // err
                     (size_t)lm_parts(V) * Mm * 8,    // amax
                     (size_t)kv->max_ctx * (D / 2) * 8,  // rope
-                    rfloats * 4};                     // residual split-K partials
+                    rfloats * 4,                     // residual split-K partials
+                    Mm * H + Mm * (H / 32),          // x8, xs8
+                    Mm * I + Mm * (I / 32)};         // a8, as8
   const int NS = sizeof(sizes) / sizeof(sizes[0]);
   size_t off[NS], total = 0;
   for (int i = 0; i < NS; ++i) {
@@ -181,6 +185,10 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   c->amax = (ArgmaxPart *)(base + off[10]);
   c->rope = (float2 *)(base + off[11]);
   c->rpart = (float *)(base + off[12]);
+  c->x8 = (uint8_t *)(base + off[13]);
+  c->xs8 = c->x8 + Mm * H;
+  c->a8 = (uint8_t *)(base + off[14]);
+  c->as8 = c->a8 + Mm * I;
   c->dump_hidden = c->dump_logits = nullptr;
 
   // RoPE table: angle = p * theta^(-2i/D), in double, stored as fp32 (cos, sin)
@@ -233,18 +241,25 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     CK(launch_embed(tokens, M, H, V, c->embed, c->h, c->kv.kv_len, max_ctx, kvl, c->err, st));
   }
   const int ns_o = residual_nsplit(M, H, Hq * D), ns_d = residual_nsplit(M, H, I);
+  const bool mx = m.act_fmt == SPEC_ACT_MXFP8;
+  const ActIn xin = mx ? ActIn{c->x8, c->xs8} : ActIn{c->x, nullptr};
+  const ActIn ain = mx ? ActIn{c->a8, c->as8} : ActIn{c->act, nullptr};
+  auto norm = [&](int nsplit, const float *gain) {
+    return mx ? launch_norm_mx8(c->h, c->rpart, nsplit, gain, M, H, m.rms_eps, c->x8, c->xs8, nullptr, st)
+              : launch_norm(c->h, c->rpart, nsplit, gain, M, H, m.rms_eps, c->x, 0, nullptr, st);
+  };
   int pending = 0;  // splits of the last residual projection not yet added to h
   for (int l = 0; l < m.n_layers; ++l) {
     const spec_layer_weights &L = c->layers[l];
     uint16_t *kc = c->kv.k_cache + l * lstride, *vc = c->kv.v_cache + l * lstride;
     {
       Timed t(c, SPEC_K_RMSNORM, st);
-      CK(launch_norm(c->h, c->rpart, pending, L.attn_norm, M, H, m.rms_eps, c->x, 0, nullptr, st));
+      CK(norm(pending, L.attn_norm));
     }
     QkvOut qo{c->q, kc, vc, c->kv.kv_len, c->rope, Hq, Hkv, max_ctx, kvl};
     {
       Timed t(c, SPEC_K_QKV, st);
-      CK(launch_qkv(c->x, M, H, D, LinearW{L.w_qkv, L.s_qkv, SPEC_WFMT_FP8_E4M3_ROW}, qo, st));
+      CK(launch_qkv(xin, M, H, D, LinearW{L.w_qkv, L.s_qkv, SPEC_WFMT_FP8_E4M3_ROW}, qo, st));
     }
     aa.k_cache = kc;
     aa.v_cache = vc;
@@ -258,20 +273,21 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     }
     {
       Timed t(c, SPEC_K_OPROJ, st);
-      CK(launch_residual_partial(c->ao, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, c->rpart,
+      CK(launch_residual_partial(ActIn{c->ao, nullptr}, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, c->rpart,
                                  st));
     }
     {
       Timed t(c, SPEC_K_RMSNORM, st);
-      CK(launch_norm(c->h, c->rpart, ns_o, L.mlp_norm, M, H, m.rms_eps, c->x, 0, nullptr, st));
+      CK(norm(ns_o, L.mlp_norm));
     }
     {
       Timed t(c, SPEC_K_GATE_UP, st);
-      CK(launch_swiglu(c->x, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, c->act, st));
+      CK(launch_swiglu(xin, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, mx ? (void *)c->a8 : c->act,
+                       mx ? c->as8 : nullptr, st));
     }
     {
       Timed t(c, SPEC_K_DOWN, st);
-      CK(launch_residual_partial(c->act, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, c->rpart, st));
+      CK(launch_residual_partial(ain, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, c->rpart, st));
     }
     pending = ns_d;
   }
@@ -385,7 +401,57 @@ int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const 
     return SPEC_E_UNSUPPORTED;
   if (!aligned16(x) || !aligned16(w) || !aligned16(y) || (wfmt == SPEC_WFMT_FP8_E4M3_ROW && !aligned16(scales)))
     return SPEC_E_ARG;
-  CK(launch_linear_f32(x, M, N, K, LinearW{w, scales, wfmt}, y, st));
+  CK(launch_linear_f32(ActIn{x, nullptr}, M, N, K, LinearW{w, scales, wfmt}, y, st));
+  CK(hipStreamSynchronize(st));
+  return SPEC_OK;
+}
+
+int spec_debug_quant_mx8(int32_t M, int32_t K, const float *x, uint8_t *codes, uint8_t *scales, hipStream_t st) {
+  if (M < 1 || K < 32 || K % 32 || !x || !codes || !scales) return SPEC_E_ARG;
+  if (!aligned16(x) || !aligned16(codes)) return SPEC_E_ARG;
+  CK(launch_quant_mx8(x, M, K, codes, scales, st));
+  CK(hipStreamSynchronize(st));
+  return SPEC_OK;
+}
+
+int spec_debug_rmsnorm(int32_t M, int32_t H, const float *h, const float *gain, float eps, int32_t act_fmt, void *x,
+                       uint8_t *xs, hipStream_t st) {
+  if (M < 1 || H < 32 || H > 4096 || H % 32 || !h || !gain || !x || !(eps > 0.f)) return SPEC_E_ARG;
+  if (!aligned16(h) || !aligned16(gain) || !aligned16(x)) return SPEC_E_ARG;
+  if (act_fmt == SPEC_ACT_FP16) {
+    CK(launch_norm(const_cast<float *>(h), nullptr, 0, gain, M, H, eps, (uint16_t *)x, 0, nullptr, st));
+  } else if (act_fmt == SPEC_ACT_MXFP8) {
+    if (!xs) return SPEC_E_ARG;
+    CK(launch_norm_mx8(const_cast<float *>(h), nullptr, 0, gain, M, H, eps, (uint8_t *)x, xs, nullptr, st));
+  } else {
+    return SPEC_E_UNSUPPORTED;
+  }
+  CK(hipStreamSynchronize(st));
+  return SPEC_OK;
+}
+
+int spec_debug_swiglu(int32_t M, int32_t H, int32_t I, const void *x, const uint8_t *x_scales, const void *w,
+                      const void *scales, int32_t wfmt, int32_t out_fmt, void *a, uint8_t *a_scales, hipStream_t st) {
+  if (M < 1 || H < 64 || I < 64 || H % 64 || I % 64 || !x || !w || !scales || !a) return SPEC_E_ARG;
+  if (wfmt != SPEC_WFMT_FP8_E4M3_ROW && wfmt != SPEC_WFMT_MXFP4) return SPEC_E_UNSUPPORTED;
+  if (out_fmt != SPEC_ACT_FP16 && out_fmt != SPEC_ACT_MXFP8) return SPEC_E_UNSUPPORTED;
+  if (out_fmt == SPEC_ACT_MXFP8 && !a_scales) return SPEC_E_ARG;
+  if (!aligned16(x) || !aligned16(w) || !aligned16(a) || (wfmt == SPEC_WFMT_FP8_E4M3_ROW && !aligned16(scales)))
+    return SPEC_E_ARG;
+  CK(launch_swiglu(ActIn{x, x_scales}, M, H, I, LinearW{w, scales, wfmt}, a,
+                   out_fmt == SPEC_ACT_MXFP8 ? a_scales : nullptr, st));
+  CK(hipStreamSynchronize(st));
+  return SPEC_OK;
+}
+
+int spec_debug_linear_mx8(int32_t M, int32_t N, int32_t K, const uint8_t *x_codes, const uint8_t *x_scales,
+                          const void *w, const void *scales, int32_t wfmt, float *y, hipStream_t st) {
+  if (M < 1 || N < 64 || K < 64 || N % 64 || K % 64 || !x_codes || !x_scales || !w || !scales || !y)
+    return SPEC_E_ARG;
+  if (wfmt != SPEC_WFMT_FP8_E4M3_ROW && wfmt != SPEC_WFMT_MXFP4) return SPEC_E_UNSUPPORTED;
+  if (!aligned16(x_codes) || !aligned16(w) || !aligned16(y) || (wfmt == SPEC_WFMT_FP8_E4M3_ROW && !aligned16(scales)))
+    return SPEC_E_ARG;
+  CK(launch_linear_f32(ActIn{x_codes, x_scales}, M, N, K, LinearW{w, scales, wfmt}, y, st));
   CK(hipStreamSynchronize(st));
   return SPEC_OK;
 }

@@ -108,6 +108,39 @@ __device__ __forceinline__ f32x16_t mfma32x32x16_f16(u32x4_t a, u32x4_t b, f32x1
                                                 __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
 }
 
+typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
+
+// D += A(32x64) * B(64x32) with OCP microscaling (v_mfma_scale_f32_32x32x64_f8f6f4).
+// Lane (c, h) supplies row c of A and column c of B.  FP8 operands (format 0,
+// e4m3): bytes 0-15 are k 16h..16h+15 and bytes 16-31 are k 32+16h..32+16h+15.
+// FP4 operands (format 4, e2m1, only the low 4 dwords read): k 32h..32h+31,
+// low nibble first.  The e8m0 scale of k block b (k 32b..32b+31) of a row or
+// column is taken from lane half h = b.  Output layout as for 32x32x16.
+// (Layout and scale attribution measured on gfx950 against a host product.)
+template <int FMT_A>
+__device__ __forceinline__ f32x16_t mfma_mx(i32x8_t a, i32x8_t b, f32x16_t c, int scale_a, int scale_b) {
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, FMT_A, 0, 0, scale_a, 0, scale_b);
+}
+
+// MXFP8 quantisation of one 32-value block held 4 values per lane by 8
+// consecutive lanes (lanes 8j .. 8j+7, values in order): X = floor(log2(amax))
+// - 8 (e8m0 = X + 127, clamped), elements RNE to e4m3 after exact scaling by
+// 2^-X, saturated at +-448.  Returns the 4 codes (byte i = value i).
+__device__ __forceinline__ uint32_t mx8_quant4(f32x4_t v, uint32_t &e8) {
+  float a = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+  a = fmaxf(a, __shfl_xor(a, 1));
+  a = fmaxf(a, __shfl_xor(a, 2));
+  a = fmaxf(a, __shfl_xor(a, 4));
+  int X = a > 0.f ? __builtin_amdgcn_frexp_expf(a) - 1 - 8 : -127;
+  X = X < -127 ? -127 : (X > 127 ? 127 : X);
+  e8 = (uint32_t)(X + 127);
+  float q[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) q[i] = fminf(fmaxf(__builtin_ldexpf(v[i], -X), -448.f), 448.f);
+  const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(q[0], q[1], 0, false);
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(q[2], q[3], lo, true);
+}
+
 // Workgroup barrier without __syncthreads()'s global-memory fence, which on
 // gfx950 waits for every outstanding global load (vmcnt(0)) and so drains
 // any prefetch in flight.  Callers wait for the loads they need themselves;

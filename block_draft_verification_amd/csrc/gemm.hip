@@ -83,14 +83,17 @@ __device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_BF16> &r) {
 }
 __device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_MXFP4> &r) { asm volatile("" ::"v"(r.c), "v"(r.e)); }
 
-// k = first of the lane's 32 k (a multiple of 32)
-template <int FMT>
+// kb = first k of the step (a multiple of 64); lane half h.  Non-A8 lanes read
+// the 32 consecutive k kb+32h..kb+32h+31; A8 (scaled FP8 MFMA) FP8 lanes read
+// k kb+16h..+15 and kb+32+16h..+15, the operand order of that instruction.
+template <int FMT, bool A8 = false>
 __device__ __forceinline__ void load_w(WRaw<FMT> &r, const uint8_t *__restrict__ w,
-                                       const uint8_t *__restrict__ s, int row, int K, int k) {
+                                       const uint8_t *__restrict__ s, int row, int K, int kb, int h) {
+  const int k = kb + 32 * h;
   if constexpr (FMT == SPEC_WFMT_FP8_E4M3_ROW) {
-    const uint8_t *p = w + (size_t)row * K + k;
-    r.c[0] = vload16(p);
-    r.c[1] = vload16(p + 16);
+    const uint8_t *p = w + (size_t)row * K + kb;
+    r.c[0] = vload16(p + (A8 ? 16 * h : 32 * h));
+    r.c[1] = vload16(p + (A8 ? 32 + 16 * h : 32 * h + 16));
   } else if constexpr (FMT == SPEC_WFMT_BF16) {
     const uint16_t *p = reinterpret_cast<const uint16_t *>(w) + (size_t)row * K + k;
 #pragma unroll
@@ -134,7 +137,8 @@ __device__ __forceinline__ f32x16_t mma(u32x4_t a, u32x4_t b, f32x16_t c) {
 }
 
 struct GemmArgs {
-  const uint16_t *x;  // activations [M][K] (fp16 or bf16 bits)
+  const void *x;      // activations [M][K]: fp16 or bf16 bits, or e4m3 codes (A8)
+  const uint8_t *xs;  // A8: e8m0 scale of each 32 activations [M][K/32]
   int M, K;
   const uint8_t *w, *s;
   int nb, mb;         // N blocks (4 units each), M blocks
@@ -172,17 +176,28 @@ __device__ __forceinline__ void lds_load16(const void *g, void *l) {
 // 128-byte window), so the reads are free of bank conflicts.
 __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
 
+// FP8 activation tile (A8): 64-byte rows of four 16-byte chunks, chunk c of
+// row r at slot r*4 + (c ^ swz8(r)); the 16 lanes of a read phase (rows r..r+15,
+// one logical chunk) land on 16 distinct bank groups of a 256-byte window.
+__device__ __forceinline__ int swz8(int row) { return (row >> 2) & 3; }
+
 // Waves per SIMD the register budget is sized for.
 template <int FMT, int NT, int MT> struct GemmOcc {
   static constexpr int value = (NT * MT <= 4 && (FMT != SPEC_WFMT_BF16 || GEMM_BF16_OCC2)) ? 2 : 1;
 };
 
-template <bool F16, int FMT, int NT, int MT, class Epi>
+// A8: activations are MXFP8 (e4m3 codes + e8m0 per 32) and the MFMA is the
+// scaled 32x32x64 FP8/FP4 one: one MFMA per tile pair and k step, FP8 weights
+// enter raw (their per-row scale stays in the epilogue) and MXFP4 weights with
+// their own e8m0 scales.
+template <bool F16, int FMT, int NT, int MT, class Epi, bool A8 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GemmOcc<FMT, NT, MT>::value, 8))) void
 gemm_kernel(GemmArgs ga, Epi epi) {
+  static_assert(!A8 || FMT != SPEC_WFMT_BF16, "A8 takes FP8 or MXFP4 weights");
   constexpr int ROWS = 32 * MT;             // activation rows per workgroup
-  constexpr int AJ = MT;                    // LDS-DMA instructions per wave per stage (ROWS*8 chunks / 256 lanes)
-  constexpr int SE = ROWS * 64;             // 16-bit elements per stage
+  // LDS-DMA instructions per wave per stage: ROWS*8 (16-bit) or ROWS*4 (FP8) chunks of 16 bytes over 256 lanes
+  constexpr int AJ = A8 ? (MT + 1) / 2 : MT;
+  constexpr int SE = A8 ? AJ * 2048 : ROWS * 64;  // 16-bit elements per stage
   constexpr int DIST = GEMM_DEPTH;          // k steps loaded ahead of the one computed
   constexpr int NS = DIST + 1;              // LDS stages = weight register sets
   // staged epilogue: per wave a [32][LD] fp32 tile of block rows x output columns
@@ -201,14 +216,25 @@ gemm_kernel(GemmArgs ga, Epi epi) {
   const int M = ga.M, K = ga.K, ksteps = K / 64;
   const int ks0 = blockIdx.z * ga.spl, nsteps = min(ks0 + ga.spl, ksteps) - ks0;
 
-  // Every wave issues AJ activation loads and NT*w_loads weight loads per
-  // step, so the vmcnt waits below are one compile-time count for all waves.
-  const uint16_t *agp[AJ];
+  // Every wave issues AJ activation loads and NT*w_loads (+ MT scale loads for
+  // A8) weight loads per step, so the vmcnt waits below are one compile-time
+  // count for all waves.  agp: byte address of the lane's 16-byte chunk at k step 0.
+  const uint8_t *agp[AJ];
 #pragma unroll
   for (int i = 0; i < AJ; ++i) {
-    const int P = (wave + 4 * i) * 64 + lane, row = P >> 3, ch = (P & 7) ^ swz(row);
-    const int m = m0 + row < M ? m0 + row : 0;  // rows past M read row 0 and are never stored
-    agp[i] = ga.x + (size_t)m * K + ks0 * 64 + ch * 8;
+    const int P = (wave + 4 * i) * 64 + lane;
+    const int row = A8 ? P >> 2 : P >> 3;
+    const int ch = A8 ? (P & 3) ^ swz8(row) : (P & 7) ^ swz(row);
+    const int m = row < ROWS && m0 + row < M ? m0 + row : 0;  // rows past M (or padding) read row 0, never stored
+    agp[i] = reinterpret_cast<const uint8_t *>(ga.x) + ((size_t)m * K + ks0 * 64) * (A8 ? 1 : 2) + ch * 16;
+  }
+  const uint8_t *asp[A8 ? MT : 1];  // A8: e8m0 of block h of block row 32*mt + c at k step 0
+  if constexpr (A8) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int m = m0 + 32 * mt + c < M ? m0 + 32 * mt + c : 0;
+      asp[mt] = ga.xs + (size_t)m * (K / 32) + ks0 * 2 + h;
+    }
   }
   int wrow[NT];
 #pragma unroll
@@ -222,6 +248,36 @@ gemm_kernel(GemmArgs ga, Epi epi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][mt][v] = 0.f;
 
+  auto compute_a8 = [&](int stage, const WRaw<FMT>(&wr)[NT], const uint32_t(&sc)[A8 ? MT : 1]) {
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(As) + stage * SE * 2;
+    i32x8_t wv[NT];
+    int sa[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      if constexpr (FMT == SPEC_WFMT_FP8_E4M3_ROW) {
+        const WRaw<SPEC_WFMT_FP8_E4M3_ROW> &r = reinterpret_cast<const WRaw<SPEC_WFMT_FP8_E4M3_ROW> &>(wr[t]);
+        wv[t] = i32x8_t{(int)r.c[0].x, (int)r.c[0].y, (int)r.c[0].z, (int)r.c[0].w,
+                        (int)r.c[1].x, (int)r.c[1].y, (int)r.c[1].z, (int)r.c[1].w};
+        sa[t] = 127;  // 2^0: the per-row fp32 scale is applied in the epilogue
+      } else {
+        const WRaw<SPEC_WFMT_MXFP4> &r = reinterpret_cast<const WRaw<SPEC_WFMT_MXFP4> &>(wr[t]);
+        wv[t] = i32x8_t{(int)r.c.x, (int)r.c.y, (int)r.c.z, (int)r.c.w, 0, 0, 0, 0};
+        sa[t] = (int)r.e;
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      const int row = 32 * mt + c, sw = swz8(row);
+      const u32x4_t b0 = *reinterpret_cast<const u32x4_t *>(base + row * 64 + ((h) ^ sw) * 16);
+      const u32x4_t b1 = *reinterpret_cast<const u32x4_t *>(base + row * 64 + ((2 + h) ^ sw) * 16);
+      const i32x8_t bv = i32x8_t{(int)b0.x, (int)b0.y, (int)b0.z, (int)b0.w, (int)b1.x, (int)b1.y, (int)b1.z, (int)b1.w};
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+        acc[t][mt] = mfma_mx<FMT == SPEC_WFMT_MXFP4 ? 4 : 0>(wv[t], bv, acc[t][mt], sa[t], (int)sc[mt]);
+    }
+    __builtin_amdgcn_sched_barrier(0);  // keep the next step's wait and barrier behind these MFMAs
+  };
   auto compute = [&](int stage, const WRaw<FMT>(&wr)[NT]) {
     __builtin_amdgcn_sched_barrier(0);
     u32x4_t wop[NT][4];
@@ -251,11 +307,16 @@ gemm_kernel(GemmArgs ga, Epi epi) {
   };
   auto issue_a = [&](int step, int stage) {
 #pragma unroll
-    for (int i = 0; i < AJ; ++i) lds_load16(agp[i] + step * 64, As + stage * SE + (wave + 4 * i) * 512);
+    for (int i = 0; i < AJ; ++i)
+      lds_load16(agp[i] + step * (A8 ? 64 : 128), As + stage * SE + (wave + 4 * i) * 512);
   };
-  auto issue_w = [&](WRaw<FMT>(&wr)[NT], int step) {
+  auto issue_w = [&](WRaw<FMT>(&wr)[NT], uint32_t(&sc)[A8 ? MT : 1], int step) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) load_w<FMT>(wr[t], ga.w, ga.s, wrow[t], K, (ks0 + step) * 64 + 32 * h);
+    for (int t = 0; t < NT; ++t) load_w<FMT, A8>(wr[t], ga.w, ga.s, wrow[t], K, (ks0 + step) * 64, h);
+    if constexpr (A8) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) sc[mt] = vload1(asp[mt] + step * 2);
+    }
   };
   // Software pipeline, DIST k steps deep.  At step s the wave issues step
   // s+DIST (weights into register set (s+DIST)%NS, then activations straight to
@@ -265,12 +326,13 @@ gemm_kernel(GemmArgs ga, Epi epi) {
   // Steps past the end re-load the last step into a set / stage nobody reads.
   // Loads complete in issue order, so "step s landed" is "at most the loads of
   // steps s+1 .. s+DIST-1 outstanding".
-  constexpr int PER_STEP = NT * w_loads<FMT>() + AJ;
+  constexpr int PER_STEP = NT * w_loads<FMT>() + (A8 ? MT : 0) + AJ;
   static_assert((DIST - 1) * PER_STEP < 64, "vmcnt holds 6 bits");
   WRaw<FMT> wr[NS][NT];
+  uint32_t scr[NS][A8 ? MT : 1];
 #pragma unroll
   for (int i = 0; i < DIST; ++i) {
-    issue_w(wr[i], min(i, nsteps - 1));
+    issue_w(wr[i], scr[i], min(i, nsteps - 1));
     issue_a(min(i, nsteps - 1), i);
   }
   for (int s0 = 0; s0 < nsteps; s0 += NS) {
@@ -280,18 +342,26 @@ gemm_kernel(GemmArgs ga, Epi epi) {
       WAIT_VMCNT((DIST - 1) * PER_STEP);
       lds_barrier();  // stage s visible to all waves; every wave is done with step s-1's stage
       __builtin_amdgcn_sched_barrier(0);
-      issue_w(wr[(ph + DIST) % NS], min(s + DIST, nsteps - 1));
+      issue_w(wr[(ph + DIST) % NS], scr[(ph + DIST) % NS], min(s + DIST, nsteps - 1));
       issue_a(min(s + DIST, nsteps - 1), (ph + DIST) % NS);
       __builtin_amdgcn_sched_barrier(0);
-      if (ph == 0 || s < nsteps) compute(ph, wr[ph]);
+      if (ph == 0 || s < nsteps) {
+        if constexpr (A8) compute_a8(ph, wr[ph], scr[ph]);
+        else compute(ph, wr[ph]);
+      }
     }
   }
   WAIT_VMCNT(0);  // nothing may still be landing in LDS or registers past this point
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int i = 0; i < NS; ++i)
+  for (int i = 0; i < NS; ++i) {
 #pragma unroll
     for (int t = 0; t < NT; ++t) hold(wr[i][t]);
+    if constexpr (A8) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) asm volatile("" ::"v"(scr[i][mt]));
+    }
+  }
   if constexpr (Epi::kStaged) {
     // Each wave writes its finished outputs (scaled, RoPE / SwiGLU applied) as
     // fp32 into its own LDS tile, then reads it back along rows so that every
@@ -464,13 +534,18 @@ struct EpiQkv {
 };
 
 // Tiles [0, NT/2) read gate rows, tiles [NT/2, NT) the matching up rows;
-// a = SiLU(gate) * up goes out as FP16.  A unit covers 16*NT outputs.
-template <int NTc>
+// a = SiLU(gate) * up goes out as FP16, or (MX8) as MXFP8: e4m3 codes [M][I]
+// plus the e8m0 exponent of each 32 outputs [M][I/32].  A unit covers 16*NT
+// outputs; with NT = 2 that is one 32-wide scale block per row, held by 8
+// consecutive lanes of the staged store.
+template <int NTc, bool MX8 = false>
 struct EpiSwiglu {
   static constexpr bool kStaged = true;
+  static_assert(!MX8 || NTc == 2, "an MXFP8 block is the 32 outputs of one row of a unit");
   int units, I;
   const float *scale;  // per-row FP8 scales [2I], NULL when decoded with the scale
-  uint16_t *a;
+  void *a;             // FP16 bits or e4m3 codes
+  uint8_t *as;         // MX8: e8m0 [M][I/32]
   __device__ int row(int unit, int t) const {
     return t < NTc / 2 ? unit * 16 * NTc + 32 * t : I + unit * 16 * NTc + 32 * (t - NTc / 2);
   }
@@ -492,7 +567,15 @@ struct EpiSwiglu {
       }
   }
   __device__ void put(int unit, int m, int col, f32x4_t v, int z) const {
-    store_f16x4(a + (size_t)m * I + unit * 16 * NTc + col, v[0], v[1], v[2], v[3]);
+    const int n = unit * 16 * NTc + col;
+    if constexpr (MX8) {
+      uint32_t e8;
+      const uint32_t codes = mx8_quant4(v, e8);  // lanes col/4 = 0..7 of this row share the block
+      *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(a) + (size_t)m * I + n) = codes;
+      if ((col & 31) == 0) as[(size_t)m * (I / 32) + n / 32] = (uint8_t)e8;
+    } else {
+      store_f16x4(static_cast<uint16_t *>(a) + (size_t)m * I + n, v[0], v[1], v[2], v[3]);
+    }
   }
 };
 
@@ -578,21 +661,21 @@ int residual_nsplit(int M, int N, int K) {
 
 // ---------------------------------------------------------------- launchers
 
-template <bool F16, int FMT, int NT, int MT, class Epi>
+template <bool F16, int FMT, int NT, int MT, bool A8, class Epi>
 static hipError_t go(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<F16, FMT, NT, MT, Epi>), dim3(p.grid_x, 1, p.nsplit), dim3(256), 0, st, ga,
-                     epi);
+  hipLaunchKernelGGL((gemm_kernel<F16, FMT, NT, MT, Epi, A8>), dim3(p.grid_x, 1, p.nsplit), dim3(256), 0, st,
+                     ga, epi);
   return hipGetLastError();
 }
 
-template <bool F16, int FMT, int NT, class Epi>
+template <bool F16, int FMT, int NT, bool A8, class Epi>
 static hipError_t go_m(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
   switch (p.MT) {
-    case 1: return go<F16, FMT, NT, 1>(p, ga, epi, st);
-    case 2: return go<F16, FMT, NT, 2>(p, ga, epi, st);
+    case 1: return go<F16, FMT, NT, 1, A8>(p, ga, epi, st);
+    case 2: return go<F16, FMT, NT, 2, A8>(p, ga, epi, st);
     default:
-      if constexpr (NT <= 2) return go<F16, FMT, NT, 4>(p, ga, epi, st);
-      else return go<F16, FMT, NT, 2>(p, ga, epi, st);
+      if constexpr (NT <= 2) return go<F16, FMT, NT, 4, A8>(p, ga, epi, st);
+      else return go<F16, FMT, NT, 2, A8>(p, ga, epi, st);
   }
 }
 
@@ -600,18 +683,24 @@ static hipError_t go_m(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hi
 // only those kernels are instantiated.
 constexpr unsigned kFp8 = 1u << SPEC_WFMT_FP8_E4M3_ROW, kMx4 = 1u << SPEC_WFMT_MXFP4, kBf16 = 1u << SPEC_WFMT_BF16;
 
+// x.xs == NULL: FP16 (BF16 for BF16 weights) activations on the 32x32x16 MFMA;
+// else MXFP8 activations on the scaled 32x32x64 MFMA (FP8 / MXFP4 weights).
 template <int NT, unsigned FMTS, class Epi, int MAXMT = (NT > 2 ? 2 : 4)>
-static hipError_t run(const uint16_t *x, int M, int K, const LinearW &w, Epi epi, bool allow_split,
-                      hipStream_t st) {
+static hipError_t run(ActIn x, int M, int K, const LinearW &w, Epi epi, bool allow_split, hipStream_t st) {
   const GemmPlan p = gemm_plan(M, epi.units, K / 64, pick_mt(M, epi.units, MAXMT), allow_split);
-  GemmArgs ga{x, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
+  GemmArgs ga{x.x, x.xs, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
               p.nb, p.mb, p.grid_x / 8, p.spl};
+  const bool a8 = x.xs != nullptr;
   if constexpr ((FMTS & kFp8) != 0)
-    if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW) return go_m<true, SPEC_WFMT_FP8_E4M3_ROW, NT>(p, ga, epi, st);
+    if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW)
+      return a8 ? go_m<true, SPEC_WFMT_FP8_E4M3_ROW, NT, true>(p, ga, epi, st)
+                : go_m<true, SPEC_WFMT_FP8_E4M3_ROW, NT, false>(p, ga, epi, st);
   if constexpr ((FMTS & kMx4) != 0)
-    if (w.wfmt == SPEC_WFMT_MXFP4) return go_m<true, SPEC_WFMT_MXFP4, NT>(p, ga, epi, st);
+    if (w.wfmt == SPEC_WFMT_MXFP4)
+      return a8 ? go_m<true, SPEC_WFMT_MXFP4, NT, true>(p, ga, epi, st)
+                : go_m<true, SPEC_WFMT_MXFP4, NT, false>(p, ga, epi, st);
   if constexpr ((FMTS & kBf16) != 0)
-    if (w.wfmt == SPEC_WFMT_BF16) return go_m<false, SPEC_WFMT_BF16, NT>(p, ga, epi, st);
+    if (w.wfmt == SPEC_WFMT_BF16 && !a8) return go_m<false, SPEC_WFMT_BF16, NT, false>(p, ga, epi, st);
   return hipErrorInvalidValue;
 }
 
@@ -619,19 +708,21 @@ static const float *fp8_scale(const LinearW &w) {
   return w.wfmt == SPEC_WFMT_FP8_E4M3_ROW ? reinterpret_cast<const float *>(w.s) : nullptr;
 }
 
-hipError_t launch_linear_f32(const uint16_t *x, int M, int N, int K, LinearW w, float *y, hipStream_t st) {
+hipError_t launch_linear_f32(ActIn x, int M, int N, int K, LinearW w, float *y, hipStream_t st) {
   return run<1, kFp8 | kMx4 | kBf16>(x, M, K, w, EpiF32<1>{N / 32, N, y, fp8_scale(w)}, false, st);
 }
 
-hipError_t launch_residual_partial(const uint16_t *x, int M, int N, int K, LinearW w, float *part, hipStream_t st) {
+hipError_t launch_residual_partial(ActIn x, int M, int N, int K, LinearW w, float *part, hipStream_t st) {
   return run<2, kFp8 | kMx4>(x, M, K, w, EpiPartial<2>{N / 64, N, M, part, fp8_scale(w)}, true, st);
 }
 
-hipError_t launch_swiglu(const uint16_t *x, int M, int H, int I, LinearW w, uint16_t *a, hipStream_t st) {
-  return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2>{I / 32, I, fp8_scale(w), a}, false, st);
+hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8_t *a_scales, hipStream_t st) {
+  if (a_scales)
+    return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2, true>{I / 32, I, fp8_scale(w), a, a_scales}, false, st);
+  return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2>{I / 32, I, fp8_scale(w), a, nullptr}, false, st);
 }
 
-hipError_t launch_qkv(const uint16_t *x, int M, int H, int D, LinearW w, QkvOut o, hipStream_t st) {
+hipError_t launch_qkv(ActIn x, int M, int H, int D, LinearW w, QkvOut o, hipStream_t st) {
   if (w.wfmt != SPEC_WFMT_FP8_E4M3_ROW) return hipErrorInvalidValue;
   const float *s = reinterpret_cast<const float *>(w.s);
   if (D == 64) return run<2, kFp8>(x, M, H, w, EpiQkv<2>{o.Hq + 2 * o.Hkv, s, o}, false, st);
@@ -641,6 +732,6 @@ hipError_t launch_qkv(const uint16_t *x, int M, int H, int D, LinearW w, QkvOut 
 
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,
                             float *logits_dump, hipStream_t st) {
-  return run<2, kBf16, EpiArgmax<2>, GEMM_LM_MAXMT>(x, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16},
+  return run<2, kBf16, EpiArgmax<2>, GEMM_LM_MAXMT>(ActIn{x, nullptr}, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16},
                                                    EpiArgmax<2>{V / 64, V, part, logits_dump}, false, st);
 }

@@ -4,7 +4,13 @@
 #include <stdint.h>
 
 // ---- weight-streaming linear: y = x W^T, W rows in wfmt ----
-// x is FP16 [M][K] for FP8 / MXFP4 weights and BF16 [M][K] for BF16 weights.
+// x is FP16 [M][K] for FP8 / MXFP4 weights and BF16 [M][K] for BF16 weights,
+// or MXFP8 (FP8 / MXFP4 weights only): e4m3 codes [M][K] in x and the e8m0
+// exponent of each 32 consecutive k in xs [M][K/32].
+struct ActIn {
+  const void *x;
+  const uint8_t *xs;  // NULL: FP16 / BF16 activations
+};
 struct LinearW {
   const void *w;   // codes / bf16 rows
   const void *s;   // fp32 per-row scales (FP8), e8m0 [rows][K/32] (MXFP4), NULL (BF16)
@@ -21,7 +27,7 @@ GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split);
 int residual_nsplit(int M, int N, int K);
 
 // y fp32 [M][N] (test hook)
-hipError_t launch_linear_f32(const uint16_t *x, int M, int N, int K, LinearW w, float *y, hipStream_t st);
+hipError_t launch_linear_f32(ActIn x, int M, int N, int K, LinearW w, float *y, hipStream_t st);
 
 // QKV projection + RoPE; q -> q_out bf16 [M][Hq*D]; k, v -> caches at slot kv_len[b] + j.
 // Where cache position `pos` of (sequence b, KV head h) lives, as a row index
@@ -52,15 +58,16 @@ struct QkvOut {
   int Hq, Hkv, max_ctx;
   KvLayout kvl;
 };
-// q (FP16) and k, v (BF16 cache) from FP16 x
-hipError_t launch_qkv(const uint16_t *x, int M, int H, int D, LinearW w, QkvOut o, hipStream_t st);
+// q (FP16) and k, v (BF16 cache) from x
+hipError_t launch_qkv(ActIn x, int M, int H, int D, LinearW w, QkvOut o, hipStream_t st);
 
-// a[m][n] = fp16(SiLU(x Wg^T) * (x Wu^T)), W = [gate; up] with I rows each
-hipError_t launch_swiglu(const uint16_t *x, int M, int H, int I, LinearW w, uint16_t *a, hipStream_t st);
+// a[m][n] = SiLU(x Wg^T) * (x Wu^T), W = [gate; up] with I rows each: FP16
+// (a_scales NULL) or MXFP8 codes in a and e8m0 [M][I/32] in a_scales
+hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8_t *a_scales, hipStream_t st);
 
 // part[z][m][n] = split z of (x W^T)[m][n] (fp32); residual_nsplit() splits.
 // The following launch_norm adds them to h.
-hipError_t launch_residual_partial(const uint16_t *x, int M, int N, int K, LinearW w, float *part, hipStream_t st);
+hipError_t launch_residual_partial(ActIn x, int M, int N, int K, LinearW w, float *part, hipStream_t st);
 
 // lm_head (BF16 x, BF16 table) + per-wave argmax partials: part[m][p] over vocab slices of 64
 struct ArgmaxPart { float v; int32_t i; };
@@ -92,6 +99,13 @@ hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16
 // x = RMSNorm(h) * gain, written as FP16 (out_bf16 = 0) or BF16 (out_bf16 = 1)
 hipError_t launch_norm(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
                        uint16_t *x, int out_bf16, float *dump, hipStream_t st);
+// the same, x written as MXFP8: e4m3 codes [M][H] in x8, e8m0 [M][H/32] in xs
+// (dump, when non-NULL, gets the decoded values code * 2^(e - 127))
+hipError_t launch_norm_mx8(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
+                           uint8_t *x8, uint8_t *xs, float *dump, hipStream_t st);
+// MXFP8 encoding of fp32 rows x [M][K] (K a multiple of 32), the one the
+// normalisation and SwiGLU steps apply
+hipError_t launch_quant_mx8(const float *x, int M, int K, uint8_t *codes, uint8_t *scales, hipStream_t st);
 hipError_t launch_accept(const ArgmaxPart *part, int nparts, int M, const int32_t *tokens, int batch,
                          int32_t *accept_len, int32_t *bonus, int32_t *argmax, int32_t *last_tau,
                          hipStream_t st);

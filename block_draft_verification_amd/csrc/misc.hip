@@ -34,10 +34,14 @@ __global__ void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
 // rounded to FP16 (decoder layers) or BF16 (lm_head input).  One 64-lane
 // workgroup per row; a lane owns the 4-column chunks c = 4*lane + 256*i, and all
 // of a chunk's partial loads are issued before they are added (in order).
-template <bool BF16>
+// OUT: 0 FP16, 1 BF16, 2 MXFP8 (x = e4m3 codes, xs = e8m0 of each 32 columns;
+// the 8 lanes holding one 32-column block share its exponent by shuffles).
+enum { kOutF16 = 0, kOutBF16 = 1, kOutMX8 = 2 };
+template <int OUT>
 __global__ __launch_bounds__(64) void norm_kernel(float *__restrict__ h, const float *__restrict__ part, int ns,
                                                   const float *__restrict__ gain, int M, int H, float eps,
-                                                  uint16_t *__restrict__ x, float *__restrict__ dump) {
+                                                  void *__restrict__ x, uint8_t *__restrict__ xs,
+                                                  float *__restrict__ dump) {
   constexpr int MAXC = 16;  // H <= 4096
   const int m = blockIdx.x, lane = threadIdx.x;
   float *hr = h + (size_t)m * H;
@@ -73,18 +77,33 @@ __global__ __launch_bounds__(64) void norm_kernel(float *__restrict__ h, const f
     const int c = lane * 4 + 256 * i;
     if (c >= H) break;
     const f32x4_t gv = *reinterpret_cast<const f32x4_t *>(gain + c);
+    if constexpr (OUT == kOutMX8) {
+      const f32x4_t y = f32x4_t{t[i][0] * rs * gv[0], t[i][1] * rs * gv[1], t[i][2] * rs * gv[2], t[i][3] * rs * gv[3]};
+      uint32_t e8;
+      const uint32_t codes = mx8_quant4(y, e8);
+      *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(x) + (size_t)m * H + c) = codes;
+      if ((lane & 7) == 0) xs[(size_t)m * (H / 32) + c / 32] = (uint8_t)e8;
+      if (dump) {
+        const float sc = __builtin_ldexpf(1.f, (int)e8 - 127);
+        const u32x2_t hv = fp8x4_to_f16x4(codes);
+        *reinterpret_cast<f32x4_t *>(dump + (size_t)m * H + c) =
+            f32x4_t{f16_to_f32(hv.x & 0xffff), f16_to_f32(hv.x >> 16), f16_to_f32(hv.y & 0xffff),
+                    f16_to_f32(hv.y >> 16)} * sc;
+      }
+      continue;
+    }
     uint32_t lo, hi;
-    if constexpr (BF16) {
+    if constexpr (OUT == kOutBF16) {
       lo = pack_bf16x2(t[i][0] * rs * gv[0], t[i][1] * rs * gv[1]);
       hi = pack_bf16x2(t[i][2] * rs * gv[2], t[i][3] * rs * gv[3]);
     } else {
       lo = pack_f16x2(t[i][0] * rs * gv[0], t[i][1] * rs * gv[1]);
       hi = pack_f16x2(t[i][2] * rs * gv[2], t[i][3] * rs * gv[3]);
     }
-    *reinterpret_cast<u32x2_t *>(x + (size_t)m * H + c) = u32x2_t{lo, hi};
+    *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(x) + (size_t)m * H + c) = u32x2_t{lo, hi};
     if (dump) {
       f32x4_t o;
-      if constexpr (BF16)
+      if constexpr (OUT == kOutBF16)
         o = f32x4_t{bf16_to_f32(lo & 0xffff), bf16_to_f32(lo >> 16), bf16_to_f32(hi & 0xffff), bf16_to_f32(hi >> 16)};
       else
         o = f32x4_t{f16_to_f32(lo & 0xffff), f16_to_f32(lo >> 16), f16_to_f32(hi & 0xffff), f16_to_f32(hi >> 16)};
@@ -223,9 +242,41 @@ hipError_t launch_norm(float *h, const float *part, int nsplit, const float *gai
                        uint16_t *x, int out_bf16, float *dump, hipStream_t st) {
   if (H > 4096 || H % 4) return hipErrorInvalidValue;
   if (out_bf16)
-    hipLaunchKernelGGL(norm_kernel<true>, dim3(M), dim3(64), 0, st, h, part, nsplit, gain, M, H, eps, x, dump);
+    hipLaunchKernelGGL(norm_kernel<kOutBF16>, dim3(M), dim3(64), 0, st, h, part, nsplit, gain, M, H, eps,
+                       (void *)x, (uint8_t *)nullptr, dump);
   else
-    hipLaunchKernelGGL(norm_kernel<false>, dim3(M), dim3(64), 0, st, h, part, nsplit, gain, M, H, eps, x, dump);
+    hipLaunchKernelGGL(norm_kernel<kOutF16>, dim3(M), dim3(64), 0, st, h, part, nsplit, gain, M, H, eps,
+                       (void *)x, (uint8_t *)nullptr, dump);
+  return hipGetLastError();
+}
+
+hipError_t launch_norm_mx8(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
+                           uint8_t *x8, uint8_t *xs, float *dump, hipStream_t st) {
+  if (H > 4096 || H % 32) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(norm_kernel<kOutMX8>, dim3(M), dim3(64), 0, st, h, part, nsplit, gain, M, H, eps, (void *)x8,
+                     xs, dump);
+  return hipGetLastError();
+}
+
+// MXFP8 encoding of fp32 rows: thread i of the grid takes 4 consecutive
+// values, 8 threads one 32-value block (n = M*K/4 threads, K % 32 == 0).
+__global__ __launch_bounds__(256) void quant_mx8_kernel(const float *__restrict__ x, size_t n, uint8_t *codes,
+                                                        uint8_t *scales) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const f32x4_t v = i < n ? *reinterpret_cast<const f32x4_t *>(x + 4 * i) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint32_t e8;
+  const uint32_t q = mx8_quant4(v, e8);  // all lanes take part in the block shuffles
+  if (i < n) {
+    *reinterpret_cast<uint32_t *>(codes + 4 * i) = q;
+    if ((i & 7) == 0) scales[i / 8] = (uint8_t)e8;
+  }
+}
+
+hipError_t launch_quant_mx8(const float *x, int M, int K, uint8_t *codes, uint8_t *scales, hipStream_t st) {
+  if (K % 32) return hipErrorInvalidValue;
+  const size_t n = (size_t)M * K / 4;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(quant_mx8_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st, x, n, codes, scales);
   return hipGetLastError();
 }
 

@@ -33,7 +33,9 @@
  * attention output, SwiGLU output); the KV cache is BF16 (converted exactly
  * to FP16 inside attention); the lm_head multiplies its BF16 table with the
  * final normed hidden state rounded to BF16; fp32 accumulation, residual
- * stream, softmax statistics and logits.
+ * stream, softmax statistics and logits.  With act_fmt = SPEC_ACT_MXFP8 the
+ * inputs of the QKV, gate/up and down projections are MXFP8 instead (see
+ * spec_act_fmt) and those products run on the scaled FP8 matrix cores.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host).
@@ -81,6 +83,22 @@ typedef enum {
   SPEC_WFMT_BF16 = 3          /* uint16 bf16 bit patterns [rows][cols]       */
 } spec_wfmt;
 
+/* Activation format of the QKV, gate/up and down projections' inputs (the
+ * two RMSNorm outputs of a layer and the SwiGLU output).  "The Inference
+ * Stack Behind OCRia" (kernel section) fuses the FP8 quantisation of these
+ * activations into the kernels that produce them; the same is done here.
+ * MXFP8 follows the OCP microscaling format: each 32 consecutive values along
+ * the reduction axis share X = floor(log2(max |v|)) - 8 (clamped to
+ * [-127, 127], -127 for an all-zero block), stored as the e8m0 byte X + 127,
+ * and each value is the e4m3 code nearest to v * 2^-X (ties to even,
+ * saturating at 448), all taken on the fp32 value.  The attention output that
+ * feeds the O projection stays FP16. */
+typedef enum {
+  SPEC_ACT_FP16 = 0,  /* FP16 activations (the default) */
+  SPEC_ACT_MXFP8 = 1  /* MXFP8 activations, FP8 / MXFP4 weights taken raw by
+                         the scaled matrix-core instruction */
+} spec_act_fmt;
+
 /* Device error bits (sticky until read by spec_get_device_error). */
 #define SPEC_DERR_TOKEN 1    /* a token id outside [0, vocab): row uses id 0  */
 #define SPEC_DERR_CAPACITY 2 /* kv_len + 16 > max_ctx: the sequence's block
@@ -99,6 +117,7 @@ typedef struct {
   int32_t attn_wfmt; /* format of w_qkv and w_o: SPEC_WFMT_FP8_E4M3_ROW       */
   int32_t mlp_wfmt;  /* format of w_gate_up and w_down: FP8_E4M3_ROW | MXFP4 */
   int32_t tied_lm_head; /* 1: logits use the embedding table */
+  int32_t act_fmt;   /* spec_act_fmt */
 } spec_model_desc;
 
 /* One decoder layer (all device pointers, caller-owned).
@@ -228,6 +247,37 @@ int spec_debug_set_dump(spec_ctx *ctx, float *hidden, float *logits);
  * Synchronous. */
 int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const void *w,
                       const void *scales, int32_t wfmt, float *y, hipStream_t stream);
+
+/* Test hook: the MXFP8 encoding (spec_act_fmt) of fp32 rows x [M][K], K a
+ * multiple of 32: e4m3 codes [M][K] and e8m0 bytes [M][K/32].  x and codes
+ * 16-byte aligned.  Synchronous. */
+int spec_debug_quant_mx8(int32_t M, int32_t K, const float *x, uint8_t *codes, uint8_t *scales,
+                         hipStream_t stream);
+
+/* Test hook: the pass's RMSNorm step on its own: x = h / sqrt(mean(h^2) +
+ * eps) * gain over rows of h fp32 [M][H] (H <= 4096, a multiple of 32), gain
+ * fp32 [H]; x written as FP16 bits [M][H] (act_fmt SPEC_ACT_FP16, xs unused)
+ * or as MXFP8 codes [M][H] + e8m0 [M][H/32] (SPEC_ACT_MXFP8).  h, gain and x
+ * 16-byte aligned.  Synchronous. */
+int spec_debug_rmsnorm(int32_t M, int32_t H, const float *h, const float *gain, float eps, int32_t act_fmt,
+                       void *x, uint8_t *xs, hipStream_t stream);
+
+/* Test hook: the gate/up projection with its SiLU-and-multiply epilogue on
+ * its own: a = SiLU(x Wg^T) * (x Wu^T), w = [gate rows; up rows] [2I][H] in
+ * FP8_E4M3_ROW or MXFP4 with scales as in spec_layer_weights.  Input x: FP16
+ * bits [M][H] (x_scales NULL) or MXFP8 codes [M][H] + e8m0 [M][H/32].  Output
+ * a: FP16 bits [M][I] (out_fmt SPEC_ACT_FP16, a_scales unused) or MXFP8 codes
+ * [M][I] + e8m0 [M][I/32] (SPEC_ACT_MXFP8).  H, I multiples of 64.
+ * Synchronous. */
+int spec_debug_swiglu(int32_t M, int32_t H, int32_t I, const void *x, const uint8_t *x_scales, const void *w,
+                      const void *scales, int32_t wfmt, int32_t out_fmt, void *a, uint8_t *a_scales,
+                      hipStream_t stream);
+
+/* Test hook: spec_debug_linear with MXFP8 activations (codes [M][K], e8m0
+ * [M][K/32]) and FP8_E4M3_ROW or MXFP4 weights (BF16 weights are rejected
+ * with SPEC_E_UNSUPPORTED).  Synchronous. */
+int spec_debug_linear_mx8(int32_t M, int32_t N, int32_t K, const uint8_t *x_codes, const uint8_t *x_scales,
+                          const void *w, const void *scales, int32_t wfmt, float *y, hipStream_t stream);
 
 /* Test hook: block-causal GQA attention on its own for sequences 0..batch-1:
  * q FP16 [batch*16][Hq*D] (already rotated), BF16 K/V caches of ONE layer

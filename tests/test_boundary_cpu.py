@@ -72,6 +72,9 @@ def test_host_side_argument_checks():
     m.mlp_wfmt = 3                                                            # BF16 MLP not supported
     assert lib.spec_verify_init(ctypes.byref(m), ctypes.byref(w), ctypes.byref(kv), None, ctypes.byref(h)) == -3
     m.mlp_wfmt = 1
+    m.act_fmt = 2                                                             # no such activation format
+    assert lib.spec_verify_init(ctypes.byref(m), ctypes.byref(w), ctypes.byref(kv), None, ctypes.byref(h)) == -3
+    m.act_fmt = 1
     m.n_q_heads = 3                                                           # Hq % Hkv != 0
     assert lib.spec_verify_init(ctypes.byref(m), ctypes.byref(w), ctypes.byref(kv), None, ctypes.byref(h)) == -2
     m.n_q_heads = 4
@@ -80,6 +83,16 @@ def test_host_side_argument_checks():
     assert h.value is None
     # debug entry points validate before launching
     assert lib.spec_debug_linear(16, 100, 64, 16, 16, 16, 1, 16, None) == -1  # N % 64
+    assert lib.spec_debug_quant_mx8(4, 48, 16, 16, 16, None) == -1              # K % 32
+    assert lib.spec_debug_quant_mx8(4, 64, 16, 24, 16, None) == -1              # codes not 16-byte aligned
+    assert lib.spec_debug_linear_mx8(16, 64, 96, 16, 16, 16, 16, 1, 16, None) == -1   # K % 64
+    assert lib.spec_debug_linear_mx8(16, 64, 64, 16, 16, 16, None, 2, 16, None) == -1  # MXFP4 without scales
+    assert lib.spec_debug_linear_mx8(16, 64, 64, 16, 16, 16, 16, 3, 16, None) == -3    # BF16 weights
+    assert lib.spec_debug_rmsnorm(4, 4096 + 32, 16, 16, 1e-6, 0, 16, None, None) == -1  # H > 4096
+    assert lib.spec_debug_rmsnorm(4, 64, 16, 16, 1e-6, 1, 16, None, None) == -1         # MXFP8 without scales
+    assert lib.spec_debug_rmsnorm(4, 64, 16, 16, 1e-6, 5, 16, 16, None) == -3           # unknown format
+    assert lib.spec_debug_swiglu(4, 64, 96, 16, None, 16, 16, 1, 0, 16, None, None) == -1  # I % 64
+    assert lib.spec_debug_swiglu(4, 64, 64, 16, None, 16, 16, 1, 1, 16, None, None) == -1  # MXFP8 out, no scales
     assert lib.spec_debug_attention(1, 4, 2, 80, 1, 128, 16, 16, 16, 16, 16, 0, None) == -2
 
 

@@ -8,7 +8,8 @@ import torch
 import oracle
 from oracle.codecs import decode_bf16, decode_e4m3, dequant_fp8_rows, dequant_mxfp4
 import workload as W
-from block_draft_verification_amd import WFMT_BF16, WFMT_FP8_E4M3_ROW, WFMT_MXFP4, debug_attention, debug_linear
+from block_draft_verification_amd import (WFMT_BF16, WFMT_FP8_E4M3_ROW, WFMT_MXFP4, debug_attention, debug_linear,
+                                          debug_rmsnorm, debug_swiglu)
 
 pytestmark = pytest.mark.gpu
 
@@ -78,6 +79,49 @@ def test_linear_bf16(M, N, K):
     xb = _x(M, K, 3, f16=False)
     y = debug_linear(_dev(xb), _dev(w), None, WFMT_BF16, N).cpu().numpy()
     _check_linear(xb, decode_bf16(w), y, f16=False)
+
+
+@pytest.mark.parametrize("M,H", [(37, 896), (16, 4096), (1, 64)])
+def test_rmsnorm_fp16(M, H):
+    """x = h / sqrt(mean(h^2) + eps) * g rounded once to FP16: within one
+    FP16 rounding (2^-11 relative, plus the subnormal step) of the float64
+    value, the fp32 normalisation adding well under 2^-16."""
+    rng = np.random.default_rng(M + H)
+    h = (rng.standard_normal((M, H)) * np.exp2(rng.integers(-6, 7, size=(M, 1)))).astype(np.float32)
+    g = (1 + 0.5 * rng.standard_normal(H)).astype(np.float32)
+    x = debug_rmsnorm(torch.from_numpy(h).cuda(), torch.from_numpy(g).cuda(), 1e-6).cpu().numpy()
+    ref = oracle.rms_norm(h, g, 1e-6)
+    err = np.abs(_dec(x.view(np.uint16)) - ref)
+    assert np.all(err <= (2.0 ** -11 + 2.0 ** -16) * np.abs(ref) + 2.0 ** -25)
+
+
+@pytest.mark.parametrize("wfmt,M,H,I", [(WFMT_FP8_E4M3_ROW, 16, 896, 4864), (WFMT_MXFP4, 40, 896, 4864),
+                                        (WFMT_FP8_E4M3_ROW, 512, 896, 4864)])
+def test_swiglu_fp16(wfmt, M, H, I):
+    """a = SiLU(x Wg^T) * (x Wu^T) rounded to FP16: the gate and up sums carry
+    the fp32 accumulation bound (3e-5 of sum |x||w|, as for the plain
+    linear), carried through SiLU(g) * u (|SiLU'| <= 1.1), then one FP16
+    rounding."""
+    rng = np.random.default_rng(I + M)
+    if wfmt == WFMT_FP8_E4M3_ROW:
+        w = rng.integers(0, 256, size=(2 * I, H)).astype(np.uint8)
+        w[(w & 0x7F) == 0x7F] = 0x3F
+        ws = (rng.random(2 * I) * 2e-3 + 1e-3).astype(np.float32)
+        wd = dequant_fp8_rows(w, ws)
+    else:
+        w = rng.integers(0, 256, size=(2 * I, H // 2)).astype(np.uint8)
+        ws = rng.integers(118, 124, size=(2 * I, H // 32)).astype(np.uint8)
+        wd = dequant_mxfp4(w, ws)
+    xb = _x(M, H, 9)
+    x = _dec(xb)
+    gate, up = x @ wd[:I].T, x @ wd[I:].T
+    ref = oracle.silu(gate) * up
+    bg, bu = 3e-5 * (np.abs(x) @ np.abs(wd[:I]).T), 3e-5 * (np.abs(x) @ np.abs(wd[I:]).T)
+    a = debug_swiglu(_dev(xb), None, _dev(w), _dev(ws), wfmt, I).cpu().numpy()
+    err = np.abs(_dec(a.view(np.uint16)) - ref)
+    bound = 1.1 * np.abs(up) * bg + np.abs(oracle.silu(gate)) * bu + bg * bu
+    assert np.all(err <= 2.0 ** -11 * (np.abs(ref) + bound) + bound + 2.0 ** -24), \
+        f"max excess {np.max(err - 2.0 ** -11 * np.abs(ref) - bound):.3g}"
 
 
 NAN_BF16 = 0x7FC0

@@ -1,0 +1,352 @@
+"""FP8-activation mode on the GPU (MXFP8 activations into the QKV, gate/up and
+down projections, on the scaled FP8 matrix cores) against the oracle.
+
+- The MXFP8 encoder, bit for bit against oracle.codecs.mxfp8_quantize on the
+  same fp32 input (block exponents, ties, saturation, the e4m3 subnormal
+  range, all-zero blocks, the clamped exponent floor).
+- The MXFP8 linear layer against the float64 product of the oracle's own
+  encoding, with FP8-row and MXFP4 weights: the products of e4m3 (and e2m1)
+  values are exact and accumulate in fp32, so the bound is the fp32
+  accumulation bound.
+- The MXFP8 linear layer's error is held to 2^-13 of sum |x||w|: the scaled
+  FP8 instruction adds each group of 8 products in a narrow truncating adder
+  (a product below about 2^-14 of the largest in its group of 8 is dropped),
+  while block and instruction partial sums add at fp32.
+- The two producers of MXFP8 activations, RMSNorm and the gate/up
+  SiLU-and-multiply epilogue, decision by decision: each block exponent and
+  code must be one the oracle's encoder gives to some value within the GPU's
+  own error bound of the float64 value (2^-16 relative for the fp32
+  normalisation; the instruction's 2^-13 accumulation bound carried through
+  SiLU(g) * u for the epilogue).
+- The pass against OracleModel(act_mx8=True), the same reading of the pages
+  in float64.  The two sides take the encoder's decisions on their own fp32
+  values, which differ (by the FP16 attention's ~1e-3 relative error, and by
+  the instruction's accumulation error); a flipped decision moves an element
+  by one e4m3 step, 1/8 of its value, while the mode itself rounds every
+  element by up to 1/16.  Already over one decoder layer the attention error
+  flips about 1% of the MLP input's decisions, so the GPU lands about a third
+  of the mode's own distance (oracle MXFP8 vs oracle exact) away from the
+  MXFP8 oracle; the bar there is 0.75 of that distance per row at most and
+  0.5 at the median, for the hidden state and the logits, with argmax equal
+  wherever the top-2 margin exceeds MARGIN_MX.  Through a whole synthetic
+  stack every rounding is amplified (the FP16 mode's 2^-11 activation
+  rounding ends as ~0.3% of the final hidden state; the encoder's ~3.6% per
+  element ends as ~30%), so the two MXFP8 computations decorrelate: the bar is
+  then the mode's own size (no farther from the MXFP8 oracle, nor from the
+  exact one, than 1.5 times the distance between the two oracles), and the
+  acceptance drift against the exact oracle is reported.
+- Greedy speculative decoding stays lossless in the mode: the block
+  quantisation is row-local, so the speculative stream equals the GPU's own
+  autoregressive stream bit for bit.
+"""
+import dataclasses
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workload as W
+from oracle.codecs import decode_e4m3, dequant_fp8_rows, dequant_mxfp4, mxfp8_quantize, round_e4m3
+from block_draft_verification_amd import (WFMT_FP8_E4M3_ROW, WFMT_MXFP4, DeviceModel, Verifier,
+                                          debug_linear_mx8, debug_quant_mx8, debug_rmsnorm, debug_swiglu)
+from block_draft_verification_amd.decode import ar_decode, planted_drafts, spec_decode
+from gpu_cases import MARGIN, REL_TOL, build_case, gpu_verify, log, oracle_verify, row_rel
+
+pytestmark = pytest.mark.gpu
+
+MARGIN_MX = 5e-2
+MX_ACC_TOL = 2.0 ** -13
+
+_POS = decode_e4m3(np.arange(127))  # 0 and the finite positive e4m3 values, increasing
+
+
+def _encode_e4m3(v):
+    """Codes of values that are already on the e4m3 grid (test-side packing of
+    the oracle's encoded values, so the GPU linear reads the oracle's own
+    encoding)."""
+    a = np.abs(v)
+    idx = np.searchsorted(_POS, a)
+    assert np.array_equal(_POS[np.minimum(idx, 126)], a), "value off the e4m3 grid"
+    return (idx | np.where(v < 0, 0x80, 0)).astype(np.uint8)
+
+
+def _mx_inputs(M, K, seed):
+    """fp32 rows whose 32-blocks span magnitudes 2^-40 .. 2^40, with planted
+    special blocks in row 0 (normal fp32 values only)."""
+    rng = np.random.default_rng(seed)
+    mag = np.exp2(rng.integers(-40, 41, size=(M, K // 32, 1)).astype(np.float64))
+    x = (rng.standard_normal((M, K // 32, 32)) * mag).reshape(M, K)
+    specials = [
+        np.zeros(32),                                                  # all-zero block: X = -127, codes 0
+        np.r_[256.0, 1.0625, -1.0625, 1.1875, 3.25, -3.75, np.zeros(26)],  # X = 0, ties to even
+        np.r_[511.0, 464.0, -500.0, 448.0, np.zeros(28)],              # X = 0: |v| above 448 saturates
+        np.r_[256.0, 1.5 * 2.0 ** -9, 2.0 ** -10, 2.0 ** -11, 3 * 2.0 ** -10, np.zeros(27)],  # e4m3 subnormals
+        np.r_[2.0 ** -122, -(2.0 ** -123), 2.0 ** -125, np.zeros(29)],  # X below -127: clamped
+        np.full(32, -7.0),                                             # one value repeated
+    ]
+    for i, s in enumerate(specials):
+        if 32 * (i + 1) <= K:
+            x[0, 32 * i:32 * (i + 1)] = s
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("M,K", [(1, 256), (37, 896), (512, 4864)])
+def test_quant_mx8_bit_exact(M, K):
+    x = _mx_inputs(M, K, seed=M + K)
+    codes, scales = debug_quant_mx8(torch.from_numpy(x).cuda())
+    codes, scales = codes.cpu().numpy(), scales.cpu().numpy()
+    el, X = mxfp8_quantize(x)
+    assert not np.any((codes & 0x7F) == 0x7F), "NaN code produced"
+    assert np.array_equal(scales.astype(np.int64) - 127, X), "block exponents differ"
+    got = decode_e4m3(codes)
+    bad = got != el
+    assert not bad.any(), f"{bad.sum()} codes differ, first at {np.argwhere(bad)[0]}: {got[bad][:4]} vs {el[bad][:4]}"
+
+
+def _mx_activations(M, K, seed):
+    """The oracle's MXFP8 encoding of seeded fp32 activations: (codes, e8m0,
+    decoded float64 values)."""
+    x = (np.random.default_rng(seed).standard_normal((M, K)) * 3.0).astype(np.float32)
+    el, X = mxfp8_quantize(x)
+    xq = (el.reshape(M, K // 32, 32) * np.ldexp(1.0, X)[..., None]).reshape(M, K)
+    return _encode_e4m3(el), (X + 127).astype(np.uint8), xq
+
+
+def _check(xq, wdeq, y):
+    ref = xq @ wdeq.T
+    bound = np.abs(xq) @ np.abs(wdeq).T
+    r = np.abs(y.astype(np.float64) - ref) / (bound + 1e-300)
+    log(f"linear mx8: max err/bound {r.max():.3g}")
+    assert np.all(r <= MX_ACC_TOL), f"max err/bound {r.max():.3g}"
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 1152, 896), (1, 64, 64), (40, 896, 4864), (512, 9728, 896)])
+def test_linear_mx8_fp8_weights(M, N, K):
+    rng = np.random.default_rng(M * 7 + N + K)
+    w = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+    w[(w & 0x7F) == 0x7F] = 0x3F
+    s = (rng.random(N) * 1e-3 + 1e-4).astype(np.float32)
+    c, e, xq = _mx_activations(M, K, seed=M + K)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    y = debug_linear_mx8(t(c), t(e), t(w), t(s), WFMT_FP8_E4M3_ROW, N).cpu().numpy()
+    _check(xq, dequant_fp8_rows(w, s), y)
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 9728, 896), (33, 128, 64), (256, 896, 4864)])
+def test_linear_mx8_mxfp4_weights(M, N, K):
+    rng = np.random.default_rng(N + K + 1)
+    w = rng.integers(0, 256, size=(N, K // 2)).astype(np.uint8)
+    we = rng.integers(110, 135, size=(N, K // 32)).astype(np.uint8)
+    c, e, xq = _mx_activations(M, K, seed=M + 2 * K)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    y = debug_linear_mx8(t(c), t(e), t(w), t(we), WFMT_MXFP4, N).cpu().numpy()
+    _check(xq, dequant_mxfp4(w, we), y)
+
+
+def _decisions_explained(x_ref, codes, scales, window):
+    """The GPU's MXFP8 encoding of values whose float64 reference is x_ref
+    [M, K], given a per-element bound `window` on the GPU's own error before
+    encoding: every block exponent equals the oracle's unless the block
+    maximum lies within the window of a power of two, and in every block
+    whose exponent X agrees each code lies between the oracle's encodings of
+    x_ref - window and x_ref + window at that X (the encoding is monotonic).
+    Returns (codes differing, exponents differing)."""
+    M, K = x_ref.shape
+    el, X = mxfp8_quantize(x_ref)
+    Xg = scales.astype(np.int64) - 127
+    blk = np.abs(x_ref).reshape(M, K // 32, 32)
+    amax, wmax = blk.max(axis=-1), window.reshape(M, K // 32, 32).max(axis=-1)
+    near_pow2 = np.abs(amax - np.exp2(np.round(np.log2(np.maximum(amax, 1e-300))))) <= wmax
+    bad_x = (Xg != X) & ~near_pow2
+    assert not bad_x.any(), f"{bad_x.sum()} block exponents differ away from a power of two"
+    same = np.repeat(Xg == X, 32, axis=1)
+    got = decode_e4m3(codes)
+    diff = (got != el) & same
+    if diff.any():
+        inv = np.ldexp(1.0, -np.repeat(X, 32, axis=1))[diff]
+        lo = round_e4m3((x_ref[diff] - window[diff]) * inv)
+        hi = round_e4m3((x_ref[diff] + window[diff]) * inv)
+        out = (got[diff] < lo) | (got[diff] > hi)
+        if out.any():
+            at = np.argwhere(diff)[out][:6]
+            det = [(tuple(int(i) for i in p), float(x_ref[tuple(p)]), float(window[tuple(p)]), float(got[tuple(p)]),
+                    float(el[tuple(p)]), int(X[p[0], p[1] // 32])) for p in at]
+            raise AssertionError(f"{out.sum()} of {diff.sum()} differing codes lie outside the encodings of the "
+                                 f"error window: (pos, x_ref, window, gpu, oracle, X) {det}")
+    return int(diff.sum()), int((Xg != X).sum())
+
+
+@pytest.mark.parametrize("M,H", [(37, 896), (16, 4096), (3, 64)])
+def test_rmsnorm_mx8_decisions(M, H):
+    """RMSNorm with its MXFP8 output: the GPU's fp32 normalisation is within
+    2^-16 of |x| (a 64-lane sum of squares), so every decision that is not
+    that close to its boundary must equal the oracle's."""
+    rng = np.random.default_rng(M * H)
+    h = (rng.standard_normal((M, H)) * np.exp2(rng.integers(-6, 7, size=(M, 1)))).astype(np.float32)
+    g = (1 + 0.5 * rng.standard_normal(H)).astype(np.float32)
+    eps = 1e-6
+    x_ref = oracle.rms_norm(h, g, eps)
+    codes, scales = debug_rmsnorm(torch.from_numpy(h).cuda(), torch.from_numpy(g).cuda(), eps, "mxfp8")
+    n_code, n_exp = _decisions_explained(x_ref, codes.cpu().numpy(), scales.cpu().numpy(),
+                                         np.abs(x_ref) * 2.0 ** -16 + 1e-30)
+    log(f"rmsnorm mx8 {M}x{H}: {n_code} codes and {n_exp} exponents at a rounding boundary")
+
+
+@pytest.mark.parametrize("wfmt,M,H,I", [(WFMT_FP8_E4M3_ROW, 16, 896, 4864), (WFMT_MXFP4, 40, 896, 4864),
+                                        (WFMT_FP8_E4M3_ROW, 3, 64, 128)])
+def test_swiglu_mx8_decisions(wfmt, M, H, I):
+    """Gate/up on MXFP8 input with the SiLU-and-multiply epilogue writing
+    MXFP8: against the oracle's float64 a = SiLU(g) * u of the same encoded
+    input, with the GPU's error before encoding bounded by the instruction's
+    2^-13 accumulation bound carried through SiLU(g) * u (|SiLU'| <= 1.1)
+    plus fp32 rounding of the epilogue."""
+    rng = np.random.default_rng(H + I + M)
+    if wfmt == WFMT_FP8_E4M3_ROW:
+        w = rng.integers(0, 256, size=(2 * I, H)).astype(np.uint8)
+        w[(w & 0x7F) == 0x7F] = 0x3F
+        ws = (rng.random(2 * I) * 2e-3 + 1e-3).astype(np.float32)
+        wd = dequant_fp8_rows(w, ws)
+    else:
+        w = rng.integers(0, 256, size=(2 * I, H // 2)).astype(np.uint8)
+        ws = rng.integers(118, 124, size=(2 * I, H // 32)).astype(np.uint8)
+        wd = dequant_mxfp4(w, ws)
+    c, e, xq = _mx_activations(M, H, seed=H + M)
+    gate, up = xq @ wd[:I].T, xq @ wd[I:].T
+    a_ref = oracle.silu(gate) * up
+    bg, bu = MX_ACC_TOL * (np.abs(xq) @ np.abs(wd[:I]).T), MX_ACC_TOL * (np.abs(xq) @ np.abs(wd[I:]).T)
+    window = 1.1 * np.abs(up) * bg + np.abs(oracle.silu(gate)) * bu + bg * bu + 2.0 ** -20 * np.abs(a_ref) + 1e-30
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    codes, scales = debug_swiglu(t(c), t(e), t(w), t(ws), wfmt, I, out_fmt="mxfp8")
+    n_code, n_exp = _decisions_explained(a_ref, codes.cpu().numpy(), scales.cpu().numpy(), window)
+    log(f"swiglu mx8 {M}x{H}x{I}: {n_code} codes and {n_exp} exponents at a rounding boundary")
+
+
+def _mx_oracle(case):
+    om = oracle.OracleModel(case.wl.model, case.weights, cache=case.om.cache, act_mx8=True)
+    om._layers, om._embed, om._lm = case.om._layers, case.om._embed, case.om._lm  # share the decoded weights
+    return om
+
+
+def _mx_compare(name, case, seqs, ref_exact, ref, got, one_layer):
+    hid = got["hidden"][seqs].astype(np.float64)
+    hid = got["hidden"][seqs].astype(np.float64)
+    rel = row_rel(hid, ref.hidden)
+    rel_mode = row_rel(ref.hidden, ref_exact.hidden)  # what the mode itself moves
+    rel_exact = row_rel(hid, ref_exact.hidden)
+    lg = row_rel(got["logits"][seqs].astype(np.float64), ref.logits)
+    g = got["argmax"].reshape(-1, 16)[seqs]
+    sure = ref.margin > MARGIN_MX
+    tau = got["accept_len"][seqs]
+    dl = np.abs(got["logits"][seqs].astype(np.float64) - ref.logits).max(axis=-1)
+    stats = {"hidden_rel_vs_mx_oracle": float(rel.max()), "hidden_rel_mx_vs_exact_oracle": float(rel_mode.max()),
+             "median_rel_vs_mx_oracle": float(np.median(rel)), "median_rel_mx_vs_exact": float(np.median(rel_mode)),
+             "median_rel_vs_exact": float(np.median(rel_exact)), "max_abs_dlogit": float(dl.max()),
+             "median_abs_dlogit": float(np.median(dl)),
+             "margin_quantiles": np.quantile(ref.margin, [0.05, 0.25, 0.5]).round(4).tolist(),
+             "hidden_rel_vs_exact_oracle": float(rel_exact.max()), "logits_rel": float(lg.max()),
+             "rows_exempt": float(1 - sure.mean()), "argmax_diff_decided": int(((g != ref.g) & sure).sum()),
+             "argmax_diff_all": int((g != ref.g).sum()),
+             "tau_gpu_mx": tau.tolist(), "tau_oracle_mx": ref.tau.tolist(), "tau_oracle_exact": ref_exact.tau.tolist(),
+             "argmax_diff_vs_exact_at_margin_1e-2": int(((g != ref_exact.g) & (ref_exact.margin > MARGIN)).sum())}
+    log(f"{name} mxfp8: {stats}")
+    assert np.all(np.isfinite(hid))
+    if one_layer:
+        assert rel.max() <= 0.75 * rel_mode.max(), f"hidden rel {rel.max():.3g} vs the mode's {rel_mode.max():.3g}"
+        assert np.median(rel) <= 0.5 * np.median(rel_mode), "not closer to the MXFP8 oracle than the mode's own size"
+        assert lg.max() <= 0.75 * row_rel(ref.logits, ref_exact.logits).max(), f"logits rel {lg.max():.3g}"
+        assert stats["argmax_diff_decided"] == 0, f"argmax differs on {stats['argmax_diff_decided']} decided rows"
+        decided = np.array([np.all(ref.margin[i, :ref.tau[i]] > MARGIN_MX) for i in range(len(seqs))])
+        assert np.array_equal(tau[decided], ref.tau[decided]), "tau differs from the MXFP8 oracle"
+    else:
+        assert rel.max() <= 1.5 * rel_mode.max(), f"hidden rel {rel.max():.3g} vs the mode's {rel_mode.max():.3g}"
+        assert rel_exact.max() <= 1.5 * rel_mode.max(), "farther from the exact oracle than the mode moves it"
+    for i, b in enumerate(seqs):  # self-consistency of tau and bonus with the GPU's own argmax
+        t = next((j for j in range(1, 16) if case.blocks[b, j] != g[i, j - 1]), 16)
+        assert tau[i] == t and got["bonus"][b] == g[i, t - 1]
+    return stats
+
+
+def _mx_pass(name, seqs=None, **kw):
+    case = build_case(name, oracle_seqs=seqs, **kw)
+    seqs = list(range(len(case.lens))) if seqs is None else list(seqs)
+    ref_exact, okv = oracle_verify(case, seqs)
+    log("oracle verify pass, MXFP8 mode")
+    ref = oracle.verify_block(_mx_oracle(case), okv, case.blocks[seqs])
+    m = case.wl.model
+    dev = DeviceModel(m, case.weights, max_batch=len(case.lens), max_ctx=case.wl.max_ctx,
+                      kv_layers=case.kv_layers, kv_len=case.lens)
+    ver = Verifier(dev, act_fmt="mxfp8")
+    got = gpu_verify(ver, case)
+    stats = _mx_compare(name, case, seqs, ref_exact, ref, got, one_layer=False)
+    assert ver.device_error() == 0
+    ver.close()
+    return stats
+
+
+@pytest.mark.parametrize("mlp", ["fp8", "mxfp4"])
+def test_mx8_one_layer_05b(mlp):
+    """One decoder layer at the 0.5B width and vocabulary, 4 sequences over a
+    synthetic cache (ragged lengths, one empty), random drafts."""
+    m = dataclasses.replace(W.M05B, name=f"0.5b-L1-{mlp}", n_layers=1, mlp_format=mlp)
+    seed, cap = 11, 1088
+    wts = W.model_weights(m, seed)
+    lens = np.array([600, 100, 0, cap - 16], np.int32)
+    kvs = [W.synthetic_kv_layer(m, seed, 0, lens, cap)]
+    rng = W.child_rng(seed, 995)
+    blocks = rng.integers(0, m.vocab, size=(len(lens), 16)).astype(np.int32)
+    om = oracle.OracleModel(m, wts)
+    okv = oracle.OracleKV.from_bf16(m, [kvs[0][0]], [kvs[0][1]], lens)
+    log("oracle verify passes, exact and MXFP8")
+    ref_exact = oracle.verify_block(om, okv, blocks)
+    omx = oracle.OracleModel(m, wts, act_mx8=True)
+    omx._layers, omx._lm = om._layers, om._lm
+    ref = oracle.verify_block(omx, okv, blocks)
+    dev = DeviceModel(m, wts, max_batch=len(lens), max_ctx=cap, kv_layers=kvs, kv_len=lens)
+    ver = Verifier(dev, act_fmt="mxfp8")
+    case = types.SimpleNamespace(wl=types.SimpleNamespace(model=m), lens=lens, blocks=blocks)
+    got = gpu_verify(ver, case)
+    _mx_compare(m.name, case, list(range(len(lens))), ref_exact, ref, got, one_layer=True)
+    assert ver.device_error() == 0
+    ver.close()
+
+
+def test_mx8_pass_tiny():
+    _mx_pass("tiny-b1-ctx128")
+
+
+def test_mx8_pass_05b_mxfp4_mlp():
+    _mx_pass("0.5b-mxfp4mlp-b16-ctx3072", seqs=[0, 7], seqs_planted=[0, 7])
+
+
+def test_mx8_pass_05b_b32():
+    _mx_pass("0.5b-fp8-b32-ctx512to4096", seqs=[0, 19], seqs_planted=[0, 19])
+
+
+def test_mx8_decode_lossless_tiny():
+    m = W.TINY
+    wts = W.model_weights(m, seed=5, gains="random")
+    rng = W.child_rng(5, 990)
+    B, cap = 2, 448
+    lens = np.array([40, 29], np.int32)
+    P = np.zeros((B, 40), np.int32)
+    for b in range(B):
+        P[b, :lens[b]] = rng.integers(0, m.vocab, size=lens[b])
+    dev = DeviceModel(m, wts, max_batch=B, max_ctx=cap)
+    ver = Verifier(dev, act_fmt="mxfp8")
+    pending = ver.prefill(torch.from_numpy(P).cuda(), torch.from_numpy(lens).cuda())
+    kv0 = dev.kv_len.clone()
+    n_rounds = 12
+    ar = ar_decode(ver, pending, n_rounds * 16 + 16)
+    dev.kv_len.copy_(kv0)
+    L = np.minimum(W.child_rng(5, 991).geometric(0.1, size=(B, n_rounds)), 16)
+    draft = planted_drafts(torch.cat([pending[:, None], ar], dim=1), torch.from_numpy(L).cuda(), m.vocab)
+    toks, counts, taus = spec_decode(ver, pending, n_rounds, draft, capacity=n_rounds * 16 + 16)
+    torch.cuda.synchronize()
+    assert np.array_equal(taus.cpu().numpy(), L)
+    for b in range(B):
+        n = int(counts[b])
+        assert n == L[b].sum() and torch.equal(toks[b, :n], ar[b, :n]), f"seq {b}: speculative != AR"
+    assert ver.device_error() == 0
+    ver.close()
