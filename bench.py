@@ -25,10 +25,30 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK = 8.0e12          # bytes/s, MI355X HBM3E
-MFMA_BF16_PEAK = 2.5e15    # flop/s, dense BF16 MFMA
+MFMA_BF16_PEAK = 2.5e15    # flop/s, dense BF16 / FP16 MFMA
+MFMA_FP8_PEAK = 5.0e15     # flop/s, dense FP8 MFMA
 RIDGE = MFMA_BF16_PEAK / HBM_PEAK
 METRIC = "verify passes/s & accepted tok/s, 0.5B FP8 target, K=16 block; % of HBM peak"
 WORKLOAD = "0.5b-fp8-b32-ctx512to4096"
+REPEAT = 20  # back-to-back launches per event pair in the per-kernel timing
+
+# HBM bytes per launch of a kernel class from two rocprofv3 --pmc runs
+# (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0: the factors that make a plain 1 GiB
+# device copy read back as 1 GiB), valid for the kernel sources whose digest
+# is recorded; any other source reports null.
+TRAFFIC_PROFILE = "profiles/verify_pass_0.5b-fp8-b32-ctx512to4096_hbm_traffic.md"
+TRAFFIC = {
+    "gate_up": {"bytes": (16.92 + 4.75) * 2 ** 20, "sources": ("gemm.hip", "common.h", "kernels.h"),
+                "sha256_16": "38077d55438202ba,230adac9725098ab,d2af339db190ecbf"},
+    "attention": {"bytes": (40.09 + 11.28) * 2 ** 20, "sources": ("attention.hip", "common.h", "kernels.h"),
+                  "sha256_16": "7ae9f732a22cba54,230adac9725098ab,d2af339db190ecbf"},
+}
+
+
+def _sources_digest(files):
+    import hashlib
+    d = os.path.join(ROOT, "block_draft_verification_amd", "csrc")
+    return ",".join(hashlib.sha256(open(os.path.join(d, f), "rb").read()).hexdigest()[:16] for f in files)
 
 
 def log(msg):
@@ -84,11 +104,11 @@ def pass_bytes(m, lens):
     return w + kv_read + kv_write + B * 16 * m.hidden * 2
 
 
-def cpu_baseline(wl, weights, kv_layers, lens, n_seq):
+def cpu_baseline(wl, weights, kv_layers, lens, n_seq, min_seconds=10.0):
     """The oracle (float64 numpy) timed on this host for a bounded sample: the
     verify pass of the first n_seq sequences (random drafts; the oracle's
-    work does not depend on draft values).  Scaled to passes/s of the whole
-    batch by n_seq / B."""
+    work does not depend on draft values), repeated until min_seconds have
+    passed.  Scaled to passes/s of the whole batch by n_seq / B."""
     import oracle
     import workload as W
     from threadpoolctl import threadpool_info
@@ -99,13 +119,16 @@ def cpu_baseline(wl, weights, kv_layers, lens, n_seq):
     blocks = np.stack([W.draft_rng(wl, b, 1).integers(0, m.vocab, size=16) for b in range(n_seq)])
     oracle.verify_block(om, okv, blocks[:1, :1], seqs=[0])  # decode weights once (untimed)
     t0 = time.time()
-    oracle.verify_block(om, okv, blocks)
-    dt = time.time() - t0
+    reps = 0
+    while reps == 0 or time.time() - t0 < min_seconds:
+        oracle.verify_block(om, okv, blocks)
+        reps += 1
+    dt = (time.time() - t0) / reps
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     return {"value": (n_seq / len(lens)) / dt, "unit": "verify passes/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"float64 numpy oracle, verify pass of {n_seq} of {len(lens)} sequences "
-                      f"({dt:.1f} s), scaled by {n_seq}/{len(lens)}; weight decoding untimed"}
+            "sample": f"float64 numpy oracle, {reps} verify passes of {n_seq} of {len(lens)} sequences "
+                      f"({dt:.2f} s each), scaled by {n_seq}/{len(lens)}; weight decoding untimed"}
 
 
 def e2e_batch1(ver, dev, m, lens, seed, n_rounds=32):
@@ -184,13 +207,17 @@ def time_graph(ver, dev, tok, kv0, steps, warmup):
     return e0.elapsed_time(e1) / steps, acc.cpu().numpy()
 
 
-def kernel_times(ver, dev, tok, kv0, kinds, reps):
-    """Per kernel class: launch durations over `reps` eager passes (events on the stream)."""
+def kernel_times(ver, dev, tok, kv0, kinds, reps, repeat=REPEAT):
+    """Per kernel class: launch durations over `reps` eager passes, events on
+    the stream; every launch of the timed class is issued `repeat` times back
+    to back between its two events (the RMSNorm class, which updates h in
+    place, once), so the events' own cost is shared."""
     import torch
     B = tok.shape[0]
     acc = torch.empty(B, dtype=torch.int32, device="cuda")
     bon = torch.empty(B, dtype=torch.int32, device="cuda")
     per_kind = {}
+    ver.set_repeat(repeat)
     for k in kinds:
         ver.time_kernel(k)
         for _ in range(reps):
@@ -199,8 +226,10 @@ def kernel_times(ver, dev, tok, kv0, kinds, reps):
             ver.commit(B)
         ver.time_kernel(None)
         tot, n = ver.kernel_time()
-        per_kind[k] = {"ms_per_pass": tot / reps, "us_per_launch": 1000 * tot / max(n, 1),
-                       "launches_per_pass": n // reps}
+        r = 1 if k in ("rmsnorm", "commit") else repeat
+        per_kind[k] = {"ms_per_pass": tot / reps / r, "us_per_launch": 1000 * tot / max(n, 1),
+                       "launches_per_pass": n // (reps * r), "back_to_back": r}
+    ver.set_repeat(1)
     dev.kv_len.copy_(kv0)
     return per_kind
 
@@ -211,14 +240,27 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=WORKLOAD)
-    ap.add_argument("--cpu-seqs", type=int, default=4)
+    ap.add_argument("--cpu-seqs", type=int, default=8)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the batch-1 decoding loops and the FP8-activation figure (for counter runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB three times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
         sys.exit(2)
 
     import torch
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
+        return
     import workload as W
     from block_draft_verification_amd import DeviceModel, Verifier
 
@@ -276,7 +318,8 @@ def main():
     else:
         roof = {"bound": "hbm", "achieved": by / t_launch / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    tr = TRAFFIC.get(dom)
+    roof["traffic"] = tr["bytes"] if tr and tr["sha256_16"] == _sources_digest(tr["sources"]) else None
     roof["kernel"] = dom
     roof["us_per_launch"] = per_kind[dom]["us_per_launch"]
     roof["algorithmic_bytes_per_launch"] = by
@@ -299,6 +342,10 @@ def main():
         "roofline": roof,
         "kernels": per_kind,
     }
+    if args.no_extras:
+        ver.close()
+        print(json.dumps(res), flush=True)
+        return
     log("end-to-end decoding at batch 1")
     res["e2e"] = e2e_batch1(ver, dev, m, lens, wl.seed)
     ver.close()
@@ -318,6 +365,10 @@ def main():
         "sum_tau": int(acc8.sum()), "tau_rows_equal_fp16_mode": int((acc8 == tau).sum()),
         "mean_tau_fp16_mode": float(tau.mean()), "mean_tau": float(acc8.mean()),
         "kernels": k8}
+    _, fl8 = kernel_work("gate_up", m, lens)
+    a8 = fl8 / (k8["gate_up"]["us_per_launch"] * 1e-6)
+    res["fp8_activations"]["roofline_gate_up"] = {"bound": "mfma", "achieved": a8 / 1e12, "peak": MFMA_FP8_PEAK / 1e12,
+                                                  "unit": "TFLOP/s", "frac": a8 / MFMA_FP8_PEAK}
     if not args.no_cpu:
         log(f"cpu baseline: oracle on {args.cpu_seqs} sequences")
         res["cpu_baseline"] = cpu_baseline(wl, weights, kv_layers, lens, args.cpu_seqs)

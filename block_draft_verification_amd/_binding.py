@@ -64,6 +64,7 @@ EXPORTS = {
     "spec_debug_swiglu": (_I, [_I, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "spec_debug_attention": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P]),
     "spec_debug_time_kernel": (_I, [_P, _I]),
+    "spec_debug_set_repeat": (_I, [_P, _I]),
     "spec_debug_kernel_time": (_I, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I)]),
 }
 
@@ -251,6 +252,10 @@ class Verifier:
         """Start (or stop, with None) event timing of one kernel class."""
         _check(load_library().spec_debug_time_kernel(self._h, 0 if kind is None else KERNEL_KINDS[kind]),
                "spec_debug_time_kernel")
+
+    def set_repeat(self, repeat: int):
+        """While a kernel class is timed, issue each of its launches `repeat` times."""
+        _check(load_library().spec_debug_set_repeat(self._h, repeat), "spec_debug_set_repeat")
 
     def kernel_time(self):
         """(total ms, launches) recorded since the last call."""

@@ -32,24 +32,33 @@ struct spec_ctx {
   float *dump_hidden, *dump_logits;
   // launch timing of one kernel class (measurement hook)
   int prof_kind = SPEC_K_NONE;
+  int prof_repeat = 1;         // back-to-back launches per timed launch (idempotent classes)
   std::vector<hipEvent_t> ev;  // pairs
-  size_t ev_used = 0;
+  size_t ev_used = 0, ev_launches = 0;
 };
 
 static const size_t kMaxTimedLaunches = 8192;
 
-// Brackets one launch with events when its class is being timed.
+// Brackets one launch with events when its class is being timed; `reps` is
+// how many times the call site issues it (the class's repeat count while it
+// is timed, else 1).  Classes whose kernel updates its own input in place
+// (the RMSNorm step adds the split partials into h; commit) are never repeated.
 struct Timed {
   spec_ctx *c;
   hipStream_t st;
   bool on;
-  Timed(spec_ctx *c_, int kind, hipStream_t s) : c(c_), st(s), on(false) {
+  int reps;
+  Timed(spec_ctx *c_, int kind, hipStream_t s) : c(c_), st(s), on(false), reps(1) {
     if (c->prof_kind != kind || c->ev_used + 2 > c->ev.size()) return;
     on = hipEventRecord(c->ev[c->ev_used], st) == hipSuccess;
+    if (on && kind != SPEC_K_RMSNORM && kind != SPEC_K_COMMIT) reps = c->prof_repeat;
   }
   ~Timed() {
     if (!on) return;
-    if (hipEventRecord(c->ev[c->ev_used + 1], st) == hipSuccess) c->ev_used += 2;
+    if (hipEventRecord(c->ev[c->ev_used + 1], st) == hipSuccess) {
+      c->ev_used += 2;
+      c->ev_launches += reps;
+    }
   }
 };
 
@@ -238,7 +247,8 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
 
   {
     Timed t(c, SPEC_K_EMBED, st);
-    CK(launch_embed(tokens, M, H, V, c->embed, c->h, c->kv.kv_len, max_ctx, kvl, c->err, st));
+    for (int r = 0; r < t.reps; ++r)
+      CK(launch_embed(tokens, M, H, V, c->embed, c->h, c->kv.kv_len, max_ctx, kvl, c->err, st));
   }
   const int ns_o = residual_nsplit(M, H, Hq * D), ns_d = residual_nsplit(M, H, I);
   const bool mx = m.act_fmt == SPEC_ACT_MXFP8;
@@ -259,22 +269,26 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     QkvOut qo{c->q, kc, vc, c->kv.kv_len, c->rope, Hq, Hkv, max_ctx, kvl};
     {
       Timed t(c, SPEC_K_QKV, st);
-      CK(launch_qkv(xin, M, H, D, LinearW{L.w_qkv, L.s_qkv, SPEC_WFMT_FP8_E4M3_ROW}, qo, st));
+      for (int r = 0; r < t.reps; ++r)
+        CK(launch_qkv(xin, M, H, D, LinearW{L.w_qkv, L.s_qkv, SPEC_WFMT_FP8_E4M3_ROW}, qo, st));
     }
     aa.k_cache = kc;
     aa.v_cache = vc;
     {
       Timed t(c, SPEC_K_ATTENTION, st);
-      CK(launch_attention_splits(aa, D, st));
+      for (int r = 0; r < t.reps; ++r)
+        CK(launch_attention_splits(aa, D, st));
     }
     {
       Timed t(c, SPEC_K_ATTN_MERGE, st);
-      CK(launch_attention_merge(aa, D, st));
+      for (int r = 0; r < t.reps; ++r)
+        CK(launch_attention_merge(aa, D, st));
     }
     {
       Timed t(c, SPEC_K_OPROJ, st);
-      CK(launch_residual_partial(ActIn{c->ao, nullptr}, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, c->rpart,
-                                 st));
+      for (int r = 0; r < t.reps; ++r)
+        CK(launch_residual_partial(ActIn{c->ao, nullptr}, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, c->rpart,
+                                   st));
     }
     {
       Timed t(c, SPEC_K_RMSNORM, st);
@@ -282,12 +296,14 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     }
     {
       Timed t(c, SPEC_K_GATE_UP, st);
-      CK(launch_swiglu(xin, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, mx ? (void *)c->a8 : c->act,
-                       mx ? c->as8 : nullptr, st));
+      for (int r = 0; r < t.reps; ++r)
+        CK(launch_swiglu(xin, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, mx ? (void *)c->a8 : c->act,
+                         mx ? c->as8 : nullptr, st));
     }
     {
       Timed t(c, SPEC_K_DOWN, st);
-      CK(launch_residual_partial(ain, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, c->rpart, st));
+      for (int r = 0; r < t.reps; ++r)
+        CK(launch_residual_partial(ain, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, c->rpart, st));
     }
     pending = ns_d;
   }
@@ -297,11 +313,13 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
   }
   {
     Timed t(c, SPEC_K_LM_HEAD, st);
-    CK(launch_lm_argmax(c->x, M, V, H, c->lm_table, c->amax, c->dump_logits, st));
+    for (int r = 0; r < t.reps; ++r)
+      CK(launch_lm_argmax(c->x, M, V, H, c->lm_table, c->amax, c->dump_logits, st));
   }
   {
     Timed t(c, SPEC_K_ACCEPT, st);
-    CK(launch_accept(c->amax, lm_parts(V), M, tokens, batch, accept_len, bonus, argmax, c->last_tau, st));
+    for (int r = 0; r < t.reps; ++r)
+      CK(launch_accept(c->amax, lm_parts(V), M, tokens, batch, accept_len, bonus, argmax, c->last_tau, st));
   }
   return SPEC_OK;
 }
@@ -359,6 +377,12 @@ int spec_get_device_error(spec_ctx *c, int32_t *code, hipStream_t st) {
   return SPEC_OK;
 }
 
+int spec_debug_set_repeat(spec_ctx *c, int32_t repeat) {
+  if (!c || repeat < 1 || repeat > 64) return SPEC_E_ARG;
+  c->prof_repeat = repeat;
+  return SPEC_OK;
+}
+
 int spec_debug_time_kernel(spec_ctx *c, int32_t kind) {
   if (!c || kind < SPEC_K_NONE || kind > SPEC_K_ATTN_MERGE) return SPEC_E_ARG;
   if (kind != SPEC_K_NONE && c->ev.empty()) {
@@ -380,8 +404,8 @@ int spec_debug_kernel_time(spec_ctx *c, float *total_ms, int32_t *launches) {
     sum += ms;
   }
   *total_ms = sum;
-  *launches = (int32_t)(c->ev_used / 2);
-  c->ev_used = 0;
+  *launches = (int32_t)c->ev_launches;
+  c->ev_used = c->ev_launches = 0;
   return SPEC_OK;
 }
 

@@ -304,8 +304,16 @@ typedef enum {
  * not under graph capture.  SPEC_K_NONE stops recording. */
 int spec_debug_time_kernel(spec_ctx *ctx, int32_t kind);
 
+/* Measurement hook: while a kernel class is timed, issue each of its launches
+ * `repeat` times back to back inside one event pair (1 <= repeat <= 64;
+ * default 1), so the events' own overhead is shared by `repeat` launches.  The
+ * repeated kernels only recompute the same outputs from the same inputs; the
+ * RMSNorm and commit classes, which update state in place, are never
+ * repeated. */
+int spec_debug_set_repeat(spec_ctx *ctx, int32_t repeat);
+
 /* Synchronises the recorded events, returns the summed duration (ms) and the
- * number of recorded launches, and clears the record. */
+ * number of recorded launches (repeats included), and clears the record. */
 int spec_debug_kernel_time(spec_ctx *ctx, float *total_ms /*host*/, int32_t *launches /*host*/);
 
 #ifdef __cplusplus
