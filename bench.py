@@ -39,9 +39,9 @@ REPEAT = 20  # back-to-back launches per event pair in the per-kernel timing
 TRAFFIC_PROFILE = "profiles/verify_pass_0.5b-fp8-b32-ctx512to4096_hbm_traffic.md"
 TRAFFIC = {
     "gate_up": {"bytes": (16.92 + 4.75) * 2 ** 20, "sources": ("gemm.hip", "common.h", "kernels.h"),
-                "sha256_16": "38077d55438202ba,230adac9725098ab,d2af339db190ecbf"},
+                "sha256_16": "38e354ee0a89d882,230adac9725098ab,2814e6bbb4576c62"},
     "attention": {"bytes": (40.09 + 11.28) * 2 ** 20, "sources": ("attention.hip", "common.h", "kernels.h"),
-                  "sha256_16": "7ae9f732a22cba54,230adac9725098ab,d2af339db190ecbf"},
+                  "sha256_16": "7ae9f732a22cba54,230adac9725098ab,2814e6bbb4576c62"},
 }
 
 

@@ -57,6 +57,7 @@ EXPORTS = {
     "spec_get_device_error": (_I, [_P, ctypes.POINTER(_I), _P]),
     "spec_status_str": (ctypes.c_char_p, [_I]),
     "spec_debug_set_dump": (_I, [_P, _P, _P]),
+    "spec_pack_weights": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
     "spec_debug_linear": (_I, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
     "spec_debug_quant_mx8": (_I, [_I, _I, _P, _P, _P, _P]),
     "spec_debug_linear_mx8": (_I, [_I, _I, _I, _P, _P, _P, _P, _I, _P, _P]),
@@ -117,6 +118,18 @@ def _wfmt(name: str) -> int:
     return {"fp8": WFMT_FP8_E4M3_ROW, "mxfp4": WFMT_MXFP4}[name]
 
 
+def pack_weights(w: torch.Tensor, scales, wfmt: int, rows: int, cols: int):
+    """Row-major device weights -> the tile-major layout the kernels read
+    (spec_pack_weights).  Returns (w_packed, scales_packed); FP8 row scales
+    and absent BF16 scales are returned as given."""
+    wp = torch.empty_like(w)
+    sp = torch.empty_like(scales) if wfmt == WFMT_MXFP4 else scales
+    _check(load_library().spec_pack_weights(wfmt, rows, cols, _ptr(w), _ptr(scales), _ptr(wp),
+                                            _ptr(sp) if wfmt == WFMT_MXFP4 else None, _stream()),
+           "spec_pack_weights")
+    return wp, sp
+
+
 class DeviceModel:
     """Caller-owned device buffers: weights in the boundary's layout, the BF16
     KV cache for K and V, and kv_len.  Contiguous cache: [L][max_batch][Hkv]
@@ -131,11 +144,20 @@ class DeviceModel:
         self.page_table = None if page_table is None else torch.as_tensor(
             np.asarray(page_table, np.int32), device=device).contiguous()
         m = shape
+        mf = _wfmt(m.mlp_format)
+        dims = {"qkv": (m.qkv_rows, m.hidden, WFMT_FP8_E4M3_ROW), "o": (m.hidden, m.n_q_heads * m.head_dim,
+                                                                       WFMT_FP8_E4M3_ROW),
+                "gate_up": (2 * m.intermediate, m.hidden, mf), "down": (m.hidden, m.intermediate, mf)}
         self.layers = []
         for lw in weights["layers"]:
-            self.layers.append({k: _dev(v, device) for k, v in lw.items()})
-        self.embed = _dev(weights["embed"], device)
-        self.lm_head = None if weights.get("lm_head") is None else _dev(weights["lm_head"], device)
+            d = {k: _dev(v, device) for k, v in lw.items()}
+            for name, (rows, cols, fmt) in dims.items():  # the kernels read tile-major weights
+                d["w_" + name], d["s_" + name] = pack_weights(d["w_" + name], d["s_" + name], fmt, rows, cols)
+            self.layers.append(d)
+        V, H = m.vocab, m.hidden
+        self.embed = pack_weights(_dev(weights["embed"], device), None, WFMT_BF16, V, H)[0]
+        self.lm_head = None if weights.get("lm_head") is None else pack_weights(
+            _dev(weights["lm_head"], device), None, WFMT_BF16, V, H)[0]
         self.final_norm = _dev(weights["final_norm"], device)
         if self.page_table is None:
             cache_shape = (m.n_layers, max_batch, m.n_kv_heads, max_ctx, m.head_dim)

@@ -430,6 +430,16 @@ int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const 
   return SPEC_OK;
 }
 
+int spec_pack_weights(int32_t wfmt, int32_t rows, int32_t cols, const void *w, const void *scales, void *w_packed,
+                      void *scales_packed, hipStream_t st) {
+  if (!w || !w_packed || rows < 32 || cols < 64 || rows % 32 || cols % 64) return SPEC_E_ARG;
+  if (wfmt != SPEC_WFMT_FP8_E4M3_ROW && wfmt != SPEC_WFMT_MXFP4 && wfmt != SPEC_WFMT_BF16) return SPEC_E_UNSUPPORTED;
+  if (wfmt == SPEC_WFMT_MXFP4 && (!scales || !scales_packed)) return SPEC_E_ARG;
+  if (!aligned16(w) || !aligned16(w_packed)) return SPEC_E_ARG;
+  CK(launch_pack_weights(wfmt, rows, cols, w, scales, w_packed, scales_packed, st));
+  return SPEC_OK;
+}
+
 int spec_debug_quant_mx8(int32_t M, int32_t K, const float *x, uint8_t *codes, uint8_t *scales, hipStream_t st) {
   if (M < 1 || K < 32 || K % 32 || !x || !codes || !scales) return SPEC_E_ARG;
   if (!aligned16(x) || !aligned16(codes)) return SPEC_E_ARG;

@@ -14,11 +14,14 @@
 // MFMA mapping (v_mfma_f32_32x32x16_{f16,bf16}, which on gfx950 issues at
 // twice the rate of the 16x16x32 shape): the weight tile is the A operand (32
 // output rows), the activation tile the B operand (32 block rows).  Per
-// 64-wide k step lane (c, h) = (lane%32, lane/32) reads the 32 consecutive k
-// 32h..32h+31 of one weight row (two 16-byte loads for FP8, one for MXFP4,
-// whose scale block is exactly those 32 k) and uses its 8-element slice i as
-// the k operand of the step's i-th MFMA; the activation side reads the same k
-// slices, so A and B always pair the same k and the sum over k is complete.
+// 64-wide k step lane (c, h) = (lane%32, lane/32) holds 32 k of one weight
+// row: for FP8, k 16h..16h+15 and 32+16h..+15 (two 16-byte loads); for BF16
+// and MXFP4 (whose scale block is exactly those k), 32h..32h+31.  It uses its
+// 8-element slice i as the k operand of the step's i-th MFMA, and the
+// activation side reads the same k slices (act_chunk), so A and B always pair
+// the same k and the sum over k is complete.  The weights are tile-major
+// (kernels.h): each wave-wide weight load is one contiguous kilobyte, which
+// streams about 2.7x faster per compute unit than 32 rows x 32 bytes.
 // Lane (c, h) ends with the outputs of block row c for the weight rows
 // 8q + 4h + (0..3), q = 0..3 of each tile, so every epilogue (scale, RoPE
 // pair, gate/up pair, residual partial, argmax) runs on registers.
@@ -27,7 +30,7 @@
 // of NT 32-row weight tiles) sharing one activation tile of 32*MT rows.  The
 // activation tile goes straight from global memory to LDS (one barrier per k
 // step); each wave streams its own weight rows into registers.  Both run
-// GEMM_DEPTH k steps ahead of the MFMAs.  Workgroups that share weight rows
+// a few k steps ahead of the MFMAs (more for narrow tiles).  Workgroups that share weight rows
 // (all M blocks of one N block) are placed on one XCD so its L2 serves the
 // re-reads.  Residual projections with too few output tiles to fill the chip
 // split K over gridDim.z and write fp32 partials; the next RMSNorm adds them
@@ -35,8 +38,17 @@
 #include "common.h"
 #include "kernels.h"
 
-#ifndef GEMM_DEPTH
-#define GEMM_DEPTH 2
+// k steps loaded ahead of the one computed, by activation tile height (32*MT
+// rows).  With tile-major weights, measured depths of 2 to 6 change the 512-
+// and 16-row passes by under 2%, deeper rings costing slightly, so 2 it is.
+#ifndef GEMM_DEPTH_MT1
+#define GEMM_DEPTH_MT1 2
+#endif
+#ifndef GEMM_DEPTH_MT2
+#define GEMM_DEPTH_MT2 2
+#endif
+#ifndef GEMM_DEPTH_MT4
+#define GEMM_DEPTH_MT4 2
 #endif
 #ifndef GEMM_BF16_OCC2
 #define GEMM_BF16_OCC2 0
@@ -56,6 +68,18 @@ template <> struct WRaw<SPEC_WFMT_MXFP4> { u32x4_t c; uint32_t e; };  // 32 nibb
 
 // VMEM instructions per tile and step
 template <int FMT> constexpr int w_loads() { return FMT == SPEC_WFMT_BF16 ? 4 : 2; }
+// registers of one tile's raw weights for one step
+template <int FMT> constexpr int w_regs() { return FMT == SPEC_WFMT_BF16 ? 16 : FMT == SPEC_WFMT_MXFP4 ? 5 : 8; }
+
+// Pipeline depth: the tile height's depth, capped so that the register ring
+// (depth + 1 sets of weights and activation exponents) stays within 112 VGPRs.
+template <int FMT, int NT, int MT, bool A8>
+constexpr int gemm_depth() {
+  const int want = MT == 1 ? GEMM_DEPTH_MT1 : MT == 2 ? GEMM_DEPTH_MT2 : GEMM_DEPTH_MT4;
+  const int cap = 112 / (NT * w_regs<FMT>() + (A8 ? MT : 0)) - 1;
+  const int d = want < cap ? want : cap;
+  return d < 2 ? 2 : d;
+}
 
 // Weight loads are issued as plain vector loads the compiler does not track:
 // its wait analysis cannot count the LDS-DMA activation loads issued after
@@ -83,25 +107,33 @@ __device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_BF16> &r) {
 }
 __device__ __forceinline__ void hold(const WRaw<SPEC_WFMT_MXFP4> &r) { asm volatile("" ::"v"(r.c), "v"(r.e)); }
 
-// kb = first k of the step (a multiple of 64); lane half h.  Non-A8 lanes read
-// the 32 consecutive k kb+32h..kb+32h+31; A8 (scaled FP8 MFMA) FP8 lanes read
-// k kb+16h..+15 and kb+32+16h..+15, the operand order of that instruction.
-template <int FMT, bool A8 = false>
-__device__ __forceinline__ void load_w(WRaw<FMT> &r, const uint8_t *__restrict__ w,
-                                       const uint8_t *__restrict__ s, int row, int K, int kb, int h) {
-  const int k = kb + 32 * h;
+// One lane's raw weights of one tile for k step `ks`, from the tile-major
+// layout: wl = the lane's chunk 0 of the tile row's first k step, sl = its
+// scale byte (MXFP4).  FP8 lanes get k 16h..16h+15 and 32+16h..+15 of the
+// step (the scaled FP8 instruction's operand order), BF16 and MXFP4 lanes the
+// 32 consecutive k 32h..32h+31.
+template <int FMT>
+__device__ __forceinline__ void load_w(WRaw<FMT> &r, const uint8_t *wl, const uint8_t *sl, int ks) {
+  const uint8_t *p = wl + (size_t)ks * tile_bytes(FMT);
   if constexpr (FMT == SPEC_WFMT_FP8_E4M3_ROW) {
-    const uint8_t *p = w + (size_t)row * K + kb;
-    r.c[0] = vload16(p + (A8 ? 16 * h : 32 * h));
-    r.c[1] = vload16(p + (A8 ? 32 + 16 * h : 32 * h + 16));
+    r.c[0] = vload16(p);
+    r.c[1] = vload16(p + 1024);
   } else if constexpr (FMT == SPEC_WFMT_BF16) {
-    const uint16_t *p = reinterpret_cast<const uint16_t *>(w) + (size_t)row * K + k;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.c[i] = vload16(p + 8 * i);
+    for (int i = 0; i < 4; ++i) r.c[i] = vload16(p + 1024 * i);
   } else {
-    r.c = vload16(w + (size_t)row * (K / 2) + k / 2);
-    r.e = vload1(s + (size_t)row * (K / 32) + k / 32);
+    r.c = vload16(p);
+    r.e = vload1(sl + (size_t)ks * 64);
   }
+}
+
+// Activation chunk (8 k, 16 bytes) that pairs with the lane's weight slice i
+// on the 32x32x16 MFMA: FP8 slices are k 16h + 8i (i < 2) and 32 + 16h +
+// 8(i - 2); BF16 and MXFP4 slices are k 32h + 8i.
+template <int FMT>
+__device__ __forceinline__ int act_chunk(int i, int h) {
+  if constexpr (FMT == SPEC_WFMT_FP8_E4M3_ROW) return (i < 2 ? 0 : 4) + 2 * h + (i & 1);
+  else return 4 * h + i;
 }
 
 // 32 weights -> four 8-element MFMA operands in the activation type
@@ -198,7 +230,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
   // LDS-DMA instructions per wave per stage: ROWS*8 (16-bit) or ROWS*4 (FP8) chunks of 16 bytes over 256 lanes
   constexpr int AJ = A8 ? (MT + 1) / 2 : MT;
   constexpr int SE = A8 ? AJ * 2048 : ROWS * 64;  // 16-bit elements per stage
-  constexpr int DIST = GEMM_DEPTH;          // k steps loaded ahead of the one computed
+  constexpr int DIST = gemm_depth<FMT, NT, MT, A8>();  // k steps loaded ahead of the one computed
   constexpr int NS = DIST + 1;              // LDS stages = weight register sets
   // staged epilogue: per wave a [32][LD] fp32 tile of block rows x output columns
   constexpr int COLS = Epi::template cols<NT>(), LD = COLS + 4;
@@ -236,9 +268,13 @@ gemm_kernel(GemmArgs ga, Epi epi) {
       asp[mt] = ga.xs + (size_t)m * (K / 32) + ks0 * 2 + h;
     }
   }
-  int wrow[NT];
+  const uint8_t *wl[NT], *sl[NT];  // the lane's chunk 0 / scale byte at k step 0 of each tile
 #pragma unroll
-  for (int t = 0; t < NT; ++t) wrow[t] = epi.row(active ? unit : 0, t) + c;
+  for (int t = 0; t < NT; ++t) {
+    const size_t tile0 = (size_t)(epi.row(active ? unit : 0, t) >> 5) * ksteps + ks0;
+    wl[t] = ga.w + tile0 * tile_bytes(FMT) + lane * 16;
+    sl[t] = FMT == SPEC_WFMT_MXFP4 ? ga.s + tile0 * 64 + lane : nullptr;
+  }
 
   f32x16_t acc[NT][MT];
 #pragma unroll
@@ -289,7 +325,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         const int row = 32 * mt + c;
-        af[mt] = *reinterpret_cast<const u32x4_t *>(base + (row * 8 + ((4 * h + i) ^ swz(row))) * 8);
+        af[mt] = *reinterpret_cast<const u32x4_t *>(base + (row * 8 + (act_chunk<FMT>(i, h) ^ swz(row))) * 8);
       }
     };
     // the fragments of slice i+1 are read while slice i's MFMAs run
@@ -312,7 +348,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
   };
   auto issue_w = [&](WRaw<FMT>(&wr)[NT], uint32_t(&sc)[A8 ? MT : 1], int step) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) load_w<FMT, A8>(wr[t], ga.w, ga.s, wrow[t], K, (ks0 + step) * 64, h);
+    for (int t = 0; t < NT; ++t) load_w<FMT>(wr[t], wl[t], sl[t], step);
     if constexpr (A8) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) sc[mt] = vload1(asp[mt] + step * 2);
@@ -345,7 +381,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
       issue_w(wr[(ph + DIST) % NS], scr[(ph + DIST) % NS], min(s + DIST, nsteps - 1));
       issue_a(min(s + DIST, nsteps - 1), (ph + DIST) % NS);
       __builtin_amdgcn_sched_barrier(0);
-      if (ph == 0 || s < nsteps) {
+      if (ph == 0 || s < nsteps) {  // phases past the last step only keep the load count uniform
         if constexpr (A8) compute_a8(ph, wr[ph], scr[ph]);
         else compute(ph, wr[ph]);
       }

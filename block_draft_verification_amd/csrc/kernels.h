@@ -11,11 +11,28 @@ struct ActIn {
   const void *x;
   const uint8_t *xs;  // NULL: FP16 / BF16 activations
 };
+// Weights are tile-major (the layout spec_pack_weights writes): 32-row x
+// 64-column tiles, tile (rt, kt) at index rt * (cols / 64) + kt, so one row
+// tile's k steps follow each other in memory.  Inside a tile, lane l = 32h + c
+// (c = row in the tile, h = 0, 1) owns 16-byte chunks, chunk j of lane l at
+// byte (j * 64 + l) * 16, in the order the GEMM's loads consume them; every
+// wave-wide load is one contiguous kilobyte.
+//   FP8   (2048 B): chunk j of lane l = row c, columns 16h + 32j .. +15
+//   BF16  (4096 B): chunk j (0..3)   = row c, columns 32h + 8j .. +7
+//   MXFP4 (1024 B): chunk 0          = row c, columns 32h .. 32h+31 (nibble
+//                   pairs, low nibble = even column); its e8m0 scales form a
+//                   64-byte tile, byte l = block h of row c
+// FP8 per-row scales stay fp32 [rows].
 struct LinearW {
-  const void *w;   // codes / bf16 rows
-  const void *s;   // fp32 per-row scales (FP8), e8m0 [rows][K/32] (MXFP4), NULL (BF16)
+  const void *w;   // tile-major codes / bf16 values
+  const void *s;   // fp32 per-row scales (FP8), tile-major e8m0 (MXFP4), NULL (BF16)
   int wfmt;
 };
+__host__ __device__ constexpr int tile_bytes(int wfmt) { return wfmt == 3 ? 4096 : wfmt == 2 ? 1024 : 2048; }
+
+// row-major -> tile-major (scales too, for MXFP4); rows % 32 == 0, cols % 64 == 0
+hipError_t launch_pack_weights(int wfmt, int rows, int cols, const void *w, const void *s, void *w_out, void *s_out,
+                               hipStream_t st);
 
 // Tiling of one launch (see gemm.hip): MT 16-row activation tiles per
 // workgroup, nb x mb output tiles, K split into nsplit pieces of spl steps.
@@ -93,6 +110,7 @@ hipError_t launch_attention_merge(const AttnArgs &a, int D, hipStream_t st);
 int attention_split_len(int batch, int Hkv, int max_ctx);
 
 // ---- small kernels ----
+// table: the tile-major BF16 embedding [V][H]
 hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16_t *table, float *h,
                         const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, hipStream_t st);
 // h += part[0] + ... + part[nsplit-1] (in that order; nsplit may be 0), then

@@ -25,8 +25,49 @@ __global__ void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
       }
     }
   }
-  const uint16_t *row = table + (size_t)t * H;
-  for (int c = threadIdx.x; c < H; c += blockDim.x) h[(size_t)m * H + c] = bf16_to_f32(row[c]);
+  // row t of the tile-major table: 8 columns (one 16-byte chunk) per thread
+  const int ktiles = H / 64;
+  for (int k0 = 8 * threadIdx.x; k0 < H; k0 += 8 * blockDim.x) {
+    const int kk = k0 & 63, l = 32 * (kk >> 5) + (t & 31), j = (kk & 31) >> 3;
+    const size_t tile = (size_t)(t >> 5) * ktiles + (k0 >> 6);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(table + tile * 2048 + (j * 64 + l) * 8);
+    float *o = h + (size_t)m * H + k0;
+    *reinterpret_cast<f32x4_t *>(o) = f32x4_t{bf16_to_f32(v.x & 0xffff), bf16_to_f32(v.x >> 16),
+                                              bf16_to_f32(v.y & 0xffff), bf16_to_f32(v.y >> 16)};
+    *reinterpret_cast<f32x4_t *>(o + 4) = f32x4_t{bf16_to_f32(v.z & 0xffff), bf16_to_f32(v.z >> 16),
+                                                  bf16_to_f32(v.w & 0xffff), bf16_to_f32(v.w >> 16)};
+  }
+}
+
+// Row-major -> tile-major weights (the layout kernels.h describes): thread i
+// writes destination chunk i (16 bytes) from one contiguous 16-byte run of its
+// source row; MXFP4 scale tiles are written one byte per thread.
+template <int FMT>
+__global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ src, int rows, int cols,
+                                                   uint8_t *__restrict__ dst, size_t nchunks) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= nchunks) return;
+  constexpr int CPT = FMT == SPEC_WFMT_BF16 ? 256 : FMT == SPEC_WFMT_MXFP4 ? 64 : 128;  // chunks per tile
+  const int ktiles = cols / 64;
+  const size_t tile = i / CPT;
+  const int q = (int)(i % CPT), j = q >> 6, l = q & 63, c = l & 31, hh = l >> 5;
+  const int row = (int)(tile / ktiles) * 32 + c, kt = (int)(tile % ktiles);
+  size_t off;  // byte offset of the chunk's first byte in the row-major source
+  if constexpr (FMT == SPEC_WFMT_FP8_E4M3_ROW) off = (size_t)row * cols + kt * 64 + 16 * hh + 32 * j;
+  else if constexpr (FMT == SPEC_WFMT_BF16) off = ((size_t)row * cols + kt * 64 + 32 * hh + 8 * j) * 2;
+  else off = (size_t)row * (cols / 2) + (kt * 64 + 32 * hh) / 2;
+  *reinterpret_cast<u32x4_t *>(dst + i * 16) = *reinterpret_cast<const u32x4_t *>(src + off);
+}
+
+__global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restrict__ src, int rows, int cols,
+                                                          uint8_t *__restrict__ dst, size_t n) {
+  const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int ktiles = cols / 64;
+  const size_t tile = i / 64;
+  const int l = (int)(i % 64), c = l & 31, hh = l >> 5;
+  const int row = (int)(tile / ktiles) * 32 + c, kt = (int)(tile % ktiles);
+  dst[i] = src[(size_t)row * (cols / 32) + 2 * kt + hh];
 }
 
 // h += part[0] + ... + part[ns-1] (split-K partials of the projection that
@@ -235,6 +276,30 @@ __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
 hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16_t *table, float *h,
                         const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, hipStream_t st) {
   hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, st, tokens, H, V, table, h, kv_len, max_ctx, kvl, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weights(int wfmt, int rows, int cols, const void *w, const void *s, void *w_out, void *s_out,
+                               hipStream_t st) {
+  if (rows % 32 || cols % 64 || rows < 32 || cols < 64) return hipErrorInvalidValue;
+  const size_t tiles = (size_t)(rows / 32) * (cols / 64);
+  const size_t chunks = tiles * (tile_bytes(wfmt) / 16);
+  const dim3 grid((unsigned)((chunks + 255) / 256));
+  const uint8_t *src = static_cast<const uint8_t *>(w);
+  uint8_t *dst = static_cast<uint8_t *>(w_out);
+  if (wfmt == SPEC_WFMT_FP8_E4M3_ROW) {
+    hipLaunchKernelGGL(pack_kernel<SPEC_WFMT_FP8_E4M3_ROW>, grid, dim3(256), 0, st, src, rows, cols, dst, chunks);
+  } else if (wfmt == SPEC_WFMT_BF16) {
+    hipLaunchKernelGGL(pack_kernel<SPEC_WFMT_BF16>, grid, dim3(256), 0, st, src, rows, cols, dst, chunks);
+  } else if (wfmt == SPEC_WFMT_MXFP4) {
+    hipLaunchKernelGGL(pack_kernel<SPEC_WFMT_MXFP4>, grid, dim3(256), 0, st, src, rows, cols, dst, chunks);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    const size_t n = tiles * 64;
+    hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                       static_cast<const uint8_t *>(s), rows, cols, static_cast<uint8_t *>(s_out), n);
+  } else {
+    return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

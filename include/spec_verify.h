@@ -120,12 +120,38 @@ typedef struct {
   int32_t act_fmt;   /* spec_act_fmt */
 } spec_model_desc;
 
-/* One decoder layer (all device pointers, caller-owned).
+/* Weight memory layout.  Every weight matrix and the BF16 embedding / lm_head
+ * tables are passed TILE-MAJOR, the order in which the kernels stream them,
+ * so that every wave-wide weight load reads one contiguous kilobyte.  The
+ * logical matrix is [rows][cols] (rows = outputs, cols = inputs, rows a
+ * multiple of 32, cols a multiple of 64), cut into 32 x 64 tiles; tile
+ * (rt, kt) is stored at tile index rt * (cols/64) + kt.  Inside a tile,
+ * "lane" l = 32h + c (c = row within the tile, h = 0 or 1) owns 16-byte
+ * chunks, chunk j of lane l at byte (j*64 + l) * 16 of the tile:
+ *   FP8_E4M3_ROW (2048-byte tiles): chunk j = row c, columns 16h + 32j .. +15
+ *   BF16         (4096-byte tiles): chunk j (0..3) = row c, columns 32h + 8j .. +7
+ *   MXFP4        (1024-byte tiles): chunk 0 = row c, columns 32h .. 32h+31 as
+ *                nibble pairs (low nibble = even column); its e8m0 scales are
+ *                tile-major too, 64 bytes per tile, byte l = the scale of
+ *                columns 32h .. 32h+31 of row c.
+ * FP8 per-row scales stay fp32 [rows].  spec_pack_weights converts from
+ * row-major. */
+
+/* Row-major -> tile-major on the device (see above).  wfmt FP8_E4M3_ROW:
+ * codes uint8 [rows][cols] -> w_packed (scales unused: FP8 row scales are
+ * passed as they are); MXFP4: nibbles [rows][cols/2] and e8m0 scales
+ * [rows][cols/32] -> w_packed and scales_packed; BF16: [rows][cols] ->
+ * w_packed.  Output buffers have the input's size, are caller-owned, must not
+ * overlap the input, and are 16-byte aligned.  Asynchronous. */
+int spec_pack_weights(int32_t wfmt, int32_t rows, int32_t cols, const void *w, const void *scales,
+                      void *w_packed, void *scales_packed, hipStream_t stream);
+
+/* One decoder layer (all device pointers, caller-owned; tile-major weights).
  *   w_qkv  [(Hq+2Hkv)*D][H], rows = q heads, then k heads, then v heads
  *   w_o    [H][Hq*D]
  *   w_gate_up [2I][H], rows = gate (I rows) then up (I rows)
  *   w_down [H][I]
- * s_* : fp32 [rows] for FP8_E4M3_ROW; uint8 e8m0 [rows][cols/32] for MXFP4.
+ * s_* : fp32 [rows] for FP8_E4M3_ROW; tile-major e8m0 for MXFP4.
  * attn_norm, mlp_norm: fp32 RMSNorm gains [H]. */
 typedef struct {
   const void *w_qkv, *s_qkv;
@@ -137,8 +163,8 @@ typedef struct {
 
 typedef struct {
   const spec_layer_weights *layers; /* (host) array of n_layers; copied at init */
-  const uint16_t *embed;            /* bf16 [V][H]                             */
-  const uint16_t *lm_head;          /* bf16 [V][H]; NULL when tied             */
+  const uint16_t *embed;            /* bf16 [V][H], tile-major                 */
+  const uint16_t *lm_head;          /* bf16 [V][H], tile-major; NULL when tied */
   const float *final_norm;          /* fp32 [H]                                */
 } spec_weights;
 
@@ -242,8 +268,8 @@ int spec_debug_set_dump(spec_ctx *ctx, float *hidden, float *logits);
 /* Test hook: one weight-streaming linear on its own,
  *   y[m][n] = sum_k x[m][k] * w(n, k)     (fp32 out, [M][N])
  * x: FP16 bits [M][K] for FP8 / MXFP4 weights, BF16 bits for BF16 weights;
- * w in format `wfmt` with scales as in spec_layer_weights (scales NULL for
- * BF16).  K and N multiples of 64.
+ * w tile-major in format `wfmt` with scales as in spec_layer_weights (scales
+ * NULL for BF16).  K and N multiples of 64.
  * Synchronous. */
 int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const void *w,
                       const void *scales, int32_t wfmt, float *y, hipStream_t stream);

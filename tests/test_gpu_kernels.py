@@ -9,7 +9,7 @@ import oracle
 from oracle.codecs import decode_bf16, decode_e4m3, dequant_fp8_rows, dequant_mxfp4
 import workload as W
 from block_draft_verification_amd import (WFMT_BF16, WFMT_FP8_E4M3_ROW, WFMT_MXFP4, debug_attention, debug_linear,
-                                          debug_rmsnorm, debug_swiglu)
+                                          debug_rmsnorm, debug_swiglu, pack_weights)
 
 pytestmark = pytest.mark.gpu
 
@@ -38,6 +38,46 @@ def _dev(a):
     return torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a).cuda()
 
 
+def _packed(w, s, wfmt, rows, cols):
+    """Row-major weights -> the tile-major device layout, through the library."""
+    return pack_weights(_dev(w), None if s is None else _dev(s), wfmt, rows, cols)
+
+
+def _pack_ref(w, wfmt, rows, cols):
+    """The tile-major layout of include/spec_verify.h written as an index
+    permutation: tiles (rt, kt) in row-tile-major order; inside a tile, chunk j
+    of lane 32h + c at chunk slot j*64 + 32h + c."""
+    RT, KT = rows // 32, cols // 64
+    if wfmt == WFMT_FP8_E4M3_ROW:      # row c, columns 16h + 32j + b
+        return w.reshape(RT, 32, KT, 2, 2, 16).transpose(0, 2, 3, 4, 1, 5).reshape(-1)
+    if wfmt == WFMT_BF16:              # row c, columns 32h + 8j + e
+        return w.reshape(RT, 32, KT, 2, 4, 8).transpose(0, 2, 4, 3, 1, 5).reshape(-1)
+    return w.reshape(RT, 32, KT, 2, 16).transpose(0, 2, 3, 1, 4).reshape(-1)  # MXFP4 nibble pairs
+
+
+def _pack_scales_ref(e8, rows, cols):
+    return e8.reshape(rows // 32, 32, cols // 64, 2).transpose(0, 2, 3, 1).reshape(-1)
+
+
+@pytest.mark.parametrize("wfmt,rows,cols", [(WFMT_FP8_E4M3_ROW, 96, 192), (WFMT_BF16, 64, 128),
+                                            (WFMT_MXFP4, 64, 320), (WFMT_FP8_E4M3_ROW, 1152, 896)])
+def test_pack_weights_layout(wfmt, rows, cols):
+    """spec_pack_weights against the header's definition, bit for bit."""
+    rng = np.random.default_rng(rows + cols)
+    if wfmt == WFMT_BF16:
+        w = rng.integers(0, 1 << 16, size=(rows, cols)).astype(np.uint16)
+    else:
+        w = rng.integers(0, 256, size=(rows, cols // 2 if wfmt == WFMT_MXFP4 else cols)).astype(np.uint8)
+    e8 = rng.integers(0, 256, size=(rows, cols // 32)).astype(np.uint8) if wfmt == WFMT_MXFP4 else None
+    wp, sp = _packed(w, e8, wfmt, rows, cols)
+    got = wp.cpu().numpy().reshape(-1)
+    if wfmt == WFMT_BF16:
+        got = got.view(np.uint16)
+    assert np.array_equal(got, _pack_ref(w, wfmt, rows, cols))
+    if e8 is not None:
+        assert np.array_equal(sp.cpu().numpy().reshape(-1), _pack_scales_ref(e8, rows, cols))
+
+
 @pytest.mark.parametrize("M,N,K", [(16, 1152, 896), (40, 896, 4864), (512, 9728, 896), (1, 64, 64)])
 def test_linear_fp8(M, N, K):
     rng = np.random.default_rng(M + N + K)
@@ -47,7 +87,7 @@ def test_linear_fp8(M, N, K):
         codes[0, :254] = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
     scales = (rng.random(N) * 1e-3 + 1e-4).astype(np.float32)
     xb = _x(M, K, 1)
-    y = debug_linear(_dev(xb), _dev(codes), _dev(scales), WFMT_FP8_E4M3_ROW, N).cpu().numpy()
+    y = debug_linear(_dev(xb), *_packed(codes, scales, WFMT_FP8_E4M3_ROW, N, K), WFMT_FP8_E4M3_ROW, N).cpu().numpy()
     _check_linear(xb, dequant_fp8_rows(codes, scales), y)
 
 
@@ -59,7 +99,7 @@ def test_linear_fp8_every_code_decodes():
     codes[:len(finite)] = finite[:, None]
     scales = np.ones(N, np.float32)
     xb = np.ones((16, 64), np.float16).view(np.uint16)
-    y = debug_linear(_dev(xb), _dev(codes), _dev(scales), WFMT_FP8_E4M3_ROW, N).cpu().numpy()
+    y = debug_linear(_dev(xb), *_packed(codes, scales, WFMT_FP8_E4M3_ROW, N, 64), WFMT_FP8_E4M3_ROW, N).cpu().numpy()
     assert np.array_equal(y[0, :len(finite)].astype(np.float64), 64 * decode_e4m3(finite))
 
 
@@ -69,7 +109,7 @@ def test_linear_mxfp4(M, N, K):
     codes = rng.integers(0, 256, size=(N, K // 2)).astype(np.uint8)
     e8 = rng.integers(110, 135, size=(N, K // 32)).astype(np.uint8)
     xb = _x(M, K, 2)
-    y = debug_linear(_dev(xb), _dev(codes), _dev(e8), WFMT_MXFP4, N).cpu().numpy()
+    y = debug_linear(_dev(xb), *_packed(codes, e8, WFMT_MXFP4, N, K), WFMT_MXFP4, N).cpu().numpy()
     _check_linear(xb, dequant_mxfp4(codes, e8), y)
 
 
@@ -77,7 +117,7 @@ def test_linear_mxfp4(M, N, K):
 def test_linear_bf16(M, N, K):
     w = W.to_bf16_bits((np.random.default_rng(5).standard_normal((N, K)) * 0.02).astype(np.float32))
     xb = _x(M, K, 3, f16=False)
-    y = debug_linear(_dev(xb), _dev(w), None, WFMT_BF16, N).cpu().numpy()
+    y = debug_linear(_dev(xb), *_packed(w, None, WFMT_BF16, N, K), WFMT_BF16, N).cpu().numpy()
     _check_linear(xb, decode_bf16(w), y, f16=False)
 
 
@@ -117,7 +157,7 @@ def test_swiglu_fp16(wfmt, M, H, I):
     gate, up = x @ wd[:I].T, x @ wd[I:].T
     ref = oracle.silu(gate) * up
     bg, bu = 3e-5 * (np.abs(x) @ np.abs(wd[:I]).T), 3e-5 * (np.abs(x) @ np.abs(wd[I:]).T)
-    a = debug_swiglu(_dev(xb), None, _dev(w), _dev(ws), wfmt, I).cpu().numpy()
+    a = debug_swiglu(_dev(xb), None, *_packed(w, ws, wfmt, 2 * I, H), wfmt, I).cpu().numpy()
     err = np.abs(_dec(a.view(np.uint16)) - ref)
     bound = 1.1 * np.abs(up) * bg + np.abs(oracle.silu(gate)) * bu + bg * bu
     assert np.all(err <= 2.0 ** -11 * (np.abs(ref) + bound) + bound + 2.0 ** -24), \
