@@ -72,58 +72,83 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restr
 
 // h += part[0] + ... + part[ns-1] (split-K partials of the projection that
 // just ran, added in split order), then x = h / sqrt(mean(h^2) + eps) * gain
-// rounded to FP16 (decoder layers) or BF16 (lm_head input).  One 64-lane
-// workgroup per row; a lane owns the 4-column chunks c = 4*lane + 256*i, and all
-// of a chunk's partial loads are issued before they are added (in order).
+// rounded to FP16 (decoder layers) or BF16 (lm_head input).  One 256-thread
+// workgroup per row; thread i owns the 4-column chunks c = 4i + 1024j (j < 4,
+// so H <= 4096), and every load a thread needs -- its h and gain chunks, then
+// the partials four splits at a time -- is issued before any of them is used,
+// so a row costs one memory round trip and one block reduction.
 // OUT: 0 FP16, 1 BF16, 2 MXFP8 (x = e4m3 codes, xs = e8m0 of each 32 columns;
-// the 8 lanes holding one 32-column block share its exponent by shuffles).
+// the 8 threads holding one 32-column block share its exponent by shuffles).
 enum { kOutF16 = 0, kOutBF16 = 1, kOutMX8 = 2 };
 template <int OUT>
-__global__ __launch_bounds__(64) void norm_kernel(float *__restrict__ h, const float *__restrict__ part, int ns,
-                                                  const float *__restrict__ gain, int M, int H, float eps,
-                                                  void *__restrict__ x, uint8_t *__restrict__ xs,
-                                                  float *__restrict__ dump) {
-  constexpr int MAXC = 16;  // H <= 4096
-  const int m = blockIdx.x, lane = threadIdx.x;
+__global__ __launch_bounds__(256) void norm_kernel(float *__restrict__ h, const float *__restrict__ part, int ns,
+                                                   const float *__restrict__ gain, int M, int H, float eps,
+                                                   void *__restrict__ x, uint8_t *__restrict__ xs,
+                                                   float *__restrict__ dump) {
+  constexpr int MAXC = 4;
+  __shared__ float red[4];
+  const int m = blockIdx.x, tid = threadIdx.x;
   float *hr = h + (size_t)m * H;
+  const float *pr = part + (size_t)m * H;
   const size_t pstride = (size_t)M * H;
-  f32x4_t t[MAXC];
+  f32x4_t t[MAXC], gv[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = 4 * tid + 1024 * i;
+    if (c < H) {
+      t[i] = *reinterpret_cast<const f32x4_t *>(hr + c);
+      gv[i] = *reinterpret_cast<const f32x4_t *>(gain + c);
+    }
+  }
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {
+    f32x4_t p[4][MAXC];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = 4 * tid + 1024 * i;
+        if (c < H) p[q][i] = *reinterpret_cast<const f32x4_t *>(pr + (s + q) * pstride + c);
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i)
+        if (4 * tid + 1024 * i < H) t[i] += p[q][i];
+  }
+  for (; s < ns; ++s) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = 4 * tid + 1024 * i;
+      if (c < H) t[i] += *reinterpret_cast<const f32x4_t *>(pr + s * pstride + c);
+    }
+  }
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
-    const int c = lane * 4 + 256 * i;
-    if (c >= H) break;
-    t[i] = *reinterpret_cast<const f32x4_t *>(hr + c);
-    const float *pp = part + (size_t)m * H + c;
-    int s = 0;
-    for (; s + 4 <= ns; s += 4) {
-      const f32x4_t p0 = *reinterpret_cast<const f32x4_t *>(pp + (s + 0) * pstride);
-      const f32x4_t p1 = *reinterpret_cast<const f32x4_t *>(pp + (s + 1) * pstride);
-      const f32x4_t p2 = *reinterpret_cast<const f32x4_t *>(pp + (s + 2) * pstride);
-      const f32x4_t p3 = *reinterpret_cast<const f32x4_t *>(pp + (s + 3) * pstride);
-      t[i] += p0;
-      t[i] += p1;
-      t[i] += p2;
-      t[i] += p3;
+    const int c = 4 * tid + 1024 * i;
+    if (c < H) {
+      if (ns) *reinterpret_cast<f32x4_t *>(hr + c) = t[i];
+      ss += t[i][0] * t[i][0] + t[i][1] * t[i][1] + t[i][2] * t[i][2] + t[i][3] * t[i][3];
     }
-    for (; s < ns; ++s) t[i] += *reinterpret_cast<const f32x4_t *>(pp + s * pstride);
-    if (ns) *reinterpret_cast<f32x4_t *>(hr + c) = t[i];
-    ss += t[i][0] * t[i][0] + t[i][1] * t[i][1] + t[i][2] * t[i][2] + t[i][3] * t[i][3];
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  ss = (red[0] + red[1]) + (red[2] + red[3]);
   const float rs = 1.0f / sqrtf(ss / (float)H + eps);
 #pragma unroll
   for (int i = 0; i < MAXC; ++i) {
-    const int c = lane * 4 + 256 * i;
+    const int c = 4 * tid + 1024 * i;
     if (c >= H) break;
-    const f32x4_t gv = *reinterpret_cast<const f32x4_t *>(gain + c);
     if constexpr (OUT == kOutMX8) {
-      const f32x4_t y = f32x4_t{t[i][0] * rs * gv[0], t[i][1] * rs * gv[1], t[i][2] * rs * gv[2], t[i][3] * rs * gv[3]};
+      const f32x4_t y = f32x4_t{t[i][0] * rs * gv[i][0], t[i][1] * rs * gv[i][1], t[i][2] * rs * gv[i][2],
+                                t[i][3] * rs * gv[i][3]};
       uint32_t e8;
-      const uint32_t codes = mx8_quant4(y, e8);
+      const uint32_t codes = mx8_quant4(y, e8);  // the block's 8 threads are all active (H % 32 == 0)
       *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(x) + (size_t)m * H + c) = codes;
-      if ((lane & 7) == 0) xs[(size_t)m * (H / 32) + c / 32] = (uint8_t)e8;
+      if ((tid & 7) == 0) xs[(size_t)m * (H / 32) + c / 32] = (uint8_t)e8;
       if (dump) {
         const float sc = __builtin_ldexpf(1.f, (int)e8 - 127);
         const u32x2_t hv = fp8x4_to_f16x4(codes);
@@ -135,11 +160,11 @@ __global__ __launch_bounds__(64) void norm_kernel(float *__restrict__ h, const f
     }
     uint32_t lo, hi;
     if constexpr (OUT == kOutBF16) {
-      lo = pack_bf16x2(t[i][0] * rs * gv[0], t[i][1] * rs * gv[1]);
-      hi = pack_bf16x2(t[i][2] * rs * gv[2], t[i][3] * rs * gv[3]);
+      lo = pack_bf16x2(t[i][0] * rs * gv[i][0], t[i][1] * rs * gv[i][1]);
+      hi = pack_bf16x2(t[i][2] * rs * gv[i][2], t[i][3] * rs * gv[i][3]);
     } else {
-      lo = pack_f16x2(t[i][0] * rs * gv[0], t[i][1] * rs * gv[1]);
-      hi = pack_f16x2(t[i][2] * rs * gv[2], t[i][3] * rs * gv[3]);
+      lo = pack_f16x2(t[i][0] * rs * gv[i][0], t[i][1] * rs * gv[i][1]);
+      hi = pack_f16x2(t[i][2] * rs * gv[i][2], t[i][3] * rs * gv[i][3]);
     }
     *reinterpret_cast<u32x2_t *>(static_cast<uint16_t *>(x) + (size_t)m * H + c) = u32x2_t{lo, hi};
     if (dump) {
@@ -307,10 +332,10 @@ hipError_t launch_norm(float *h, const float *part, int nsplit, const float *gai
                        uint16_t *x, int out_bf16, float *dump, hipStream_t st) {
   if (H > 4096 || H % 4) return hipErrorInvalidValue;
   if (out_bf16)
-    hipLaunchKernelGGL(norm_kernel<kOutBF16>, dim3(M), dim3(64), 0, st, h, part, nsplit, gain, M, H, eps,
+    hipLaunchKernelGGL(norm_kernel<kOutBF16>, dim3(M), dim3(256), 0, st, h, part, nsplit, gain, M, H, eps,
                        (void *)x, (uint8_t *)nullptr, dump);
   else
-    hipLaunchKernelGGL(norm_kernel<kOutF16>, dim3(M), dim3(64), 0, st, h, part, nsplit, gain, M, H, eps,
+    hipLaunchKernelGGL(norm_kernel<kOutF16>, dim3(M), dim3(256), 0, st, h, part, nsplit, gain, M, H, eps,
                        (void *)x, (uint8_t *)nullptr, dump);
   return hipGetLastError();
 }
@@ -318,7 +343,7 @@ hipError_t launch_norm(float *h, const float *part, int nsplit, const float *gai
 hipError_t launch_norm_mx8(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
                            uint8_t *x8, uint8_t *xs, float *dump, hipStream_t st) {
   if (H > 4096 || H % 32) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(norm_kernel<kOutMX8>, dim3(M), dim3(64), 0, st, h, part, nsplit, gain, M, H, eps, (void *)x8,
+  hipLaunchKernelGGL(norm_kernel<kOutMX8>, dim3(M), dim3(256), 0, st, h, part, nsplit, gain, M, H, eps, (void *)x8,
                      xs, dump);
   return hipGetLastError();
 }
