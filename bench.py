@@ -241,6 +241,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--cpu-seqs", type=int, default=8)
+    ap.add_argument("--lanes", type=int, default=1, help="concurrent sequence ranges per pass (spec_verify_set_lanes)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the batch-1 decoding loops and the FP8-activation figure (for counter runs)")
@@ -274,7 +275,7 @@ def main():
     kv_layers = [W.synthetic_kv_layer(m, wl.seed, l, lens, wl.max_ctx) for l in range(m.n_layers)]
     log("upload")
     dev = DeviceModel(m, weights, max_batch=B, max_ctx=wl.max_ctx, kv_layers=kv_layers, kv_len=lens)
-    ver = Verifier(dev)
+    ver = Verifier(dev, lanes=args.lanes)
     torch.cuda.synchronize()
 
     # plant drafts from the pass's own greedy continuation: row j-1's argmax

@@ -50,6 +50,7 @@ EXPORTS = {
     "spec_verify_init": (_I, [ctypes.POINTER(SpecModelDesc), ctypes.POINTER(SpecWeights), ctypes.POINTER(SpecKV),
                               _P, ctypes.POINTER(_P)]),
     "spec_verify_block": (_I, [_P, _I, _P, _P, _P, _P, _P]),
+    "spec_verify_set_lanes": (_I, [_P, _I]),
     "spec_commit_kv": (_I, [_P, _I, _P, _P]),
     "spec_prefill": (_I, [_P, _I, _P, _I, _P, _P, _P, _P]),
     "spec_export_hidden": (_I, [_P, _I, _P, _P]),
@@ -216,7 +217,7 @@ class Verifier:
     """One spec_ctx bound to a DeviceModel.  act_fmt: "fp16" or "mxfp8" (the
     activation format of the QKV, gate/up and down projections)."""
 
-    def __init__(self, dev: DeviceModel, act_fmt: str = "fp16"):
+    def __init__(self, dev: DeviceModel, act_fmt: str = "fp16", lanes: int = 1):
         lib = load_library()
         self.dev = dev
         self._desc, self._arr, self._w, self._kv = dev.structs()
@@ -226,6 +227,12 @@ class Verifier:
                                     _stream(), ctypes.byref(h)), "spec_verify_init")
         self._h = h
         self._dump = (None, None)
+        if lanes != 1:
+            self.set_lanes(lanes)
+
+    def set_lanes(self, lanes: int):
+        """Run the batch as `lanes` concurrent sequence ranges (spec_verify_set_lanes)."""
+        _check(load_library().spec_verify_set_lanes(self._h, lanes), "spec_verify_set_lanes")
 
     def verify(self, tokens: torch.Tensor, accept_len=None, bonus=None, argmax="alloc"):
         """tokens int32 [B, 16] on the device.  Returns the output tensors."""

@@ -30,6 +30,20 @@ struct spec_ctx {
   // prefill scratch: chunk tokens [Mmax], argmax [Mmax], commit counts, tau, bonus [max_batch]
   int32_t *pf_tokens, *pf_argmax, *pf_ncommit, *pf_acc, *pf_bonus;
   float *dump_hidden, *dump_logits;
+  // Lanes: the batch is cut into contiguous sequence ranges, each run as a
+  // complete pass on its own stream (lane 0 on the caller's).  Row-indexed
+  // buffers are shared (a lane touches only its own rows); the split partials
+  // of attention and of the residual projections are per lane.
+  int lanes = 1;
+  struct LaneBufs {
+    float *part_o, *rpart;
+    float2 *part_ml;
+  };
+  LaneBufs lane_buf[SPEC_MAX_LANES] = {};
+  void *lane_ws = nullptr;                      // lanes 1.. (one allocation)
+  size_t lane_bytes[3] = {0, 0, 0};             // part_o, part_ml, rpart sizes of one lane
+  hipStream_t lane_st[SPEC_MAX_LANES] = {};     // [0] unused (the caller's stream)
+  hipEvent_t lane_ev[SPEC_MAX_LANES] = {};      // [0] fork, [i] join of lane i
   // launch timing of one kernel class (measurement hook)
   int prof_kind = SPEC_K_NONE;
   int prof_repeat = 1;         // back-to-back launches per timed launch (idempotent classes)
@@ -199,6 +213,10 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   c->a8 = (uint8_t *)(base + off[14]);
   c->as8 = c->a8 + Mm * I;
   c->dump_hidden = c->dump_logits = nullptr;
+  c->lane_buf[0] = spec_ctx::LaneBufs{c->part_o, c->rpart, c->part_ml};
+  c->lane_bytes[0] = sizes[5];
+  c->lane_bytes[1] = sizes[6];
+  c->lane_bytes[2] = sizes[12];
 
   // RoPE table: angle = p * theta^(-2i/D), in double, stored as fp32 (cos, sin)
   std::vector<float2> rope((size_t)kv->max_ctx * (D / 2));
@@ -220,23 +238,39 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   return SPEC_OK;
 }
 
-int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t *accept_len, int32_t *bonus,
-                      int32_t *argmax, hipStream_t st) {
-  if (!c || !tokens || !accept_len || !bonus) return SPEC_E_ARG;
-  if (batch < 1 || batch > c->kv.max_batch) return SPEC_E_ARG;
+}  // extern "C"
+
+// One complete pass for sequences b0 .. b0+batch-1 on stream st, with lane
+// `lane`'s split buffers: every sequence-indexed pointer is offset to b0 and
+// every row-indexed one to row 16*b0, so the kernels see sequences 0..batch-1.
+static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tokens, int32_t *accept_len,
+                    int32_t *bonus, int32_t *argmax, hipStream_t st) {
   const spec_model_desc &m = c->m;
   const int M = batch * 16, H = m.hidden, D = m.head_dim, Hq = m.n_q_heads, Hkv = m.n_kv_heads;
   const int I = m.intermediate, V = m.vocab, max_ctx = c->kv.max_ctx;
-  const KvLayout kvl = kv_layout(c->kv);
+  KvLayout kvl = kv_layout(c->kv);
   const size_t lstride = (kvl.pages ? (size_t)c->kv.num_pages * kvl.page_size : (size_t)c->kv.max_batch * max_ctx) *
                          Hkv * D;
+  // sequence offset b0: contiguous caches move their base, paged ones their page-table rows
+  size_t seq0 = 0;
+  if (kvl.pages) kvl.pages += (size_t)b0 * kvl.max_pages;
+  else seq0 = (size_t)b0 * Hkv * max_ctx * D;
+  const size_t r0 = (size_t)b0 * 16;
+  const int32_t *kv_len = c->kv.kv_len + b0;
+  float *h = c->h + r0 * H, *rpart = c->lane_buf[lane].rpart;
+  uint16_t *x = c->x + r0 * H, *q = c->q + r0 * Hq * D, *ao = c->ao + r0 * Hq * D, *act = c->act + r0 * I;
+  uint8_t *x8 = c->x8 + r0 * H, *xs8 = c->xs8 + r0 * (H / 32), *a8 = c->a8 + r0 * I, *as8 = c->as8 + r0 * (I / 32);
+  ArgmaxPart *amax = c->amax + r0 * lm_parts(V);
+  float *dump_hidden = c->dump_hidden ? c->dump_hidden + r0 * H : nullptr;
+  float *dump_logits = c->dump_logits ? c->dump_logits + r0 * V : nullptr;
+  int32_t *last_tau = c->last_tau + b0;
 
   AttnArgs aa{};
-  aa.q = c->q;
-  aa.kv_len = c->kv.kv_len;
-  aa.o = c->ao;
-  aa.part_o = c->part_o;
-  aa.part_ml = c->part_ml;
+  aa.q = q;
+  aa.kv_len = kv_len;
+  aa.o = ao;
+  aa.part_o = c->lane_buf[lane].part_o;
+  aa.part_ml = c->lane_buf[lane].part_ml;
   aa.batch = batch;
   aa.Hq = Hq;
   aa.Hkv = Hkv;
@@ -248,25 +282,25 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
   {
     Timed t(c, SPEC_K_EMBED, st);
     for (int r = 0; r < t.reps; ++r)
-      CK(launch_embed(tokens, M, H, V, c->embed, c->h, c->kv.kv_len, max_ctx, kvl, c->err, st));
+      CK(launch_embed(tokens, M, H, V, c->embed, h, kv_len, max_ctx, kvl, c->err, st));
   }
   const int ns_o = residual_nsplit(M, H, Hq * D), ns_d = residual_nsplit(M, H, I);
   const bool mx = m.act_fmt == SPEC_ACT_MXFP8;
-  const ActIn xin = mx ? ActIn{c->x8, c->xs8} : ActIn{c->x, nullptr};
-  const ActIn ain = mx ? ActIn{c->a8, c->as8} : ActIn{c->act, nullptr};
+  const ActIn xin = mx ? ActIn{x8, xs8} : ActIn{x, nullptr};
+  const ActIn ain = mx ? ActIn{a8, as8} : ActIn{act, nullptr};
   auto norm = [&](int nsplit, const float *gain) {
-    return mx ? launch_norm_mx8(c->h, c->rpart, nsplit, gain, M, H, m.rms_eps, c->x8, c->xs8, nullptr, st)
-              : launch_norm(c->h, c->rpart, nsplit, gain, M, H, m.rms_eps, c->x, 0, nullptr, st);
+    return mx ? launch_norm_mx8(h, rpart, nsplit, gain, M, H, m.rms_eps, x8, xs8, nullptr, st)
+              : launch_norm(h, rpart, nsplit, gain, M, H, m.rms_eps, x, 0, nullptr, st);
   };
   int pending = 0;  // splits of the last residual projection not yet added to h
   for (int l = 0; l < m.n_layers; ++l) {
     const spec_layer_weights &L = c->layers[l];
-    uint16_t *kc = c->kv.k_cache + l * lstride, *vc = c->kv.v_cache + l * lstride;
+    uint16_t *kc = c->kv.k_cache + l * lstride + seq0, *vc = c->kv.v_cache + l * lstride + seq0;
     {
       Timed t(c, SPEC_K_RMSNORM, st);
       CK(norm(pending, L.attn_norm));
     }
-    QkvOut qo{c->q, kc, vc, c->kv.kv_len, c->rope, Hq, Hkv, max_ctx, kvl};
+    QkvOut qo{q, kc, vc, kv_len, c->rope, Hq, Hkv, max_ctx, kvl};
     {
       Timed t(c, SPEC_K_QKV, st);
       for (int r = 0; r < t.reps; ++r)
@@ -287,7 +321,7 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     {
       Timed t(c, SPEC_K_OPROJ, st);
       for (int r = 0; r < t.reps; ++r)
-        CK(launch_residual_partial(ActIn{c->ao, nullptr}, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, c->rpart,
+        CK(launch_residual_partial(ActIn{ao, nullptr}, M, H, Hq * D, LinearW{L.w_o, L.s_o, SPEC_WFMT_FP8_E4M3_ROW}, rpart,
                                    st));
     }
     {
@@ -297,30 +331,82 @@ int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t
     {
       Timed t(c, SPEC_K_GATE_UP, st);
       for (int r = 0; r < t.reps; ++r)
-        CK(launch_swiglu(xin, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, mx ? (void *)c->a8 : c->act,
-                         mx ? c->as8 : nullptr, st));
+        CK(launch_swiglu(xin, M, H, I, LinearW{L.w_gate_up, L.s_gate_up, m.mlp_wfmt}, mx ? (void *)a8 : act,
+                         mx ? as8 : nullptr, st));
     }
     {
       Timed t(c, SPEC_K_DOWN, st);
       for (int r = 0; r < t.reps; ++r)
-        CK(launch_residual_partial(ain, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, c->rpart, st));
+        CK(launch_residual_partial(ain, M, H, I, LinearW{L.w_down, L.s_down, m.mlp_wfmt}, rpart, st));
     }
     pending = ns_d;
   }
   {
     Timed t(c, SPEC_K_RMSNORM, st);
-    CK(launch_norm(c->h, c->rpart, pending, c->final_norm, M, H, m.rms_eps, c->x, 1, c->dump_hidden, st));
+    CK(launch_norm(h, rpart, pending, c->final_norm, M, H, m.rms_eps, x, 1, dump_hidden, st));
   }
   {
     Timed t(c, SPEC_K_LM_HEAD, st);
     for (int r = 0; r < t.reps; ++r)
-      CK(launch_lm_argmax(c->x, M, V, H, c->lm_table, c->amax, c->dump_logits, st));
+      CK(launch_lm_argmax(x, M, V, H, c->lm_table, amax, dump_logits, st));
   }
   {
     Timed t(c, SPEC_K_ACCEPT, st);
     for (int r = 0; r < t.reps; ++r)
-      CK(launch_accept(c->amax, lm_parts(V), M, tokens, batch, accept_len, bonus, argmax, c->last_tau, st));
+      CK(launch_accept(amax, lm_parts(V), M, tokens, batch, accept_len, bonus, argmax, last_tau, st));
   }
+  return SPEC_OK;
+}
+
+extern "C" {
+
+int spec_verify_block(spec_ctx *c, int32_t batch, const int32_t *tokens, int32_t *accept_len, int32_t *bonus,
+                      int32_t *argmax, hipStream_t st) {
+  if (!c || !tokens || !accept_len || !bonus) return SPEC_E_ARG;
+  if (batch < 1 || batch > c->kv.max_batch) return SPEC_E_ARG;
+  // a timed kernel class is measured on one stream
+  const int nl = c->prof_kind != SPEC_K_NONE ? 1 : std::min<int>(c->lanes, batch);
+  if (nl == 1) return run_pass(c, 0, 0, batch, tokens, accept_len, bonus, argmax, st);
+  // fork: lanes 1.. wait for the caller's stream; join: the caller waits for them
+  CK(hipEventRecord(c->lane_ev[0], st));
+  for (int i = 1; i < nl; ++i) CK(hipStreamWaitEvent(c->lane_st[i], c->lane_ev[0], 0));
+  for (int i = 0; i < nl; ++i) {
+    const int b0 = batch * i / nl, b1 = batch * (i + 1) / nl;
+    const int rc = run_pass(c, i, b0, b1 - b0, tokens + 16 * b0, accept_len + b0, bonus + b0,
+                            argmax ? argmax + 16 * b0 : nullptr, i ? c->lane_st[i] : st);
+    if (rc != SPEC_OK) return rc;
+  }
+  for (int i = 1; i < nl; ++i) {
+    CK(hipEventRecord(c->lane_ev[i], c->lane_st[i]));
+    CK(hipStreamWaitEvent(st, c->lane_ev[i], 0));
+  }
+  return SPEC_OK;
+}
+
+int spec_verify_set_lanes(spec_ctx *c, int32_t lanes) {
+  if (!c || lanes < 1 || lanes > SPEC_MAX_LANES) return SPEC_E_ARG;
+  if (lanes > 1 && !c->lane_ws) {
+    size_t per = 0;
+    for (size_t b : c->lane_bytes) per += (b + 255) & ~(size_t)255;
+    void *ws = nullptr;
+    if (hipMalloc(&ws, per * (SPEC_MAX_LANES - 1)) != hipSuccess) return SPEC_E_NOMEM;
+    c->lane_ws = ws;
+    char *p = (char *)ws;
+    for (int i = 1; i < SPEC_MAX_LANES; ++i) {
+      spec_ctx::LaneBufs &lb = c->lane_buf[i];
+      lb.part_o = (float *)p;
+      p += (c->lane_bytes[0] + 255) & ~(size_t)255;
+      lb.part_ml = (float2 *)p;
+      p += (c->lane_bytes[1] + 255) & ~(size_t)255;
+      lb.rpart = (float *)p;
+      p += (c->lane_bytes[2] + 255) & ~(size_t)255;
+    }
+    for (int i = 1; i < SPEC_MAX_LANES; ++i)
+      if (hipStreamCreateWithFlags(&c->lane_st[i], hipStreamNonBlocking) != hipSuccess) return SPEC_E_HIP;
+    for (hipEvent_t &e : c->lane_ev)
+      if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) return SPEC_E_HIP;
+  }
+  c->lanes = lanes;
   return SPEC_OK;
 }
 
@@ -361,6 +447,11 @@ int spec_commit_kv(spec_ctx *c, int32_t batch, const int32_t *n_commit, hipStrea
 int spec_verify_destroy(spec_ctx *c) {
   if (!c) return SPEC_OK;
   for (hipEvent_t e : c->ev) (void)hipEventDestroy(e);
+  for (hipEvent_t e : c->lane_ev)
+    if (e) (void)hipEventDestroy(e);
+  for (hipStream_t s : c->lane_st)
+    if (s) (void)hipStreamDestroy(s);
+  if (c->lane_ws) (void)hipFree(c->lane_ws);
   const hipError_t e = hipFree(c->ws);
   delete c;
   return e == hipSuccess ? SPEC_OK : SPEC_E_HIP;

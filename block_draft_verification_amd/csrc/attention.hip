@@ -21,8 +21,11 @@
 // statistics therefore need one xor-32 shuffle, and the FP16 probabilities
 // are already the B operand of O^T = V^T P^T, whose 16-key slices use the
 // keys 16s + 4h + (0..3) and 16s + 8 + 4h + (0..3) of lane half h.  Online
-// softmax in fp32, base 2; rows that have seen no visible key yet use 0 as
-// their running maximum, so exp2(-inf) = 0 and nothing becomes NaN.
+// softmax in fp32, base 2, with a lazily moved reference: the reference only
+// follows the running maximum when a tile exceeds it by more than 2^8, so
+// most tiles skip the rescale of the accumulators.  Rows that have seen no
+// visible key yet use 0 as their reference, so exp2(-inf) = 0 and nothing
+// becomes NaN.
 //
 // Splits write unnormalised partials (m, l, o); a second kernel merges them
 // in split order per (query head, sequence), so the result does not depend on
@@ -32,6 +35,7 @@
 #include "kernels.h"
 
 #define KT 64  // keys per LDS tile
+#define RESCALE 8.f  // log2 headroom of the lazily moved softmax reference
 
 template <int D, int NW>  // NW = waves = ceil(G/2)
 __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_log2) {
@@ -143,44 +147,50 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
       for (int i = 0; i < DS; ++i)
         st[blk] = mfma32x32x16_f16(*reinterpret_cast<const u32x4_t *>(krow + 8 * i), qf[i], st[blk]);
     }
-    float tmax = -INFINITY;
-    if (kt0 + KT <= n && kt0 + KT <= key_hi) {  // whole tile in the committed prefix: nothing to mask
-#pragma unroll
-      for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          st[blk][v] *= scale_log2;
-          tmax = fmaxf(tmax, st[blk][v]);
-        }
-    } else {
+    if (!(kt0 + KT <= n && kt0 + KT <= key_hi)) {  // the tile reaches past the committed prefix: mask
       const int last_visible = min(n + j, key_hi - 1);
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int key = kt0 + 32 * blk + 8 * (v >> 2) + 4 * h + (v & 3);
-          const float x = key <= last_visible ? st[blk][v] * scale_log2 : -INFINITY;
-          st[blk][v] = x;
-          tmax = fmaxf(tmax, x);
+          st[blk][v] = key <= last_visible ? st[blk][v] : -INFINITY;
         }
     }
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float mnew = fmaxf(mrow, tmax);
-    const float mref = mnew == -INFINITY ? 0.f : mnew;
-    const float alpha = __builtin_amdgcn_exp2f(mrow - mref);
-    float psum = 0.f;
+    // tile maximum of the raw scores (a tree, not a 32-deep chain), both lane halves
+    float t[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) t[v] = fmaxf(st[0][v], st[1][v]);
+#pragma unroll
+    for (int w = 8; w > 0; w >>= 1)
+#pragma unroll
+      for (int v = 0; v < w; ++v) t[v] = fmaxf(t[v], t[v + w]);
+    const float tm = fmaxf(t[0], __shfl_xor(t[0], 32)) * scale_log2;
+    // Lazy rescaling: the reference maximum mrow only moves when a tile's
+    // maximum exceeds it by more than 2^RESCALE, so the probabilities stay
+    // <= 2^RESCALE (exact in FP16's range) and the accumulators are rescaled
+    // only on those rare tiles (a wave-uniform branch).
+    const bool need = tm > mrow + RESCALE;
+    if (__builtin_amdgcn_ballot_w64(need)) {
+      const float mnew = need ? tm : mrow;
+      const float alpha = need ? __builtin_amdgcn_exp2f(mrow - mnew) : 1.f;  // mrow = -inf gives 0
+      lrow *= alpha;
+      mrow = mnew;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    }
+    const float mref = mrow == -INFINITY ? 0.f : mrow;  // a row with no visible key yet: every p is 0
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        st[blk][v] = __builtin_amdgcn_exp2f(st[blk][v] - mref);
-        psum += st[blk][v];
-      }
-    psum += __shfl_xor(psum, 32);
-    mrow = mnew;
-    lrow = lrow * alpha + psum;
+      for (int v = 0; v < 16; ++v) st[blk][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[blk][v], scale_log2, -mref));
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) oacc[dt] *= alpha;
+    for (int v = 0; v < 16; ++v) t[v] = st[0][v] + st[1][v];
+#pragma unroll
+    for (int w = 8; w > 0; w >>= 1)
+#pragma unroll
+      for (int v = 0; v < w; ++v) t[v] += t[v + w];
+    lrow += t[0] + __shfl_xor(t[0], 32);
     // O^T += V^T P^T over 4 slices of 16 keys
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
@@ -240,6 +250,9 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
 // columns over the splits with independent loads.  A split that saw no key of
 // a row has m_s = -inf and weight 0 (its partial is 0, never NaN).
 #define MAX_SPLITS 64
+#ifndef ATTN_WG_TARGET
+#define ATTN_WG_TARGET 768
+#endif
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
@@ -283,7 +296,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 int attention_split_len(int batch, int Hkv, int max_ctx) {
   // aim for about 768 workgroups across the batch; splits are whole 64-key
   // tiles and a sequence has at most MAX_SPLITS of them
-  const long target = 768;
+  const long target = ATTN_WG_TARGET;
   long sl = ((long)batch * Hkv * max_ctx + target - 1) / target;
   const long min_sl = (max_ctx + MAX_SPLITS - 1) / MAX_SPLITS;
   if (sl < min_sl) sl = min_sl;

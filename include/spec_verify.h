@@ -216,6 +216,22 @@ int spec_verify_init(const spec_model_desc *model /*host*/, const spec_weights *
 int spec_verify_block(spec_ctx *ctx, int32_t batch, const int32_t *tokens, int32_t *accept_len,
                       int32_t *bonus, int32_t *argmax, hipStream_t stream);
 
+/* Lanes (a performance setting of the context; default 1).  With n > 1,
+ * spec_verify_block cuts the batch into n contiguous ranges of sequences
+ * (as equal as possible; fewer lanes when batch < n) and runs the complete
+ * pass of each range on its own internal HIP stream, forked from and joined
+ * back to the caller's stream with events: the call stays ordered on
+ * `stream`, and a graph capture of the call records the lanes as parallel
+ * branches, so the kernels of one lane fill the GPU while another waits.
+ * Each range is computed exactly as a pass over that range alone would be
+ * (the split-K and attention key splits follow the range's size), so
+ * results are deterministic for a given lane count and agree with one lane
+ * to rounding.  The first call with n > 1 allocates the per-lane split
+ * buffers for SPEC_MAX_LANES lanes and creates the streams (synchronous);
+ * later calls only set n.  SPEC_E_ARG for n outside [1, SPEC_MAX_LANES]. */
+#define SPEC_MAX_LANES 4
+int spec_verify_set_lanes(spec_ctx *ctx, int32_t lanes);
+
 /* Commit: kv_len[b] += n_commit[b] for b < batch, or += the tau of the last
  * verify when n_commit is NULL (the K/V rows are already in place; this is a
  * length bump, so a rejected suffix is rolled back by not counting it).

@@ -56,6 +56,7 @@ def test_host_side_argument_checks():
     assert lib.spec_debug_set_dump(None, None, None) == -1
     assert lib.spec_prefill(None, 1, 16, 16, 16, 16, None, None) == -1
     assert lib.spec_export_hidden(None, 1, 16, None) == -1
+    assert lib.spec_verify_set_lanes(None, 2) == -1
     m0 = B.SpecModelDesc(2, 4096 + 64, 4, 2, 64, 704, 1024, 1e-6, 1e4, 1, 1, 1)  # hidden > 4096
     w0 = B.SpecWeights((B.SpecLayerWeights * 2)(), 16, None, 16)
     kv0 = B.SpecKV(16, 16, 16, 1, 128)

@@ -182,3 +182,44 @@ def test_batch_bounds_rejected():
     with pytest.raises(Exception):
         ver.verify(torch.zeros(2, 16, dtype=torch.int32, device="cuda"))   # batch > max_batch
     ver.close()
+
+
+def test_lanes_parity_and_graph_replay():
+    """spec_verify_set_lanes: a batch of 7 ragged sequences cut into 2 and 3
+    concurrent ranges meets the same oracle parity rule as one lane; a captured
+    graph of verify + commit with 3 lanes replays to the eager outputs."""
+    case = build_case("0.5b-fp8-b32-ctx512to4096", batch=7)
+    ref, _ = oracle_verify(case)
+    dev, ver = gpu_setup(case)
+    B = len(case.lens)
+    for lanes in (2, 3):
+        ver.set_lanes(lanes)
+        got = gpu_verify(ver, case)
+        log(f"lanes {lanes}: {compare(ref, got, case.blocks)}")
+    tokens = torch.from_numpy(case.blocks).cuda()
+    eager = ver.verify(tokens)
+    torch.cuda.synchronize()
+    outs = {k: torch.empty(B, dtype=torch.int32, device="cuda") for k in ("tau", "bonus")}
+    amax = torch.empty(B, 16, dtype=torch.int32, device="cuda")
+    kv0 = dev.kv_len.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ver.verify(tokens, outs["tau"], outs["bonus"], amax)
+        ver.commit(B)
+    torch.cuda.current_stream().wait_stream(s)
+    dev.kv_len.copy_(kv0)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ver.verify(tokens, outs["tau"], outs["bonus"], amax)
+        ver.commit(B)
+    for rep in range(3):
+        dev.kv_len.copy_(kv0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs["tau"], eager["accept_len"]) and torch.equal(outs["bonus"], eager["bonus"])
+        assert torch.equal(amax, eager["argmax"])
+        assert torch.equal(dev.kv_len[:B], kv0[:B] + eager["accept_len"])
+    assert ver.device_error() == 0
+    ver.close()
