@@ -12,7 +12,8 @@
 // G are padding and never stored).  The split's keys are walked in tiles of
 // 64: the next tile's K/V is loaded into registers while the current one is
 // computed, converted from the BF16 cache to FP16 and stored in LDS (K
-// row-major, V transposed; two LDS buffers, one barrier per tile).
+// row-major, V transposed with swizzled columns; two LDS buffers, one barrier
+// per tile).
 //
 // MFMA v_mfma_f32_32x32x16_f16.  Scores are computed transposed, S^T = K Q^T,
 // 32 keys x 32 queries per block: lane (c, h) supplies key c (A) and query c
@@ -37,12 +38,18 @@
 #define KT 64  // keys per LDS tile
 #define RESCALE 8.f  // log2 headroom of the lazily moved softmax reference
 
+// V^T tile in LDS: key k of row d sits at column k ^ vsw(d).  The XOR moves
+// whole 4-key groups (so key pairs and the 4-key pieces the MFMA reads stay
+// contiguous) and makes the transposing stores free of bank conflicts (the
+// operand reads stay at the 2-way minimum of 8-byte accesses).
+__device__ __forceinline__ int vsw(int d) { return 4 * ((d ^ (d >> 2)) & 15); }
+
 template <int D, int NW>  // NW = waves = ceil(G/2)
 __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_log2) {
   constexpr int DS = D / 16;           // S MFMAs per 32-key block (k = 16 each)
   constexpr int DT = D / 32;           // 32-wide d tiles of O^T
   constexpr int KP = D + 8;            // K row pitch (16-bit elements): rows land on distinct bank groups
-  constexpr int VP = KT + 4;           // V^T row pitch (16-bit elements), rows 8-byte aligned
+  constexpr int VP = KT;               // V^T row pitch (16-bit elements); columns swizzled by vsw()
   constexpr int KCH = KT * D / 8;      // K: 16-byte chunks (one key, 8 d) per tile
   constexpr int VCH = KT * D / 8;      // V: chunks of (2 keys, 4 d)
   __shared__ __align__(16) uint16_t Ks[2][KT * KP];
@@ -126,10 +133,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
       const uint32_t b0 = bf16x2_to_f16x2(tr.v[i][1].x), b1 = bf16x2_to_f16x2(tr.v[i][1].y);
       // (key kk, key kk+1) pairs for d0 .. d0+3
       uint16_t *vt = &Vt[buf][0];
-      *reinterpret_cast<uint32_t *>(&vt[(d0 + 0) * VP + kk]) = (a0 & 0xffff) | (b0 << 16);
-      *reinterpret_cast<uint32_t *>(&vt[(d0 + 1) * VP + kk]) = (a0 >> 16) | (b0 & 0xffff0000u);
-      *reinterpret_cast<uint32_t *>(&vt[(d0 + 2) * VP + kk]) = (a1 & 0xffff) | (b1 << 16);
-      *reinterpret_cast<uint32_t *>(&vt[(d0 + 3) * VP + kk]) = (a1 >> 16) | (b1 & 0xffff0000u);
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 0) * VP + (kk ^ vsw(d0 + 0))]) = (a0 & 0xffff) | (b0 << 16);
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 1) * VP + (kk ^ vsw(d0 + 1))]) = (a0 >> 16) | (b0 & 0xffff0000u);
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 2) * VP + (kk ^ vsw(d0 + 2))]) = (a1 & 0xffff) | (b1 << 16);
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 3) * VP + (kk ^ vsw(d0 + 3))]) = (a1 >> 16) | (b1 & 0xffff0000u);
     }
   };
 
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
     for (int w = 8; w > 0; w >>= 1)
 #pragma unroll
       for (int v = 0; v < w; ++v) t[v] = fmaxf(t[v], t[v + w]);
-    const float tm = fmaxf(t[0], __shfl_xor(t[0], 32)) * scale_log2;
+    const float tm = halves_max(t[0]) * scale_log2;
     // Lazy rescaling: the reference maximum mrow only moves when a tile's
     // maximum exceeds it by more than 2^RESCALE, so the probabilities stay
     // <= 2^RESCALE (exact in FP16's range) and the accumulators are rescaled
@@ -190,7 +197,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
     for (int w = 8; w > 0; w >>= 1)
 #pragma unroll
       for (int v = 0; v < w; ++v) t[v] += t[v + w];
-    lrow += t[0] + __shfl_xor(t[0], 32);
+    lrow += halves_sum(t[0]);
     // O^T += V^T P^T over 4 slices of 16 keys
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
@@ -201,9 +208,10 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
                                  pack_f16x2(st[blk][4 * q0 + 6], st[blk][4 * q0 + 7])};
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
-        const uint16_t *vrow = vt + (32 * dt + c) * VP + 16 * sl + 4 * h;
-        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow);
-        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + 8);
+        const int d = 32 * dt + c, sw = vsw(d);
+        const uint16_t *vrow = vt + d * VP;
+        const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow + ((16 * sl + 4 * h) ^ sw));
+        const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + ((16 * sl + 8 + 4 * h) ^ sw));
         oacc[dt] = mfma32x32x16_f16(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb, oacc[dt]);
       }
     }

@@ -154,6 +154,18 @@ __device__ __forceinline__ void set_error(int32_t *err, int32_t bit) {
   if (err) atomicOr(err, bit);
 }
 
+// max / sum of x over lanes l and l ^ 32 (the two halves of the wave), in
+// every lane: v_permlane32_swap exchanges the halves of its two operands, so
+// with x in both, the two results hold x[l] and x[l ^ 32] in every lane.
+__device__ __forceinline__ float halves_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float halves_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // argmax pair ordering: larger value wins, lower index on equal values.
 __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi) {
   return (v > bv) | ((v == bv) & (i < bi));  // bitwise: no short-circuit branches
