@@ -153,7 +153,7 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   c->Mmax = kv->max_batch * 16;
   int units = 0;
   for (int b = 1; b <= kv->max_batch; ++b) {
-    const int u = b * Hkv * attn_nsplit(attention_split_len(b, Hkv, kv->max_ctx), kv->max_ctx);
+    const int u = b * Hkv * attn_nsplit(attention_split_len(b, Hkv, kv->max_ctx, D), kv->max_ctx);
     if (u > units) units = u;
   }
   c->part_units = units;
@@ -276,7 +276,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
   aa.Hkv = Hkv;
   aa.max_ctx = max_ctx;
   aa.kvl = kvl;
-  aa.split_len = attention_split_len(batch, Hkv, max_ctx);
+  aa.split_len = attention_split_len(batch, Hkv, max_ctx, D);
   aa.nsplit = attn_nsplit(aa.split_len, max_ctx);
 
   {
@@ -599,7 +599,7 @@ int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int3
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.max_ctx = max_ctx;
-  a.split_len = split_len ? split_len : attention_split_len(batch, Hkv, max_ctx);
+  a.split_len = split_len ? split_len : attention_split_len(batch, Hkv, max_ctx, D);
   a.nsplit = attn_nsplit(a.split_len, max_ctx);
   if (a.nsplit > 64) return SPEC_E_ARG;  // the merge step holds at most 64 splits per sequence
   const size_t units = (size_t)batch * Hkv * a.nsplit, R = (size_t)(Hq / Hkv) * 16;

@@ -37,6 +37,12 @@
 
 #define KT 64  // keys per LDS tile
 #define RESCALE 8.f  // log2 headroom of the lazily moved softmax reference
+#ifndef ATTN_TEAMS
+#define ATTN_TEAMS 2  // wave groups per workgroup splitting a split's key tiles
+#endif
+#ifndef ATTN_NR
+#define ATTN_NR 2  // K/V tiles in flight in registers
+#endif
 
 // V^T tile in LDS: key k of row d sits at column k ^ vsw(d).  The XOR moves
 // whole 4-key groups (so key pairs and the 4-key pieces the MFMA reads stay
@@ -44,16 +50,19 @@
 // operand reads stay at the 2-way minimum of 8-byte accesses).
 __device__ __forceinline__ int vsw(int d) { return 4 * ((d ^ (d >> 2)) & 15); }
 
-template <int D, int NW>  // NW = waves = ceil(G/2)
-__global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_log2) {
+// LDS of one team: two K tiles and two V^T tiles (16-bit elements)
+template <int D>
+constexpr int attn_team_halfs() { return 2 * KT * (D + 8) + 2 * D * KT; }
+
+template <int D, int NW, int NTEAM, int NR = ATTN_NR>  // NW = waves per team = ceil(G/2)
+__global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float scale_log2) {
   constexpr int DS = D / 16;           // S MFMAs per 32-key block (k = 16 each)
   constexpr int DT = D / 32;           // 32-wide d tiles of O^T
   constexpr int KP = D + 8;            // K row pitch (16-bit elements): rows land on distinct bank groups
   constexpr int VP = KT;               // V^T row pitch (16-bit elements); columns swizzled by vsw()
   constexpr int KCH = KT * D / 8;      // K: 16-byte chunks (one key, 8 d) per tile
   constexpr int VCH = KT * D / 8;      // V: chunks of (2 keys, 4 d)
-  __shared__ __align__(16) uint16_t Ks[2][KT * KP];
-  __shared__ __align__(16) uint16_t Vt[2][D * VP];
+  extern __shared__ __align__(16) uint16_t attn_lds[];  // NTEAM x attn_team_halfs<D>()
 
   const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int G = a.Hq / a.Hkv;
@@ -63,9 +72,15 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
   if (sp >= nsplit) return;  // whole workgroup
   const int key_lo = sp * a.split_len, key_hi = min(key_lo + a.split_len, L);
 
-  constexpr int T = 64 * NW;
-  const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, h = lane >> 5;
+  constexpr int T = 64 * NW;  // threads per team
+  // Teams: NTEAM groups of NW waves walk alternate key tiles of the split
+  // (tile i of the split goes to team i % NTEAM), each with its own LDS tiles,
+  // and combine their softmax states through LDS at the end, so the split
+  // still leaves one partial.  tid, lane and wave below are team-local.
+  const int team = threadIdx.x / T, tid = threadIdx.x % T, lane = tid & 63, c = lane & 31, h = lane >> 5;
   const int wave = tid >> 6;
+  uint16_t *const Ks = attn_lds + team * attn_team_halfs<D>();  // [2][KT * KP]
+  uint16_t *const Vt = Ks + 2 * KT * KP;                         // [2][D * VP]
   const size_t unit = (size_t)b * a.Hkv + kvh;
 
   // this wave's queries: lane (c, h) -> head 2*wave + c/16 of the group, block row c%16
@@ -95,7 +110,6 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
     u32x4_t k[KPT];
     u32x2_t v[VPT][2];
   };
-  TileRegs ra, rb;
   auto load_tile = [&](TileRegs &tr, int kt0) {
     const int tb = min(kt0, (key_hi - 1) & ~(KT - 1));
     bool ok;
@@ -122,7 +136,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
       const int ch = tid + T * i, kk = ch / (D / 8), d0 = (ch % (D / 8)) * 8;
       if (KCH % T != 0 && ch >= KCH) break;  // NW = 3: the last round is partial
       const u32x4_t v = tr.k[i];
-      *reinterpret_cast<u32x4_t *>(&Ks[buf][kk * KP + d0]) =
+      *reinterpret_cast<u32x4_t *>(Ks + buf * KT * KP + kk * KP + d0) =
           u32x4_t{bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w)};
     }
 #pragma unroll
@@ -132,7 +146,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
       const uint32_t a0 = bf16x2_to_f16x2(tr.v[i][0].x), a1 = bf16x2_to_f16x2(tr.v[i][0].y);
       const uint32_t b0 = bf16x2_to_f16x2(tr.v[i][1].x), b1 = bf16x2_to_f16x2(tr.v[i][1].y);
       // (key kk, key kk+1) pairs for d0 .. d0+3
-      uint16_t *vt = &Vt[buf][0];
+      uint16_t *vt = Vt + buf * D * VP;
       *reinterpret_cast<uint32_t *>(&vt[(d0 + 0) * VP + (kk ^ vsw(d0 + 0))]) = (a0 & 0xffff) | (b0 << 16);
       *reinterpret_cast<uint32_t *>(&vt[(d0 + 1) * VP + (kk ^ vsw(d0 + 1))]) = (a0 >> 16) | (b0 & 0xffff0000u);
       *reinterpret_cast<uint32_t *>(&vt[(d0 + 2) * VP + (kk ^ vsw(d0 + 2))]) = (a1 & 0xffff) | (b1 << 16);
@@ -141,8 +155,8 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
   };
 
   auto compute = [&](int kt0, int buf) {
-    const uint16_t *ks = &Ks[buf][0];
-    const uint16_t *vt = &Vt[buf][0];
+    const uint16_t *ks = Ks + buf * KT * KP;
+    const uint16_t *vt = Vt + buf * D * VP;
     // S^T for the tile's two 32-key blocks
     f32x16_t st[2];
 #pragma unroll
@@ -217,24 +231,59 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
     }
   };
 
-  // Tile t is computed from LDS buffer t&1 while tiles t+1 and t+2 are in
-  // flight in two register sets (the loop is unrolled by two so the sets have
-  // fixed names).  The barrier at each step makes tile t visible and frees
+  // Tile t is computed from LDS buffer t&1 while tiles t+1 .. t+NR are in
+  // flight in NR register sets (the loop is unrolled by NR so every set has a
+  // fixed name).  The barrier at each step makes tile t visible and frees
   // buffer (t+1)&1.  Loads and stores past the split end are unconditional
   // (clamped keys into a buffer nobody reads) so the body does not branch.
-  load_tile(ra, key_lo);
-  load_tile(rb, key_lo + KT);
-  store_tile(ra, 0);
-  load_tile(ra, key_lo + 2 * KT);
-  for (int kt0 = key_lo; kt0 < key_hi; kt0 += 2 * KT) {
+  auto tile_key = [&](int ti) { return key_lo + (ti * NTEAM + team) * KT; };  // the team's ti-th tile
+  const int ntiles = (key_hi - key_lo + KT - 1) / KT, nteam = (ntiles + NTEAM - 1) / NTEAM;  // same for every team
+  TileRegs rr[NR];
+#pragma unroll
+  for (int i = 0; i < NR; ++i) load_tile(rr[i], tile_key(i));
+  store_tile(rr[0], 0);
+  load_tile(rr[0], tile_key(NR));
+  for (int ti0 = 0; ti0 < nteam; ti0 += NR) {
+#pragma unroll
+    for (int ph = 0; ph < NR; ++ph) {
+      const int ti = ti0 + ph, par = ti & 1, t0 = tile_key(ti);
+      lds_barrier();
+      store_tile(rr[(ph + 1) % NR], par ^ 1);
+      load_tile(rr[(ph + 1) % NR], tile_key(ti + NR + 1));
+      if (t0 < key_hi) compute(t0, par);
+    }
+  }
+  if constexpr (NTEAM > 1) {
+    // teams 1.. leave (m, l, o) in their own LDS (lane-contiguous, same lane
+    // layout as team 0's registers); team 0 folds them in team order
+    constexpr int NV = DT * 16 + 2;
+    static_assert(NV * NW * 64 * 4 <= attn_team_halfs<D>() * 2, "team state fits the team's LDS");
+    lds_barrier();  // every team is done with its tiles
+    float *mine = reinterpret_cast<float *>(Ks) + wave * NV * 64 + lane;
+    if (team > 0) {
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mine[(dt * 16 + v) * 64] = oacc[dt][v];
+      mine[DT * 16 * 64] = mrow;
+      mine[(DT * 16 + 1) * 64] = lrow;
+    }
     lds_barrier();
-    store_tile(rb, 1);
-    load_tile(rb, kt0 + 3 * KT);
-    compute(kt0, 0);
-    lds_barrier();
-    store_tile(ra, 0);
-    load_tile(ra, kt0 + 4 * KT);
-    if (kt0 + KT < key_hi) compute(kt0 + KT, 1);
+    if (team > 0) return;
+#pragma unroll
+    for (int tm = 1; tm < NTEAM; ++tm) {
+      const float *o = reinterpret_cast<const float *>(attn_lds + tm * attn_team_halfs<D>()) + wave * NV * 64 + lane;
+      const float m1 = o[DT * 16 * 64], l1 = o[(DT * 16 + 1) * 64];
+      const float mx = fmaxf(mrow, m1);
+      if (mx == -INFINITY) continue;  // neither team saw a visible key of this row
+      const float a0 = __builtin_amdgcn_exp2f(mrow - mx), a1 = __builtin_amdgcn_exp2f(m1 - mx);  // -inf gives 0
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) oacc[dt][v] = oacc[dt][v] * a0 + o[(dt * 16 + v) * 64] * a1;
+      lrow = lrow * a0 + l1 * a1;
+      mrow = mx;
+    }
   }
 
   // partials: group row R = head*16 + j = 32*wave + c; lane (c, h) holds d = 32dt + 8q + 4h + (0..3)
@@ -259,7 +308,7 @@ __global__ __launch_bounds__(64 * NW) void attn_kernel(AttnArgs a, float scale_l
 // a row has m_s = -inf and weight 0 (its partial is 0, never NaN).
 #define MAX_SPLITS 64
 #ifndef ATTN_WG_TARGET
-#define ATTN_WG_TARGET 768
+#define ATTN_WG_TARGET 256
 #endif
 
 template <int D>
@@ -301,10 +350,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   }
 }
 
-int attention_split_len(int batch, int Hkv, int max_ctx) {
-  // aim for about 768 workgroups across the batch; splits are whole 64-key
-  // tiles and a sequence has at most MAX_SPLITS of them
-  const long target = ATTN_WG_TARGET;
+// teams per workgroup: two for head_dim 64; one for 128, whose per-wave state
+// would not fit the registers of a second team without spilling
+static int attn_teams(int D) { return D == 64 ? ATTN_TEAMS : 1; }
+
+int attention_split_len(int batch, int Hkv, int max_ctx, int D) {
+  // Aim for about ATTN_WG_TARGET workgroups (with full contexts) across the
+  // batch when two teams share a split, 768 with one; measured on the
+  // 32-sequence 0.5B workload, fewer and longer splits win once a workgroup
+  // holds two teams.  Splits are whole 64-key tiles and a sequence has at
+  // most MAX_SPLITS of them.
+  const long target = attn_teams(D) > 1 ? ATTN_WG_TARGET : 768;
   long sl = ((long)batch * Hkv * max_ctx + target - 1) / target;
   const long min_sl = (max_ctx + MAX_SPLITS - 1) / MAX_SPLITS;
   if (sl < min_sl) sl = min_sl;
@@ -313,31 +369,39 @@ int attention_split_len(int batch, int Hkv, int max_ctx) {
   return (int)sl;
 }
 
+template <int D, int NW, int NTEAM>
+static hipError_t go_attn(const AttnArgs &a, dim3 grid, float sc, hipStream_t st) {
+  const int lds = NTEAM * attn_team_halfs<D>() * 2;
+  static const hipError_t attr =  // once per instantiation: allow more than 64 KB of LDS
+      hipFuncSetAttribute((const void *)attn_kernel<D, NW, NTEAM>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((attn_kernel<D, NW, NTEAM>), grid, dim3(64 * NW * NTEAM), lds, st, a, sc);
+  return hipGetLastError();
+}
+
 hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   if (G < 1 || G > 8) return hipErrorInvalidValue;
   const int nw = (G + 1) / 2;
-  dim3 grid(a.nsplit, a.Hkv, a.batch), block(64 * nw);
+  const dim3 grid(a.nsplit, a.Hkv, a.batch);
   if (D == 64) {
     const float sc = (float)(1.4426950408889634 / 8.0);
     switch (nw) {
-      case 1: hipLaunchKernelGGL((attn_kernel<64, 1>), grid, block, 0, st, a, sc); break;
-      case 2: hipLaunchKernelGGL((attn_kernel<64, 2>), grid, block, 0, st, a, sc); break;
-      case 3: hipLaunchKernelGGL((attn_kernel<64, 3>), grid, block, 0, st, a, sc); break;
-      default: hipLaunchKernelGGL((attn_kernel<64, 4>), grid, block, 0, st, a, sc); break;
+      case 1: return go_attn<64, 1, ATTN_TEAMS>(a, grid, sc, st);
+      case 2: return go_attn<64, 2, ATTN_TEAMS>(a, grid, sc, st);
+      case 3: return go_attn<64, 3, ATTN_TEAMS>(a, grid, sc, st);
+      default: return go_attn<64, 4, ATTN_TEAMS>(a, grid, sc, st);
     }
   } else if (D == 128) {
     const float sc = (float)(1.4426950408889634 / 11.313708498984761);
     switch (nw) {
-      case 1: hipLaunchKernelGGL((attn_kernel<128, 1>), grid, block, 0, st, a, sc); break;
-      case 2: hipLaunchKernelGGL((attn_kernel<128, 2>), grid, block, 0, st, a, sc); break;
-      case 3: hipLaunchKernelGGL((attn_kernel<128, 3>), grid, block, 0, st, a, sc); break;
-      default: hipLaunchKernelGGL((attn_kernel<128, 4>), grid, block, 0, st, a, sc); break;
+      case 1: return go_attn<128, 1, 1>(a, grid, sc, st);
+      case 2: return go_attn<128, 2, 1>(a, grid, sc, st);
+      case 3: return go_attn<128, 3, 1>(a, grid, sc, st);
+      default: return go_attn<128, 4, 1>(a, grid, sc, st);
     }
-  } else {
-    return hipErrorInvalidValue;
   }
-  return hipGetLastError();
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_attention_merge(const AttnArgs &a, int D, hipStream_t st) {

@@ -107,7 +107,7 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs &a, int D, hipStream_t st);  // splits, then merge
 hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st);
 hipError_t launch_attention_merge(const AttnArgs &a, int D, hipStream_t st);
-int attention_split_len(int batch, int Hkv, int max_ctx);
+int attention_split_len(int batch, int Hkv, int max_ctx, int D);
 
 // ---- small kernels ----
 // table: the tile-major BF16 embedding [V][H]
