@@ -210,8 +210,8 @@ def time_graph(ver, dev, tok, kv0, steps, warmup):
 def kernel_times(ver, dev, tok, kv0, kinds, reps, repeat=REPEAT):
     """Per kernel class: launch durations over `reps` eager passes, events on
     the stream; every launch of the timed class is issued `repeat` times back
-    to back between its two events (the RMSNorm class, which updates h in
-    place, once), so the events' own cost is shared."""
+    to back between its two events (commit, which updates kv_len in place,
+    once), so the events' own cost is shared."""
     import torch
     B = tok.shape[0]
     acc = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -226,7 +226,7 @@ def kernel_times(ver, dev, tok, kv0, kinds, reps, repeat=REPEAT):
             ver.commit(B)
         ver.time_kernel(None)
         tot, n = ver.kernel_time()
-        r = 1 if k in ("rmsnorm", "commit") else repeat
+        r = 1 if k == "commit" else repeat
         per_kind[k] = {"ms_per_pass": tot / reps / r, "us_per_launch": 1000 * tot / max(n, 1),
                        "launches_per_pass": n // (reps * r), "back_to_back": r}
     ver.set_repeat(1)

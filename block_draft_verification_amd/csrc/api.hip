@@ -18,7 +18,7 @@ struct spec_ctx {
   int Mmax, part_units;  // part_units: (sequence, kv head, split) slots for attention partials
   // workspace (one allocation)
   void *ws;
-  float *h;
+  float *h, *h2;  // residual stream, ping-ponged by the RMSNorm steps
   uint16_t *x, *q, *ao, *act;
   uint8_t *x8, *xs8, *a8, *as8;  // MXFP8 activations: normed x [Mmax][H] (+ e8m0 [Mmax][H/32]), SwiGLU [Mmax][I]
   float *part_o;
@@ -55,8 +55,8 @@ static const size_t kMaxTimedLaunches = 8192;
 
 // Brackets one launch with events when its class is being timed; `reps` is
 // how many times the call site issues it (the class's repeat count while it
-// is timed, else 1).  Classes whose kernel updates its own input in place
-// (the RMSNorm step adds the split partials into h; commit) are never repeated.
+// is timed, else 1).  Commit, which updates its own input in place, is never
+// repeated.
 struct Timed {
   spec_ctx *c;
   hipStream_t st;
@@ -65,7 +65,7 @@ struct Timed {
   Timed(spec_ctx *c_, int kind, hipStream_t s) : c(c_), st(s), on(false), reps(1) {
     if (c->prof_kind != kind || c->ev_used + 2 > c->ev.size()) return;
     on = hipEventRecord(c->ev[c->ev_used], st) == hipSuccess;
-    if (on && kind != SPEC_K_RMSNORM && kind != SPEC_K_COMMIT) reps = c->prof_repeat;
+    if (on && kind != SPEC_K_COMMIT) reps = c->prof_repeat;
   }
   ~Timed() {
     if (!on) return;
@@ -165,7 +165,7 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   }
 
   const size_t Mm = c->Mmax;
-  size_t sizes[] = {Mm * H * 4,                      // h
+  size_t sizes[] = {2 * Mm * H * 4,                  // h, h2
                     Mm * H * 2,                      // x
                     Mm * Hq * D * 2,                 // q
                     Mm * Hq * D * 2,                 // ao
@@ -192,6 +192,7 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   }
   char *base = (char *)c->ws;
   c->h = (float *)(base + off[0]);
+  c->h2 = c->h + Mm * H;
   c->x = (uint16_t *)(base + off[1]);
   c->q = (uint16_t *)(base + off[2]);
   c->ao = (uint16_t *)(base + off[3]);
@@ -257,7 +258,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
   else seq0 = (size_t)b0 * Hkv * max_ctx * D;
   const size_t r0 = (size_t)b0 * 16;
   const int32_t *kv_len = c->kv.kv_len + b0;
-  float *h = c->h + r0 * H, *rpart = c->lane_buf[lane].rpart;
+  float *h = c->h + r0 * H, *h2 = c->h2 + r0 * H, *rpart = c->lane_buf[lane].rpart;
   uint16_t *x = c->x + r0 * H, *q = c->q + r0 * Hq * D, *ao = c->ao + r0 * Hq * D, *act = c->act + r0 * I;
   uint8_t *x8 = c->x8 + r0 * H, *xs8 = c->xs8 + r0 * (H / 32), *a8 = c->a8 + r0 * I, *as8 = c->as8 + r0 * (I / 32);
   ArgmaxPart *amax = c->amax + r0 * lm_parts(V);
@@ -288,9 +289,13 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
   const bool mx = m.act_fmt == SPEC_ACT_MXFP8;
   const ActIn xin = mx ? ActIn{x8, xs8} : ActIn{x, nullptr};
   const ActIn ain = mx ? ActIn{a8, as8} : ActIn{act, nullptr};
+  // Each RMSNorm step reads the residual stream from one buffer and writes the
+  // updated stream to the other (h, h2 alternate), so it can be repeated.
   auto norm = [&](int nsplit, const float *gain) {
-    return mx ? launch_norm_mx8(h, rpart, nsplit, gain, M, H, m.rms_eps, x8, xs8, nullptr, st)
-              : launch_norm(h, rpart, nsplit, gain, M, H, m.rms_eps, x, 0, nullptr, st);
+    const hipError_t e = mx ? launch_norm_mx8(h, h2, rpart, nsplit, gain, M, H, m.rms_eps, x8, xs8, nullptr, st)
+                            : launch_norm(h, h2, rpart, nsplit, gain, M, H, m.rms_eps, x, 0, nullptr, st);
+    std::swap(h, h2);
+    return e;
   };
   int pending = 0;  // splits of the last residual projection not yet added to h
   for (int l = 0; l < m.n_layers; ++l) {
@@ -298,6 +303,10 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
     uint16_t *kc = c->kv.k_cache + l * lstride + seq0, *vc = c->kv.v_cache + l * lstride + seq0;
     {
       Timed t(c, SPEC_K_RMSNORM, st);
+      for (int r = 0; r + 1 < t.reps; ++r) {  // repeats recompute the same output from the same input
+        CK(norm(pending, L.attn_norm));
+        std::swap(h, h2);
+      }
       CK(norm(pending, L.attn_norm));
     }
     QkvOut qo{q, kc, vc, kv_len, c->rope, Hq, Hkv, max_ctx, kvl};
@@ -326,6 +335,10 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
     }
     {
       Timed t(c, SPEC_K_RMSNORM, st);
+      for (int r = 0; r + 1 < t.reps; ++r) {  // repeats recompute the same output from the same input
+        CK(norm(ns_o, L.mlp_norm));
+        std::swap(h, h2);
+      }
       CK(norm(ns_o, L.mlp_norm));
     }
     {
@@ -343,7 +356,8 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
   }
   {
     Timed t(c, SPEC_K_RMSNORM, st);
-    CK(launch_norm(h, rpart, pending, c->final_norm, M, H, m.rms_eps, x, 1, dump_hidden, st));
+    for (int r = 0; r < t.reps; ++r)
+      CK(launch_norm(h, nullptr, rpart, pending, c->final_norm, M, H, m.rms_eps, x, 1, dump_hidden, st));
   }
   {
     Timed t(c, SPEC_K_LM_HEAD, st);
@@ -544,10 +558,10 @@ int spec_debug_rmsnorm(int32_t M, int32_t H, const float *h, const float *gain, 
   if (M < 1 || H < 32 || H > 4096 || H % 32 || !h || !gain || !x || !(eps > 0.f)) return SPEC_E_ARG;
   if (!aligned16(h) || !aligned16(gain) || !aligned16(x)) return SPEC_E_ARG;
   if (act_fmt == SPEC_ACT_FP16) {
-    CK(launch_norm(const_cast<float *>(h), nullptr, 0, gain, M, H, eps, (uint16_t *)x, 0, nullptr, st));
+    CK(launch_norm(h, nullptr, nullptr, 0, gain, M, H, eps, (uint16_t *)x, 0, nullptr, st));
   } else if (act_fmt == SPEC_ACT_MXFP8) {
     if (!xs) return SPEC_E_ARG;
-    CK(launch_norm_mx8(const_cast<float *>(h), nullptr, 0, gain, M, H, eps, (uint8_t *)x, xs, nullptr, st));
+    CK(launch_norm_mx8(h, nullptr, nullptr, 0, gain, M, H, eps, (uint8_t *)x, xs, nullptr, st));
   } else {
     return SPEC_E_UNSUPPORTED;
   }

@@ -113,14 +113,15 @@ int attention_split_len(int batch, int Hkv, int max_ctx, int D);
 // table: the tile-major BF16 embedding [V][H]
 hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16_t *table, float *h,
                         const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, hipStream_t st);
-// h += part[0] + ... + part[nsplit-1] (in that order; nsplit may be 0), then
-// x = RMSNorm(h) * gain, written as FP16 (out_bf16 = 0) or BF16 (out_bf16 = 1)
-hipError_t launch_norm(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
-                       uint16_t *x, int out_bf16, float *dump, hipStream_t st);
+// h_out = h + part[0] + ... + part[nsplit-1] (in that order; nsplit may be 0;
+// h_out may be NULL, and is never h, so a launch can be repeated), then
+// x = RMSNorm(h_out) * gain, written as FP16 (out_bf16 = 0) or BF16 (out_bf16 = 1)
+hipError_t launch_norm(const float *h, float *h_out, const float *part, int nsplit, const float *gain, int M, int H,
+                       float eps, uint16_t *x, int out_bf16, float *dump, hipStream_t st);
 // the same, x written as MXFP8: e4m3 codes [M][H] in x8, e8m0 [M][H/32] in xs
 // (dump, when non-NULL, gets the decoded values code * 2^(e - 127))
-hipError_t launch_norm_mx8(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
-                           uint8_t *x8, uint8_t *xs, float *dump, hipStream_t st);
+hipError_t launch_norm_mx8(const float *h, float *h_out, const float *part, int nsplit, const float *gain, int M,
+                           int H, float eps, uint8_t *x8, uint8_t *xs, float *dump, hipStream_t st);
 // MXFP8 encoding of fp32 rows x [M][K] (K a multiple of 32), the one the
 // normalisation and SwiGLU steps apply
 hipError_t launch_quant_mx8(const float *x, int M, int K, uint8_t *codes, uint8_t *scales, hipStream_t st);

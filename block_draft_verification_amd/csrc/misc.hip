@@ -70,8 +70,9 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restr
   dst[i] = src[(size_t)row * (cols / 32) + 2 * kt + hh];
 }
 
-// h += part[0] + ... + part[ns-1] (split-K partials of the projection that
-// just ran, added in split order), then x = h / sqrt(mean(h^2) + eps) * gain
+// h_out = h + part[0] + ... + part[ns-1] (split-K partials of the projection
+// that just ran, added in split order; h_out may be NULL), then
+// x = h_out / sqrt(mean(h_out^2) + eps) * gain
 // rounded to FP16 (decoder layers) or BF16 (lm_head input).  One 256-thread
 // workgroup per row; thread i owns the 4-column chunks c = 4i + 1024j (j < 4,
 // so H <= 4096), and every load a thread needs -- its h and gain chunks, then
@@ -81,14 +82,16 @@ __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restr
 // the 8 threads holding one 32-column block share its exponent by shuffles).
 enum { kOutF16 = 0, kOutBF16 = 1, kOutMX8 = 2 };
 template <int OUT>
-__global__ __launch_bounds__(256) void norm_kernel(float *__restrict__ h, const float *__restrict__ part, int ns,
+__global__ __launch_bounds__(256) void norm_kernel(const float *__restrict__ h, float *__restrict__ h_out,
+                                                   const float *__restrict__ part, int ns,
                                                    const float *__restrict__ gain, int M, int H, float eps,
                                                    void *__restrict__ x, uint8_t *__restrict__ xs,
                                                    float *__restrict__ dump) {
   constexpr int MAXC = 4;
   __shared__ float red[4];
   const int m = blockIdx.x, tid = threadIdx.x;
-  float *hr = h + (size_t)m * H;
+  const float *hr = h + (size_t)m * H;
+  float *ho = h_out ? h_out + (size_t)m * H : nullptr;
   const float *pr = part + (size_t)m * H;
   const size_t pstride = (size_t)M * H;
   f32x4_t t[MAXC], gv[MAXC];
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(256) void norm_kernel(float *__restrict__ h, const 
   for (int i = 0; i < MAXC; ++i) {
     const int c = 4 * tid + 1024 * i;
     if (c < H) {
-      if (ns) *reinterpret_cast<f32x4_t *>(hr + c) = t[i];
+      if (ho) *reinterpret_cast<f32x4_t *>(ho + c) = t[i];
       ss += t[i][0] * t[i][0] + t[i][1] * t[i][1] + t[i][2] * t[i][2] + t[i][3] * t[i][3];
     }
   }
@@ -328,23 +331,23 @@ hipError_t launch_pack_weights(int wfmt, int rows, int cols, const void *w, cons
   return hipGetLastError();
 }
 
-hipError_t launch_norm(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
-                       uint16_t *x, int out_bf16, float *dump, hipStream_t st) {
-  if (H > 4096 || H % 4) return hipErrorInvalidValue;
+hipError_t launch_norm(const float *h, float *h_out, const float *part, int nsplit, const float *gain, int M, int H,
+                       float eps, uint16_t *x, int out_bf16, float *dump, hipStream_t st) {
+  if (H > 4096 || H % 4 || h == h_out) return hipErrorInvalidValue;
   if (out_bf16)
-    hipLaunchKernelGGL(norm_kernel<kOutBF16>, dim3(M), dim3(256), 0, st, h, part, nsplit, gain, M, H, eps,
+    hipLaunchKernelGGL(norm_kernel<kOutBF16>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, eps,
                        (void *)x, (uint8_t *)nullptr, dump);
   else
-    hipLaunchKernelGGL(norm_kernel<kOutF16>, dim3(M), dim3(256), 0, st, h, part, nsplit, gain, M, H, eps,
+    hipLaunchKernelGGL(norm_kernel<kOutF16>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, eps,
                        (void *)x, (uint8_t *)nullptr, dump);
   return hipGetLastError();
 }
 
-hipError_t launch_norm_mx8(float *h, const float *part, int nsplit, const float *gain, int M, int H, float eps,
-                           uint8_t *x8, uint8_t *xs, float *dump, hipStream_t st) {
-  if (H > 4096 || H % 32) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(norm_kernel<kOutMX8>, dim3(M), dim3(256), 0, st, h, part, nsplit, gain, M, H, eps, (void *)x8,
-                     xs, dump);
+hipError_t launch_norm_mx8(const float *h, float *h_out, const float *part, int nsplit, const float *gain, int M,
+                           int H, float eps, uint8_t *x8, uint8_t *xs, float *dump, hipStream_t st) {
+  if (H > 4096 || H % 32 || h == h_out) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(norm_kernel<kOutMX8>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, eps,
+                     (void *)x8, xs, dump);
   return hipGetLastError();
 }
 
