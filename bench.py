@@ -38,10 +38,12 @@ REPEAT = 20  # back-to-back launches per event pair in the per-kernel timing
 # is recorded; any other source reports null.
 TRAFFIC_PROFILE = "profiles/verify_pass_0.5b-fp8-b32-ctx512to4096_hbm_traffic.md"
 TRAFFIC = {
-    "gate_up": {"bytes": (16.92 + 4.75) * 2 ** 20, "sources": ("gemm.hip", "common.h", "kernels.h"),
-                "sha256_16": "38e354ee0a89d882,230adac9725098ab,2814e6bbb4576c62"},
-    "attention": {"bytes": (40.09 + 11.28) * 2 ** 20, "sources": ("attention.hip", "common.h", "kernels.h"),
-                  "sha256_16": "7ae9f732a22cba54,230adac9725098ab,2814e6bbb4576c62"},
+    "attention": {"bytes": (37.21 + 4.57) * 2 ** 20, "sources": ("attention.hip", "common.h", "kernels.h"),
+                  "sha256_16": "692f4a86b72ef399,b066466dcfc25a14,62212f1a1be0a465"},
+    "gate_up": {"bytes": (16.74 + 4.75) * 2 ** 20, "sources": ("gemm.hip", "common.h", "kernels.h"),
+                "sha256_16": "26f8863784ac1905,b066466dcfc25a14,62212f1a1be0a465"},
+    "rmsnorm": {"bytes": (7.08 + 2.62) * 2 ** 20, "sources": ("misc.hip", "common.h", "kernels.h"),
+                "sha256_16": "98099c6c9152ebf8,b066466dcfc25a14,62212f1a1be0a465"},
 }
 
 
