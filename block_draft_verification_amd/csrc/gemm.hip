@@ -284,6 +284,14 @@ gemm_kernel(GemmArgs ga, Epi epi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][mt][v] = 0.f;
 
+  // Epilogue inputs (the per-row weight scales of the lane's output rows, the
+  // cache lengths of the tile's sequences) are loaded here, before the main
+  // loop, and used only after its final wait: the epilogue then starts
+  // without a dependent memory round trip.
+  f32x4_t esc[NT][4];
+  int ekv[2 * MT];
+  if constexpr (Epi::kStaged) epi.template prefetch<NT, MT>(active ? unit : 0, m0, M, h, esc, ekv);
+
   auto compute_a8 = [&](int stage, const WRaw<FMT>(&wr)[NT], const uint32_t(&sc)[A8 ? MT : 1]) {
     __builtin_amdgcn_sched_barrier(0);
     const uint8_t *base = reinterpret_cast<const uint8_t *>(As) + stage * SE * 2;
@@ -412,12 +420,12 @@ gemm_kernel(GemmArgs ga, Epi epi) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (m0 + 32 * mt >= M) break;
-        epi.template emit<NT, MT>(unit, mt, m0, M, c, h, acc, st, LD);
+        epi.template emit<NT, MT>(unit, mt, m0, M, c, h, acc, esc, ekv, st, LD);
 #pragma unroll
         for (int r0 = 0; r0 < 32; r0 += RPP) {
           const int row = r0 + lane / LPR, col = 4 * (lane % LPR), m = m0 + 32 * mt + row;
           const f32x4_t v = *reinterpret_cast<const f32x4_t *>(st + row * LD + col);
-          if (m < M) epi.put(unit, m, col, v, blockIdx.z);
+          if (m < M) epi.template put<MT>(unit, m, m0, col, v, blockIdx.z, ekv);
         }
       }
     }
@@ -436,6 +444,29 @@ __device__ __forceinline__ void store_bf16x4(uint16_t *p, float a, float b, floa
 __device__ __forceinline__ f32x4_t row_scale4(const float *s, int n) {
   if (!s) return f32x4_t{1.f, 1.f, 1.f, 1.f};
   return *reinterpret_cast<const f32x4_t *>(s + n);
+}
+
+// Per-row scales of weight rows row(unit, t) + 8q + 4h + (0..3), the rows lane
+// (., h) holds for tile t (1 without per-row scales).  Prefetched for up to two
+// tiles per wave; with four (head_dim 128) the 64 registers would spill, so
+// those are read in the epilogue instead (scale_at).
+template <int NT>
+constexpr bool kPrefetchScales = NT <= 2;
+template <int NT, class E>
+__device__ __forceinline__ void prefetch_scales(const E &e, const float *scale, int unit, int h,
+                                                f32x4_t (&sc)[NT][4]) {
+  if constexpr (kPrefetchScales<NT>) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sc[t][q] = row_scale4(scale, e.row(unit, t) + 8 * q + 4 * h);
+  }
+}
+template <int NT, class E>
+__device__ __forceinline__ f32x4_t scale_at(const E &e, const float *scale, const f32x4_t (&sc)[NT][4], int unit,
+                                            int t, int q, int h) {
+  if constexpr (kPrefetchScales<NT>) return sc[t][q];
+  else return row_scale4(scale, e.row(unit, t) + 8 * q + 4 * h);
 }
 
 // Outputs of lane (c, h) for weight rows 8q + 4h + (0..3) of a tile.
@@ -459,17 +490,20 @@ struct EpiF32 {  // y = acc * scale, fp32 out
   __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
   template <int NT> static constexpr int cols() { return 32 * NT; }
   template <int NT, int MT>
-  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT], float *st,
-                       int ld) const {
+  __device__ void prefetch(int unit, int m0, int M, int h, f32x4_t (&sc)[NT][4], int (&kvl)[2 * MT]) const {
+    prefetch_scales<NT>(*this, scale, unit, h, sc);
+  }
+  template <int NT, int MT>
+  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT],
+                       const f32x4_t (&sc)[NT][4], const int (&kvl)[2 * MT], float *st, int ld) const {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = 32 * t + 8 * q + 4 * h;
-        *reinterpret_cast<f32x4_t *>(st + c * ld + col) = quad(acc[t][mt], q) * row_scale4(scale, row(unit, 0) + col);
-      }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t *>(st + c * ld + 32 * t + 8 * q + 4 * h) = quad(acc[t][mt], q) * scale_at<NT>(*this, scale, sc, unit, t, q, h);
   }
-  __device__ void put(int unit, int m, int col, f32x4_t v, int z) const {
+  template <int MT>
+  __device__ void put(int unit, int m, int m0, int col, f32x4_t v, int z, const int (&kvl)[2 * MT]) const {
     *reinterpret_cast<f32x4_t *>(y + (size_t)m * N + row(unit, 0) + col) = v;
   }
 };
@@ -485,17 +519,20 @@ struct EpiPartial {
   __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
   template <int NT> static constexpr int cols() { return 32 * NT; }
   template <int NT, int MT>
-  __device__ void emit(int unit, int mt, int m0, int Mr, int c, int h, const f32x16_t (&acc)[NT][MT], float *st,
-                       int ld) const {
+  __device__ void prefetch(int unit, int m0, int Mr, int h, f32x4_t (&sc)[NT][4], int (&kvl)[2 * MT]) const {
+    prefetch_scales<NT>(*this, scale, unit, h, sc);
+  }
+  template <int NT, int MT>
+  __device__ void emit(int unit, int mt, int m0, int Mr, int c, int h, const f32x16_t (&acc)[NT][MT],
+                       const f32x4_t (&sc)[NT][4], const int (&kvl)[2 * MT], float *st, int ld) const {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = 32 * t + 8 * q + 4 * h;
-        *reinterpret_cast<f32x4_t *>(st + c * ld + col) = quad(acc[t][mt], q) * row_scale4(scale, row(unit, 0) + col);
-      }
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t *>(st + c * ld + 32 * t + 8 * q + 4 * h) = quad(acc[t][mt], q) * scale_at<NT>(*this, scale, sc, unit, t, q, h);
   }
-  __device__ void put(int unit, int m, int col, f32x4_t v, int z) const {
+  template <int MT>
+  __device__ void put(int unit, int m, int m0, int col, f32x4_t v, int z, const int (&kvl)[2 * MT]) const {
     *reinterpret_cast<f32x4_t *>(part + ((size_t)z * M + m) * N + row(unit, 0) + col) = v;
   }
 };
@@ -513,13 +550,23 @@ struct EpiQkv {
   __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
   template <int NT> static constexpr int cols() { return 32 * NT; }
   __device__ bool slot_ok(int n0) const { return n0 >= 0 && n0 + 16 <= o.max_ctx; }  // else flagged by embed
+  // also the cache length of each of the tile's 2*MT sequences (uniform loads)
   template <int NT, int MT>
-  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT], float *st,
-                       int ld) const {
+  __device__ void prefetch(int unit, int m0, int M, int h, f32x4_t (&sc)[NT][4], int (&kvl)[2 * MT]) const {
+    prefetch_scales<NT>(*this, scale, unit, h, sc);
+#pragma unroll
+    for (int i = 0; i < 2 * MT; ++i) {
+      const int b = (m0 >> 4) + i;
+      kvl[i] = b < (M >> 4) ? o.kv_len[b] : 0;
+    }
+  }
+  template <int NT, int MT>
+  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT],
+                       const f32x4_t (&sc)[NT][4], const int (&kvl)[2 * MT], float *st, int ld) const {
     constexpr int HALF = 16 * NT;
     const int m = m0 + 32 * mt + c;
     if (m >= M) return;
-    const int n0 = o.kv_len[m >> 4], pos = n0 + (m & 15);
+    const int n0 = kvl[2 * mt + (c >> 4)], pos = n0 + (m & 15);
     if (!slot_ok(n0)) return;
     if (unit < o.Hq + o.Hkv) {
 #pragma unroll
@@ -527,8 +574,8 @@ struct EpiQkv {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int d = 32 * t + 8 * q + 4 * h;
-          const f32x4_t y1 = quad(acc[t][mt], q) * row_scale4(scale, row(unit, 0) + d);
-          const f32x4_t y2 = quad(acc[t + NT / 2][mt], q) * row_scale4(scale, row(unit, 0) + d + HALF);
+          const f32x4_t y1 = quad(acc[t][mt], q) * scale_at<NT>(*this, scale, sc, unit, t, q, h);
+          const f32x4_t y2 = quad(acc[t + NT / 2][mt], q) * scale_at<NT>(*this, scale, sc, unit, t + NT / 2, q, h);
           const f32x4_t cs01 = *reinterpret_cast<const f32x4_t *>(o.rope + (size_t)pos * HALF + d);
           const f32x4_t cs23 = *reinterpret_cast<const f32x4_t *>(o.rope + (size_t)pos * HALF + d + 2);
           const float cs[4] = {cs01[0], cs01[2], cs23[0], cs23[2]}, sn[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
@@ -547,13 +594,14 @@ struct EpiQkv {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           const int d = 32 * t + 8 * q + 4 * h;
-          *reinterpret_cast<f32x4_t *>(st + c * ld + d) = quad(acc[t][mt], q) * row_scale4(scale, row(unit, 0) + d);
+          *reinterpret_cast<f32x4_t *>(st + c * ld + d) = quad(acc[t][mt], q) * scale_at<NT>(*this, scale, sc, unit, t, q, h);
         }
     }
   }
-  __device__ void put(int unit, int m, int col, f32x4_t v, int z) const {
+  template <int MT>
+  __device__ void put(int unit, int m, int m0, int col, f32x4_t v, int z, const int (&kvl)[2 * MT]) const {
     constexpr int D = 32 * NTc;
-    const int b = m >> 4, n0 = o.kv_len[b];
+    const int b = m >> 4, n0 = kvl[(m - m0) >> 4];
     if (!slot_ok(n0)) return;
     const int pos = n0 + (m & 15);
     if (unit < o.Hq) {
@@ -587,22 +635,27 @@ struct EpiSwiglu {
   }
   template <int NT> static constexpr int cols() { return 16 * NT; }
   template <int NT, int MT>
-  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT], float *st,
-                       int ld) const {
+  __device__ void prefetch(int unit, int m0, int M, int h, f32x4_t (&sc)[NT][4], int (&kvl)[2 * MT]) const {
+    prefetch_scales<NT>(*this, scale, unit, h, sc);  // gate rows, then the matching up rows
+  }
+  template <int NT, int MT>
+  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT],
+                       const f32x4_t (&sc)[NT][4], const int (&kvl)[2 * MT], float *st, int ld) const {
 #pragma unroll
     for (int t = 0; t < NT / 2; ++t)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int col = 32 * t + 8 * q + 4 * h, n = unit * 16 * NT + col;
-        const f32x4_t gv = quad(acc[t][mt], q) * row_scale4(scale, n);
-        const f32x4_t uv = quad(acc[t + NT / 2][mt], q) * row_scale4(scale ? scale + I : nullptr, n);
+        const int col = 32 * t + 8 * q + 4 * h;
+        const f32x4_t gv = quad(acc[t][mt], q) * scale_at<NT>(*this, scale, sc, unit, t, q, h);
+        const f32x4_t uv = quad(acc[t + NT / 2][mt], q) * scale_at<NT>(*this, scale, sc, unit, t + NT / 2, q, h);
         f32x4_t v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = gv[i] * __builtin_amdgcn_rcpf(1.f + __expf(-gv[i])) * uv[i];  // SiLU(g) * u
         *reinterpret_cast<f32x4_t *>(st + c * ld + col) = v;
       }
   }
-  __device__ void put(int unit, int m, int col, f32x4_t v, int z) const {
+  template <int MT>
+  __device__ void put(int unit, int m, int m0, int col, f32x4_t v, int z, const int (&kvl)[2 * MT]) const {
     const int n = unit * 16 * NTc + col;
     if constexpr (MX8) {
       uint32_t e8;
