@@ -430,7 +430,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
       }
     }
   } else {
-    if (active) epi.template store<NT, MT>(unit, m0, M, c, h, acc, blockIdx.z);
+    epi.template store<NT, MT>(active ? unit : 0, nblk, active, wave, m0, M, c, h, acc, As);
   }
 }
 
@@ -668,17 +668,24 @@ struct EpiSwiglu {
   }
 };
 
-// lm_head tile -> per (row, unit) argmax partial, lowest index on ties.
+// lm_head tile -> one argmax partial per (row, workgroup), lowest index on
+// ties: each wave reduces its 32*NT vocab rows in registers, the workgroup's
+// waves meet in LDS, and wave 0 folds them in wave order (increasing vocab
+// index).  Called by every wave of the workgroup (inactive ones contribute
+// nothing), after the main loop.
 template <int NTc>
 struct EpiArgmax {
   static constexpr bool kStaged = false;
   template <int NT> static constexpr int cols() { return 4; }
-  int units, V;
-  ArgmaxPart *part;  // [M][units]
+  int units, V, nparts;
+  ArgmaxPart *part;  // [M][nparts], nparts = workgroups along the vocab
   float *logits;     // optional [M][V]
   __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
   template <int NT, int MT>
-  __device__ void store(int unit, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT], int z) const {
+  __device__ void store(int unit, int nblk, bool active, int wave, int m0, int M, int c, int h,
+                        const f32x16_t (&acc)[NT][MT], void *lds) const {
+    ArgmaxPart *red = static_cast<ArgmaxPart *>(lds);  // [4 waves][32 * MT rows]
+    lds_barrier();  // every wave is done reading the activation stages
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
       const int m = m0 + 32 * mt + c;
@@ -698,19 +705,29 @@ struct EpiArgmax {
       const float ov = __shfl_xor(bv, 32);  // the other half holds the other rows of the same block row
       const int32_t oi = __shfl_xor(bi, 32);
       const bool take = better(ov, oi, bv, bi);
-      bv = take ? ov : bv;
-      bi = take ? oi : bi;
-      if (m < M) {
-        if (h == 0) part[(size_t)m * units + unit] = ArgmaxPart{bv, bi};
-        if (logits) {
+      bv = active && take ? ov : (active ? bv : -INFINITY);
+      bi = active && take ? oi : (active ? bi : 0x7fffffff);
+      if (h == 0) red[wave * 32 * MT + 32 * mt + c] = ArgmaxPart{bv, bi};
+      if (active && m < M && logits) {
 #pragma unroll
-          for (int t = 0; t < NT; ++t)
+        for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-              *reinterpret_cast<f32x4_t *>(logits + (size_t)m * V + row(unit, t) + 8 * q + 4 * h) =
-                  quad(acc[t][mt], q);
-        }
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<f32x4_t *>(logits + (size_t)m * V + row(unit, t) + 8 * q + 4 * h) = quad(acc[t][mt], q);
       }
+    }
+    lds_barrier();
+    if (wave != 0) return;
+    const int lane = 32 * h + c;
+#pragma unroll
+    for (int r = lane; r < 32 * MT; r += 64) {
+      ArgmaxPart b = red[r];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        const ArgmaxPart o = red[w * 32 * MT + r];
+        if (better(o.v, o.i, b.v, b.i)) b = o;
+      }
+      if (m0 + r < M) part[(size_t)(m0 + r) * nparts + nblk] = b;
     }
   }
 };
@@ -822,6 +839,7 @@ hipError_t launch_qkv(ActIn x, int M, int H, int D, LinearW w, QkvOut o, hipStre
 
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,
                             float *logits_dump, hipStream_t st) {
-  return run<2, kBf16, EpiArgmax<2>, GEMM_LM_MAXMT>(ActIn{x, nullptr}, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16},
-                                                   EpiArgmax<2>{V / 64, V, part, logits_dump}, false, st);
+  return run<kLmNT, kBf16, EpiArgmax<kLmNT>, GEMM_LM_MAXMT>(
+      ActIn{x, nullptr}, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16},
+      EpiArgmax<kLmNT>{V / (32 * kLmNT), V, lm_parts(V), part, logits_dump}, false, st);
 }

@@ -86,11 +86,16 @@ hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8
 // The following launch_norm adds them to h.
 hipError_t launch_residual_partial(ActIn x, int M, int N, int K, LinearW w, float *part, hipStream_t st);
 
-// lm_head (BF16 x, BF16 table) + per-wave argmax partials: part[m][p] over vocab slices of 64
+// lm_head (BF16 x, BF16 table) + argmax partials, one per (row, workgroup):
+// part[m][p] over vocab slices of 4 * 32 * kLmNT rows
 struct ArgmaxPart { float v; int32_t i; };
+#ifndef GEMM_LM_NT
+#define GEMM_LM_NT 2
+#endif
+constexpr int kLmNT = GEMM_LM_NT;  // 32-row vocab tiles per wave
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,
                             float *logits_dump, hipStream_t st);
-inline int lm_parts(int V) { return V / 64; }
+inline int lm_parts(int V) { return (V / (32 * kLmNT) + 3) / 4; }
 
 // ---- attention ----
 struct AttnArgs {
