@@ -38,10 +38,11 @@ struct spec_ctx {
   struct LaneBufs {
     float *part_o, *rpart;
     float2 *part_ml;
+    int4 *plan;  // attention split plan of the lane's pass
   };
   LaneBufs lane_buf[SPEC_MAX_LANES] = {};
   void *lane_ws = nullptr;                      // lanes 1.. (one allocation)
-  size_t lane_bytes[3] = {0, 0, 0};             // part_o, part_ml, rpart sizes of one lane
+  size_t lane_bytes[4] = {0, 0, 0, 0};          // part_o, part_ml, rpart, plan sizes of one lane
   hipStream_t lane_st[SPEC_MAX_LANES] = {};     // [0] unused (the caller's stream)
   hipEvent_t lane_ev[SPEC_MAX_LANES] = {};      // [0] fork, [i] join of lane i
   // launch timing of one kernel class (measurement hook)
@@ -103,8 +104,6 @@ static int check_model(const spec_model_desc *m) {
   return SPEC_OK;
 }
 
-static int attn_nsplit(int split_len, int max_ctx) { return (max_ctx + split_len - 1) / split_len; }
-
 extern "C" {
 
 const char *spec_status_str(int s) {
@@ -152,10 +151,7 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   const int G = Hq / Hkv, I = m->intermediate, V = m->vocab;
   c->Mmax = kv->max_batch * 16;
   int units = 0;
-  for (int b = 1; b <= kv->max_batch; ++b) {
-    const int u = b * Hkv * attn_nsplit(attention_split_len(b, Hkv, kv->max_ctx, D), kv->max_ctx);
-    if (u > units) units = u;
-  }
+  for (int b = 1; b <= kv->max_batch; ++b) units = std::max(units, attention_grid(b, Hkv, kv->max_ctx, D, 0));
   c->part_units = units;
   size_t rfloats = 0;
   for (int b = 1; b <= kv->max_batch; ++b) {
@@ -179,7 +175,8 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
                     (size_t)kv->max_ctx * (D / 2) * 8,  // rope
                     rfloats * 4,                     // residual split-K partials
                     Mm * H + Mm * (H / 32),          // x8, xs8
-                    Mm * I + Mm * (I / 32)};         // a8, as8
+                    Mm * I + Mm * (I / 32),          // a8, as8
+                    (1 + (size_t)kv->max_batch) * 16};  // attention split plan
   const int NS = sizeof(sizes) / sizeof(sizes[0]);
   size_t off[NS], total = 0;
   for (int i = 0; i < NS; ++i) {
@@ -214,10 +211,11 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   c->a8 = (uint8_t *)(base + off[14]);
   c->as8 = c->a8 + Mm * I;
   c->dump_hidden = c->dump_logits = nullptr;
-  c->lane_buf[0] = spec_ctx::LaneBufs{c->part_o, c->rpart, c->part_ml};
+  c->lane_buf[0] = spec_ctx::LaneBufs{c->part_o, c->rpart, c->part_ml, (int4 *)(base + off[15])};
   c->lane_bytes[0] = sizes[5];
   c->lane_bytes[1] = sizes[6];
   c->lane_bytes[2] = sizes[12];
+  c->lane_bytes[3] = sizes[15];
 
   // RoPE table: angle = p * theta^(-2i/D), in double, stored as fp32 (cos, sin)
   std::vector<float2> rope((size_t)kv->max_ctx * (D / 2));
@@ -266,9 +264,11 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
   float *dump_logits = c->dump_logits ? c->dump_logits + r0 * V : nullptr;
   int32_t *last_tau = c->last_tau + b0;
 
+  const AttnPlanArgs plan = attention_plan_args(c->lane_buf[lane].plan, batch, Hkv, max_ctx, D, 0);
   AttnArgs aa{};
   aa.q = q;
-  aa.kv_len = kv_len;
+  aa.plan = plan.plan;
+  aa.grid = plan.grid;
   aa.o = ao;
   aa.part_o = c->lane_buf[lane].part_o;
   aa.part_ml = c->lane_buf[lane].part_ml;
@@ -277,13 +277,11 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
   aa.Hkv = Hkv;
   aa.max_ctx = max_ctx;
   aa.kvl = kvl;
-  aa.split_len = attention_split_len(batch, Hkv, max_ctx, D);
-  aa.nsplit = attn_nsplit(aa.split_len, max_ctx);
 
   {
     Timed t(c, SPEC_K_EMBED, st);
     for (int r = 0; r < t.reps; ++r)
-      CK(launch_embed(tokens, M, H, V, c->embed, h, kv_len, max_ctx, kvl, c->err, st));
+      CK(launch_embed(tokens, M, H, V, c->embed, h, kv_len, max_ctx, kvl, c->err, plan, st));
   }
   const int ns_o = residual_nsplit(M, H, Hq * D), ns_d = residual_nsplit(M, H, I);
   const bool mx = m.act_fmt == SPEC_ACT_MXFP8;
@@ -414,6 +412,8 @@ int spec_verify_set_lanes(spec_ctx *c, int32_t lanes) {
       p += (c->lane_bytes[1] + 255) & ~(size_t)255;
       lb.rpart = (float *)p;
       p += (c->lane_bytes[2] + 255) & ~(size_t)255;
+      lb.plan = (int4 *)p;
+      p += (c->lane_bytes[3] + 255) & ~(size_t)255;
     }
     for (int i = 1; i < SPEC_MAX_LANES; ++i)
       if (hipStreamCreateWithFlags(&c->lane_st[i], hipStreamNonBlocking) != hipSuccess) return SPEC_E_HIP;
@@ -603,26 +603,30 @@ int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int3
   if (D != 64 && D != 128) return SPEC_E_SHAPE;
   if (split_len < 0 || split_len % 64) return SPEC_E_ARG;
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return SPEC_E_ARG;
+  // the merge step holds at most 64 splits per sequence
+  if (split_len && (max_ctx + split_len - 1) / split_len > 64) return SPEC_E_ARG;
+  AttnPlanArgs p = attention_plan_args(nullptr, batch, Hkv, max_ctx, D, split_len);
   AttnArgs a{};
   a.q = q;
   a.k_cache = k_cache;
   a.v_cache = v_cache;
-  a.kv_len = kv_len;
   a.o = o;
   a.batch = batch;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.max_ctx = max_ctx;
-  a.split_len = split_len ? split_len : attention_split_len(batch, Hkv, max_ctx, D);
-  a.nsplit = attn_nsplit(a.split_len, max_ctx);
-  if (a.nsplit > 64) return SPEC_E_ARG;  // the merge step holds at most 64 splits per sequence
-  const size_t units = (size_t)batch * Hkv * a.nsplit, R = (size_t)(Hq / Hkv) * 16;
+  a.grid = p.grid;
+  const size_t units = (size_t)p.grid, R = (size_t)(Hq / Hkv) * 16;
   void *buf = nullptr;
-  if (hipMalloc(&buf, units * R * D * 4 + units * R * 8) != hipSuccess) return SPEC_E_NOMEM;
+  if (hipMalloc(&buf, units * R * D * 4 + units * R * 8 + (1 + (size_t)batch) * 16) != hipSuccess) return SPEC_E_NOMEM;
   a.part_o = (float *)buf;
   a.part_ml = (float2 *)((char *)buf + units * R * D * 4);
+  p.plan = (int4 *)((char *)buf + units * R * D * 4 + units * R * 8);
+  a.plan = p.plan;
   int rc = SPEC_OK;
-  if (launch_attention(a, D, st) != hipSuccess || hipStreamSynchronize(st) != hipSuccess) rc = SPEC_E_HIP;
+  if (launch_attention_plan(kv_len, p, st) != hipSuccess || launch_attention(a, D, st) != hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    rc = SPEC_E_HIP;
   (void)hipFree(buf);
   return rc;
 }

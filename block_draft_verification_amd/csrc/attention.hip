@@ -7,13 +7,15 @@
 // Query head h reads KV head h / G, so the G*16 query rows of one KV head
 // share every K/V tile: the pass is bound by reading the cache once.
 //
-// Work unit = (key split, kv head, sequence): one workgroup of ceil(G/2)
-// waves; wave w owns the 32 query rows of heads 2w, 2w+1 (rows of a head past
-// G are padding and never stored).  The split's keys are walked in tiles of
-// 64: the next tile's K/V is loaded into registers while the current one is
-// computed, converted from the BF16 cache to FP16 and stored in LDS (K
-// row-major, V transposed with swizzled columns; two LDS buffers, one barrier
-// per tile).
+// Work unit = (key split, kv head, sequence), taken from the pass's split
+// plan (attn_plan.h: equal splits sized from the actual cache lengths so that
+// one resident round of workgroups covers every key); one team of ceil(G/2)
+// waves per key tile; wave w owns the 32 query rows of heads 2w, 2w+1 (rows
+// of a head past G are padding and never stored).  The split's keys are
+// walked in tiles of 64: the next tile's K/V is loaded into registers while
+// the current one is computed, converted from the BF16 cache to FP16 and
+// stored in LDS (K row-major, V transposed with swizzled columns; two LDS
+// buffers, one barrier per tile).
 //
 // MFMA v_mfma_f32_32x32x16_f16.  Scores are computed transposed, S^T = K Q^T,
 // 32 keys x 32 queries per block: lane (c, h) supplies key c (A) and query c
@@ -32,6 +34,7 @@
 // in split order per (query head, sequence), so the result does not depend on
 // timing and no workgroup waits on another (a device-wide fence inside the
 // kernel would flush the XCD's L2).
+#include "attn_plan.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -64,24 +67,41 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
   constexpr int VCH = KT * D / 8;      // V: chunks of (2 keys, 4 d)
   extern __shared__ __align__(16) uint16_t attn_lds[];  // NTEAM x attn_team_halfs<D>()
 
-  const int sp = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  // Workgroup w takes slot w of the pass's split plan: find its sequence b
+  // (entries hold increasing first slots), KV head and split.
+  const int w = blockIdx.x;
+  const int4 hdr = a.plan[0];
+  if (w >= hdr.y) return;  // whole workgroup: past the plan's splits
+  int b = 0, first = 0, nsp = 1, n = 0;
+  {
+    const int ln = threadIdx.x & 63;
+    for (int b0 = 0; b0 < a.batch; b0 += 64) {
+      const int4 e = a.plan[1 + min(b0 + ln, a.batch - 1)];
+      const int k = __popcll(__builtin_amdgcn_ballot_w64(b0 + ln < a.batch && e.x <= w));
+      if (k > 0) {
+        b = b0 + k - 1;
+        first = __builtin_amdgcn_readlane(e.x, k - 1);
+        nsp = __builtin_amdgcn_readlane(e.y, k - 1);
+        n = __builtin_amdgcn_readlane(e.z, k - 1);
+      }
+      if (k < 64) break;
+    }
+  }
+  const int kvh = (w - first) / nsp, sp = (w - first) - kvh * nsp;
   const int G = a.Hq / a.Hkv;
-  const int n = a.kv_len[b];
-  const int L = min(max(n, 0) + 16, a.max_ctx);
-  const int nsplit = (L + a.split_len - 1) / a.split_len;
-  if (sp >= nsplit) return;  // whole workgroup
-  const int key_lo = sp * a.split_len, key_hi = min(key_lo + a.split_len, L);
+  const int L = min(max(n, 0) + 16, a.max_ctx), split_len = hdr.x * KT;
+  const int key_lo = sp * split_len, key_hi = min(key_lo + split_len, L);
 
   constexpr int T = 64 * NW;  // threads per team
   // Teams: NTEAM groups of NW waves walk alternate key tiles of the split
   // (tile i of the split goes to team i % NTEAM), each with its own LDS tiles,
   // and combine their softmax states through LDS at the end, so the split
   // still leaves one partial.  tid, lane and wave below are team-local.
-  const int team = threadIdx.x / T, tid = threadIdx.x % T, lane = tid & 63, c = lane & 31, h = lane >> 5;
-  const int wave = tid >> 6;
+  const int team = __builtin_amdgcn_readfirstlane(threadIdx.x / T);
+  const int tid = threadIdx.x % T, lane = tid & 63, c = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint16_t *const Ks = attn_lds + team * attn_team_halfs<D>();  // [2][KT * KP]
   uint16_t *const Vt = Ks + 2 * KT * KP;                         // [2][D * VP]
-  const size_t unit = (size_t)b * a.Hkv + kvh;
 
   // this wave's queries: lane (c, h) -> head 2*wave + c/16 of the group, block row c%16
   const int hg = 2 * wave + (c >> 4), j = c & 15;
@@ -104,30 +124,59 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
   // whose finite values are masked out) so the wave never branches around them.
   // A tile's 64 keys share one cache page (pages hold a multiple of 64 rows), so
   // one row lookup per tile serves both layouts; tb = 64-aligned start of the
-  // tile that holds the (clamped) keys.
+  // tile that holds the (clamped) keys.  A thread's chunks sit at fixed byte
+  // offsets inside a tile (rows of 2D bytes), so a whole tile is loaded from
+  // one scalar base with no per-load address arithmetic; only a tile that
+  // reaches past the split clamps its rows.
   constexpr int KPT = (KCH + T - 1) / T, VPT = (VCH + T - 1) / T;  // chunks per thread (last one partial for NW = 3)
   struct TileRegs {
     u32x4_t k[KPT];
     u32x2_t v[VPT][2];
   };
+  int kk_k[KPT], kk_v[VPT];            // tile row of each chunk (V: the first of its two keys)
+  uint32_t dk[KPT], dv[VPT];           // byte offset of its d slice inside a row
+  uint32_t ok[KPT], ov[VPT][2];        // byte offset of the chunk inside a whole tile
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int ch = min(tid + T * i, KCH - 1);
+    kk_k[i] = ch / (D / 8);
+    dk[i] = (ch % (D / 8)) * 16;
+    ok[i] = kk_k[i] * 2 * D + dk[i];
+  }
+#pragma unroll
+  for (int i = 0; i < VPT; ++i) {
+    const int ch = min(tid + T * i, VCH - 1);
+    kk_v[i] = 2 * (ch / (D / 4));
+    dv[i] = (ch % (D / 4)) * 8;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) ov[i][e] = (kk_v[i] + e) * 2 * D + dv[i];
+  }
+  // scalar tile base + a 32-bit per-lane offset: the loads take the
+  // SGPR-base form, with no 64-bit address arithmetic per load
   auto load_tile = [&](TileRegs &tr, int kt0) {
     const int tb = min(kt0, (key_hi - 1) & ~(KT - 1));
-    bool ok;
-    const size_t trow = a.kvl.row(b, kvh, a.Hkv, a.max_ctx, tb, ok);
+    bool okp;
+    const size_t trow = a.kvl.row(b, kvh, a.Hkv, a.max_ctx, tb, okp);
+    const char *kb = reinterpret_cast<const char *>(a.k_cache + trow * D);
+    const char *vb = reinterpret_cast<const char *>(a.v_cache + trow * D);
+    const int off = kt0 - tb, lim = key_hi - 1 - tb;  // row of key kt0 + kk is min(kk + off, lim)
+    if (off == 0 && lim >= KT - 1) {  // the whole tile lies inside the split
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int ch = min(tid + T * i, KCH - 1), kk = ch / (D / 8), d0 = (ch % (D / 8)) * 8,
-                key = min(kt0 + kk, key_hi - 1);
-      tr.k[i] = *reinterpret_cast<const u32x4_t *>(a.k_cache + (trow + key - tb) * D + d0);
-    }
+      for (int i = 0; i < KPT; ++i) tr.k[i] = *reinterpret_cast<const u32x4_t *>(kb + ok[i]);
 #pragma unroll
-    for (int i = 0; i < VPT; ++i) {
-      const int ch = min(tid + T * i, VCH - 1), kk = 2 * (ch / (D / 4)), d0 = (ch % (D / 4)) * 4;
+      for (int i = 0; i < VPT; ++i)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int key = min(kt0 + kk + e, key_hi - 1);
-        tr.v[i][e] = *reinterpret_cast<const u32x2_t *>(a.v_cache + (trow + key - tb) * D + d0);
-      }
+        for (int e = 0; e < 2; ++e) tr.v[i][e] = *reinterpret_cast<const u32x2_t *>(vb + ov[i][e]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i)
+        tr.k[i] = *reinterpret_cast<const u32x4_t *>(kb + (uint32_t)(min(kk_k[i] + off, lim) * 2 * D + dk[i]));
+#pragma unroll
+      for (int i = 0; i < VPT; ++i)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+          tr.v[i][e] =
+              *reinterpret_cast<const u32x2_t *>(vb + (uint32_t)(min(kk_v[i] + e + off, lim) * 2 * D + dv[i]));
     }
   };
   auto store_tile = [&](const TileRegs &tr, int buf) {
@@ -143,14 +192,19 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
     for (int i = 0; i < VPT; ++i) {
       const int ch = tid + T * i, kk = 2 * (ch / (D / 4)), d0 = (ch % (D / 4)) * 4;
       if (VCH % T != 0 && ch >= VCH) break;
-      const uint32_t a0 = bf16x2_to_f16x2(tr.v[i][0].x), a1 = bf16x2_to_f16x2(tr.v[i][0].y);
-      const uint32_t b0 = bf16x2_to_f16x2(tr.v[i][1].x), b1 = bf16x2_to_f16x2(tr.v[i][1].y);
-      // (key kk, key kk+1) pairs for d0 .. d0+3
+      // (key kk, key kk+1) pairs of column d0 + e, converted straight into
+      // their FP16 pair: the low bf16 of a dword is column d0 + 2i, the high
+      // one d0 + 2i + 1
+      const u32x2_t x = tr.v[i][0], y = tr.v[i][1];
       uint16_t *vt = Vt + buf * D * VP;
-      *reinterpret_cast<uint32_t *>(&vt[(d0 + 0) * VP + (kk ^ vsw(d0 + 0))]) = (a0 & 0xffff) | (b0 << 16);
-      *reinterpret_cast<uint32_t *>(&vt[(d0 + 1) * VP + (kk ^ vsw(d0 + 1))]) = (a0 >> 16) | (b0 & 0xffff0000u);
-      *reinterpret_cast<uint32_t *>(&vt[(d0 + 2) * VP + (kk ^ vsw(d0 + 2))]) = (a1 & 0xffff) | (b1 << 16);
-      *reinterpret_cast<uint32_t *>(&vt[(d0 + 3) * VP + (kk ^ vsw(d0 + 3))]) = (a1 >> 16) | (b1 & 0xffff0000u);
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 0) * VP + (kk ^ vsw(d0 + 0))]) =
+          pack_f16x2(__uint_as_float(x.x << 16), __uint_as_float(y.x << 16));
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 1) * VP + (kk ^ vsw(d0 + 1))]) =
+          pack_f16x2(__uint_as_float(x.x & 0xffff0000u), __uint_as_float(y.x & 0xffff0000u));
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 2) * VP + (kk ^ vsw(d0 + 2))]) =
+          pack_f16x2(__uint_as_float(x.y << 16), __uint_as_float(y.y << 16));
+      *reinterpret_cast<uint32_t *>(&vt[(d0 + 3) * VP + (kk ^ vsw(d0 + 3))]) =
+          pack_f16x2(__uint_as_float(x.y & 0xffff0000u), __uint_as_float(y.y & 0xffff0000u));
     }
   };
 
@@ -178,7 +232,10 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
           st[blk][v] = key <= last_visible ? st[blk][v] : -INFINITY;
         }
     }
-    // tile maximum of the raw scores (a tree, not a 32-deep chain), both lane halves
+    // tile maximum of the raw scores (a tree, not a 32-deep chain), both lane
+    // halves.  The file is built without NaN semantics and with the IEEE mode
+    // bit off, so fmaxf is one v_max (or a third of a v_max3) per value
+    // instead of first quieting every MFMA result.
     float t[16];
 #pragma unroll
     for (int v = 0; v < 16; ++v) t[v] = fmaxf(st[0][v], st[1][v]);
@@ -205,6 +262,8 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
     for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
       for (int v = 0; v < 16; ++v) st[blk][v] = __builtin_amdgcn_exp2f(__builtin_fmaf(st[blk][v], scale_log2, -mref));
+    // row sum (a tree), then the FP16 probabilities, already in the B operand
+    // layout of the 4 key slices
 #pragma unroll
     for (int v = 0; v < 16; ++v) t[v] = st[0][v] + st[1][v];
 #pragma unroll
@@ -212,21 +271,23 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
 #pragma unroll
       for (int v = 0; v < w; ++v) t[v] += t[v + w];
     lrow += halves_sum(t[0]);
-    // O^T += V^T P^T over 4 slices of 16 keys
+    u32x4_t pb[4];
 #pragma unroll
     for (int sl = 0; sl < 4; ++sl) {
       const int blk = sl >> 1, q0 = 2 * (sl & 1);
-      const u32x4_t pb = u32x4_t{pack_f16x2(st[blk][4 * q0 + 0], st[blk][4 * q0 + 1]),
-                                 pack_f16x2(st[blk][4 * q0 + 2], st[blk][4 * q0 + 3]),
-                                 pack_f16x2(st[blk][4 * q0 + 4], st[blk][4 * q0 + 5]),
-                                 pack_f16x2(st[blk][4 * q0 + 6], st[blk][4 * q0 + 7])};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pb[sl][i] = pack_f16x2(st[blk][4 * q0 + 2 * i], st[blk][4 * q0 + 2 * i + 1]);
+    }
+    // O^T += V^T P^T over 4 slices of 16 keys
+#pragma unroll
+    for (int sl = 0; sl < 4; ++sl) {
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt) {
         const int d = 32 * dt + c, sw = vsw(d);
         const uint16_t *vrow = vt + d * VP;
         const u32x2_t lo = *reinterpret_cast<const u32x2_t *>(vrow + ((16 * sl + 4 * h) ^ sw));
         const u32x2_t hi = *reinterpret_cast<const u32x2_t *>(vrow + ((16 * sl + 8 + 4 * h) ^ sw));
-        oacc[dt] = mfma32x32x16_f16(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb, oacc[dt]);
+        oacc[dt] = mfma32x32x16_f16(u32x4_t{lo.x, lo.y, hi.x, hi.y}, pb[sl], oacc[dt]);
       }
     }
   };
@@ -247,6 +308,7 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
 #pragma unroll
     for (int ph = 0; ph < NR; ++ph) {
       const int ti = ti0 + ph, par = ti & 1, t0 = tile_key(ti);
+      if (ti >= nteam) break;  // every team runs the same nteam steps
       lds_barrier();
       store_tile(rr[(ph + 1) % NR], par ^ 1);
       load_tile(rr[(ph + 1) % NR], tile_key(ti + NR + 1));
@@ -289,14 +351,14 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
   // partials: group row R = head*16 + j = 32*wave + c; lane (c, h) holds d = 32dt + 8q + 4h + (0..3)
   if (qvalid) {
     const int R = G * 16, row = 32 * wave + c;
-    float *po = a.part_o + ((unit * a.nsplit + sp) * R + row) * D;
+    float *po = a.part_o + ((size_t)w * R + row) * D;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         *reinterpret_cast<f32x4_t *>(po + 32 * dt + 8 * q + 4 * h) =
             f32x4_t{oacc[dt][4 * q], oacc[dt][4 * q + 1], oacc[dt][4 * q + 2], oacc[dt][4 * q + 3]};
-    if (h == 0) a.part_ml[(unit * a.nsplit + sp) * R + row] = make_float2(mrow, lrow);
+    if (h == 0) a.part_ml[(size_t)w * R + row] = make_float2(mrow, lrow);
   }
 }
 
@@ -306,23 +368,18 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
 // w_s = 2^(m_s - M) / den are formed once, then every thread sums its 4
 // columns over the splits with independent loads.  A split that saw no key of
 // a row has m_s = -inf and weight 0 (its partial is 0, never NaN).
-#define MAX_SPLITS 64
-#ifndef ATTN_WG_TARGET
-#define ATTN_WG_TARGET 256
-#endif
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  __shared__ float2 sML[MAX_SPLITS][16];
-  __shared__ float sW[MAX_SPLITS][16];
+  __shared__ float2 sML[ATTN_MAX_SPLITS][16];
+  __shared__ float sW[ATTN_MAX_SPLITS][16];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int G = a.Hq / a.Hkv, kvh = hq / G, tq = hq % G, R = G * 16;
-  const int n = a.kv_len[b];
-  const int L = min(max(n, 0) + 16, a.max_ctx);
-  const int nsplit = (L + a.split_len - 1) / a.split_len;
-  const size_t unit = (size_t)b * a.Hkv + kvh;
-  const float *po0 = a.part_o + (unit * a.nsplit) * R * D;
-  const float2 *pml0 = a.part_ml + (unit * a.nsplit) * R;
+  const int4 e = a.plan[1 + b];
+  const int nsplit = e.y;
+  const size_t slot0 = (size_t)e.x + (size_t)kvh * nsplit;  // the unit's splits, in key order
+  const float *po0 = a.part_o + slot0 * R * D;
+  const float2 *pml0 = a.part_ml + slot0 * R;
   for (int i = tid; i < nsplit * 16; i += 256) sML[i >> 4][i & 15] = pml0[(i >> 4) * R + tq * 16 + (i & 15)];
   __syncthreads();
   if (tid < 16) {
@@ -354,19 +411,43 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 // would not fit the registers of a second team without spilling
 static int attn_teams(int D) { return D == 64 ? ATTN_TEAMS : 1; }
 
-int attention_split_len(int batch, int Hkv, int max_ctx, int D) {
-  // Aim for about ATTN_WG_TARGET workgroups (with full contexts) across the
-  // batch when two teams share a split, 768 with one; measured on the
-  // 32-sequence 0.5B workload, fewer and longer splits win once a workgroup
-  // holds two teams.  Splits are whole 64-key tiles and a sequence has at
-  // most MAX_SPLITS of them.
-  const long target = attn_teams(D) > 1 ? ATTN_WG_TARGET : 768;
-  long sl = ((long)batch * Hkv * max_ctx + target - 1) / target;
-  const long min_sl = (max_ctx + MAX_SPLITS - 1) / MAX_SPLITS;
-  if (sl < min_sl) sl = min_sl;
-  sl = ((sl + KT - 1) / KT) * KT;
-  if (sl < KT) sl = KT;
-  return (int)sl;
+// compute units of the current device (cached per device)
+static int attn_cu_count() {
+  static int cached[64] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    cached[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return cached[dev];
+}
+
+int attention_grid(int batch, int Hkv, int max_ctx, int D, int split_len) {
+  const int units = batch * Hkv;
+  if (split_len > 0) {  // at most ceil(ceil(max_ctx / 64) / t) splits per unit
+    const int t = split_len / KT, tiles = (max_ctx + KT - 1) / KT;
+    return units * ((tiles + t - 1) / t);
+  }
+  // One resident round: a two-team workgroup (8 waves, ~180 VGPRs each)
+  // takes a whole CU; one-team workgroups of head_dim 128, three per CU.
+  // Every unit needs at least one workgroup.
+  const int resident = attn_cu_count() * (attn_teams(D) > 1 ? 1 : 3);
+  return units > resident ? units : resident;
+}
+
+AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hkv, int max_ctx, int D, int split_len) {
+  return AttnPlanArgs{plan, batch, Hkv, max_ctx, attention_grid(batch, Hkv, max_ctx, D, split_len), attn_teams(D),
+                      split_len > 0 ? split_len / KT : 0};
+}
+
+__global__ __launch_bounds__(64) void attn_plan_kernel(const int32_t *__restrict__ kv_len, AttnPlanArgs p) {
+  attn_plan_wave(kv_len, p, threadIdx.x);
+}
+
+hipError_t launch_attention_plan(const int32_t *kv_len, const AttnPlanArgs &p, hipStream_t st) {
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(64), 0, st, kv_len, p);
+  return hipGetLastError();
 }
 
 template <int D, int NW, int NTEAM>
@@ -383,7 +464,7 @@ hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st) {
   const int G = a.Hq / a.Hkv;
   if (G < 1 || G > 8) return hipErrorInvalidValue;
   const int nw = (G + 1) / 2;
-  const dim3 grid(a.nsplit, a.Hkv, a.batch);
+  const dim3 grid(a.grid);
   if (D == 64) {
     const float sc = (float)(1.4426950408889634 / 8.0);
     switch (nw) {

@@ -98,26 +98,43 @@ hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16
 inline int lm_parts(int V) { return (V / (32 * kLmNT) + 3) / 4; }
 
 // ---- attention ----
+// Split plan of one pass (attn_plan.h): plan[0] = {t, splits}, plan[1 + b] =
+// {first slot of sequence b, splits per KV head of b, kv_len[b]}.
+struct AttnPlanArgs {
+  int4 *plan;   // [1 + batch]
+  int batch, Hkv, max_ctx;
+  int grid;     // workgroups of the attention launch (>= batch * Hkv)
+  int nteam;    // key-tile teams per workgroup: t is a multiple of it
+  int fixed_t;  // > 0: every split has fixed_t tiles; 0: the plan chooses
+};
 struct AttnArgs {
   const uint16_t *q;                 // FP16 [M][Hq*D]
   const uint16_t *k_cache, *v_cache; // BF16, layer base (contiguous or page pool)
   KvLayout kvl;
-  const int32_t *kv_len;
+  const int4 *plan;                  // the pass's split plan
   uint16_t *o;                       // FP16 [M][Hq*D]
-  float *part_o;                     // [B][Hkv][nsplit][G*16][D]
-  float2 *part_ml;                   // [B][Hkv][nsplit][G*16]
-  int batch, Hq, Hkv, max_ctx, split_len, nsplit;
+  float *part_o;                     // [grid][G*16][D], one slot per split
+  float2 *part_ml;                   // [grid][G*16]
+  int batch, Hq, Hkv, max_ctx, grid;
 };
 // split attention (partials) followed by the merge kernel (writes o)
 hipError_t launch_attention(const AttnArgs &a, int D, hipStream_t st);  // splits, then merge
 hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st);
 hipError_t launch_attention_merge(const AttnArgs &a, int D, hipStream_t st);
-int attention_split_len(int batch, int Hkv, int max_ctx, int D);
+// workgroups (= partial slots) of the attention launch: split_len > 0 fixes
+// the split length (keys, a multiple of 64), 0 lets the plan choose
+int attention_grid(int batch, int Hkv, int max_ctx, int D, int split_len);
+// the plan's arguments for a launch of attention_grid(...) workgroups
+AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hkv, int max_ctx, int D, int split_len);
+// the plan on its own (one wave); the pass computes it inside launch_embed
+hipError_t launch_attention_plan(const int32_t *kv_len, const AttnPlanArgs &p, hipStream_t st);
 
 // ---- small kernels ----
 // table: the tile-major BF16 embedding [V][H]
+// (and, with plan.plan non-NULL, the attention split plan of the pass)
 hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16_t *table, float *h,
-                        const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, hipStream_t st);
+                        const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, const AttnPlanArgs &plan,
+                        hipStream_t st);
 // h_out = h + part[0] + ... + part[nsplit-1] (in that order; nsplit may be 0;
 // h_out may be NULL, and is never h, so a launch can be repeated), then
 // x = RMSNorm(h_out) * gain, written as FP16 (out_bf16 = 0) or BF16 (out_bf16 = 1)

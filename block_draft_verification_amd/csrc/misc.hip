@@ -1,14 +1,21 @@
 // Embedding gather, RMSNorm, argmax reduction + prefix accept, KV commit.
+#include "attn_plan.h"
 #include "common.h"
 #include "kernels.h"
 
 // h[m][:] = E[t[m]][:] (BF16 -> fp32).  Also checks that every sequence's
 // block fits its cache (kv_len + 16 <= max_ctx); the QKV step skips the K/V
-// writes of a sequence that does not.
+// writes of a sequence that does not.  One wave of the launch also computes
+// the attention split plan of the pass (attn_plan.h), which depends only on
+// kv_len: every attention launch of the pass then reads it.
 __global__ void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
                              const uint16_t *__restrict__ table, float *__restrict__ h,
-                             const int32_t *__restrict__ kv_len, int max_ctx, KvLayout kvl, int32_t *err) {
+                             const int32_t *__restrict__ kv_len, int max_ctx, KvLayout kvl, int32_t *err,
+                             AttnPlanArgs plan) {
   const int m = blockIdx.x;
+  // the last workgroup's last wave also writes the pass's attention split plan
+  if (plan.plan && m == (int)gridDim.x - 1 && threadIdx.x >= blockDim.x - 64)
+    attn_plan_wave(kv_len, plan, threadIdx.x & 63);
   int t = tokens[m];
   if (t < 0 || t >= V) {
     if (threadIdx.x == 0) set_error(err, SPEC_DERR_TOKEN);
@@ -302,8 +309,10 @@ __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
 }
 
 hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16_t *table, float *h,
-                        const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, hipStream_t st) {
-  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, st, tokens, H, V, table, h, kv_len, max_ctx, kvl, err);
+                        const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, const AttnPlanArgs &plan,
+                        hipStream_t st) {
+  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, st, tokens, H, V, table, h, kv_len, max_ctx, kvl, err,
+                     plan);
   return hipGetLastError();
 }
 
