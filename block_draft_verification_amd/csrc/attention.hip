@@ -363,16 +363,16 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
 }
 
 // o[b*16+j][hq*D + d] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the
-// splits of sequence b, in split order.  One workgroup per (query head, seq):
-// the split statistics are loaded in parallel into LDS, each row's weights
-// w_s = 2^(m_s - M) / den are formed once, then every thread sums its 4
-// columns over the splits with independent loads.  A split that saw no key of
-// a row has m_s = -inf and weight 0 (its partial is 0, never NaN).
+// splits of sequence b, in split order.  One workgroup per (query head, seq);
+// each thread owns 4 columns of one row and walks the splits in chunks of 8,
+// issuing a chunk's (m, l) and o loads together (one memory round trip per
+// chunk; every split of the batch-32 workload fits one chunk), and keeps a
+// running maximum, rescaling its sums when a chunk raises it.  A split that
+// saw no key of a row has m_s = -inf and weight 0 (its partial is 0).
+#define MERGE_CHUNK 8
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
-  __shared__ float2 sML[ATTN_MAX_SPLITS][16];
-  __shared__ float sW[ATTN_MAX_SPLITS][16];
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int G = a.Hq / a.Hkv, kvh = hq / G, tq = hq % G, R = G * 16;
   const int4 e = a.plan[1 + b];
@@ -380,30 +380,39 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const size_t slot0 = (size_t)e.x + (size_t)kvh * nsplit;  // the unit's splits, in key order
   const float *po0 = a.part_o + slot0 * R * D;
   const float2 *pml0 = a.part_ml + slot0 * R;
-  for (int i = tid; i < nsplit * 16; i += 256) sML[i >> 4][i & 15] = pml0[(i >> 4) * R + tq * 16 + (i & 15)];
-  __syncthreads();
-  if (tid < 16) {
-    float M = -INFINITY;
-    for (int s = 0; s < nsplit; ++s) M = fmaxf(M, sML[s][tid].x);
-    float den = 0.f;
-    for (int s = 0; s < nsplit; ++s) {
-      const float2 ml = sML[s][tid];
-      const float e = ml.x == -INFINITY ? 0.f : exp2f(ml.x - M);
-      sW[s][tid] = e;
-      den += e * ml.y;
-    }
-    const float inv = 1.f / den;
-    for (int s = 0; s < nsplit; ++s) sW[s][tid] *= inv;
-  }
-  __syncthreads();
+#pragma unroll
   for (int idx = tid; idx < 16 * D / 4; idx += 256) {
     const int j = idx / (D / 4), d = (idx % (D / 4)) * 4, row = tq * 16 + j;
     const float *p = po0 + (size_t)row * D + d;
+    float mx = -INFINITY, den = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int s = 0; s < nsplit; ++s) acc += sW[s][j] * *reinterpret_cast<const f32x4_t *>(p + (size_t)s * R * D);
+    for (int s0 = 0; s0 < nsplit; s0 += MERGE_CHUNK) {
+      float2 ml[MERGE_CHUNK];
+      f32x4_t o[MERGE_CHUNK];
+#pragma unroll
+      for (int k = 0; k < MERGE_CHUNK; ++k) {
+        const bool in = s0 + k < nsplit;
+        ml[k] = in ? pml0[(size_t)(s0 + k) * R + row] : make_float2(-INFINITY, 0.f);
+        o[k] = in ? *reinterpret_cast<const f32x4_t *>(p + (size_t)(s0 + k) * R * D) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+      float cm = mx;
+#pragma unroll
+      for (int k = 0; k < MERGE_CHUNK; ++k) cm = fmaxf(cm, ml[k].x);
+      if (cm == -INFINITY) continue;  // no split so far saw a key of this row
+      const float sc = mx == -INFINITY ? 0.f : exp2f(mx - cm);
+      acc *= sc;
+      den *= sc;
+#pragma unroll
+      for (int k = 0; k < MERGE_CHUNK; ++k) {
+        const float w = ml[k].x == -INFINITY ? 0.f : exp2f(ml[k].x - cm);
+        acc += w * o[k];
+        den += w * ml[k].y;
+      }
+      mx = cm;
+    }
+    const float inv = 1.f / den;
     *reinterpret_cast<u32x2_t *>(a.o + (size_t)(b * 16 + j) * (a.Hq * D) + hq * D + d) =
-        u32x2_t{pack_f16x2(acc[0], acc[1]), pack_f16x2(acc[2], acc[3])};
+        u32x2_t{pack_f16x2(acc[0] * inv, acc[1] * inv), pack_f16x2(acc[2] * inv, acc[3] * inv)};
   }
 }
 

@@ -16,7 +16,7 @@
 #include "common.h"
 #include "kernels.h"
 
-#define ATTN_MAX_SPLITS 64  // splits per unit the merge step holds
+#define ATTN_MAX_SPLITS 64  // splits per unit: bounds the merge step's work per row
 
 __device__ __forceinline__ int plan_wave_sum(int x) {
 #pragma unroll
