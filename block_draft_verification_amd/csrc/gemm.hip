@@ -50,9 +50,6 @@
 #ifndef GEMM_DEPTH_MT4
 #define GEMM_DEPTH_MT4 2
 #endif
-#ifndef GEMM_BF16_OCC2
-#define GEMM_BF16_OCC2 0
-#endif
 #ifndef GEMM_LM_MAXMT
 #define GEMM_LM_MAXMT 4
 #endif
@@ -213,9 +210,11 @@ __device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1
 // one logical chunk) land on 16 distinct bank groups of a 256-byte window.
 __device__ __forceinline__ int swz8(int row) { return (row >> 2) & 3; }
 
-// Waves per SIMD the register budget is sized for.
+// Waves per SIMD the register budget is sized for: two while a wave holds at
+// most four 32x32 accumulator tiles (BF16 weights included: the lm_head's one
+// vocab tile per wave and 128 rows run two waves per SIMD).
 template <int FMT, int NT, int MT> struct GemmOcc {
-  static constexpr int value = (NT * MT <= 4 && (FMT != SPEC_WFMT_BF16 || GEMM_BF16_OCC2)) ? 2 : 1;
+  static constexpr int value = NT * MT <= 4 ? 2 : 1;
 };
 
 // A8: activations are MXFP8 (e4m3 codes + e8m0 per 32) and the MFMA is the

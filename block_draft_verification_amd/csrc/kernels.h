@@ -90,9 +90,9 @@ hipError_t launch_residual_partial(ActIn x, int M, int N, int K, LinearW w, floa
 // part[m][p] over vocab slices of 4 * 32 * kLmNT rows
 struct ArgmaxPart { float v; int32_t i; };
 #ifndef GEMM_LM_NT
-#define GEMM_LM_NT 2
+#define GEMM_LM_NT 1
 #endif
-constexpr int kLmNT = GEMM_LM_NT;  // 32-row vocab tiles per wave
+constexpr int kLmNT = GEMM_LM_NT;  // 32-row vocab tiles per wave (one: two waves per SIMD fit)
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,
                             float *logits_dump, hipStream_t st);
 inline int lm_parts(int V) { return (V / (32 * kLmNT) + 3) / 4; }
