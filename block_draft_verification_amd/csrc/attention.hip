@@ -69,6 +69,7 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
 
   // Workgroup w takes slot w of the pass's split plan: find its sequence b
   // (entries hold increasing first slots), KV head and split.
+  pin_args(a, scale_log2);
   const int w = blockIdx.x;
   const int4 hdr = a.plan[0];
   if (w >= hdr.y) return;  // whole workgroup: past the plan's splits
@@ -373,6 +374,7 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
 
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
+  pin_args(a);
   const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
   const int G = a.Hq / a.Hkv, kvh = hq / G, tq = hq % G, R = G * 16;
   const int4 e = a.plan[1 + b];

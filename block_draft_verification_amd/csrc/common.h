@@ -150,6 +150,28 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Kernel arguments sit in memory that waves read with scalar loads, which the
+// compiler places where each value is first used; a load whose line is not in
+// the scalar cache yet costs a round trip to L2 or memory, and a kernel whose
+// argument uses are spread out pays several of them in a row.  pin_args, at
+// kernel entry, makes every argument dword live there, so all the loads go out
+// together and later uses hit the scalar cache.
+template <class T>
+__device__ __forceinline__ void pin_arg(const T &v) {
+  if constexpr (sizeof(T) == 4 || sizeof(T) == 8) {
+    asm volatile("" ::"s"(v));
+  } else {
+    static_assert(sizeof(T) % 4 == 0, "dword-sized argument");
+    const uint32_t *p = reinterpret_cast<const uint32_t *>(&v);
+#pragma unroll
+    for (int i = 0; i < (int)(sizeof(T) / 4); ++i) asm volatile("" ::"s"(p[i]));
+  }
+}
+template <class... T>
+__device__ __forceinline__ void pin_args(const T &...v) {
+  (pin_arg(v), ...);
+}
+
 __device__ __forceinline__ void set_error(int32_t *err, int32_t bit) {
   if (err) atomicOr(err, bit);
 }

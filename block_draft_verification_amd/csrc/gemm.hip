@@ -237,6 +237,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
   constexpr int LDS_BYTES = NS * SE * 2 > STAGE_BYTES ? NS * SE * 2 : STAGE_BYTES;
   __shared__ __align__(16) uint16_t As[LDS_BYTES / 2];
 
+  pin_args(ga, epi);
   int nblk, mblk;
   if (!tile_of(blockIdx.x, ga.nb, ga.mb, ga.per_xcd, nblk, mblk)) return;  // whole workgroup
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, h = lane >> 5;

@@ -94,6 +94,7 @@ __global__ __launch_bounds__(256) void norm_kernel(const float *__restrict__ h, 
                                                    const float *__restrict__ gain, int M, int H, float eps,
                                                    void *__restrict__ x, uint8_t *__restrict__ xs,
                                                    float *__restrict__ dump) {
+  pin_args(h, h_out, part, ns, gain, M, H, eps, x, xs, dump);
   constexpr int MAXC = 4;
   __shared__ float red[4];
   const int m = blockIdx.x, tid = threadIdx.x;
