@@ -39,10 +39,12 @@
 #include "kernels.h"
 
 // k steps loaded ahead of the one computed, by activation tile height (32*MT
-// rows).  With tile-major weights, measured depths of 2 to 6 change the 512-
-// and 16-row passes by under 2%, deeper rings costing slightly, so 2 it is.
+// rows).  Measured over whole passes, where every layer's weights come from
+// HBM: 3 for 32-row tiles (QKV, O and down at 512 rows) is 0.6% faster than 2,
+// while deeper rings for 64-row tiles cost; back-to-back repeats of a single
+// launch, whose weights stay cached, favour 2 throughout.
 #ifndef GEMM_DEPTH_MT1
-#define GEMM_DEPTH_MT1 2
+#define GEMM_DEPTH_MT1 3
 #endif
 #ifndef GEMM_DEPTH_MT2
 #define GEMM_DEPTH_MT2 2
@@ -54,7 +56,7 @@
 #define GEMM_LM_MAXMT 4
 #endif
 #ifndef GEMM_MIN_TILES
-#define GEMM_MIN_TILES 512
+#define GEMM_MIN_TILES 256
 #endif
 
 // Raw weight bytes of one 32-row tile for one lane and one k step.
@@ -751,8 +753,9 @@ GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split) {
 }
 
 // 32-row activation tiles per workgroup: wide tiles unless that leaves fewer
-// than GEMM_MIN_TILES workgroups (measured: at 512 rows the gate/up step is
-// fastest with 32-row tiles, 608 workgroups)
+// than GEMM_MIN_TILES workgroups (measured over whole passes: at 512 rows the
+// gate/up step runs 64-row tiles, 304 workgroups, 0.6% faster per pass than
+// 32-row tiles; repeats of a single launch with cached weights favour 32)
 static int pick_mt(int M, int units, int maxMT) {
   int mt = M <= 32 ? 1 : M <= 64 ? 2 : 4;
   if (mt > maxMT) mt = maxMT;
