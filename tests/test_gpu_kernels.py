@@ -188,6 +188,25 @@ def _attn_ref(q, K, V, lens, Hq, Hkv, D):
     return np.concatenate(out)
 
 
+@pytest.mark.parametrize("B,maxlen,seed", [(70, 300, 1), (140, 100, 2)])
+def test_attention_many_sequences(B, maxlen, seed):
+    """The split plan over more than 64 sequences (its scans run in chunks of
+    64) and over more (sequence, KV head) units than one resident round of
+    workgroups (then every unit gets one workgroup)."""
+    Hq, Hkv, D = 4, 2, 64
+    lens = [int(x) for x in np.random.default_rng(seed).integers(0, maxlen, size=B)]
+    max_ctx = maxlen + 16 + 64
+    q, K, V = _attn_case(B, Hq, Hkv, D, lens, max_ctx, seed=seed)
+    ln = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    o = debug_attention(_dev(q), _dev(K), _dev(V), ln, B, Hq, Hkv, D, 0).cpu().numpy()
+    got = _dec(o.view(np.uint16))
+    ref = _attn_ref(q, K, V, lens, Hq, Hkv, D)
+    for h in range(Hq):
+        blk = slice(h * D, (h + 1) * D)
+        rel = np.linalg.norm(got[:, blk] - ref[:, blk], axis=1) / np.linalg.norm(ref[:, blk], axis=1)
+        assert np.all(np.isfinite(got[:, blk])) and rel.max() < 1e-2, f"head {h}: rel {rel.max():.3g}"
+
+
 @pytest.mark.parametrize("Hq,Hkv,D,lens,split", [
     (14, 2, 64, [0, 37, 200], 0),
     (14, 2, 64, [0, 37, 200], 64),
