@@ -21,7 +21,7 @@ struct spec_ctx {
   float *h, *h2;  // residual stream, ping-ponged by the RMSNorm steps
   uint16_t *x, *q, *ao, *act;
   uint8_t *x8, *xs8, *a8, *as8;  // MXFP8 activations: normed x [Mmax][H] (+ e8m0 [Mmax][H/32]), SwiGLU [Mmax][I]
-  float *part_o;
+  uint16_t *part_o;  // attention split outputs, FP16
   float2 *part_ml;
   int32_t *last_tau, *err;
   ArgmaxPart *amax;
@@ -36,7 +36,8 @@ struct spec_ctx {
   // of attention and of the residual projections are per lane.
   int lanes = 1;
   struct LaneBufs {
-    float *part_o, *rpart;
+    uint16_t *part_o;
+    float *rpart;
     float2 *part_ml;
     int4 *plan;  // attention split plan of the lane's pass
   };
@@ -166,7 +167,7 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
                     Mm * Hq * D * 2,                 // q
                     Mm * Hq * D * 2,                 // ao
                     Mm * I * 2,                      // act
-                    (size_t)units * G * 16 * D * 4,  // part_o
+                    (size_t)units * G * 16 * D * 2,  // part_o
                     (size_t)units * G * 16 * 8,      // part_ml
                     (2 * Mm + 3 * (size_t)kv->max_batch) * 4,  // prefill scratch
                     (size_t)kv->max_batch * 4,       // last_tau
@@ -194,7 +195,7 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   c->q = (uint16_t *)(base + off[2]);
   c->ao = (uint16_t *)(base + off[3]);
   c->act = (uint16_t *)(base + off[4]);
-  c->part_o = (float *)(base + off[5]);
+  c->part_o = (uint16_t *)(base + off[5]);
   c->part_ml = (float2 *)(base + off[6]);
   c->pf_tokens = (int32_t *)(base + off[7]);
   c->pf_argmax = c->pf_tokens + Mm;
@@ -406,7 +407,7 @@ int spec_verify_set_lanes(spec_ctx *c, int32_t lanes) {
     char *p = (char *)ws;
     for (int i = 1; i < SPEC_MAX_LANES; ++i) {
       spec_ctx::LaneBufs &lb = c->lane_buf[i];
-      lb.part_o = (float *)p;
+      lb.part_o = (uint16_t *)p;
       p += (c->lane_bytes[0] + 255) & ~(size_t)255;
       lb.part_ml = (float2 *)p;
       p += (c->lane_bytes[1] + 255) & ~(size_t)255;
@@ -618,10 +619,10 @@ int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int3
   a.grid = p.grid;
   const size_t units = (size_t)p.grid, R = (size_t)(Hq / Hkv) * 16;
   void *buf = nullptr;
-  if (hipMalloc(&buf, units * R * D * 4 + units * R * 8 + (1 + (size_t)batch) * 16) != hipSuccess) return SPEC_E_NOMEM;
-  a.part_o = (float *)buf;
-  a.part_ml = (float2 *)((char *)buf + units * R * D * 4);
-  p.plan = (int4 *)((char *)buf + units * R * D * 4 + units * R * 8);
+  if (hipMalloc(&buf, units * R * D * 2 + units * R * 8 + (1 + (size_t)batch) * 16) != hipSuccess) return SPEC_E_NOMEM;
+  a.part_o = (uint16_t *)buf;
+  a.part_ml = (float2 *)((char *)buf + units * R * D * 2);
+  p.plan = (int4 *)((char *)buf + units * R * D * 2 + units * R * 8);
   a.plan = p.plan;
   int rc = SPEC_OK;
   if (launch_attention_plan(kv_len, p, st) != hipSuccess || launch_attention(a, D, st) != hipSuccess ||

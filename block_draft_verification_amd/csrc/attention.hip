@@ -349,22 +349,29 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
     }
   }
 
-  // partials: group row R = head*16 + j = 32*wave + c; lane (c, h) holds d = 32dt + 8q + 4h + (0..3)
+  // partials: group row R = head*16 + j = 32*wave + c; lane (c, h) holds d =
+  // 32dt + 8q + 4h + (0..3).  The split's output is stored normalised, o / l
+  // in FP16 (a convex combination of V rows, so within V's FP16 range), with
+  // (m, l) in fp32: half the bytes of fp32 o, whose stores and re-reads by the
+  // merge cost more than the rounding (2^-12 relative) that the merge then
+  // averages.  A row that saw no key of this split stores 0 and l = 0.
   if (qvalid) {
     const int R = G * 16, row = 32 * wave + c;
-    float *po = a.part_o + ((size_t)w * R + row) * D;
+    uint16_t *po = a.part_o + ((size_t)w * R + row) * D;
+    const float inv = lrow > 0.f ? 1.f / lrow : 0.f;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4_t *>(po + 32 * dt + 8 * q + 4 * h) =
-            f32x4_t{oacc[dt][4 * q], oacc[dt][4 * q + 1], oacc[dt][4 * q + 2], oacc[dt][4 * q + 3]};
+        *reinterpret_cast<u32x2_t *>(po + 32 * dt + 8 * q + 4 * h) =
+            u32x2_t{pack_f16x2(oacc[dt][4 * q] * inv, oacc[dt][4 * q + 1] * inv),
+                    pack_f16x2(oacc[dt][4 * q + 2] * inv, oacc[dt][4 * q + 3] * inv)};
     if (h == 0) a.part_ml[(size_t)w * R + row] = make_float2(mrow, lrow);
   }
 }
 
-// o[b*16+j][hq*D + d] = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s over the
-// splits of sequence b, in split order.  One workgroup per (query head, seq);
+// o[b*16+j][hq*D + d] = sum_s 2^(m_s - M) l_s (o_s / l_s) / sum_s 2^(m_s - M) l_s
+// over the splits of sequence b, in split order (o_s / l_s as stored, FP16).  One workgroup per (query head, seq);
 // each thread owns 4 columns of one row and walks the splits in chunks of 8,
 // issuing a chunk's (m, l) and o loads together (one memory round trip per
 // chunk; every split of the batch-32 workload fits one chunk), and keeps a
@@ -380,12 +387,12 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   const int4 e = a.plan[1 + b];
   const int nsplit = e.y;
   const size_t slot0 = (size_t)e.x + (size_t)kvh * nsplit;  // the unit's splits, in key order
-  const float *po0 = a.part_o + slot0 * R * D;
+  const uint16_t *po0 = a.part_o + slot0 * R * D;
   const float2 *pml0 = a.part_ml + slot0 * R;
 #pragma unroll
   for (int idx = tid; idx < 16 * D / 4; idx += 256) {
     const int j = idx / (D / 4), d = (idx % (D / 4)) * 4, row = tq * 16 + j;
-    const float *p = po0 + (size_t)row * D + d;
+    const uint16_t *p = po0 + (size_t)row * D + d;
     float mx = -INFINITY, den = 0.f;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = 0; s0 < nsplit; s0 += MERGE_CHUNK) {
@@ -395,7 +402,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
       for (int k = 0; k < MERGE_CHUNK; ++k) {
         const bool in = s0 + k < nsplit;
         ml[k] = in ? pml0[(size_t)(s0 + k) * R + row] : make_float2(-INFINITY, 0.f);
-        o[k] = in ? *reinterpret_cast<const f32x4_t *>(p + (size_t)(s0 + k) * R * D) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        const u32x2_t ob = in ? *reinterpret_cast<const u32x2_t *>(p + (size_t)(s0 + k) * R * D) : u32x2_t{0u, 0u};
+        o[k] = f32x4_t{f16_to_f32(ob.x & 0xffff), f16_to_f32(ob.x >> 16), f16_to_f32(ob.y & 0xffff),
+                       f16_to_f32(ob.y >> 16)};
       }
       float cm = mx;
 #pragma unroll
@@ -406,9 +415,9 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
       den *= sc;
 #pragma unroll
       for (int k = 0; k < MERGE_CHUNK; ++k) {
-        const float w = ml[k].x == -INFINITY ? 0.f : exp2f(ml[k].x - cm);
+        const float w = ml[k].x == -INFINITY ? 0.f : exp2f(ml[k].x - cm) * ml[k].y;
         acc += w * o[k];
-        den += w * ml[k].y;
+        den += w;
       }
       mx = cm;
     }

@@ -113,8 +113,8 @@ struct AttnArgs {
   KvLayout kvl;
   const int4 *plan;                  // the pass's split plan
   uint16_t *o;                       // FP16 [M][Hq*D]
-  float *part_o;                     // [grid][G*16][D], one slot per split
-  float2 *part_ml;                   // [grid][G*16]
+  uint16_t *part_o;                  // FP16 [grid][G*16][D]: o / l of each split (slot)
+  float2 *part_ml;                   // [grid][G*16]: (m, l) of each split
   int batch, Hq, Hkv, max_ctx, grid;
 };
 // split attention (partials) followed by the merge kernel (writes o)
