@@ -55,6 +55,9 @@
 #ifndef GEMM_LM_MAXMT
 #define GEMM_LM_MAXMT 4
 #endif
+#ifndef GEMM_SPLIT_TARGET
+#define GEMM_SPLIT_TARGET 256  // split-K workgroup target; 128 and 512 measured 4% slower per pass
+#endif
 #ifndef GEMM_MIN_TILES
 #define GEMM_MIN_TILES 256
 #endif
@@ -742,8 +745,9 @@ GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split) {
   p.nb = (units + 3) / 4;
   p.mb = (M + 32 * MT - 1) / (32 * MT);
   const int tiles = p.nb * p.mb;
-  // split K (residual projections only) until about 256 workgroups, >= 4 k steps per split
-  int s = allow_split ? (256 + tiles - 1) / tiles : 1;
+  // split K (residual projections only) until about GEMM_SPLIT_TARGET
+  // workgroups, >= 4 k steps per split
+  int s = allow_split ? (GEMM_SPLIT_TARGET + tiles - 1) / tiles : 1;
   if (s > ksteps / 4) s = ksteps / 4;
   if (s < 1) s = 1;
   p.spl = (ksteps + s - 1) / s;
