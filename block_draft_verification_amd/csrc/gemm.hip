@@ -559,10 +559,14 @@ struct EpiQkv {
   template <int NT, int MT>
   __device__ void prefetch(int unit, int m0, int M, int h, f32x4_t (&sc)[NT][4], int (&kvl)[2 * MT]) const {
     prefetch_scales<NT>(*this, scale, unit, h, sc);
+    // through the constant address space: scalar loads, which the vector
+    // loads in flight need not wait for (kv_len does not change during the
+    // kernel, and the scalar cache is invalidated at each launch)
+    const __attribute__((address_space(4))) int32_t *kl = (const __attribute__((address_space(4))) int32_t *)o.kv_len;
 #pragma unroll
     for (int i = 0; i < 2 * MT; ++i) {
       const int b = (m0 >> 4) + i;
-      kvl[i] = b < (M >> 4) ? o.kv_len[b] : 0;
+      kvl[i] = b < (M >> 4) ? kl[b] : 0;
     }
   }
   template <int NT, int MT>
