@@ -70,14 +70,18 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
   // Workgroup w takes slot w of the pass's split plan: find its sequence b
   // (entries hold increasing first slots), KV head and split.
   pin_args(a, scale_log2);
-  const int w = blockIdx.x;
+  const int w = blockIdx.x, ln = threadIdx.x & 63;
+  // the header and the first 64 sequences' entries go out together and are
+  // waited for once (the compiler would otherwise order three round trips:
+  // header, then the entries' first slots, then the rest)
   const int4 hdr = a.plan[0];
+  int4 e = a.plan[1 + min(ln, a.batch - 1)];
+  asm volatile("" ::"v"(hdr.x), "v"(hdr.y), "v"(e.x), "v"(e.y), "v"(e.z));
   if (w >= hdr.y) return;  // whole workgroup: past the plan's splits
   int b = 0, first = 0, nsp = 1, n = 0;
   {
-    const int ln = threadIdx.x & 63;
     for (int b0 = 0; b0 < a.batch; b0 += 64) {
-      const int4 e = a.plan[1 + min(b0 + ln, a.batch - 1)];
+      if (b0 > 0) e = a.plan[1 + min(b0 + ln, a.batch - 1)];
       const int k = __popcll(__builtin_amdgcn_ballot_w64(b0 + ln < a.batch && e.x <= w));
       if (k > 0) {
         b = b0 + k - 1;
