@@ -453,7 +453,7 @@ int attention_grid(int batch, int Hkv, int max_ctx, int D, int split_len) {
     const int t = split_len / KT, tiles = (max_ctx + KT - 1) / KT;
     return units * ((tiles + t - 1) / t);
   }
-  // One resident round: a two-team workgroup (8 waves, ~180 VGPRs each)
+  // One resident round: a two-team workgroup (8 waves, ~200 VGPRs each)
   // takes a whole CU; one-team workgroups of head_dim 128, three per CU.
   // Every unit needs at least one workgroup.
   const int resident = attn_cu_count() * (attn_teams(D) > 1 ? 1 : 3);
