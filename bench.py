@@ -251,7 +251,7 @@ def main():
                     help="only run a plain device copy of MIB MiB three times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a single device)", file=sys.stderr)
         sys.exit(2)
 
     import torch
