@@ -16,6 +16,7 @@ struct spec_ctx {
   const float *final_norm;
   spec_kv kv;
   int Mmax, part_units;  // part_units: (sequence, kv head, split) slots for attention partials
+  int attn_cus;          // compute units the attention launches are sized for (fixed at init)
   // workspace (one allocation)
   void *ws;
   float *h, *h2;  // residual stream, ping-ponged by the RMSNorm steps
@@ -152,7 +153,9 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   const int G = Hq / Hkv, I = m->intermediate, V = m->vocab;
   c->Mmax = kv->max_batch * 16;
   int units = 0;
-  for (int b = 1; b <= kv->max_batch; ++b) units = std::max(units, attention_grid(b, Hkv, kv->max_ctx, D, 0));
+  c->attn_cus = attention_device_cus();
+  for (int b = 1; b <= kv->max_batch; ++b)
+    units = std::max(units, attention_grid(b, Hkv, kv->max_ctx, D, 0, c->attn_cus));
   c->part_units = units;
   size_t rfloats = 0;
   for (int b = 1; b <= kv->max_batch; ++b) {
@@ -265,7 +268,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
   float *dump_logits = c->dump_logits ? c->dump_logits + r0 * V : nullptr;
   int32_t *last_tau = c->last_tau + b0;
 
-  const AttnPlanArgs plan = attention_plan_args(c->lane_buf[lane].plan, batch, Hkv, max_ctx, D, 0);
+  const AttnPlanArgs plan = attention_plan_args(c->lane_buf[lane].plan, batch, Hkv, max_ctx, D, 0, c->attn_cus);
   AttnArgs aa{};
   aa.q = q;
   aa.plan = plan.plan;
@@ -606,7 +609,7 @@ int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int3
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return SPEC_E_ARG;
   // the merge step holds at most 64 splits per sequence
   if (split_len && (max_ctx + split_len - 1) / split_len > 64) return SPEC_E_ARG;
-  AttnPlanArgs p = attention_plan_args(nullptr, batch, Hkv, max_ctx, D, split_len);
+  AttnPlanArgs p = attention_plan_args(nullptr, batch, Hkv, max_ctx, D, split_len, attention_device_cus());
   AttnArgs a{};
   a.q = q;
   a.k_cache = k_cache;

@@ -436,7 +436,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
 static int attn_teams(int D) { return D == 64 ? ATTN_TEAMS : 1; }
 
 // compute units of the current device (cached per device)
-static int attn_cu_count() {
+int attention_device_cus() {
   static int cached[64] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -447,7 +447,7 @@ static int attn_cu_count() {
   return cached[dev];
 }
 
-int attention_grid(int batch, int Hkv, int max_ctx, int D, int split_len) {
+int attention_grid(int batch, int Hkv, int max_ctx, int D, int split_len, int cus) {
   const int units = batch * Hkv;
   if (split_len > 0) {  // at most ceil(ceil(max_ctx / 64) / t) splits per unit
     const int t = split_len / KT, tiles = (max_ctx + KT - 1) / KT;
@@ -456,12 +456,12 @@ int attention_grid(int batch, int Hkv, int max_ctx, int D, int split_len) {
   // One resident round: a two-team workgroup (8 waves, ~200 VGPRs each)
   // takes a whole CU; one-team workgroups of head_dim 128, three per CU.
   // Every unit needs at least one workgroup.
-  const int resident = attn_cu_count() * (attn_teams(D) > 1 ? 1 : 3);
+  const int resident = (cus > 0 ? cus : 256) * (attn_teams(D) > 1 ? 1 : 3);
   return units > resident ? units : resident;
 }
 
-AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hkv, int max_ctx, int D, int split_len) {
-  return AttnPlanArgs{plan, batch, Hkv, max_ctx, attention_grid(batch, Hkv, max_ctx, D, split_len), attn_teams(D),
+AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hkv, int max_ctx, int D, int split_len, int cus) {
+  return AttnPlanArgs{plan, batch, Hkv, max_ctx, attention_grid(batch, Hkv, max_ctx, D, split_len, cus), attn_teams(D),
                       split_len > 0 ? split_len / KT : 0};
 }
 

@@ -121,11 +121,15 @@ struct AttnArgs {
 hipError_t launch_attention(const AttnArgs &a, int D, hipStream_t st);  // splits, then merge
 hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st);
 hipError_t launch_attention_merge(const AttnArgs &a, int D, hipStream_t st);
-// workgroups (= partial slots) of the attention launch: split_len > 0 fixes
-// the split length (keys, a multiple of 64), 0 lets the plan choose
-int attention_grid(int batch, int Hkv, int max_ctx, int D, int split_len);
+// compute units of the current device
+int attention_device_cus();
+// workgroups (= partial slots) of the attention launch on a device with `cus`
+// compute units: split_len > 0 fixes the split length (keys, a multiple of
+// 64), 0 lets the plan choose.  A context fixes `cus` when it sizes its
+// buffers, so its launches never outgrow them.
+int attention_grid(int batch, int Hkv, int max_ctx, int D, int split_len, int cus);
 // the plan's arguments for a launch of attention_grid(...) workgroups
-AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hkv, int max_ctx, int D, int split_len);
+AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hkv, int max_ctx, int D, int split_len, int cus);
 // the plan on its own (one wave); the pass computes it inside launch_embed
 hipError_t launch_attention_plan(const int32_t *kv_len, const AttnPlanArgs &p, hipStream_t st);
 
