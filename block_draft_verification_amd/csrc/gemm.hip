@@ -58,6 +58,13 @@
 #ifndef GEMM_SPLIT_TARGET
 #define GEMM_SPLIT_TARGET 256  // split-K workgroup target; 128 and 512 measured 4% slower per pass
 #endif
+#ifndef GEMM_SWIGLU_WAVES
+// waves per workgroup of the 64-row FP16 gate/up tiles (4 or 8).  With 8, a
+// workgroup covers 512 weight rows and two waves share each SIMD: at 512 rows
+// the step runs 152 workgroups, 16.05 against 16.3 us per launch with 304
+// four-wave workgroups (whose 48 doubled-up CUs set the kernel's end).
+#define GEMM_SWIGLU_WAVES 8
+#endif
 #ifndef GEMM_MIN_TILES
 #define GEMM_MIN_TILES 256
 #endif
@@ -226,19 +233,20 @@ template <int FMT, int NT, int MT> struct GemmOcc {
 // scaled 32x32x64 FP8/FP4 one: one MFMA per tile pair and k step, FP8 weights
 // enter raw (their per-row scale stays in the epilogue) and MXFP4 weights with
 // their own e8m0 scales.
-template <bool F16, int FMT, int NT, int MT, class Epi, bool A8 = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(GemmOcc<FMT, NT, MT>::value, 8))) void
+template <bool F16, int FMT, int NT, int MT, class Epi, bool A8 = false, int NWV = 4>  // NWV = waves per workgroup
+__global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(GemmOcc<FMT, NT, MT>::value, 8))) void
 gemm_kernel(GemmArgs ga, Epi epi) {
   static_assert(!A8 || FMT != SPEC_WFMT_BF16, "A8 takes FP8 or MXFP4 weights");
+  static_assert(NWV == 4 || (NWV == 8 && !A8 && MT % 2 == 0), "8-wave workgroups: 16-bit activations, even MT");
   constexpr int ROWS = 32 * MT;             // activation rows per workgroup
   // LDS-DMA instructions per wave per stage: ROWS*8 (16-bit) or ROWS*4 (FP8) chunks of 16 bytes over 256 lanes
-  constexpr int AJ = A8 ? (MT + 1) / 2 : MT;
+  constexpr int AJ = A8 ? (MT + 1) / 2 : 4 * MT / NWV;
   constexpr int SE = A8 ? AJ * 2048 : ROWS * 64;  // 16-bit elements per stage
   constexpr int DIST = gemm_depth<FMT, NT, MT, A8>();  // k steps loaded ahead of the one computed
   constexpr int NS = DIST + 1;              // LDS stages = weight register sets
   // staged epilogue: per wave a [32][LD] fp32 tile of block rows x output columns
   constexpr int COLS = Epi::template cols<NT>(), LD = COLS + 4;
-  constexpr int STAGE_BYTES = Epi::kStaged ? 4 * 32 * LD * 4 : 0;
+  constexpr int STAGE_BYTES = Epi::kStaged ? NWV * 32 * LD * 4 : 0;
   constexpr int LDS_BYTES = NS * SE * 2 > STAGE_BYTES ? NS * SE * 2 : STAGE_BYTES;
   __shared__ __align__(16) uint16_t As[LDS_BYTES / 2];
 
@@ -247,7 +255,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
   if (!tile_of(blockIdx.x, ga.nb, ga.mb, ga.per_xcd, nblk, mblk)) return;  // whole workgroup
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int unit = nblk * 4 + wave;
+  const int unit = nblk * NWV + wave;
   const bool active = unit < epi.units;  // wave-uniform; inactive waves compute on unit 0 and store nothing
   const int m0 = mblk * ROWS;
   const int M = ga.M, K = ga.K, ksteps = K / 64;
@@ -259,7 +267,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
   const uint8_t *agp[AJ];
 #pragma unroll
   for (int i = 0; i < AJ; ++i) {
-    const int P = (wave + 4 * i) * 64 + lane;
+    const int P = (wave + NWV * i) * 64 + lane;
     const int row = A8 ? P >> 2 : P >> 3;
     const int ch = A8 ? (P & 3) ^ swz8(row) : (P & 7) ^ swz(row);
     const int m = row < ROWS && m0 + row < M ? m0 + row : 0;  // rows past M (or padding) read row 0, never stored
@@ -357,7 +365,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
   auto issue_a = [&](int step, int stage) {
 #pragma unroll
     for (int i = 0; i < AJ; ++i)
-      lds_load16(agp[i] + step * (A8 ? 64 : 128), As + stage * SE + (wave + 4 * i) * 512);
+      lds_load16(agp[i] + step * (A8 ? 64 : 128), As + stage * SE + (wave + NWV * i) * 512);
   };
   auto issue_w = [&](WRaw<FMT>(&wr)[NT], uint32_t(&sc)[A8 ? MT : 1], int step) {
 #pragma unroll
@@ -743,10 +751,10 @@ struct EpiArgmax {
 
 // ---------------------------------------------------------------- planning
 
-GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split) {
+GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split, int nwv) {
   GemmPlan p;
   p.MT = MT;
-  p.nb = (units + 3) / 4;
+  p.nb = (units + nwv - 1) / nwv;
   p.mb = (M + 32 * MT - 1) / (32 * MT);
   const int tiles = p.nb * p.mb;
   // split K (residual projections only) until about GEMM_SPLIT_TARGET
@@ -779,10 +787,10 @@ int residual_nsplit(int M, int N, int K) {
 
 // ---------------------------------------------------------------- launchers
 
-template <bool F16, int FMT, int NT, int MT, bool A8, class Epi>
+template <bool F16, int FMT, int NT, int MT, bool A8, class Epi, int NWV = 4>
 static hipError_t go(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<F16, FMT, NT, MT, Epi, A8>), dim3(p.grid_x, 1, p.nsplit), dim3(256), 0, st,
-                     ga, epi);
+  hipLaunchKernelGGL((gemm_kernel<F16, FMT, NT, MT, Epi, A8, NWV>), dim3(p.grid_x, 1, p.nsplit), dim3(64 * NWV), 0,
+                     st, ga, epi);
   return hipGetLastError();
 }
 
@@ -805,7 +813,7 @@ constexpr unsigned kFp8 = 1u << SPEC_WFMT_FP8_E4M3_ROW, kMx4 = 1u << SPEC_WFMT_M
 // else MXFP8 activations on the scaled 32x32x64 MFMA (FP8 / MXFP4 weights).
 template <int NT, unsigned FMTS, class Epi, int MAXMT = (NT > 2 ? 2 : 4)>
 static hipError_t run(ActIn x, int M, int K, const LinearW &w, Epi epi, bool allow_split, hipStream_t st) {
-  const GemmPlan p = gemm_plan(M, epi.units, K / 64, pick_mt(M, epi.units, MAXMT), allow_split);
+  const GemmPlan p = gemm_plan(M, epi.units, K / 64, pick_mt(M, epi.units, MAXMT), allow_split, 4);
   GemmArgs ga{x.x, x.xs, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
               p.nb, p.mb, p.grid_x / 8, p.spl};
   const bool a8 = x.xs != nullptr;
@@ -834,9 +842,22 @@ hipError_t launch_residual_partial(ActIn x, int M, int N, int K, LinearW w, floa
   return run<2, kFp8 | kMx4>(x, M, K, w, EpiPartial<2>{N / 64, N, M, part, fp8_scale(w)}, true, st);
 }
 
+// 64-row FP16-activation tiles in 8-wave workgroups (512 weight rows each)
+template <class Epi>
+static hipError_t run_wide(ActIn x, int M, int K, const LinearW &w, Epi epi, hipStream_t st) {
+  const GemmPlan p = gemm_plan(M, epi.units, K / 64, 2, false, 8);
+  GemmArgs ga{x.x, x.xs, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
+              p.nb, p.mb, p.grid_x / 8, p.spl};
+  if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW) return go<true, SPEC_WFMT_FP8_E4M3_ROW, 2, 2, false, Epi, 8>(p, ga, epi, st);
+  if (w.wfmt == SPEC_WFMT_MXFP4) return go<true, SPEC_WFMT_MXFP4, 2, 2, false, Epi, 8>(p, ga, epi, st);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8_t *a_scales, hipStream_t st) {
   if (a_scales)
     return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2, true>{I / 32, I, fp8_scale(w), a, a_scales}, false, st);
+  if (GEMM_SWIGLU_WAVES == 8 && pick_mt(M, I / 32, 4) == 2)
+    return run_wide(x, M, H, w, EpiSwiglu<2>{I / 32, I, fp8_scale(w), a, nullptr}, st);
   return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2>{I / 32, I, fp8_scale(w), a, nullptr}, false, st);
 }
 

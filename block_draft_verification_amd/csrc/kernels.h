@@ -39,7 +39,7 @@ hipError_t launch_pack_weights(int wfmt, int rows, int cols, const void *w, cons
 struct GemmPlan {
   int MT, nb, mb, spl, nsplit, grid_x;
 };
-GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split);
+GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split, int nwv = 4);  // nwv waves per workgroup
 // splits the residual projection [M][K] x [N][K]^T will use (partials to reduce)
 int residual_nsplit(int M, int N, int K);
 
