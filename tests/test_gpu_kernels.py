@@ -207,16 +207,21 @@ def test_attention_many_sequences(B, maxlen, seed):
         assert np.all(np.isfinite(got[:, blk])) and rel.max() < 1e-2, f"head {h}: rel {rel.max():.3g}"
 
 
-@pytest.mark.parametrize("Hq,Hkv,D,lens,split", [
-    (14, 2, 64, [0, 37, 200], 0),
-    (14, 2, 64, [0, 37, 200], 64),
-    (4, 2, 64, [1000, 5], 0),
-    (32, 8, 128, [300, 64], 0),
-    (8, 1, 128, [700], 128),
-    (2, 2, 64, [63, 64, 65, 127], 64),
+# pad = cache rows beyond the longest sequence's block; 0: that block ends at
+# the cache's last row (the cache is full), so the last tile is clamped there
+@pytest.mark.parametrize("Hq,Hkv,D,lens,split,pad", [
+    (14, 2, 64, [0, 37, 200], 0, 64),
+    (14, 2, 64, [0, 37, 200], 64, 64),
+    (4, 2, 64, [1000, 5], 0, 64),
+    (4, 2, 64, [1000, 5], 0, 0),
+    (32, 8, 128, [300, 64], 0, 64),
+    (8, 1, 128, [700], 128, 64),
+    (8, 1, 128, [700], 128, 0),
+    (2, 2, 64, [63, 64, 65, 127], 64, 64),
+    (2, 2, 64, [48, 3], 64, 0),
 ])
-def test_attention(Hq, Hkv, D, lens, split):
-    B, max_ctx = len(lens), max(lens) + 16 + 64
+def test_attention(Hq, Hkv, D, lens, split, pad):
+    B, max_ctx = len(lens), max(lens) + 16 + pad
     q, K, V = _attn_case(B, Hq, Hkv, D, lens, max_ctx, seed=sum(lens) + Hq)
     ln = torch.tensor(lens, dtype=torch.int32, device="cuda")
     o = debug_attention(_dev(q), _dev(K), _dev(V), ln, B, Hq, Hkv, D, split).cpu().numpy()
