@@ -217,6 +217,8 @@ def test_attention_many_sequences(B, maxlen, seed):
     (32, 8, 128, [300, 64], 0, 64),
     (8, 1, 128, [700], 128, 64),
     (8, 1, 128, [700], 128, 0),
+    (4, 2, 128, [300, 64, 0], 0, 64),
+    (3, 3, 128, [129, 1000], 0, 0),
     (2, 2, 64, [63, 64, 65, 127], 64, 64),
     (2, 2, 64, [48, 3], 64, 0),
 ])
