@@ -474,13 +474,13 @@ hipError_t launch_attention_plan(const int32_t *kv_len, const AttnPlanArgs &p, h
   return hipGetLastError();
 }
 
-template <int D, int NW, int NTEAM>
+template <int D, int NW, int NTEAM, int NR = ATTN_NR>
 static hipError_t go_attn(const AttnArgs &a, dim3 grid, float sc, hipStream_t st) {
   const int lds = NTEAM * attn_team_halfs<D>() * 2;
   static const hipError_t attr =  // once per instantiation: allow more than 64 KB of LDS
-      hipFuncSetAttribute((const void *)attn_kernel<D, NW, NTEAM>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+      hipFuncSetAttribute((const void *)attn_kernel<D, NW, NTEAM, NR>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((attn_kernel<D, NW, NTEAM>), grid, dim3(64 * NW * NTEAM), lds, st, a, sc);
+  hipLaunchKernelGGL((attn_kernel<D, NW, NTEAM, NR>), grid, dim3(64 * NW * NTEAM), lds, st, a, sc);
   return hipGetLastError();
 }
 
@@ -500,7 +500,9 @@ hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st) {
   } else if (D == 128) {
     const float sc = (float)(1.4426950408889634 / 11.313708498984761);
     switch (nw) {
-      case 1: return go_attn<128, 1, 1>(a, grid, sc, st);
+      // one wave holds a whole 64 x 128 K and V tile per register set: one set
+      // in flight, as two would spill
+      case 1: return go_attn<128, 1, 1, 1>(a, grid, sc, st);
       case 2: return go_attn<128, 2, 1>(a, grid, sc, st);
       case 3: return go_attn<128, 3, 1>(a, grid, sc, st);
       default: return go_attn<128, 4, 1>(a, grid, sc, st);
