@@ -38,6 +38,14 @@
 #include "common.h"
 #include "kernels.h"
 
+// Work-item and workgroup ids as intrinsics: this file is built without IEEE
+// mode, and the device library's id functions, built with it, are then not
+// inlined (each kernel would call them, and the workgroup id would come back
+// in a vector register).
+__device__ __forceinline__ int wg_x() { return __builtin_amdgcn_workgroup_id_x(); }
+__device__ __forceinline__ int wg_y() { return __builtin_amdgcn_workgroup_id_y(); }
+__device__ __forceinline__ int wi_x() { return __builtin_amdgcn_workitem_id_x(); }
+
 #define KT 64  // keys per LDS tile
 #define RESCALE 8.f  // log2 headroom of the lazily moved softmax reference
 #ifndef ATTN_TEAMS
@@ -70,7 +78,7 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
   // Workgroup w takes slot w of the pass's split plan: find its sequence b
   // (entries hold increasing first slots), KV head and split.
   pin_args(a, scale_log2);
-  const int w = blockIdx.x, ln = threadIdx.x & 63;
+  const int w = wg_x(), ln = wi_x() & 63;
   // the header and the first 64 sequences' entries go out together and are
   // waited for once (the compiler would otherwise order three round trips:
   // header, then the entries' first slots, then the rest)
@@ -102,8 +110,8 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
   // (tile i of the split goes to team i % NTEAM), each with its own LDS tiles,
   // and combine their softmax states through LDS at the end, so the split
   // still leaves one partial.  tid, lane and wave below are team-local.
-  const int team = __builtin_amdgcn_readfirstlane(threadIdx.x / T);
-  const int tid = threadIdx.x % T, lane = tid & 63, c = lane & 31, h = lane >> 5;
+  const int team = __builtin_amdgcn_readfirstlane(wi_x() / T);
+  const int tid = wi_x() % T, lane = tid & 63, c = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   uint16_t *const Ks = attn_lds + team * attn_team_halfs<D>();  // [2][KT * KP]
   uint16_t *const Vt = Ks + 2 * KT * KP;                         // [2][D * VP]
@@ -386,11 +394,14 @@ __global__ __launch_bounds__(64 * NW * NTEAM) void attn_kernel(AttnArgs a, float
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(AttnArgs a) {
   pin_args(a);
-  const int hq = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int hq = wg_x(), b = wg_y(), tid = wi_x();
   const int G = a.Hq / a.Hkv, kvh = hq / G, tq = hq % G, R = G * 16;
-  const int4 e = a.plan[1 + b];
-  const int nsplit = e.y;
-  const size_t slot0 = (size_t)e.x + (size_t)kvh * nsplit;  // the unit's splits, in key order
+  // the plan entry is uniform: a scalar load (the plan does not change during
+  // the kernel, and the scalar cache is invalidated at each launch), one
+  // shorter round trip before the partials' loads
+  const __attribute__((address_space(4))) int32_t *e = (const __attribute__((address_space(4))) int32_t *)(a.plan + 1 + b);
+  const int nsplit = e[1];
+  const size_t slot0 = (size_t)e[0] + (size_t)kvh * nsplit;  // the unit's splits, in key order
   const uint16_t *po0 = a.part_o + slot0 * R * D;
   const float2 *pml0 = a.part_ml + slot0 * R;
 #pragma unroll
@@ -466,7 +477,7 @@ AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hkv, int max_ctx, in
 }
 
 __global__ __launch_bounds__(64) void attn_plan_kernel(const int32_t *__restrict__ kv_len, AttnPlanArgs p) {
-  attn_plan_wave(kv_len, p, threadIdx.x);
+  attn_plan_wave(kv_len, p, wi_x());
 }
 
 hipError_t launch_attention_plan(const int32_t *kv_len, const AttnPlanArgs &p, hipStream_t st) {
