@@ -73,3 +73,20 @@ def test_gemm_weight_loads_waited(tmp_path):
     n, hz = find_hazards(out.read_text())
     assert n >= 10, "no gemm kernels found in the assembly"
     assert not hz, "\n".join(hz[:10])
+
+
+@pytest.mark.skipif(not shutil.which(HIPCC) and not os.path.exists(HIPCC), reason="hipcc not available")
+@pytest.mark.parametrize("src", ["attention.hip", "misc.hip"])
+def test_kernels_make_no_calls(tmp_path, src):
+    """Device code is fully inlined: no out-of-line calls, in particular to the
+    device library's id functions, which the inliner leaves alone in a file
+    built with a different IEEE mode (attention.hip's flags)."""
+    import sys
+    sys.path.insert(0, ROOT)
+    import __graft_entry__ as g
+    out = tmp_path / (src + ".s")
+    subprocess.run([HIPCC, *g.FLAGS, *g.SOURCE_FLAGS.get(src, []), "-I", g.CSRC, "--cuda-device-only", "-S",
+                    os.path.join(g.CSRC, src), "-o", str(out)], check=True, capture_output=True)
+    asm = out.read_text()
+    assert "s_endpgm" in asm
+    assert "s_swappc" not in asm and "__ockl_" not in asm
