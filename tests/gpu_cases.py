@@ -16,6 +16,8 @@ argmax (self-consistency).
 """
 from __future__ import annotations
 
+import json
+import os
 import sys
 import time
 from dataclasses import dataclass
@@ -29,6 +31,9 @@ from block_draft_verification_amd import DeviceModel, Verifier
 
 MARGIN = 1e-2
 REL_TOL = 2e-2
+# When set, every comparison appends its statistics (rows and sequences
+# exempt under the margin rule, largest relative errors) as one JSON line.
+PARITY_LOG = os.environ.get("SPEC_PARITY_LOG")
 
 
 def log(msg):
@@ -178,6 +183,19 @@ def compare(ref, got, blocks, seqs=None, check_logits=True):
     stats["seqs_exempt"] = float(1 - decided.mean())
     assert np.array_equal(tau[decided], ref.tau[decided]), "tau differs from the oracle"
     assert np.array_equal(bonus[decided], ref.bonus[decided]), "bonus differs from the oracle"
+    stats["seqs_compared"] = len(seqs)
+    stats["seqs_decided"] = int(decided.sum())
     stats["tau_gpu"] = tau.tolist()
     stats["tau_oracle"] = ref.tau.tolist()
+    record(stats)
     return stats
+
+
+def record(stats):
+    """Print the parity statistics and, with SPEC_PARITY_LOG set, append them
+    (tagged with the running test) to that file."""
+    test = os.environ.get("PYTEST_CURRENT_TEST", "").split(" ")[0]
+    log(f"parity {test}: {json.dumps(stats)}")
+    if PARITY_LOG:
+        with open(PARITY_LOG, "a") as f:
+            f.write(json.dumps({"test": test, **stats}) + "\n")

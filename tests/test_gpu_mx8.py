@@ -261,6 +261,12 @@ def _mx_compare(name, case, seqs, ref_exact, ref, got, one_layer):
         decided = np.array([np.all(ref.margin[i, :ref.tau[i]] > MARGIN_MX) for i in range(len(seqs))])
         assert np.array_equal(tau[decided], ref.tau[decided]), "tau differs from the MXFP8 oracle"
     else:
+        # A smoke bar, not a parity bar: through a whole random-weight stack
+        # the GPU's and the oracle's MXFP8 computations decorrelate (an
+        # encoder decision flipped by ~1e-3 of upstream difference moves a
+        # value by a whole e4m3 step, and each layer amplifies it ~10x), so
+        # the result is only bounded by the size of the mode's own effect.
+        # The one-layer cases above carry the per-row check.
         assert rel.max() <= 1.5 * rel_mode.max(), f"hidden rel {rel.max():.3g} vs the mode's {rel_mode.max():.3g}"
         assert rel_exact.max() <= 1.5 * rel_mode.max(), "farther from the exact oracle than the mode moves it"
     for i, b in enumerate(seqs):  # self-consistency of tau and bonus with the GPU's own argmax

@@ -1,15 +1,17 @@
-"""Paged KV cache: the same verify pass over a page pool reached through a
-page table.  Paging only moves where rows live, so every result must be
-bit-identical to the contiguous layout (and the contiguous layout is the one
-held to the oracle elsewhere)."""
+"""Paged KV cache ("The Inference Stack Behind OCRia", KV-cache section:
+block table and slot mapping): the same verify pass over a page pool reached
+through a page table.  The paged pass is held to the float64 oracle on its
+own, and, since paging only moves where rows live, every result must also be
+bit-identical to the contiguous layout."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 import workload as W
 from block_draft_verification_amd import DeviceModel, Verifier
 from block_draft_verification_amd.decode import ar_decode, planted_drafts, spec_decode
-from gpu_cases import log
+from gpu_cases import compare, log
 
 pytestmark = pytest.mark.gpu
 
@@ -28,6 +30,57 @@ def _verify_dump(dev, ver, blocks):
     torch.cuda.synchronize()
     ver.set_dump(None, None)
     return {k: v.cpu().numpy() for k, v in out.items()}, hid.cpu().numpy()
+
+
+def test_paged_vs_oracle_05b():
+    """The 0.5B model over a shuffled pool of 64-row pages (4 ragged
+    sequences, blocks planted from the oracle's greedy continuation with L =
+    16, 5, 9, 1): hidden states, logits, argmax, tau and bonus against the
+    oracle under the whole-pass parity rule; every block K/V row written
+    through the page table within 2e-2 of the oracle's, committed rows
+    untouched bit for bit."""
+    m = W.M05B
+    wts = W.model_weights(m, seed=0)
+    B, cap, ps = 4, 1024, 64
+    lens = np.array([600, 512, 700, 531], np.int32)
+    kvs = [W.synthetic_kv_layer(m, 0, l, lens, cap) for l in range(m.n_layers)]
+    num_pages = B * (cap // ps) + 7
+    table = _shuffled_table(B, cap // ps, num_pages, seed=3)
+    om = oracle.OracleModel(m, wts)
+    okv = oracle.OracleKV.from_bf16(m, [k for k, _ in kvs], [v for _, v in kvs], lens)
+    pend = W.child_rng(0, 975).integers(0, m.vocab, size=B)
+    log("oracle greedy continuation of 4 sequences")
+    cont = oracle.greedy_continuation(om, okv, pend)
+    L = [16, 5, 9, 1]
+    blocks = np.stack([W.plant_block(cont[b], L[b], m.vocab, W.child_rng(0, 976, b)) for b in range(B)])
+    ref = oracle.verify_block(om, okv, blocks)
+    assert ref.tau.tolist() == L
+    dp = DeviceModel(m, wts, max_batch=B, max_ctx=cap, kv_layers=kvs, kv_len=lens,
+                     page_table=table, page_size=ps, num_pages=num_pages)
+    vp = Verifier(dp)
+    hid = torch.full((B * 16, m.hidden), float("nan"), device="cuda")
+    lg = torch.full((B * 16, m.vocab), float("nan"), device="cuda")
+    vp.set_dump(hidden=hid, logits=lg)
+    out = vp.verify(torch.from_numpy(blocks.astype(np.int32)).cuda())
+    torch.cuda.synchronize()
+    vp.set_dump(None, None)
+    got = {k: v.cpu().numpy() for k, v in out.items()}
+    got["hidden"] = hid.cpu().numpy().reshape(B, 16, -1)
+    got["logits"] = lg.cpu().numpy().reshape(B, 16, -1)
+    stats = compare(ref, got, blocks)
+    log(f"paged vs oracle: {stats}")
+    for l in (0, m.n_layers - 1):
+        for b in range(B):
+            n = int(lens[b])
+            for which, cache0, ocache in (("k", kvs[l][0], okv.K[l][b]), ("v", kvs[l][1], okv.V[l][b])):
+                rows = dp.cache_rows(l, b, n + 16, which).cpu().numpy().view(np.uint16)
+                assert np.array_equal(rows[:, :n], cache0[b, :, :n]), f"layer {l} seq {b} {which}: prefix changed"
+                blk = oracle.decode_bf16(rows[:, n:])
+                ref_rows = ocache[:, n:n + 16]
+                rel = np.linalg.norm(blk - ref_rows, axis=-1) / np.linalg.norm(ref_rows, axis=-1)
+                assert rel.max() < 2e-2, f"layer {l} seq {b} {which}: block rows {rel.max():.3g}"
+    assert vp.device_error() == 0
+    vp.close()
 
 
 def test_paged_equals_contiguous_05b():
