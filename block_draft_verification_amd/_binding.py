@@ -1,9 +1,10 @@
 """ctypes binding of libspecverify.so: argument marshalling only.
 
 Every step of the verify pass runs in the HIP library; this module only
-places caller-owned buffers in device memory (torch tensors), fills the
-descriptor structs of include/spec_verify.h and forwards pointers and the
-current HIP stream.  It fails loudly when the library is missing.
+places caller-owned buffers in device memory (torch tensors, weights in the
+row-major layout a checkpoint holds), fills the descriptor structs of
+include/spec_verify.h and forwards pointers and the current HIP stream.  It
+fails loudly when the library is missing.
 """
 from __future__ import annotations
 
@@ -19,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libspecverify.so")
 SPEC_OK = 0
 WFMT_FP8_E4M3_ROW, WFMT_MXFP4, WFMT_BF16 = 1, 2, 3
 ACT_FMTS = {"fp16": 0, "mxfp8": 1}
-DERR_TOKEN, DERR_CAPACITY, DERR_COMMIT = 1, 2, 4
+DERR_TOKEN, DERR_CAPACITY, DERR_COMMIT, DERR_LENGTH, DERR_PAGE, DERR_RANGE = 1, 2, 4, 8, 16, 32
 BLOCK = 16
 
 _P = ctypes.c_void_p
@@ -57,9 +58,10 @@ EXPORTS = {
     "spec_verify_destroy": (_I, [_P]),
     "spec_get_device_error": (_I, [_P, ctypes.POINTER(_I), _P]),
     "spec_status_str": (ctypes.c_char_p, [_I]),
+    "spec_last_error": (ctypes.c_char_p, []),
     "spec_debug_set_dump": (_I, [_P, _P, _P]),
-    "spec_pack_weights": (_I, [_I, _I, _I, _P, _P, _P, _P, _P]),
     "spec_debug_linear": (_I, [_I, _I, _I, _P, _P, _P, _I, _P, _P]),
+    "spec_debug_residual": (_I, [_I, _I, _I, _P, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P]),
     "spec_debug_quant_mx8": (_I, [_I, _I, _P, _P, _P, _P]),
     "spec_debug_linear_mx8": (_I, [_I, _I, _I, _P, _P, _P, _P, _I, _P, _P]),
     "spec_debug_rmsnorm": (_I, [_I, _I, _P, _P, ctypes.c_float, _I, _P, _P, _P]),
@@ -97,7 +99,8 @@ class SpecError(RuntimeError):
 
 def _check(rc: int, what: str):
     if rc != SPEC_OK:
-        raise SpecError(f"{what}: {load_library().spec_status_str(rc).decode()} ({rc})")
+        lib = load_library()
+        raise SpecError(f"{what}: {lib.spec_status_str(rc).decode()} ({rc}): {lib.spec_last_error().decode()}")
 
 
 def _stream():
@@ -119,21 +122,9 @@ def _wfmt(name: str) -> int:
     return {"fp8": WFMT_FP8_E4M3_ROW, "mxfp4": WFMT_MXFP4}[name]
 
 
-def pack_weights(w: torch.Tensor, scales, wfmt: int, rows: int, cols: int):
-    """Row-major device weights -> the tile-major layout the kernels read
-    (spec_pack_weights).  Returns (w_packed, scales_packed); FP8 row scales
-    and absent BF16 scales are returned as given."""
-    wp = torch.empty_like(w)
-    sp = torch.empty_like(scales) if wfmt == WFMT_MXFP4 else scales
-    _check(load_library().spec_pack_weights(wfmt, rows, cols, _ptr(w), _ptr(scales), _ptr(wp),
-                                            _ptr(sp) if wfmt == WFMT_MXFP4 else None, _stream()),
-           "spec_pack_weights")
-    return wp, sp
-
-
 class DeviceModel:
-    """Caller-owned device buffers: weights in the boundary's layout, the BF16
-    KV cache for K and V, and kv_len.  Contiguous cache: [L][max_batch][Hkv]
+    """Caller-owned device buffers: row-major weights (the library repacks its
+    own copy at init), the BF16 KV cache for K and V, and kv_len.  Contiguous cache: [L][max_batch][Hkv]
     [max_ctx][D].  Paged cache (page_table given, int [max_batch][max_ctx /
     page_size]): a pool [L][num_pages][Hkv][page_size][D]; kv_layers are then
     given in the contiguous shape and scattered into the pages."""
@@ -145,20 +136,9 @@ class DeviceModel:
         self.page_table = None if page_table is None else torch.as_tensor(
             np.asarray(page_table, np.int32), device=device).contiguous()
         m = shape
-        mf = _wfmt(m.mlp_format)
-        dims = {"qkv": (m.qkv_rows, m.hidden, WFMT_FP8_E4M3_ROW), "o": (m.hidden, m.n_q_heads * m.head_dim,
-                                                                       WFMT_FP8_E4M3_ROW),
-                "gate_up": (2 * m.intermediate, m.hidden, mf), "down": (m.hidden, m.intermediate, mf)}
-        self.layers = []
-        for lw in weights["layers"]:
-            d = {k: _dev(v, device) for k, v in lw.items()}
-            for name, (rows, cols, fmt) in dims.items():  # the kernels read tile-major weights
-                d["w_" + name], d["s_" + name] = pack_weights(d["w_" + name], d["s_" + name], fmt, rows, cols)
-            self.layers.append(d)
-        V, H = m.vocab, m.hidden
-        self.embed = pack_weights(_dev(weights["embed"], device), None, WFMT_BF16, V, H)[0]
-        self.lm_head = None if weights.get("lm_head") is None else pack_weights(
-            _dev(weights["lm_head"], device), None, WFMT_BF16, V, H)[0]
+        self.layers = [{k: _dev(v, device) for k, v in lw.items()} for lw in weights["layers"]]
+        self.embed = _dev(weights["embed"], device)
+        self.lm_head = None if weights.get("lm_head") is None else _dev(weights["lm_head"], device)
         self.final_norm = _dev(weights["final_norm"], device)
         if self.page_table is None:
             cache_shape = (m.n_layers, max_batch, m.n_kv_heads, max_ctx, m.head_dim)
@@ -312,6 +292,22 @@ def debug_linear(x_bf16: torch.Tensor, w: torch.Tensor, scales, wfmt: int, N: in
     _check(load_library().spec_debug_linear(M, N, K, _ptr(x_bf16), _ptr(w), _ptr(scales), wfmt, _ptr(y),
                                             _stream()), "spec_debug_linear")
     return y
+
+
+def debug_residual(x_f16: torch.Tensor, w: torch.Tensor, scales, wfmt: int, h_in: torch.Tensor,
+                   gain: torch.Tensor, xg_bf16: bool = False):
+    """One residual projection with the next RMSNorm folded in (spec_debug_residual):
+    returns (h_out fp32 [M, N], xg 16-bit bits int16 [M, N], ssp fp32 [M, ld])."""
+    M, K = x_f16.shape
+    N = h_in.shape[1]
+    ld = ((N // 32 + 3) // 4) * 4
+    h_out = torch.empty_like(h_in)
+    xg = torch.empty(M, N, dtype=torch.int16, device=h_in.device)
+    ssp = torch.full((M, ld), float("nan"), dtype=torch.float32, device=h_in.device)
+    _check(load_library().spec_debug_residual(M, N, K, _ptr(x_f16), _ptr(w), _ptr(scales), wfmt, _ptr(h_in),
+                                              _ptr(gain), 1 if xg_bf16 else 0, _ptr(h_out), _ptr(xg), _ptr(ssp),
+                                              _stream()), "spec_debug_residual")
+    return h_out, xg, ssp
 
 
 def debug_quant_mx8(x: torch.Tensor):

@@ -20,29 +20,32 @@
 // 8-element slice i as the k operand of the step's i-th MFMA, and the
 // activation side reads the same k slices (act_chunk), so A and B always pair
 // the same k and the sum over k is complete.  The weights are tile-major
-// (kernels.h): each wave-wide weight load is one contiguous kilobyte, which
-// streams about 2.7x faster per compute unit than 32 rows x 32 bytes.
-// Lane (c, h) ends with the outputs of block row c for the weight rows
-// 8q + 4h + (0..3), q = 0..3 of each tile, so every epilogue (scale, RoPE
-// pair, gate/up pair, residual partial, argmax) runs on registers.
+// (kernels.h): each wave-wide weight load is one contiguous kilobyte.
+// Lane (c, h) ends with the outputs of block row c for the tile rows
+// 8q + 4h + (0..3), q = 0..3, so rows r and r + 16 of a tile sit in the same
+// lane: the library's packing puts the two rows an epilogue must combine
+// (a RoPE pair, a gate row and its up row) at exactly those positions.
 //
-// Work split: a workgroup = 4 waves side by side along N (wave = one "unit"
-// of NT 32-row weight tiles) sharing one activation tile of 32*MT rows.  The
-// activation tile goes straight from global memory to LDS (one barrier per k
-// step); each wave streams its own weight rows into registers.  Both run
-// a few k steps ahead of the MFMAs (more for narrow tiles).  Workgroups that share weight rows
-// (all M blocks of one N block) are placed on one XCD so its L2 serves the
-// re-reads.  Residual projections with too few output tiles to fill the chip
-// split K over gridDim.z and write fp32 partials; the next RMSNorm adds them
-// in split order, so results do not depend on timing.
+// Work split: a workgroup = NWV waves, NG side by side along N (a wave = a
+// "unit" of NT 32-row weight tiles) times KS along K, sharing one activation
+// tile of 32*MT rows.  A pipeline stage holds KS consecutive 64-wide k steps
+// of the activation tile; the waves of k group g compute step g of each
+// stage, and the groups' accumulators are added in group order at the end.
+// The activation tile goes straight from global memory to LDS (one barrier
+// per stage); each wave streams its own weight rows into registers.  Both run
+// a few stages ahead of the MFMAs.  Workgroups that share weight rows (all M
+// blocks of one N block) are placed on one XCD so its L2 serves the re-reads.
+//
+// Inputs that are an RMSNorm's product h * g (gain folded in, normalisation
+// left out) come with per-row partial sums of squares of h: the kernel adds
+// them up, in a fixed order, into r = 1 / sqrt(mean(h^2) + eps) and scales
+// its outputs by r.  The residual projections produce exactly that: the new
+// residual stream, h * g of the next RMSNorm, and the partial sums.
 #include "common.h"
 #include "kernels.h"
 
-// k steps loaded ahead of the one computed, by activation tile height (32*MT
-// rows).  Measured over whole passes, where every layer's weights come from
-// HBM: 3 for 32-row tiles (QKV, O and down at 512 rows) is 0.6% faster than 2,
-// while deeper rings for 64-row tiles cost; back-to-back repeats of a single
-// launch, whose weights stay cached, favour 2 throughout.
+// Stages loaded ahead of the one computed, by activation tile height (32*MT
+// rows): 3 for 32-row tiles, 2 for taller ones (measured over whole passes).
 #ifndef GEMM_DEPTH_MT1
 #define GEMM_DEPTH_MT1 3
 #endif
@@ -56,17 +59,10 @@
 #define GEMM_LM_MAXMT 4
 #endif
 #ifndef GEMM_SPLIT_TARGET
-#define GEMM_SPLIT_TARGET 256  // split-K workgroup target; 128 and 512 measured 4% slower per pass
+#define GEMM_SPLIT_TARGET 256  // split-K workgroup target of the MXFP8 mode's residual projections
 #endif
-#ifndef GEMM_SWIGLU_WAVES
-// waves per workgroup of the 64-row FP16 gate/up tiles (4 or 8).  With 8, a
-// workgroup covers 512 weight rows and two waves share each SIMD: at 512 rows
-// the step runs 152 workgroups, 16.05 against 16.3 us per launch with 304
-// four-wave workgroups (whose 48 doubled-up CUs set the kernel's end).
-#define GEMM_SWIGLU_WAVES 8
-#endif
-#ifndef GEMM_MIN_TILES
-#define GEMM_MIN_TILES 256
+#ifndef GEMM_WG_TARGET
+#define GEMM_WG_TARGET 200  // workgroups a decoder GEMM launch aims for (the chip has 256 compute units)
 #endif
 
 // Raw weight bytes of one 32-row tile for one lane and one k step.
@@ -80,11 +76,12 @@ template <int FMT> constexpr int w_loads() { return FMT == SPEC_WFMT_BF16 ? 4 : 
 // registers of one tile's raw weights for one step
 template <int FMT> constexpr int w_regs() { return FMT == SPEC_WFMT_BF16 ? 16 : FMT == SPEC_WFMT_MXFP4 ? 5 : 8; }
 
-// Pipeline depth: the tile height's depth, capped so that the register ring
-// (depth + 1 sets of weights and activation exponents) stays within 112 VGPRs.
-template <int FMT, int NT, int MT, bool A8>
+// Pipeline depth in stages: the tile height's depth (two when a stage holds
+// several k steps), capped so that the register ring (depth + 1 sets of
+// weights and activation exponents) stays within 112 VGPRs.
+template <int FMT, int NT, int MT, bool A8, int KS>
 constexpr int gemm_depth() {
-  const int want = MT == 1 ? GEMM_DEPTH_MT1 : MT == 2 ? GEMM_DEPTH_MT2 : GEMM_DEPTH_MT4;
+  const int want = KS > 1 ? 2 : MT == 1 ? GEMM_DEPTH_MT1 : MT == 2 ? GEMM_DEPTH_MT2 : GEMM_DEPTH_MT4;
   const int cap = 112 / (NT * w_regs<FMT>() + (A8 ? MT : 0)) - 1;
   const int d = want < cap ? want : cap;
   return d < 2 ? 2 : d;
@@ -182,9 +179,10 @@ struct GemmArgs {
   const uint8_t *xs;  // A8: e8m0 scale of each 32 activations [M][K/32]
   int M, K;
   const uint8_t *w, *s;
-  int nb, mb;         // N blocks (4 units each), M blocks
+  int nb, mb;         // N blocks (NG units each), M blocks
   int per_xcd;        // tiles per XCD (gridDim.x = 8 * per_xcd)
   int spl;            // k steps (of 64) per split; gridDim.z splits
+  NormRows nr;        // per-row normalisation of the input rows (nr.ssp NULL: none)
 };
 
 // Linear workgroup id -> (N block, M block).  Workgroup L runs on XCD L % 8;
@@ -229,47 +227,70 @@ template <int FMT, int NT, int MT> struct GemmOcc {
   static constexpr int value = NT * MT <= 4 ? 2 : 1;
 };
 
+// Lane (c, h) of wave w reads the partial sums of squares of block row
+// m0 + 32mt + c in 16-byte chunks j = 2w + h + 2*NWV*i, i < kNormLoads.
+constexpr int kNormLoads = 4;
+
 // A8: activations are MXFP8 (e4m3 codes + e8m0 per 32) and the MFMA is the
 // scaled 32x32x64 FP8/FP4 one: one MFMA per tile pair and k step, FP8 weights
 // enter raw (their per-row scale stays in the epilogue) and MXFP4 weights with
 // their own e8m0 scales.
-template <bool F16, int FMT, int NT, int MT, class Epi, bool A8 = false, int NWV = 4>  // NWV = waves per workgroup
+template <bool F16, int FMT, int NT, int MT, class Epi, bool A8, int NWV, int KS>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(GemmOcc<FMT, NT, MT>::value, 8))) void
 gemm_kernel(GemmArgs ga, Epi epi) {
   static_assert(!A8 || FMT != SPEC_WFMT_BF16, "A8 takes FP8 or MXFP4 weights");
-  static_assert(NWV == 4 || (NWV == 8 && !A8 && MT % 2 == 0), "8-wave workgroups: 16-bit activations, even MT");
+  static_assert(NWV % KS == 0 && (!A8 || KS == 1), "k groups divide the waves; A8 runs one k group");
+  constexpr int NG = NWV / KS;              // waves side by side along N
   constexpr int ROWS = 32 * MT;             // activation rows per workgroup
-  // LDS-DMA instructions per wave per stage: ROWS*8 (16-bit) or ROWS*4 (FP8) chunks of 16 bytes over 256 lanes
-  constexpr int AJ = A8 ? (MT + 1) / 2 : 4 * MT / NWV;
-  constexpr int SE = A8 ? AJ * 2048 : ROWS * 64;  // 16-bit elements per stage
-  constexpr int DIST = gemm_depth<FMT, NT, MT, A8>();  // k steps loaded ahead of the one computed
+  constexpr int SUB = ROWS * 64;            // 16-bit elements of one k step's activation tile
+  // LDS-DMA instructions per wave per stage: KS * ROWS * 8 (16-bit) or ROWS * 4 (FP8) chunks of 16 bytes
+  constexpr int AJ = A8 ? (MT + 1) / 2 : 4 * MT * KS / NWV;
+  static_assert(A8 || (AJ >= 1 && (4 * MT * KS) % NWV == 0), "a stage's activation chunks fill whole waves");
+  constexpr int SE = A8 ? AJ * 2048 : SUB * KS;  // 16-bit elements per stage
+  constexpr int DIST = gemm_depth<FMT, NT, MT, A8, KS>();  // stages loaded ahead of the one computed
   constexpr int NS = DIST + 1;              // LDS stages = weight register sets
   // staged epilogue: per wave a [32][LD] fp32 tile of block rows x output columns
   constexpr int COLS = Epi::template cols<NT>(), LD = COLS + 4;
-  constexpr int STAGE_BYTES = Epi::kStaged ? NWV * 32 * LD * 4 : 0;
-  constexpr int LDS_BYTES = NS * SE * 2 > STAGE_BYTES ? NS * SE * 2 : STAGE_BYTES;
+  constexpr int STAGE_BYTES = Epi::kStaged ? NG * 32 * LD * 4 : 0;
+  constexpr int RED_BYTES = (KS - 1) * NG * NT * MT * 4096;  // k groups' accumulators
+  constexpr int LDS_A = NS * SE * 2 > STAGE_BYTES ? NS * SE * 2 : STAGE_BYTES;
+  constexpr int LDS_BYTES = LDS_A > RED_BYTES ? LDS_A : RED_BYTES;
   __shared__ __align__(16) uint16_t As[LDS_BYTES / 2];
+  __shared__ float rsum[MT][2 * NWV][32];  // per-lane partial sums of squares of the input rows
 
   pin_args(ga, epi);
   int nblk, mblk;
   if (!tile_of(blockIdx.x, ga.nb, ga.mb, ga.per_xcd, nblk, mblk)) return;  // whole workgroup
   const int tid = threadIdx.x, lane = tid & 63, c = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int unit = nblk * NWV + wave;
+  const int ng = wave % NG, kg = wave / NG;
+  const int unit = nblk * NG + ng;
   const bool active = unit < epi.units;  // wave-uniform; inactive waves compute on unit 0 and store nothing
   const int m0 = mblk * ROWS;
   const int M = ga.M, K = ga.K, ksteps = K / 64;
   const int ks0 = blockIdx.z * ga.spl, nsteps = min(ks0 + ga.spl, ksteps) - ks0;
+  const int nstage = (nsteps + KS - 1) / KS;  // stages of KS k steps
 
   // Every wave issues AJ activation loads and NT*w_loads (+ MT scale loads for
-  // A8) weight loads per step, so the vmcnt waits below are one compile-time
-  // count for all waves.  agp: byte address of the lane's 16-byte chunk at k step 0.
+  // A8) weight loads per stage, so the vmcnt waits below are one compile-time
+  // count for all waves.  agp: byte address of the lane's 16-byte chunk at k
+  // step 0; agk: the k step of the stage it carries (wave-uniform).
   const uint8_t *agp[AJ];
+  int agk[AJ];
 #pragma unroll
   for (int i = 0; i < AJ; ++i) {
     const int P = (wave + NWV * i) * 64 + lane;
-    const int row = A8 ? P >> 2 : P >> 3;
-    const int ch = A8 ? (P & 3) ^ swz8(row) : (P & 7) ^ swz(row);
+    int row, ch;
+    if constexpr (A8) {
+      row = P >> 2;
+      ch = (P & 3) ^ swz8(row);
+      agk[i] = 0;
+    } else {
+      const int p = P % (ROWS * 8);
+      row = p >> 3;
+      ch = (p & 7) ^ swz(row);
+      agk[i] = P / (ROWS * 8);
+    }
     const int m = row < ROWS && m0 + row < M ? m0 + row : 0;  // rows past M (or padding) read row 0, never stored
     agp[i] = reinterpret_cast<const uint8_t *>(ga.x) + ((size_t)m * K + ks0 * 64) * (A8 ? 1 : 2) + ch * 16;
   }
@@ -297,13 +318,28 @@ gemm_kernel(GemmArgs ga, Epi epi) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[t][mt][v] = 0.f;
 
-  // Epilogue inputs (the per-row weight scales of the lane's output rows, the
-  // cache lengths of the tile's sequences) are loaded here, before the main
-  // loop, and used only after its final wait: the epilogue then starts
-  // without a dependent memory round trip.
-  f32x4_t esc[NT][4];
-  int ekv[2 * MT];
-  if constexpr (Epi::kStaged) epi.template prefetch<NT, MT>(active ? unit : 0, m0, M, h, esc, ekv);
+  // Partial sums of squares of the input rows (when the input is h * g),
+  // loaded like the epilogue inputs below and added up after the main loop.
+  const bool norm = ga.nr.ssp != nullptr;
+  f32x4_t nrr[MT][kNormLoads];
+  const int nch = ga.nr.ld / 4, nnl = (nch + 2 * NWV - 1) / (2 * NWV);  // chunks per row, loads per lane
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = min(m0 + 32 * mt + c, M - 1);
+#pragma unroll
+    for (int i = 0; i < kNormLoads; ++i) {
+      const int j = 2 * wave + h + 2 * NWV * i;
+      nrr[mt][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (norm && i < nnl && j < nch) nrr[mt][i] = *reinterpret_cast<const f32x4_t *>(ga.nr.ssp + (size_t)m * ga.nr.ld + 4 * j);
+    }
+  }
+
+  // Epilogue inputs (per-row weight scales, cache lengths, the residual rows a
+  // residual projection adds to) are loaded here, before the main loop, and
+  // used only after its final wait: the epilogue then starts without a
+  // dependent memory round trip.
+  typename Epi::template Pre<NT, MT> pre;
+  if (kg == 0) epi.template prefetch<NT, MT>(active ? unit : 0, m0, M, lane, pre);
 
   auto compute_a8 = [&](int stage, const WRaw<FMT>(&wr)[NT], const uint32_t(&sc)[A8 ? MT : 1]) {
     __builtin_amdgcn_sched_barrier(0);
@@ -340,7 +376,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
     u32x4_t wop[NT][4];
 #pragma unroll
     for (int t = 0; t < NT; ++t) cvt_w<F16, FMT>(wr[t], wop[t]);
-    const uint16_t *base = As + stage * SE;
+    const uint16_t *base = As + stage * SE + kg * SUB;  // this k group's step of the stage
     // slice i of block row 32*mt + c: logical chunk 4h + i
     auto read_a = [&](int i, u32x4_t (&af)[MT]) {
 #pragma unroll
@@ -362,12 +398,14 @@ gemm_kernel(GemmArgs ga, Epi epi) {
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  auto issue_a = [&](int step, int stage) {
+  auto issue_a = [&](int st, int stage) {
 #pragma unroll
     for (int i = 0; i < AJ; ++i)
-      lds_load16(agp[i] + step * (A8 ? 64 : 128), As + stage * SE + (wave + NWV * i) * 512);
+      lds_load16(agp[i] + min(st * KS + agk[i], nsteps - 1) * (A8 ? 64 : 128),
+                 As + stage * SE + (wave + NWV * i) * 512);
   };
-  auto issue_w = [&](WRaw<FMT>(&wr)[NT], uint32_t(&sc)[A8 ? MT : 1], int step) {
+  auto issue_w = [&](WRaw<FMT>(&wr)[NT], uint32_t(&sc)[A8 ? MT : 1], int st) {
+    const int step = min(st * KS + kg, nsteps - 1);
 #pragma unroll
     for (int t = 0; t < NT; ++t) load_w<FMT>(wr[t], wl[t], sl[t], step);
     if constexpr (A8) {
@@ -375,34 +413,35 @@ gemm_kernel(GemmArgs ga, Epi epi) {
       for (int mt = 0; mt < MT; ++mt) sc[mt] = vload1(asp[mt] + step * 2);
     }
   };
-  // Software pipeline, DIST k steps deep.  At step s the wave issues step
-  // s+DIST (weights into register set (s+DIST)%NS, then activations straight to
-  // LDS stage (s+DIST)%NS) and computes step s from set / stage s%NS.  The loop
-  // is unrolled NS times so every register set has a fixed name: a register
-  // copy of a load destination would be placed before the wait that covers it.
-  // Steps past the end re-load the last step into a set / stage nobody reads.
-  // Loads complete in issue order, so "step s landed" is "at most the loads of
-  // steps s+1 .. s+DIST-1 outstanding".
+  // Software pipeline, DIST stages deep.  At stage s the wave issues stage
+  // s+DIST (weights into register set (s+DIST)%NS, then activations straight
+  // to LDS stage (s+DIST)%NS) and computes its k step of stage s from set /
+  // stage s%NS.  The loop is unrolled NS times so every register set has a
+  // fixed name: a register copy of a load destination would be placed before
+  // the wait that covers it.  Stages past the end re-load the last k step
+  // into a set / stage nobody reads.  Loads complete in issue order, so
+  // "stage s landed" is "at most the loads of stages s+1 .. s+DIST-1
+  // outstanding".
   constexpr int PER_STEP = NT * w_loads<FMT>() + (A8 ? MT : 0) + AJ;
-  static_assert((DIST - 1) * PER_STEP < 64, "vmcnt holds 6 bits");
+  static_assert(DIST * PER_STEP < 64, "vmcnt holds 6 bits");
   WRaw<FMT> wr[NS][NT];
   uint32_t scr[NS][A8 ? MT : 1];
 #pragma unroll
   for (int i = 0; i < DIST; ++i) {
-    issue_w(wr[i], scr[i], min(i, nsteps - 1));
-    issue_a(min(i, nsteps - 1), i);
+    issue_w(wr[i], scr[i], min(i, nstage - 1));
+    issue_a(min(i, nstage - 1), i);
   }
-  for (int s0 = 0; s0 < nsteps; s0 += NS) {
+  for (int s0 = 0; s0 < nstage; s0 += NS) {
 #pragma unroll
     for (int ph = 0; ph < NS; ++ph) {
       const int s = s0 + ph;
       WAIT_VMCNT((DIST - 1) * PER_STEP);
-      lds_barrier();  // stage s visible to all waves; every wave is done with step s-1's stage
+      lds_barrier();  // stage s visible to all waves; every wave is done with stage s-1
       __builtin_amdgcn_sched_barrier(0);
-      issue_w(wr[(ph + DIST) % NS], scr[(ph + DIST) % NS], min(s + DIST, nsteps - 1));
-      issue_a(min(s + DIST, nsteps - 1), (ph + DIST) % NS);
+      issue_w(wr[(ph + DIST) % NS], scr[(ph + DIST) % NS], min(s + DIST, nstage - 1));
+      issue_a(min(s + DIST, nstage - 1), (ph + DIST) % NS);
       __builtin_amdgcn_sched_barrier(0);
-      if (ph == 0 || s < nsteps) {  // phases past the last step only keep the load count uniform
+      if (s * KS + kg < nsteps) {  // stages past the last (or a k group past the last step) only keep the counts uniform
         if constexpr (A8) compute_a8(ph, wr[ph], scr[ph]);
         else compute(ph, wr[ph]);
       }
@@ -419,31 +458,81 @@ gemm_kernel(GemmArgs ga, Epi epi) {
       for (int mt = 0; mt < MT; ++mt) asm volatile("" ::"v"(scr[i][mt]));
     }
   }
+  if constexpr (KS > 1) {
+    // k groups 1.. hand their accumulators to group 0 through LDS, which adds
+    // them in group order (the result does not depend on timing)
+    float *red = reinterpret_cast<float *>(As);
+    lds_barrier();  // every wave is done reading the activation stages
+    if (kg > 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int v = 0; v < 16; ++v)
+            red[((((kg - 1) * NG + ng) * NT + t) * MT + mt) * 1024 + v * 64 + lane] = acc[t][mt][v];
+    }
+    lds_barrier();
+    if (kg == 0) {
+#pragma unroll
+      for (int g = 1; g < KS; ++g)
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[t][mt][v] += red[((((g - 1) * NG + ng) * NT + t) * MT + mt) * 1024 + v * 64 + lane];
+    }
+  }
+  // per-row normalisation of the input: r = 1 / sqrt(sum / H + eps), each
+  // lane's chunks summed in order, then the lanes' sums in a fixed order
+  float rs[MT];
+  if (norm) {
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) {
+      float ps = 0.f;
+#pragma unroll
+      for (int i = 0; i < kNormLoads; ++i) ps += (nrr[mt][i][0] + nrr[mt][i][1]) + (nrr[mt][i][2] + nrr[mt][i][3]);
+      rsum[mt][2 * wave + h][c] = ps;
+    }
+    lds_barrier();
+  }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    rs[mt] = 1.f;
+    if (norm) {
+      float ss = 0.f;
+#pragma unroll
+      for (int q = 0; q < 2 * NWV; ++q) ss += rsum[mt][q][c];
+      rs[mt] = 1.0f / sqrtf(ss / (float)ga.nr.H + ga.nr.eps);
+    }
+  }
+  const bool emit_ok = active && kg == 0;
   if constexpr (Epi::kStaged) {
-    // Each wave writes its finished outputs (scaled, RoPE / SwiGLU applied) as
-    // fp32 into its own LDS tile, then reads it back along rows so that every
-    // global store covers consecutive columns of one row.  The tile is wave
-    // private and a wave's LDS operations run in order, so only the barrier
-    // that retires the activation stages is needed.
+    // Each wave of k group 0 writes its finished outputs (scaled, RoPE /
+    // SwiGLU applied) as fp32 into its own LDS tile, then reads it back along
+    // rows so that every global store covers consecutive columns of one row.
+    // The tile is wave private and a wave's LDS operations run in order, so
+    // only the barrier that retires the activation stages is needed.
     constexpr int LPR = COLS / 4, RPP = 64 / LPR;  // lanes per row, rows per pass
     static_assert(COLS % 4 == 0 && 64 % LPR == 0 && LPR <= 64, "staged tile shape");
-    lds_barrier();  // every wave is done reading the activation stages
-    float *st = reinterpret_cast<float *>(As) + wave * 32 * LD;
-    if (active) {
+    lds_barrier();  // every wave is done reading the activation stages (or the k groups' sums)
+    float *st = reinterpret_cast<float *>(As) + ng * 32 * LD;
+    if (emit_ok) {
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
         if (m0 + 32 * mt >= M) break;
-        epi.template emit<NT, MT>(unit, mt, m0, M, c, h, acc, esc, ekv, st, LD);
+        epi.template emit<NT, MT>(unit, mt, c, h, acc, rs[mt], pre, st, LD);
 #pragma unroll
         for (int r0 = 0; r0 < 32; r0 += RPP) {
           const int row = r0 + lane / LPR, col = 4 * (lane % LPR), m = m0 + 32 * mt + row;
           const f32x4_t v = *reinterpret_cast<const f32x4_t *>(st + row * LD + col);
-          if (m < M) epi.template put<MT>(unit, m, m0, col, v, blockIdx.z, ekv);
+          epi.template put<NT, MT>(unit, m, M, col, v, blockIdx.z, mt, r0 / RPP, pre);
         }
       }
     }
   } else {
-    epi.template store<NT, MT>(active ? unit : 0, nblk, active, wave, m0, M, c, h, acc, As);
+    epi.template store<NT, MT, NWV>(active ? unit : 0, nblk, emit_ok, wave, m0, M, c, h, acc, rs, As);
   }
 }
 
@@ -459,40 +548,35 @@ __device__ __forceinline__ f32x4_t row_scale4(const float *s, int n) {
   return *reinterpret_cast<const f32x4_t *>(s + n);
 }
 
-// Per-row scales of weight rows row(unit, t) + 8q + 4h + (0..3), the rows lane
-// (., h) holds for tile t (1 without per-row scales).  Prefetched for up to two
-// tiles per wave; with four (head_dim 128) the 64 registers would spill, so
-// those are read in the epilogue instead (scale_at).
-template <int NT>
-constexpr bool kPrefetchScales = NT <= 2;
-template <int NT, class E>
-__device__ __forceinline__ void prefetch_scales(const E &e, const float *scale, int unit, int h,
-                                                f32x4_t (&sc)[NT][4]) {
-  if constexpr (kPrefetchScales<NT>) {
-#pragma unroll
-    for (int t = 0; t < NT; ++t)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) sc[t][q] = row_scale4(scale, e.row(unit, t) + 8 * q + 4 * h);
-  }
-}
-template <int NT, class E>
-__device__ __forceinline__ f32x4_t scale_at(const E &e, const float *scale, const f32x4_t (&sc)[NT][4], int unit,
-                                            int t, int q, int h) {
-  if constexpr (kPrefetchScales<NT>) return sc[t][q];
-  else return row_scale4(scale, e.row(unit, t) + 8 * q + 4 * h);
-}
-
-// Outputs of lane (c, h) for weight rows 8q + 4h + (0..3) of a tile.
+// Outputs of lane (c, h) for tile rows 8q + 4h + (0..3) of a tile.
 __device__ __forceinline__ f32x4_t quad(const f32x16_t &a, int q) {
   return f32x4_t{a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]};
 }
 
+// Per-row scales of tile rows row(unit, t) + 8q + 4h + (0..3), the rows lane
+// (., h) holds for tile t (1 without per-row scales), for up to two tiles per
+// wave.
+template <int NT>
+struct ScalePre {
+  f32x4_t s[NT][4];
+};
+template <int NT, class E>
+__device__ __forceinline__ void prefetch_scales(const E &e, const float *scale, int unit, int h, ScalePre<NT> &p) {
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) p.s[t][q] = row_scale4(scale, e.row(unit, t) + 8 * q + 4 * h);
+}
+
 // ---------------------------------------------------------------- epilogues
-// Each epilogue maps (unit, tile t) to the first of the tile's 32 weight rows
-// (row()).  Lane (c, h) holds block row m0 + 32*mt + c and weight rows
-// row(unit, t) + 8q + 4h + (0..3).  Staged epilogues emit() a wave's finished
-// values for one 32-row block into the LDS tile st[block row][output column]
-// (cols() columns) and put() stores 4 consecutive output columns of one row.
+// Each epilogue maps (unit, tile t) to the first of the tile's 32 packed
+// weight rows (row()).  Lane (c, h) holds block row m0 + 32*mt + c and tile
+// rows 8q + 4h + (0..3).  Staged epilogues emit() a wave's finished values
+// for one 32-row block into the LDS tile st[block row][output column] (cols()
+// columns), and put() stores 4 consecutive output columns of one row (pass p
+// of the wave's row passes over block mt; m may be >= M: store nothing).
+// prefetch() loads, before the main loop, what the epilogue will need into a
+// Pre; r is the block row's normalisation (1 when the input is not h * g).
 
 template <int NTc>
 struct EpiF32 {  // y = acc * scale, fp32 out
@@ -502,27 +586,29 @@ struct EpiF32 {  // y = acc * scale, fp32 out
   const float *scale;
   __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
   template <int NT> static constexpr int cols() { return 32 * NT; }
+  template <int NT, int MT> using Pre = ScalePre<NT>;
   template <int NT, int MT>
-  __device__ void prefetch(int unit, int m0, int M, int h, f32x4_t (&sc)[NT][4], int (&kvl)[2 * MT]) const {
-    prefetch_scales<NT>(*this, scale, unit, h, sc);
+  __device__ void prefetch(int unit, int m0, int M, int lane, Pre<NT, MT> &p) const {
+    prefetch_scales<NT>(*this, scale, unit, lane >> 5, p);
   }
   template <int NT, int MT>
-  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT],
-                       const f32x4_t (&sc)[NT][4], const int (&kvl)[2 * MT], float *st, int ld) const {
+  __device__ void emit(int unit, int mt, int c, int h, const f32x16_t (&acc)[NT][MT], float r, const Pre<NT, MT> &p,
+                       float *st, int ld) const {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4_t *>(st + c * ld + 32 * t + 8 * q + 4 * h) = quad(acc[t][mt], q) * scale_at<NT>(*this, scale, sc, unit, t, q, h);
+        *reinterpret_cast<f32x4_t *>(st + c * ld + 32 * t + 8 * q + 4 * h) = quad(acc[t][mt], q) * (p.s[t][q] * r);
   }
-  template <int MT>
-  __device__ void put(int unit, int m, int m0, int col, f32x4_t v, int z, const int (&kvl)[2 * MT]) const {
-    *reinterpret_cast<f32x4_t *>(y + (size_t)m * N + row(unit, 0) + col) = v;
+  template <int NT, int MT>
+  __device__ void put(int unit, int m, int M, int col, f32x4_t v, int z, int mt, int pass, const Pre<NT, MT> &p) const {
+    if (m < M) *reinterpret_cast<f32x4_t *>(y + (size_t)m * N + row(unit, 0) + col) = v;
   }
 };
 
 // Split-K partial of a residual projection: P[z][m][n] = acc * scale.  The
-// next RMSNorm adds the partials of every split to h in split order.
+// next RMSNorm adds the partials of every split to h in split order (the
+// MXFP8-activation mode, whose RMSNorm steps quantise their output).
 template <int NTc>
 struct EpiPartial {
   static constexpr bool kStaged = true;
@@ -531,42 +617,121 @@ struct EpiPartial {
   const float *scale;
   __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
   template <int NT> static constexpr int cols() { return 32 * NT; }
+  template <int NT, int MT> using Pre = ScalePre<NT>;
   template <int NT, int MT>
-  __device__ void prefetch(int unit, int m0, int Mr, int h, f32x4_t (&sc)[NT][4], int (&kvl)[2 * MT]) const {
-    prefetch_scales<NT>(*this, scale, unit, h, sc);
+  __device__ void prefetch(int unit, int m0, int Mr, int lane, Pre<NT, MT> &p) const {
+    prefetch_scales<NT>(*this, scale, unit, lane >> 5, p);
   }
   template <int NT, int MT>
-  __device__ void emit(int unit, int mt, int m0, int Mr, int c, int h, const f32x16_t (&acc)[NT][MT],
-                       const f32x4_t (&sc)[NT][4], const int (&kvl)[2 * MT], float *st, int ld) const {
+  __device__ void emit(int unit, int mt, int c, int h, const f32x16_t (&acc)[NT][MT], float r, const Pre<NT, MT> &p,
+                       float *st, int ld) const {
 #pragma unroll
     for (int t = 0; t < NT; ++t)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        *reinterpret_cast<f32x4_t *>(st + c * ld + 32 * t + 8 * q + 4 * h) = quad(acc[t][mt], q) * scale_at<NT>(*this, scale, sc, unit, t, q, h);
+        *reinterpret_cast<f32x4_t *>(st + c * ld + 32 * t + 8 * q + 4 * h) = quad(acc[t][mt], q) * p.s[t][q];
   }
-  template <int MT>
-  __device__ void put(int unit, int m, int m0, int col, f32x4_t v, int z, const int (&kvl)[2 * MT]) const {
-    *reinterpret_cast<f32x4_t *>(part + ((size_t)z * M + m) * N + row(unit, 0) + col) = v;
+  template <int NT, int MT>
+  __device__ void put(int unit, int m, int Mr, int col, f32x4_t v, int z, int mt, int pass, const Pre<NT, MT> &p) const {
+    if (m < Mr) *reinterpret_cast<f32x4_t *>(part + ((size_t)z * M + m) * N + row(unit, 0) + col) = v;
   }
 };
 
-// One unit = one head of D = 32*NT rows: q heads, then k heads, then v heads.
-// Rotate-half RoPE pairs d and d + D/2, which are tiles t and t + NT/2 in the
-// same lane and register slot.  q goes out as FP16, k and v into the BF16 cache
-// at slot kv_len[b] + j of block row m = 16b + j.
+// Residual projection with the next RMSNorm folded in: h_out = h_in + acc *
+// scale (fp32), xg = h_out * g of the RMSNorm that reads h_out (FP16, or BF16
+// for the lm_head's input), and the sum of h_out^2 over each 32-column tile
+// into ssp[m][n / 32] (the normalisation itself is applied by the consumer).
+// An FP16 xg beyond the format's range sets SPEC_DERR_RANGE.
+template <int NTc>
+struct EpiResidual {
+  static constexpr bool kStaged = true;
+  int units, N;
+  const float *scale;
+  ResidualOut o;
+  __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
+  template <int NT> static constexpr int cols() { return 32 * NT; }
+  static constexpr int kPasses = 32 / (64 / (8 * NTc));  // row passes of a 32-row block (LPR = 8 NT lanes per row)
+  template <int NT, int MT>
+  struct Pre {
+    f32x4_t s[NT][4];
+    f32x4_t hin[MT][kPasses];  // h_in at the lane's put() positions
+    f32x4_t g;                 // the gain of the lane's 4 columns
+  };
+  template <int NT, int MT>
+  __device__ void prefetch(int unit, int m0, int M, int lane, Pre<NT, MT> &p) const {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p.s[t][q] = row_scale4(scale, row(unit, t) + 8 * q + 4 * (lane >> 5));
+    constexpr int LPR = 8 * NT, RPP = 64 / LPR;
+    const int n = row(unit, 0) + 4 * (lane % LPR);
+    p.g = *reinterpret_cast<const f32x4_t *>(o.gain + n);
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int ps = 0; ps < kPasses; ++ps) {
+        const int m = min(m0 + 32 * mt + ps * RPP + lane / LPR, M - 1);
+        p.hin[mt][ps] = *reinterpret_cast<const f32x4_t *>(o.h_in + (size_t)m * N + n);
+      }
+  }
+  template <int NT, int MT>
+  __device__ void emit(int unit, int mt, int c, int h, const f32x16_t (&acc)[NT][MT], float r, const Pre<NT, MT> &p,
+                       float *st, int ld) const {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        *reinterpret_cast<f32x4_t *>(st + c * ld + 32 * t + 8 * q + 4 * h) = quad(acc[t][mt], q) * p.s[t][q];
+  }
+  template <int NT, int MT>
+  __device__ void put(int unit, int m, int M, int col, f32x4_t v, int z, int mt, int pass, const Pre<NT, MT> &p) const {
+    const int n = row(unit, 0) + col;
+    const f32x4_t hv = p.hin[mt][pass] + v;
+    const f32x4_t xg = hv * p.g;
+    // sum of squares over the 32-column tile: its 8 lanes are consecutive
+    float ss = (hv[0] * hv[0] + hv[1] * hv[1]) + (hv[2] * hv[2] + hv[3] * hv[3]);
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    if (m >= M) return;
+    *reinterpret_cast<f32x4_t *>(o.h_out + (size_t)m * N + n) = hv;
+    if (o.xg_bf16) {
+      store_bf16x4(o.xg + (size_t)m * N + n, xg[0], xg[1], xg[2], xg[3]);
+    } else {
+      store_f16x4(o.xg + (size_t)m * N + n, xg[0], xg[1], xg[2], xg[3]);
+      const float mx = fmaxf(fmaxf(fabsf(xg[0]), fabsf(xg[1])), fmaxf(fabsf(xg[2]), fabsf(xg[3])));
+      if (!(mx <= 65504.f)) set_error(o.err, SPEC_DERR_RANGE);
+    }
+    if ((col & 31) == 0) o.ssp[(size_t)m * o.ssp_ld + n / 32] = ss;
+  }
+};
+
+// QKV projection: a unit is NT tiles of the packed QKV rows.  Each head's D
+// rows are packed so that tile tp of the head holds dimensions 16tp .. 16tp+15
+// in tile rows 0..15 and D/2 + 16tp .. +15 in rows 16..31: the rotate-half
+// RoPE pair (d, d + D/2) is then tile rows (r, r + 16), held by the same lane.
+// Heads: q heads, then k heads, then v heads.  q goes out as FP16, k and v
+// into the BF16 cache at slot kv_len[b] + j of block row m = 16b + j.
 template <int NTc>
 struct EpiQkv {
   static constexpr bool kStaged = true;
-  int units;
-  const float *scale;
+  int units;  // units of NTc tiles
+  const float *scale;  // packed per-row scales
   QkvOut o;
   __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
   template <int NT> static constexpr int cols() { return 32 * NT; }
   __device__ bool slot_ok(int n0) const { return n0 >= 0 && n0 + 16 <= o.max_ctx; }  // else flagged by embed
-  // also the cache length of each of the tile's 2*MT sequences (uniform loads)
   template <int NT, int MT>
-  __device__ void prefetch(int unit, int m0, int M, int h, f32x4_t (&sc)[NT][4], int (&kvl)[2 * MT]) const {
-    prefetch_scales<NT>(*this, scale, unit, h, sc);
+  struct Pre {
+    f32x4_t s[NT][4];
+    int kvl[2 * MT];  // cache length of each of the block's sequences
+  };
+  template <int NT, int MT>
+  __device__ void prefetch(int unit, int m0, int M, int lane, Pre<NT, MT> &p) const {
+#pragma unroll
+    for (int t = 0; t < NT; ++t)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) p.s[t][q] = row_scale4(scale, row(unit, t) + 8 * q + 4 * (lane >> 5));
     // through the constant address space: scalar loads, which the vector
     // loads in flight need not wait for (kv_len does not change during the
     // kernel, and the scalar cache is invalidated at each launch)
@@ -574,27 +739,26 @@ struct EpiQkv {
 #pragma unroll
     for (int i = 0; i < 2 * MT; ++i) {
       const int b = (m0 >> 4) + i;
-      kvl[i] = b < (M >> 4) ? kl[b] : 0;
+      p.kvl[i] = b < (M >> 4) ? kl[b] : 0;
     }
   }
   template <int NT, int MT>
-  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT],
-                       const f32x4_t (&sc)[NT][4], const int (&kvl)[2 * MT], float *st, int ld) const {
-    constexpr int HALF = 16 * NT;
-    const int m = m0 + 32 * mt + c;
-    if (m >= M) return;
-    const int n0 = kvl[2 * mt + (c >> 4)], pos = n0 + (m & 15);
-    if (!slot_ok(n0)) return;
-    if (unit < o.Hq + o.Hkv) {
+  __device__ void emit(int unit, int mt, int c, int h, const f32x16_t (&acc)[NT][MT], float r, const Pre<NT, MT> &p,
+                       float *st, int ld) const {
+    const int D = o.D, TPH = D / 32;
+    const int n0 = (c >> 4) ? p.kvl[2 * mt + 1] : p.kvl[2 * mt], pos = n0 + (c & 15);  // selects: no indexed registers
+    const int half = D / 2;
 #pragma unroll
-      for (int t = 0; t < NT / 2; ++t)
+    for (int t = 0; t < NT; ++t) {
+      const int T = unit * NTc + t, head = T / TPH, tp = T % TPH;
+      if (head < o.Hq + o.Hkv && slot_ok(n0)) {  // q and k heads are rotated
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int d = 32 * t + 8 * q + 4 * h;
-          const f32x4_t y1 = quad(acc[t][mt], q) * scale_at<NT>(*this, scale, sc, unit, t, q, h);
-          const f32x4_t y2 = quad(acc[t + NT / 2][mt], q) * scale_at<NT>(*this, scale, sc, unit, t + NT / 2, q, h);
-          const f32x4_t cs01 = *reinterpret_cast<const f32x4_t *>(o.rope + (size_t)pos * HALF + d);
-          const f32x4_t cs23 = *reinterpret_cast<const f32x4_t *>(o.rope + (size_t)pos * HALF + d + 2);
+        for (int q = 0; q < 2; ++q) {
+          const int d = 16 * tp + 8 * q + 4 * h;  // < D/2; its pair is d + D/2
+          const f32x4_t y1 = quad(acc[t][mt], q) * (p.s[t][q] * r);
+          const f32x4_t y2 = quad(acc[t][mt], q + 2) * (p.s[t][q + 2] * r);
+          const f32x4_t cs01 = *reinterpret_cast<const f32x4_t *>(o.rope + (size_t)pos * half + d);
+          const f32x4_t cs23 = *reinterpret_cast<const f32x4_t *>(o.rope + (size_t)pos * half + d + 2);
           const float cs[4] = {cs01[0], cs01[2], cs23[0], cs23[2]}, sn[4] = {cs01[1], cs01[3], cs23[1], cs23[3]};
           f32x4_t o1, o2;
 #pragma unroll
@@ -602,106 +766,114 @@ struct EpiQkv {
             o1[i] = y1[i] * cs[i] - y2[i] * sn[i];
             o2[i] = y2[i] * cs[i] + y1[i] * sn[i];
           }
-          *reinterpret_cast<f32x4_t *>(st + c * ld + d) = o1;
-          *reinterpret_cast<f32x4_t *>(st + c * ld + d + HALF) = o2;
+          *reinterpret_cast<f32x4_t *>(st + c * ld + 32 * t + 8 * q + 4 * h) = o1;
+          *reinterpret_cast<f32x4_t *>(st + c * ld + 32 * t + 8 * (q + 2) + 4 * h) = o2;
         }
-    } else {
+      } else {
 #pragma unroll
-      for (int t = 0; t < NT; ++t)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int d = 32 * t + 8 * q + 4 * h;
-          *reinterpret_cast<f32x4_t *>(st + c * ld + d) = quad(acc[t][mt], q) * scale_at<NT>(*this, scale, sc, unit, t, q, h);
-        }
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f32x4_t *>(st + c * ld + 32 * t + 8 * q + 4 * h) = quad(acc[t][mt], q) * (p.s[t][q] * r);
+      }
     }
   }
-  template <int MT>
-  __device__ void put(int unit, int m, int m0, int col, f32x4_t v, int z, const int (&kvl)[2 * MT]) const {
-    constexpr int D = 32 * NTc;
-    const int b = m >> 4, n0 = kvl[(m - m0) >> 4];
+  template <int NT, int MT>
+  __device__ void put(int unit, int m, int M, int col, f32x4_t v, int z, int mt, int pass, const Pre<NT, MT> &p) const {
+    if (m >= M) return;
+    const int D = o.D, TPH = D / 32;
+    const int b = m >> 4, n0 = ((m & 31) >> 4) ? p.kvl[2 * mt + 1] : p.kvl[2 * mt];
     if (!slot_ok(n0)) return;
-    const int pos = n0 + (m & 15);
-    if (unit < o.Hq) {
-      store_f16x4(o.q_out + (size_t)m * (o.Hq * D) + unit * D + col, v[0], v[1], v[2], v[3]);
+    const int T = unit * NTc + col / 32, head = T / TPH, tp = T % TPH, rr = col % 32;
+    const int d = rr < 16 ? 16 * tp + rr : D / 2 + 16 * tp + (rr - 16);
+    const float mx = fmaxf(fmaxf(fabsf(v[0]), fabsf(v[1])), fmaxf(fabsf(v[2]), fabsf(v[3])));
+    if (!(mx <= 65504.f)) set_error(o.err, SPEC_DERR_RANGE);  // attention reads q, k, v as FP16
+    if (head < o.Hq) {
+      store_f16x4(o.q_out + (size_t)m * (o.Hq * D) + head * D + d, v[0], v[1], v[2], v[3]);
     } else {
-      const bool isk = unit < o.Hq + o.Hkv;
-      const int kvh = isk ? unit - o.Hq : unit - o.Hq - o.Hkv;
+      const int pos = n0 + (m & 15);
+      const bool isk = head < o.Hq + o.Hkv;
+      const int kvh = isk ? head - o.Hq : head - o.Hq - o.Hkv;
       uint16_t *cache = isk ? o.k_cache : o.v_cache;
       bool ok;
-      const size_t r = o.kvl.row(b, kvh, o.Hkv, o.max_ctx, pos, ok);
-      if (ok) store_bf16x4(cache + r * D + col, v[0], v[1], v[2], v[3]);
+      const size_t rrow = o.kvl.row(b, kvh, o.Hkv, o.max_ctx, pos, ok);
+      if (ok) store_bf16x4(cache + rrow * D + d, v[0], v[1], v[2], v[3]);
     }
   }
 };
 
-// Tiles [0, NT/2) read gate rows, tiles [NT/2, NT) the matching up rows;
-// a = SiLU(gate) * up goes out as FP16, or (MX8) as MXFP8: e4m3 codes [M][I]
-// plus the e8m0 exponent of each 32 outputs [M][I/32].  A unit covers 16*NT
-// outputs; with NT = 2 that is one 32-wide scale block per row, held by 8
+// Gate/up projection with SiLU(gate) * up: tile T of the packed rows holds
+// gate rows 16T .. 16T+15 in tile rows 0..15 and the matching up rows in rows
+// 16..31, so each lane holds its gate values and their up partners.  A unit
+// of NT tiles yields 16*NT outputs per row; a = SiLU(gate) * up goes out as
+// FP16, or (MX8, NT = 2) as MXFP8: e4m3 codes [M][I] plus the e8m0 exponent of
+// each 32 outputs [M][I/32], one block per unit and row, held by 8
 // consecutive lanes of the staged store.
 template <int NTc, bool MX8 = false>
 struct EpiSwiglu {
   static constexpr bool kStaged = true;
   static_assert(!MX8 || NTc == 2, "an MXFP8 block is the 32 outputs of one row of a unit");
   int units, I;
-  const float *scale;  // per-row FP8 scales [2I], NULL when decoded with the scale
+  const float *scale;  // packed per-row FP8 scales [2I], NULL when decoded with the scale
   void *a;             // FP16 bits or e4m3 codes
   uint8_t *as;         // MX8: e8m0 [M][I/32]
-  __device__ int row(int unit, int t) const {
-    return t < NTc / 2 ? unit * 16 * NTc + 32 * t : I + unit * 16 * NTc + 32 * (t - NTc / 2);
-  }
+  __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
   template <int NT> static constexpr int cols() { return 16 * NT; }
+  template <int NT, int MT> using Pre = ScalePre<NT>;
   template <int NT, int MT>
-  __device__ void prefetch(int unit, int m0, int M, int h, f32x4_t (&sc)[NT][4], int (&kvl)[2 * MT]) const {
-    prefetch_scales<NT>(*this, scale, unit, h, sc);  // gate rows, then the matching up rows
+  __device__ void prefetch(int unit, int m0, int M, int lane, Pre<NT, MT> &p) const {
+    prefetch_scales<NT>(*this, scale, unit, lane >> 5, p);
   }
   template <int NT, int MT>
-  __device__ void emit(int unit, int mt, int m0, int M, int c, int h, const f32x16_t (&acc)[NT][MT],
-                       const f32x4_t (&sc)[NT][4], const int (&kvl)[2 * MT], float *st, int ld) const {
+  __device__ void emit(int unit, int mt, int c, int h, const f32x16_t (&acc)[NT][MT], float r, const Pre<NT, MT> &p,
+                       float *st, int ld) const {
 #pragma unroll
-    for (int t = 0; t < NT / 2; ++t)
+    for (int t = 0; t < NT; ++t)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = 32 * t + 8 * q + 4 * h;
-        const f32x4_t gv = quad(acc[t][mt], q) * scale_at<NT>(*this, scale, sc, unit, t, q, h);
-        const f32x4_t uv = quad(acc[t + NT / 2][mt], q) * scale_at<NT>(*this, scale, sc, unit, t + NT / 2, q, h);
+      for (int q = 0; q < 2; ++q) {
+        const f32x4_t gv = quad(acc[t][mt], q) * (p.s[t][q] * r);
+        const f32x4_t uv = quad(acc[t][mt], q + 2) * (p.s[t][q + 2] * r);
         f32x4_t v;
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = gv[i] * __builtin_amdgcn_rcpf(1.f + __expf(-gv[i])) * uv[i];  // SiLU(g) * u
-        *reinterpret_cast<f32x4_t *>(st + c * ld + col) = v;
+        *reinterpret_cast<f32x4_t *>(st + c * ld + 16 * t + 8 * q + 4 * h) = v;
       }
   }
-  template <int MT>
-  __device__ void put(int unit, int m, int m0, int col, f32x4_t v, int z, const int (&kvl)[2 * MT]) const {
+  template <int NT, int MT>
+  __device__ void put(int unit, int m, int M, int col, f32x4_t v, int z, int mt, int pass, const Pre<NT, MT> &p) const {
     const int n = unit * 16 * NTc + col;
     if constexpr (MX8) {
       uint32_t e8;
       const uint32_t codes = mx8_quant4(v, e8);  // lanes col/4 = 0..7 of this row share the block
+      if (m >= M) return;
       *reinterpret_cast<uint32_t *>(static_cast<uint8_t *>(a) + (size_t)m * I + n) = codes;
       if ((col & 31) == 0) as[(size_t)m * (I / 32) + n / 32] = (uint8_t)e8;
     } else {
-      store_f16x4(static_cast<uint16_t *>(a) + (size_t)m * I + n, v[0], v[1], v[2], v[3]);
+      if (m < M) store_f16x4(static_cast<uint16_t *>(a) + (size_t)m * I + n, v[0], v[1], v[2], v[3]);
     }
   }
 };
 
 // lm_head tile -> one argmax partial per (row, workgroup), lowest index on
-// ties: each wave reduces its 32*NT vocab rows in registers, the workgroup's
-// waves meet in LDS, and wave 0 folds them in wave order (increasing vocab
-// index).  Called by every wave of the workgroup (inactive ones contribute
-// nothing), after the main loop.
+// ties: each wave reduces its 32*NT vocab rows in registers (logits scaled by
+// the row's normalisation r first), the workgroup's waves meet in LDS, and
+// wave 0 folds them in wave order (increasing vocab index).  Called by every
+// wave of the workgroup (inactive ones contribute nothing), after the main
+// loop.
 template <int NTc>
 struct EpiArgmax {
   static constexpr bool kStaged = false;
   template <int NT> static constexpr int cols() { return 4; }
+  template <int NT, int MT>
+  struct Pre {};
   int units, V, nparts;
   ArgmaxPart *part;  // [M][nparts], nparts = workgroups along the vocab
   float *logits;     // optional [M][V]
   __device__ int row(int unit, int t) const { return unit * 32 * NTc + 32 * t; }
   template <int NT, int MT>
+  __device__ void prefetch(int unit, int m0, int M, int lane, Pre<NT, MT> &p) const {}
+  template <int NT, int MT, int NWV>
   __device__ void store(int unit, int nblk, bool active, int wave, int m0, int M, int c, int h,
-                        const f32x16_t (&acc)[NT][MT], void *lds) const {
-    ArgmaxPart *red = static_cast<ArgmaxPart *>(lds);  // [4 waves][32 * MT rows]
+                        const f32x16_t (&acc)[NT][MT], const float (&rs)[MT], void *lds) const {
+    ArgmaxPart *red = static_cast<ArgmaxPart *>(lds);  // [NWV waves][32 * MT rows]
     lds_barrier();  // every wave is done reading the activation stages
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -715,8 +887,9 @@ struct EpiArgmax {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int n = row(unit, t) + 8 * (v >> 2) + 4 * h + (v & 3);
-          const bool gt = acc[t][mt][v] > bv;
-          bv = gt ? acc[t][mt][v] : bv;
+          const float lv = acc[t][mt][v] * rs[mt];
+          const bool gt = lv > bv;
+          bv = gt ? lv : bv;
           bi = gt ? n : bi;
         }
       const float ov = __shfl_xor(bv, 32);  // the other half holds the other rows of the same block row
@@ -730,7 +903,7 @@ struct EpiArgmax {
         for (int t = 0; t < NT; ++t)
 #pragma unroll
           for (int q = 0; q < 4; ++q)
-            *reinterpret_cast<f32x4_t *>(logits + (size_t)m * V + row(unit, t) + 8 * q + 4 * h) = quad(acc[t][mt], q);
+            *reinterpret_cast<f32x4_t *>(logits + (size_t)m * V + row(unit, t) + 8 * q + 4 * h) = quad(acc[t][mt], q) * rs[mt];
       }
     }
     lds_barrier();
@@ -740,7 +913,7 @@ struct EpiArgmax {
     for (int r = lane; r < 32 * MT; r += 64) {
       ArgmaxPart b = red[r];
 #pragma unroll
-      for (int w = 1; w < 4; ++w) {
+      for (int w = 1; w < NWV; ++w) {
         const ArgmaxPart o = red[w * 32 * MT + r];
         if (better(o.v, o.i, b.v, b.i)) b = o;
       }
@@ -751,14 +924,16 @@ struct EpiArgmax {
 
 // ---------------------------------------------------------------- planning
 
-GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split, int nwv) {
+GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split, int ng) {
   GemmPlan p;
   p.MT = MT;
-  p.nb = (units + nwv - 1) / nwv;
+  p.NG = ng;
+  p.KS = 1;
+  p.nb = (units + ng - 1) / ng;
   p.mb = (M + 32 * MT - 1) / (32 * MT);
   const int tiles = p.nb * p.mb;
-  // split K (residual projections only) until about GEMM_SPLIT_TARGET
-  // workgroups, >= 4 k steps per split
+  // split K (the MXFP8 mode's residual projections only) until about
+  // GEMM_SPLIT_TARGET workgroups, >= 4 k steps per split
   int s = allow_split ? (GEMM_SPLIT_TARGET + tiles - 1) / tiles : 1;
   if (s > ksteps / 4) s = ksteps / 4;
   if (s < 1) s = 1;
@@ -769,28 +944,40 @@ GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split, int n
 }
 
 // 32-row activation tiles per workgroup: wide tiles unless that leaves fewer
-// than GEMM_MIN_TILES workgroups (measured over whole passes: at 512 rows the
-// gate/up step runs 64-row tiles, 304 workgroups, 0.6% faster per pass than
-// 32-row tiles; repeats of a single launch with cached weights favour 32)
+// than 256 workgroups (the MXFP8 mode and the lm_head)
 static int pick_mt(int M, int units, int maxMT) {
   int mt = M <= 32 ? 1 : M <= 64 ? 2 : 4;
   if (mt > maxMT) mt = maxMT;
-  while (mt > 1 && ((units + 3) / 4) * ((M + 32 * mt - 1) / (32 * mt)) < GEMM_MIN_TILES) mt /= 2;
+  while (mt > 1 && ((units + 3) / 4) * ((M + 32 * mt - 1) / (32 * mt)) < 256) mt /= 2;
   return mt;
 }
 
-// Residual projections run NT = 2 (64 weight rows per wave).
-int residual_nsplit(int M, int N, int K) {
-  const int units = N / 64;
-  return gemm_plan(M, units, K / 64, pick_mt(M, units, 4), true).nsplit;
+// Decoder GEMMs with 16-bit activations (one 32-row tile per wave): the
+// shape of a four-wave workgroup, NG waves along N by KS along K, and its
+// activation tile height, taken in order of the bytes a workgroup moves per
+// flop (tall shared tiles first) until one gives GEMM_WG_TARGET workgroups;
+// failing that, the one with the most.
+GemmPlan decoder_plan(int M, int tiles, int ksteps) {
+  static const int kShapes[][3] = {{4, 1, 2}, {2, 2, 2}, {4, 1, 1}, {2, 2, 1}, {1, 4, 1}};  // NG, KS, MT
+  GemmPlan best{};
+  int best_wg = -1;
+  for (const auto &s : kShapes) {
+    if (s[2] > 1 && M <= 32) continue;
+    GemmPlan p = gemm_plan(M, tiles, ksteps, s[2], false, s[0]);
+    p.KS = s[1];
+    const int wg = p.nb * p.mb;
+    if (wg >= GEMM_WG_TARGET) return p;
+    if (wg > best_wg) best = p, best_wg = wg;
+  }
+  return best;
 }
 
 // ---------------------------------------------------------------- launchers
 
-template <bool F16, int FMT, int NT, int MT, bool A8, class Epi, int NWV = 4>
+template <bool F16, int FMT, int NT, int MT, bool A8, class Epi, int NWV = 4, int KS = 1>
 static hipError_t go(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<F16, FMT, NT, MT, Epi, A8, NWV>), dim3(p.grid_x, 1, p.nsplit), dim3(64 * NWV), 0,
-                     st, ga, epi);
+  hipLaunchKernelGGL((gemm_kernel<F16, FMT, NT, MT, Epi, A8, NWV, KS>), dim3(p.grid_x, 1, p.nsplit), dim3(64 * NWV),
+                     0, st, ga, epi);
   return hipGetLastError();
 }
 
@@ -805,17 +992,34 @@ static hipError_t go_m(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hi
   }
 }
 
+// the decoder shapes of decoder_plan, FP16 activations, NT = 1
+template <int FMT, class Epi>
+static hipError_t go_decoder(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
+  if (p.MT == 2 && p.NG == 4) return go<true, FMT, 1, 2, false, Epi, 4, 1>(p, ga, epi, st);
+  if (p.MT == 2 && p.NG == 2) return go<true, FMT, 1, 2, false, Epi, 4, 2>(p, ga, epi, st);
+  if (p.MT == 1 && p.NG == 4) return go<true, FMT, 1, 1, false, Epi, 4, 1>(p, ga, epi, st);
+  if (p.MT == 1 && p.NG == 2) return go<true, FMT, 1, 1, false, Epi, 4, 2>(p, ga, epi, st);
+  if (p.MT == 1 && p.NG == 1) return go<true, FMT, 1, 1, false, Epi, 4, 4>(p, ga, epi, st);
+  return hipErrorInvalidValue;
+}
+
 // FMTS: bit (1 << format) set for each weight format a call site may pass;
 // only those kernels are instantiated.
 constexpr unsigned kFp8 = 1u << SPEC_WFMT_FP8_E4M3_ROW, kMx4 = 1u << SPEC_WFMT_MXFP4, kBf16 = 1u << SPEC_WFMT_BF16;
 
+static GemmArgs gemm_args(ActIn x, int M, int K, const LinearW &w, const GemmPlan &p, NormRows nr) {
+  return GemmArgs{x.x, x.xs, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
+                  p.nb, p.mb, p.grid_x / 8, p.spl, nr};
+}
+
 // x.xs == NULL: FP16 (BF16 for BF16 weights) activations on the 32x32x16 MFMA;
 // else MXFP8 activations on the scaled 32x32x64 MFMA (FP8 / MXFP4 weights).
+// Four waves side by side along N, one k group.
 template <int NT, unsigned FMTS, class Epi, int MAXMT = (NT > 2 ? 2 : 4)>
-static hipError_t run(ActIn x, int M, int K, const LinearW &w, Epi epi, bool allow_split, hipStream_t st) {
+static hipError_t run(ActIn x, int M, int K, const LinearW &w, Epi epi, bool allow_split, NormRows nr,
+                      hipStream_t st) {
   const GemmPlan p = gemm_plan(M, epi.units, K / 64, pick_mt(M, epi.units, MAXMT), allow_split, 4);
-  GemmArgs ga{x.x, x.xs, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
-              p.nb, p.mb, p.grid_x / 8, p.spl};
+  const GemmArgs ga = gemm_args(x, M, K, w, p, nr);
   const bool a8 = x.xs != nullptr;
   if constexpr ((FMTS & kFp8) != 0)
     if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW)
@@ -830,48 +1034,58 @@ static hipError_t run(ActIn x, int M, int K, const LinearW &w, Epi epi, bool all
   return hipErrorInvalidValue;
 }
 
+// FP16 activations, one tile per wave, the workgroup shape of decoder_plan
+template <unsigned FMTS, class Epi>
+static hipError_t run_decoder(ActIn x, int M, int K, const LinearW &w, Epi epi, NormRows nr, hipStream_t st) {
+  if (x.xs) return hipErrorInvalidValue;
+  const GemmPlan p = decoder_plan(M, epi.units, K / 64);
+  const GemmArgs ga = gemm_args(x, M, K, w, p, nr);
+  if constexpr ((FMTS & kFp8) != 0)
+    if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW) return go_decoder<SPEC_WFMT_FP8_E4M3_ROW>(p, ga, epi, st);
+  if constexpr ((FMTS & kMx4) != 0)
+    if (w.wfmt == SPEC_WFMT_MXFP4) return go_decoder<SPEC_WFMT_MXFP4>(p, ga, epi, st);
+  return hipErrorInvalidValue;
+}
+
 static const float *fp8_scale(const LinearW &w) {
   return w.wfmt == SPEC_WFMT_FP8_E4M3_ROW ? reinterpret_cast<const float *>(w.s) : nullptr;
 }
 
 hipError_t launch_linear_f32(ActIn x, int M, int N, int K, LinearW w, float *y, hipStream_t st) {
-  return run<1, kFp8 | kMx4 | kBf16>(x, M, K, w, EpiF32<1>{N / 32, N, y, fp8_scale(w)}, false, st);
+  return run<1, kFp8 | kMx4 | kBf16>(x, M, K, w, EpiF32<1>{N / 32, N, y, fp8_scale(w)}, false, NormRows{}, st);
 }
 
 hipError_t launch_residual_partial(ActIn x, int M, int N, int K, LinearW w, float *part, hipStream_t st) {
-  return run<2, kFp8 | kMx4>(x, M, K, w, EpiPartial<2>{N / 64, N, M, part, fp8_scale(w)}, true, st);
+  return run<2, kFp8 | kMx4>(x, M, K, w, EpiPartial<2>{N / 64, N, M, part, fp8_scale(w)}, true, NormRows{}, st);
 }
 
-// 64-row FP16-activation tiles in 8-wave workgroups (512 weight rows each)
-template <class Epi>
-static hipError_t run_wide(ActIn x, int M, int K, const LinearW &w, Epi epi, hipStream_t st) {
-  const GemmPlan p = gemm_plan(M, epi.units, K / 64, 2, false, 8);
-  GemmArgs ga{x.x, x.xs, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
-              p.nb, p.mb, p.grid_x / 8, p.spl};
-  if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW) return go<true, SPEC_WFMT_FP8_E4M3_ROW, 2, 2, false, Epi, 8>(p, ga, epi, st);
-  if (w.wfmt == SPEC_WFMT_MXFP4) return go<true, SPEC_WFMT_MXFP4, 2, 2, false, Epi, 8>(p, ga, epi, st);
-  return hipErrorInvalidValue;
+int residual_nsplit(int M, int N, int K) {
+  const int units = N / 64;
+  return gemm_plan(M, units, K / 64, pick_mt(M, units, 4), true, 4).nsplit;
 }
 
-hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8_t *a_scales, hipStream_t st) {
-  if (a_scales)
-    return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2, true>{I / 32, I, fp8_scale(w), a, a_scales}, false, st);
-  if (GEMM_SWIGLU_WAVES == 8 && pick_mt(M, I / 32, 4) == 2)
-    return run_wide(x, M, H, w, EpiSwiglu<2>{I / 32, I, fp8_scale(w), a, nullptr}, st);
-  return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2>{I / 32, I, fp8_scale(w), a, nullptr}, false, st);
+hipError_t launch_residual(ActIn x, int M, int N, int K, LinearW w, const ResidualOut &o, hipStream_t st) {
+  return run_decoder<kFp8 | kMx4>(x, M, K, w, EpiResidual<1>{N / 32, N, fp8_scale(w), o}, NormRows{}, st);
 }
 
-hipError_t launch_qkv(ActIn x, int M, int H, int D, LinearW w, QkvOut o, hipStream_t st) {
-  if (w.wfmt != SPEC_WFMT_FP8_E4M3_ROW) return hipErrorInvalidValue;
+hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8_t *a_scales, NormRows nr,
+                         hipStream_t st) {
+  if (a_scales)  // MXFP8 output: a unit of two tiles gives one 32-wide block per row
+    return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2, true>{I / 32, I, fp8_scale(w), a, a_scales}, false, nr, st);
+  return run_decoder<kFp8 | kMx4>(x, M, H, w, EpiSwiglu<1>{I / 16, I, fp8_scale(w), a, nullptr}, nr, st);
+}
+
+hipError_t launch_qkv(ActIn x, int M, int H, LinearW w, QkvOut o, NormRows nr, hipStream_t st) {
+  if (w.wfmt != SPEC_WFMT_FP8_E4M3_ROW || (o.D != 64 && o.D != 128)) return hipErrorInvalidValue;
   const float *s = reinterpret_cast<const float *>(w.s);
-  if (D == 64) return run<2, kFp8>(x, M, H, w, EpiQkv<2>{o.Hq + 2 * o.Hkv, s, o}, false, st);
-  if (D == 128) return run<4, kFp8>(x, M, H, w, EpiQkv<4>{o.Hq + 2 * o.Hkv, s, o}, false, st);
-  return hipErrorInvalidValue;
+  const int tiles = (o.Hq + 2 * o.Hkv) * o.D / 32;
+  if (x.xs) return run<1, kFp8>(x, M, H, w, EpiQkv<1>{tiles, s, o}, false, nr, st);
+  return run_decoder<kFp8>(x, M, H, w, EpiQkv<1>{tiles, s, o}, nr, st);
 }
 
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,
-                            float *logits_dump, hipStream_t st) {
+                            float *logits_dump, NormRows nr, hipStream_t st) {
   return run<kLmNT, kBf16, EpiArgmax<kLmNT>, GEMM_LM_MAXMT>(
       ActIn{x, nullptr}, M, H, LinearW{table, nullptr, SPEC_WFMT_BF16},
-      EpiArgmax<kLmNT>{V / (32 * kLmNT), V, lm_parts(V), part, logits_dump}, false, st);
+      EpiArgmax<kLmNT>{V / (32 * kLmNT), V, lm_parts(V), part, logits_dump}, false, nr, st);
 }

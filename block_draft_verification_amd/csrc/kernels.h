@@ -30,23 +30,73 @@ struct LinearW {
 };
 __host__ __device__ constexpr int tile_bytes(int wfmt) { return wfmt == 3 ? 4096 : wfmt == 2 ? 1024 : 2048; }
 
-// row-major -> tile-major (scales too, for MXFP4); rows % 32 == 0, cols % 64 == 0
+// Row order of a packed matrix: packed row p holds logical row map(p).
+//   kRowsPlain:  p
+//   kRowsRope:   groups of D rows (one head); packed row 32t + i of a head is
+//                dimension 16t + i (i < 16) or D/2 + 16t + (i - 16): a tile
+//                holds 16 rotate-half RoPE pairs (d, d + D/2) as rows (i, i+16)
+//   kRowsSwiglu: [gate; up] with I rows each; packed row 32t + i is gate row
+//                16t + i (i < 16) or up row 16t + (i - 16)
+enum RowMap { kRowsPlain = 0, kRowsRope = 1, kRowsSwiglu = 2 };
+__host__ __device__ inline int packed_row_source(int map, int p, int param /* D or I */) {
+  if (map == kRowsRope) {
+    const int head = p / param, r = p % param, t = r >> 5, i = r & 31;
+    return head * param + (i < 16 ? 16 * t + i : param / 2 + 16 * t + (i - 16));
+  }
+  if (map == kRowsSwiglu) {
+    const int t = p >> 5, i = p & 31;
+    return i < 16 ? 16 * t + i : param + 16 * t + (i - 16);
+  }
+  return p;
+}
+// Row-major -> tile-major in the row order of `map` (MXFP4 scales too, and
+// FP8 per-row scales permuted into s_out); rows % 32 == 0, cols % 64 == 0
 hipError_t launch_pack_weights(int wfmt, int rows, int cols, const void *w, const void *s, void *w_out, void *s_out,
-                               hipStream_t st);
+                               int map, int map_param, hipStream_t st);
 
-// Tiling of one launch (see gemm.hip): MT 16-row activation tiles per
-// workgroup, nb x mb output tiles, K split into nsplit pieces of spl steps.
+// Tiling of one launch (see gemm.hip): MT 32-row activation tiles per
+// workgroup, NG waves along N by KS along K, nb x mb output tiles, K split
+// across workgroups into nsplit pieces of spl steps.
 struct GemmPlan {
-  int MT, nb, mb, spl, nsplit, grid_x;
+  int MT, NG, KS, nb, mb, spl, nsplit, grid_x;
 };
-GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split, int nwv = 4);  // nwv waves per workgroup
-// splits the residual projection [M][K] x [N][K]^T will use (partials to reduce)
+GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split, int ng = 4);  // ng waves along N
+// the workgroup shape of a decoder GEMM with 16-bit activations, one tile per wave
+GemmPlan decoder_plan(int M, int tiles, int ksteps);
+// splits the MXFP8 mode's residual projection [M][K] x [N][K]^T uses (partials to reduce)
 int residual_nsplit(int M, int N, int K);
+
+// The input rows of a GEMM given as h * g (an RMSNorm's gain folded in, its
+// normalisation left to the GEMM): ssp [M][ld] holds partial sums of h^2
+// (entries past the real ones zero); the GEMM scales its outputs of row m by
+// 1 / sqrt(sum_j ssp[m][j] / H + eps).  ssp NULL: the rows are used as given.
+struct NormRows {
+  const float *ssp;
+  int ld, H;
+  float eps;
+};
+// floats per row of the partial-sum buffer: one per 32 columns, padded to 4
+inline int ssp_ld(int H) { return ((H / 32 + 3) / 4) * 4; }
+
+// What a residual projection writes: h_out = h_in + y (fp32 [M][N]); xg =
+// h_out * gain (FP16, or BF16 when xg_bf16), the input of the GEMM after the
+// next RMSNorm; ssp[m][n / 32] = sum of h_out^2 over each 32 columns.
+struct ResidualOut {
+  const float *h_in;
+  float *h_out;
+  const float *gain;
+  uint16_t *xg;
+  int xg_bf16;
+  float *ssp;
+  int ssp_ld;
+  int32_t *err;
+};
+hipError_t launch_residual(ActIn x, int M, int N, int K, LinearW w, const ResidualOut &o, hipStream_t st);
 
 // y fp32 [M][N] (test hook)
 hipError_t launch_linear_f32(ActIn x, int M, int N, int K, LinearW w, float *y, hipStream_t st);
 
-// QKV projection + RoPE; q -> q_out bf16 [M][Hq*D]; k, v -> caches at slot kv_len[b] + j.
+// QKV projection + RoPE; q -> q_out FP16 [M][Hq*D]; k, v -> BF16 caches at slot kv_len[b] + j.
 // Where cache position `pos` of (sequence b, KV head h) lives, as a row index
 // into one layer's K or V array (rows of D elements): contiguous
 // [max_batch][Hkv][max_ctx], or paged [num_pages][Hkv][page_size] through
@@ -72,18 +122,21 @@ struct QkvOut {
   uint16_t *k_cache, *v_cache;  // layer base (contiguous or page pool)
   const int32_t *kv_len;
   const float2 *rope;           // [max_ctx][D/2] (cos, sin)
-  int Hq, Hkv, max_ctx;
+  int Hq, Hkv, D, max_ctx;
   KvLayout kvl;
+  int32_t *err;                 // SPEC_DERR_RANGE: a q, k or v value beyond FP16's range
 };
-// q (FP16) and k, v (BF16 cache) from x
-hipError_t launch_qkv(ActIn x, int M, int H, int D, LinearW w, QkvOut o, hipStream_t st);
+// q (FP16) and k, v (BF16 cache) from x; w packed with kRowsRope
+hipError_t launch_qkv(ActIn x, int M, int H, LinearW w, QkvOut o, NormRows nr, hipStream_t st);
 
-// a[m][n] = SiLU(x Wg^T) * (x Wu^T), W = [gate; up] with I rows each: FP16
-// (a_scales NULL) or MXFP8 codes in a and e8m0 [M][I/32] in a_scales
-hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8_t *a_scales, hipStream_t st);
+// a[m][n] = SiLU(x Wg^T) * (x Wu^T), W = [gate; up] with I rows each, packed
+// with kRowsSwiglu: FP16 (a_scales NULL) or MXFP8 codes in a and e8m0
+// [M][I/32] in a_scales
+hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8_t *a_scales, NormRows nr,
+                         hipStream_t st);
 
 // part[z][m][n] = split z of (x W^T)[m][n] (fp32); residual_nsplit() splits.
-// The following launch_norm adds them to h.
+// The following launch_norm adds them to h (the MXFP8-activation mode).
 hipError_t launch_residual_partial(ActIn x, int M, int N, int K, LinearW w, float *part, hipStream_t st);
 
 // lm_head (BF16 x, BF16 table) + argmax partials, one per (row, workgroup):
@@ -94,7 +147,7 @@ struct ArgmaxPart { float v; int32_t i; };
 #endif
 constexpr int kLmNT = GEMM_LM_NT;  // 32-row vocab tiles per wave (one: two waves per SIMD fit)
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,
-                            float *logits_dump, hipStream_t st);
+                            float *logits_dump, NormRows nr, hipStream_t st);
 inline int lm_parts(int V) { return (V / (32 * kLmNT) + 3) / 4; }
 
 // ---- attention ----
@@ -134,11 +187,20 @@ AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hkv, int max_ctx, in
 hipError_t launch_attention_plan(const int32_t *kv_len, const AttnPlanArgs &p, hipStream_t st);
 
 // ---- small kernels ----
-// table: the tile-major BF16 embedding [V][H]
-// (and, with plan.plan non-NULL, the attention split plan of the pass)
+// h = E[t] (table: the row-major BF16 embedding [V][H]); with xg non-NULL
+// also xg = h * gain (FP16) and the partial sums of h^2 per 32 columns into
+// ssp [M][ld] (the first RMSNorm, folded into the QKV step); with plan.plan
+// non-NULL, the attention split plan of the pass.
 hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16_t *table, float *h,
-                        const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, const AttnPlanArgs &plan,
-                        hipStream_t st);
+                        const float *gain, uint16_t *xg, float *ssp, int ld, const int32_t *kv_len, int max_ctx,
+                        KvLayout kvl, int32_t *err, const AttnPlanArgs &plan, hipStream_t st);
+// The final normed hidden state of the rows the lm_head read, from its input
+// xg = h * g (BF16 [M][H]) and the partial sums ssp: x = xg / sqrt(sum/H +
+// eps).  rows: every row (row_of NULL, n rows) or row b*16 + row_of[b] - 1 for
+// b < n (row_of = the accepted lengths; b is skipped when row_of[b] is outside
+// [1, 16]).  Written as fp32 [n][H] (out_f32) or BF16 [n][H] (out_bf16).
+hipError_t launch_final_hidden(const uint16_t *xg, const float *ssp, int ld, int H, float eps, int n,
+                               const int32_t *row_of, float *out_f32, uint16_t *out_bf16, hipStream_t st);
 // h_out = h + part[0] + ... + part[nsplit-1] (in that order; nsplit may be 0;
 // h_out may be NULL, and is never h, so a launch can be repeated), then
 // x = RMSNorm(h_out) * gain, written as FP16 (out_bf16 = 0) or BF16 (out_bf16 = 1)
@@ -159,8 +221,10 @@ hipError_t launch_commit(int batch, const int32_t *n_commit, const int32_t *last
 hipError_t launch_fill_i32(int32_t *p, int n, int32_t v, hipStream_t st);
 hipError_t launch_prefill_gather(const int32_t *prompt, int T, const int32_t *lens, int chunk, int batch,
                                  int32_t *tokens, int32_t *err, hipStream_t st);
+// (the prompt's last row's final hidden state is written by
+// launch_final_hidden with row_of = last_tau once the finish step has set it)
+// sel[b] = the row count r of the chunk that holds prompt b's last token (the
+// anchor row is r - 1), 0 for the other sequences
 hipError_t launch_prefill_finish(const int32_t *lens, int T, int chunk, int batch, const int32_t *argmax,
-                                 const uint16_t *x, int H, int32_t *n_commit, int32_t *pending, int32_t *last_tau,
-                                 uint16_t *anchor, hipStream_t st);
-hipError_t launch_export_hidden(int batch, const int32_t *last_tau, const uint16_t *x, int H, uint16_t *out,
-                                hipStream_t st);
+                                 int32_t *n_commit, int32_t *pending, int32_t *last_tau, int32_t *sel,
+                                 hipStream_t st);

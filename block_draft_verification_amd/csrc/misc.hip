@@ -1,17 +1,27 @@
-// Embedding gather, RMSNorm, argmax reduction + prefix accept, KV commit.
+// Embedding gather, RMSNorm, argmax reduction + prefix accept, KV commit,
+// weight packing, the final hidden state.
 #include "attn_plan.h"
 #include "common.h"
 #include "kernels.h"
 
-// h[m][:] = E[t[m]][:] (BF16 -> fp32).  Also checks that every sequence's
-// block fits its cache (kv_len + 16 <= max_ctx); the QKV step skips the K/V
-// writes of a sequence that does not.  One wave of the launch also computes
-// the attention split plan of the pass (attn_plan.h), which depends only on
-// kv_len: every attention launch of the pass then reads it.
-__global__ void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
-                             const uint16_t *__restrict__ table, float *__restrict__ h,
-                             const int32_t *__restrict__ kv_len, int max_ctx, KvLayout kvl, int32_t *err,
-                             AttnPlanArgs plan) {
+__device__ __forceinline__ void store_bf16x4_misc(uint16_t *p, f32x4_t v) {
+  *reinterpret_cast<u32x2_t *>(p) = u32x2_t{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+
+// h[m][:] = E[t[m]][:] (BF16 -> fp32, the row-major table).  With xg set,
+// also the first RMSNorm's input for the QKV step: xg = h * gain (FP16) and
+// the sum of h^2 over each 32 columns into ssp[m][.] (the row's remaining
+// entries zeroed).  Also checks that every sequence's block fits its cache
+// (kv_len + 16 <= max_ctx); the QKV step skips the K/V writes of a sequence
+// that does not.  One wave of the launch also computes the attention split
+// plan of the pass (attn_plan.h), which depends only on kv_len: every
+// attention launch of the pass then reads it.
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
+                                                    const uint16_t *__restrict__ table, float *__restrict__ h,
+                                                    const float *__restrict__ gain, uint16_t *__restrict__ xg,
+                                                    float *__restrict__ ssp, int ld,
+                                                    const int32_t *__restrict__ kv_len, int max_ctx, KvLayout kvl,
+                                                    int32_t *err, AttnPlanArgs plan) {
   const int m = blockIdx.x;
   // the last workgroup's last wave also writes the pass's attention split plan
   if (plan.plan && m == (int)gridDim.x - 1 && threadIdx.x >= blockDim.x - 64)
@@ -32,33 +42,52 @@ __global__ void embed_kernel(const int32_t *__restrict__ tokens, int H, int V,
       }
     }
   }
-  // row t of the tile-major table: 8 columns (one 16-byte chunk) per thread
-  const int ktiles = H / 64;
-  for (int k0 = 8 * threadIdx.x; k0 < H; k0 += 8 * blockDim.x) {
-    const int kk = k0 & 63, l = 32 * (kk >> 5) + (t & 31), j = (kk & 31) >> 3;
-    const size_t tile = (size_t)(t >> 5) * ktiles + (k0 >> 6);
-    const u32x4_t v = *reinterpret_cast<const u32x4_t *>(table + tile * 2048 + (j * 64 + l) * 8);
+  // 8 columns (one 16-byte chunk of the row) per thread; the 4 threads of a
+  // 32-column group are consecutive lanes and run every iteration together
+  const uint16_t *src = table + (size_t)t * H;
+  for (int k0 = 8 * threadIdx.x; k0 - 8 * (int)threadIdx.x < H; k0 += 8 * blockDim.x) {
+    const bool in = k0 < H;
+    const u32x4_t v = in ? *reinterpret_cast<const u32x4_t *>(src + k0) : u32x4_t{0u, 0u, 0u, 0u};
+    const f32x4_t a = f32x4_t{bf16_to_f32(v.x & 0xffff), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xffff),
+                              bf16_to_f32(v.y >> 16)};
+    const f32x4_t b = f32x4_t{bf16_to_f32(v.z & 0xffff), bf16_to_f32(v.z >> 16), bf16_to_f32(v.w & 0xffff),
+                              bf16_to_f32(v.w >> 16)};
+    float ss = ((a[0] * a[0] + a[1] * a[1]) + (a[2] * a[2] + a[3] * a[3])) +
+               ((b[0] * b[0] + b[1] * b[1]) + (b[2] * b[2] + b[3] * b[3]));
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    if (!in) continue;
     float *o = h + (size_t)m * H + k0;
-    *reinterpret_cast<f32x4_t *>(o) = f32x4_t{bf16_to_f32(v.x & 0xffff), bf16_to_f32(v.x >> 16),
-                                              bf16_to_f32(v.y & 0xffff), bf16_to_f32(v.y >> 16)};
-    *reinterpret_cast<f32x4_t *>(o + 4) = f32x4_t{bf16_to_f32(v.z & 0xffff), bf16_to_f32(v.z >> 16),
-                                                  bf16_to_f32(v.w & 0xffff), bf16_to_f32(v.w >> 16)};
+    *reinterpret_cast<f32x4_t *>(o) = a;
+    *reinterpret_cast<f32x4_t *>(o + 4) = b;
+    if (xg) {
+      const f32x4_t g0 = *reinterpret_cast<const f32x4_t *>(gain + k0), g1 = *reinterpret_cast<const f32x4_t *>(gain + k0 + 4);
+      const f32x4_t x0 = a * g0, x1 = b * g1;
+      *reinterpret_cast<u32x4_t *>(xg + (size_t)m * H + k0) =
+          u32x4_t{pack_f16x2(x0[0], x0[1]), pack_f16x2(x0[2], x0[3]), pack_f16x2(x1[0], x1[1]), pack_f16x2(x1[2], x1[3])};
+      const float mx = fmaxf(fmaxf(fmaxf(fabsf(x0[0]), fabsf(x0[1])), fmaxf(fabsf(x0[2]), fabsf(x0[3]))),
+                             fmaxf(fmaxf(fabsf(x1[0]), fabsf(x1[1])), fmaxf(fabsf(x1[2]), fabsf(x1[3]))));
+      if (!(mx <= 65504.f)) set_error(err, SPEC_DERR_RANGE);
+      if ((k0 & 31) == 0) ssp[(size_t)m * ld + k0 / 32] = ss;
+    }
   }
+  if (xg && (int)threadIdx.x < ld - H / 32) ssp[(size_t)m * ld + H / 32 + threadIdx.x] = 0.f;
 }
 
-// Row-major -> tile-major weights (the layout kernels.h describes): thread i
-// writes destination chunk i (16 bytes) from one contiguous 16-byte run of its
-// source row; MXFP4 scale tiles are written one byte per thread.
+// Row-major -> tile-major weights (the layout kernels.h describes) in the row
+// order of `map`: thread i writes destination chunk i (16 bytes) from one
+// contiguous 16-byte run of its source row; MXFP4 scale tiles are written one
+// byte per thread, FP8 row scales one float per thread.
 template <int FMT>
 __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ src, int rows, int cols,
-                                                   uint8_t *__restrict__ dst, size_t nchunks) {
+                                                   uint8_t *__restrict__ dst, size_t nchunks, int map, int mp) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= nchunks) return;
   constexpr int CPT = FMT == SPEC_WFMT_BF16 ? 256 : FMT == SPEC_WFMT_MXFP4 ? 64 : 128;  // chunks per tile
   const int ktiles = cols / 64;
   const size_t tile = i / CPT;
   const int q = (int)(i % CPT), j = q >> 6, l = q & 63, c = l & 31, hh = l >> 5;
-  const int row = (int)(tile / ktiles) * 32 + c, kt = (int)(tile % ktiles);
+  const int row = packed_row_source(map, (int)(tile / ktiles) * 32 + c, mp), kt = (int)(tile % ktiles);
   size_t off;  // byte offset of the chunk's first byte in the row-major source
   if constexpr (FMT == SPEC_WFMT_FP8_E4M3_ROW) off = (size_t)row * cols + kt * 64 + 16 * hh + 32 * j;
   else if constexpr (FMT == SPEC_WFMT_BF16) off = ((size_t)row * cols + kt * 64 + 32 * hh + 8 * j) * 2;
@@ -67,14 +96,60 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint8_t *__restrict__ s
 }
 
 __global__ __launch_bounds__(256) void pack_scales_kernel(const uint8_t *__restrict__ src, int rows, int cols,
-                                                          uint8_t *__restrict__ dst, size_t n) {
+                                                          uint8_t *__restrict__ dst, size_t n, int map, int mp) {
   const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   if (i >= n) return;
   const int ktiles = cols / 64;
   const size_t tile = i / 64;
   const int l = (int)(i % 64), c = l & 31, hh = l >> 5;
-  const int row = (int)(tile / ktiles) * 32 + c, kt = (int)(tile % ktiles);
+  const int row = packed_row_source(map, (int)(tile / ktiles) * 32 + c, mp), kt = (int)(tile % ktiles);
   dst[i] = src[(size_t)row * (cols / 32) + 2 * kt + hh];
+}
+
+__global__ __launch_bounds__(256) void permute_rows_f32_kernel(const float *__restrict__ src, int rows,
+                                                               float *__restrict__ dst, int map, int mp) {
+  const int p = blockIdx.x * 256 + threadIdx.x;
+  if (p < rows) dst[p] = src[packed_row_source(map, p, mp)];
+}
+
+// Final normed hidden state from the lm_head's input: x = xg * r with r =
+// 1 / sqrt(sum / H + eps) over the row's partial sums, added in the order the
+// lm_head kernel adds them (lane chunks j = q + 8i summed per q, then over q),
+// so x is the hidden state whose logits it took.
+__global__ __launch_bounds__(256) void final_hidden_kernel(const uint16_t *__restrict__ xg,
+                                                           const float *__restrict__ ssp, int ld, int H, float eps,
+                                                           const int32_t *__restrict__ row_of, float *out_f32,
+                                                           uint16_t *out_bf16) {
+  __shared__ float rsh;
+  const int b = blockIdx.x;
+  int row = b;
+  if (row_of) {
+    const int r = row_of[b];
+    if (r < 1 || r > 16) return;  // whole workgroup
+    row = 16 * b + r - 1;
+  }
+  if (threadIdx.x == 0) {
+    const int nch = ld / 4;
+    float ss = 0.f;
+    for (int q = 0; q < 8; ++q) {  // the lm_head's four-wave workgroup: 8 lane groups
+      float ps = 0.f;
+      for (int j = q; j < nch; j += 8) {
+        const float *p = ssp + (size_t)row * ld + 4 * j;
+        ps += (p[0] + p[1]) + (p[2] + p[3]);
+      }
+      ss += ps;
+    }
+    rsh = 1.0f / sqrtf(ss / (float)H + eps);
+  }
+  __syncthreads();
+  const float r = rsh;
+  for (int k = 4 * threadIdx.x; k < H; k += 4 * blockDim.x) {
+    const u32x2_t v = *reinterpret_cast<const u32x2_t *>(xg + (size_t)row * H + k);
+    const f32x4_t x = f32x4_t{bf16_to_f32(v.x & 0xffff), bf16_to_f32(v.x >> 16), bf16_to_f32(v.y & 0xffff),
+                              bf16_to_f32(v.y >> 16)} * r;
+    if (out_f32) *reinterpret_cast<f32x4_t *>(out_f32 + (size_t)b * H + k) = x;
+    if (out_bf16) store_bf16x4_misc(out_bf16 + (size_t)b * H + k, x);
+  }
 }
 
 // h_out = h + part[0] + ... + part[ns-1] (split-K partials of the projection
@@ -270,38 +345,23 @@ __global__ void prefill_gather_kernel(const int32_t *__restrict__ prompt, int T,
 
 // After chunk c: commit min(max(len - 16c, 0), 16) rows.  The chunk that holds
 // a prompt's last token (r = len - 16c rows of it) also yields the pending token
-// (the argmax at row r-1: the greedy next token after the prompt) and, when
-// asked, that row's final normed hidden state (BF16), the feature a block
-// drafter is conditioned on.  last_tau = r, so the anchor row is last_tau - 1
-// as after a verify pass.
+// (the argmax at row r-1: the greedy next token after the prompt); sel[b] = r
+// for it (0 otherwise) selects that row's final hidden state, the feature a
+// block drafter is conditioned on.  last_tau = r, so the anchor row is
+// last_tau - 1 as after a verify pass.
 __global__ void prefill_finish_kernel(const int32_t *__restrict__ lens, int T, int chunk,
-                                      const int32_t *__restrict__ argmax, const uint16_t *__restrict__ x, int H,
-                                      int32_t *n_commit, int32_t *pending, int32_t *last_tau, uint16_t *anchor) {
-  const int b = blockIdx.x, tid = threadIdx.x;
+                                      const int32_t *__restrict__ argmax, int32_t *n_commit, int32_t *pending,
+                                      int32_t *last_tau, int32_t *sel) {
+  const int b = blockIdx.x;
   const int len = lens[b];
   const int rem = (len >= 1 && len <= T) ? len - 16 * chunk : 0;
-  if (tid == 0) n_commit[b] = min(max(rem, 0), 16);
-  if (rem < 1 || rem > 16) return;
-  if (tid == 0) {
+  n_commit[b] = min(max(rem, 0), 16);
+  const bool last = rem >= 1 && rem <= 16;
+  sel[b] = last ? rem : 0;
+  if (last) {
     pending[b] = argmax[b * 16 + rem - 1];
     last_tau[b] = rem;
   }
-  if (anchor) {
-    const uint16_t *src = x + (size_t)(b * 16 + rem - 1) * H;
-    for (int i = tid * 8; i < H; i += 8 * blockDim.x)
-      *reinterpret_cast<u32x4_t *>(anchor + (size_t)b * H + i) = *reinterpret_cast<const u32x4_t *>(src + i);
-  }
-}
-
-// out[b] = final normed hidden state (BF16) of row last_tau[b] - 1 of the last
-// pass: the position whose argmax gave the bonus token.
-__global__ void export_hidden_kernel(const int32_t *__restrict__ last_tau, const uint16_t *__restrict__ x, int H,
-                                     uint16_t *out) {
-  const int b = blockIdx.x;
-  const int r = min(max(last_tau[b], 1), 16);
-  const uint16_t *src = x + (size_t)(b * 16 + r - 1) * H;
-  for (int i = threadIdx.x * 8; i < H; i += 8 * blockDim.x)
-    *reinterpret_cast<u32x4_t *>(out + (size_t)b * H + i) = *reinterpret_cast<const u32x4_t *>(src + i);
 }
 
 __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
@@ -310,31 +370,47 @@ __global__ void fill_i32_kernel(int32_t *p, int n, int32_t v) {
 }
 
 hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16_t *table, float *h,
-                        const int32_t *kv_len, int max_ctx, KvLayout kvl, int32_t *err, const AttnPlanArgs &plan,
-                        hipStream_t st) {
-  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, st, tokens, H, V, table, h, kv_len, max_ctx, kvl, err,
-                     plan);
+                        const float *gain, uint16_t *xg, float *ssp, int ld, const int32_t *kv_len, int max_ctx,
+                        KvLayout kvl, int32_t *err, const AttnPlanArgs &plan, hipStream_t st) {
+  if (H % 32 || (xg && ld - H / 32 > 256)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, st, tokens, H, V, table, h, gain, xg, ssp, ld, kv_len,
+                     max_ctx, kvl, err, plan);
+  return hipGetLastError();
+}
+
+hipError_t launch_final_hidden(const uint16_t *xg, const float *ssp, int ld, int H, float eps, int n,
+                               const int32_t *row_of, float *out_f32, uint16_t *out_bf16, hipStream_t st) {
+  if (H % 4 || n < 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(final_hidden_kernel, dim3(n), dim3(256), 0, st, xg, ssp, ld, H, eps, row_of, out_f32, out_bf16);
   return hipGetLastError();
 }
 
 hipError_t launch_pack_weights(int wfmt, int rows, int cols, const void *w, const void *s, void *w_out, void *s_out,
-                               hipStream_t st) {
+                               int map, int mp, hipStream_t st) {
   if (rows % 32 || cols % 64 || rows < 32 || cols < 64) return hipErrorInvalidValue;
+  if ((map == kRowsRope && (mp < 32 || mp % 32 || rows % mp)) || (map == kRowsSwiglu && (mp % 16 || rows != 2 * mp)))
+    return hipErrorInvalidValue;
   const size_t tiles = (size_t)(rows / 32) * (cols / 64);
   const size_t chunks = tiles * (tile_bytes(wfmt) / 16);
   const dim3 grid((unsigned)((chunks + 255) / 256));
   const uint8_t *src = static_cast<const uint8_t *>(w);
   uint8_t *dst = static_cast<uint8_t *>(w_out);
   if (wfmt == SPEC_WFMT_FP8_E4M3_ROW) {
-    hipLaunchKernelGGL(pack_kernel<SPEC_WFMT_FP8_E4M3_ROW>, grid, dim3(256), 0, st, src, rows, cols, dst, chunks);
+    hipLaunchKernelGGL(pack_kernel<SPEC_WFMT_FP8_E4M3_ROW>, grid, dim3(256), 0, st, src, rows, cols, dst, chunks, map,
+                       mp);
+    if (s && s_out) {
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+      hipLaunchKernelGGL(permute_rows_f32_kernel, dim3((rows + 255) / 256), dim3(256), 0, st,
+                         static_cast<const float *>(s), rows, static_cast<float *>(s_out), map, mp);
+    }
   } else if (wfmt == SPEC_WFMT_BF16) {
-    hipLaunchKernelGGL(pack_kernel<SPEC_WFMT_BF16>, grid, dim3(256), 0, st, src, rows, cols, dst, chunks);
+    hipLaunchKernelGGL(pack_kernel<SPEC_WFMT_BF16>, grid, dim3(256), 0, st, src, rows, cols, dst, chunks, map, mp);
   } else if (wfmt == SPEC_WFMT_MXFP4) {
-    hipLaunchKernelGGL(pack_kernel<SPEC_WFMT_MXFP4>, grid, dim3(256), 0, st, src, rows, cols, dst, chunks);
+    hipLaunchKernelGGL(pack_kernel<SPEC_WFMT_MXFP4>, grid, dim3(256), 0, st, src, rows, cols, dst, chunks, map, mp);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     const size_t n = tiles * 64;
     hipLaunchKernelGGL(pack_scales_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                       static_cast<const uint8_t *>(s), rows, cols, static_cast<uint8_t *>(s_out), n);
+                       static_cast<const uint8_t *>(s), rows, cols, static_cast<uint8_t *>(s_out), n, map, mp);
   } else {
     return hipErrorInvalidValue;
   }
@@ -405,16 +481,10 @@ hipError_t launch_prefill_gather(const int32_t *prompt, int T, const int32_t *le
 }
 
 hipError_t launch_prefill_finish(const int32_t *lens, int T, int chunk, int batch, const int32_t *argmax,
-                                 const uint16_t *x, int H, int32_t *n_commit, int32_t *pending, int32_t *last_tau,
-                                 uint16_t *anchor, hipStream_t st) {
-  hipLaunchKernelGGL(prefill_finish_kernel, dim3(batch), dim3(128), 0, st, lens, T, chunk, argmax, x, H, n_commit,
-                     pending, last_tau, anchor);
-  return hipGetLastError();
-}
-
-hipError_t launch_export_hidden(int batch, const int32_t *last_tau, const uint16_t *x, int H, uint16_t *out,
-                                hipStream_t st) {
-  hipLaunchKernelGGL(export_hidden_kernel, dim3(batch), dim3(128), 0, st, last_tau, x, H, out);
+                                 int32_t *n_commit, int32_t *pending, int32_t *last_tau, int32_t *sel,
+                                 hipStream_t st) {
+  hipLaunchKernelGGL(prefill_finish_kernel, dim3(batch), dim3(1), 0, st, lens, T, chunk, argmax, n_commit, pending,
+                     last_tau, sel);
   return hipGetLastError();
 }
 

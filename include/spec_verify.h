@@ -29,26 +29,34 @@
  *   final x = RMSNorm(h); logits = x E^T (or x Wlm^T for an untied head).
  *
  * Numerics of this implementation: FP8 / MXFP4 weights decoded exactly to
- * FP16 and multiplied with FP16 activations (normed x, q, softmax weights,
- * attention output, SwiGLU output); the KV cache is BF16 (converted exactly
- * to FP16 inside attention); the lm_head multiplies its BF16 table with the
- * final normed hidden state rounded to BF16; fp32 accumulation, residual
- * stream, softmax statistics and logits.  With act_fmt = SPEC_ACT_MXFP8 the
- * inputs of the QKV, gate/up and down projections are MXFP8 instead (see
- * spec_act_fmt) and those products run on the scaled FP8 matrix cores.
+ * FP16 and multiplied with FP16 activations (q, softmax weights, attention
+ * output, SwiGLU output, and each RMSNorm's input h * g, whose normalisation
+ * 1/sqrt(mean(h^2) + eps) the next projection applies to its fp32 outputs);
+ * the KV cache is BF16, converted to FP16 inside attention (exact for
+ * |v| < 65520 apart from FP16's subnormal range; larger values are not
+ * supported); the lm_head multiplies its BF16 table with h * g of the final
+ * RMSNorm rounded to BF16 and normalises its fp32 logits; fp32 accumulation,
+ * residual stream, softmax statistics and logits.  A q, k, v or normed-input
+ * value beyond FP16's range sets SPEC_DERR_RANGE.  With act_fmt =
+ * SPEC_ACT_MXFP8 the inputs of the QKV, gate/up and down projections are
+ * MXFP8 instead (see spec_act_fmt) and those products run on the scaled FP8
+ * matrix cores.
  *
  * Conventions for every call:
  *   - Pointers are DEVICE pointers unless marked (host).
  *   - The caller owns all device memory it passes in (weights, KV caches,
- *     kv_len, tokens, outputs).  The library owns only the workspace it
- *     allocates in spec_verify_init and frees in spec_verify_destroy.
+ *     kv_len, tokens, outputs).  The library owns only what it allocates in
+ *     spec_verify_init (its workspace and its packed copy of the weights)
+ *     and frees in spec_verify_destroy.
  *   - Work is enqueued on the given stream and returns without waiting;
  *     nothing is copied device->host except in spec_get_device_error.
- *   - Return values: SPEC_OK (0) or a negative spec_status.  Argument errors
- *     are detected on the host before anything is enqueued.  Conditions only
- *     the device can see (a token id >= vocab, a cache that would overflow)
- *     set bits in a sticky device error word; affected rows skip their
- *     writes, so no access ever leaves its buffer.
+ *   - Return values: SPEC_OK (0) or a negative spec_status; spec_last_error()
+ *     describes the latest failure of the calling thread (for SPEC_E_HIP:
+ *     which launch or runtime call failed, with the HIP error).  Argument
+ *     errors are detected on the host before anything is enqueued.
+ *     Conditions only the device can see (a token id >= vocab, a cache that
+ *     would overflow) set bits in a sticky device error word; affected rows
+ *     skip their writes, so no access ever leaves its buffer.
  *   - One context per stream; calls on one context must not overlap.
  */
 #ifndef SPEC_VERIFY_H
@@ -109,6 +117,8 @@ typedef enum {
                                 that sequence is not advanced                 */
 #define SPEC_DERR_PAGE 16    /* paged cache: a page index the pass needs lies
                                 outside [0, num_pages)                        */
+#define SPEC_DERR_RANGE 32   /* a q, k, v or RMSNorm-input value beyond FP16's
+                                range (|v| > 65504): results are not valid   */
 
 typedef struct {
   int32_t n_layers, hidden, n_q_heads, n_kv_heads, head_dim, intermediate, vocab;
@@ -120,38 +130,24 @@ typedef struct {
   int32_t act_fmt;   /* spec_act_fmt */
 } spec_model_desc;
 
-/* Weight memory layout.  Every weight matrix and the BF16 embedding / lm_head
- * tables are passed TILE-MAJOR, the order in which the kernels stream them,
- * so that every wave-wide weight load reads one contiguous kilobyte.  The
- * logical matrix is [rows][cols] (rows = outputs, cols = inputs, rows a
- * multiple of 32, cols a multiple of 64), cut into 32 x 64 tiles; tile
- * (rt, kt) is stored at tile index rt * (cols/64) + kt.  Inside a tile,
- * "lane" l = 32h + c (c = row within the tile, h = 0 or 1) owns 16-byte
- * chunks, chunk j of lane l at byte (j*64 + l) * 16 of the tile:
- *   FP8_E4M3_ROW (2048-byte tiles): chunk j = row c, columns 16h + 32j .. +15
- *   BF16         (4096-byte tiles): chunk j (0..3) = row c, columns 32h + 8j .. +7
- *   MXFP4        (1024-byte tiles): chunk 0 = row c, columns 32h .. 32h+31 as
- *                nibble pairs (low nibble = even column); its e8m0 scales are
- *                tile-major too, 64 bytes per tile, byte l = the scale of
- *                columns 32h .. 32h+31 of row c.
- * FP8 per-row scales stay fp32 [rows].  spec_pack_weights converts from
- * row-major. */
+/* Weight memory layout: row-major, outputs by inputs, as a checkpoint
+ * stores them.  FP8_E4M3_ROW: uint8 codes [rows][cols] + fp32 scale [rows];
+ * MXFP4: uint8 [rows][cols/2] (low nibble = even column) + uint8 e8m0
+ * [rows][cols/32]; BF16: uint16 [rows][cols].  Rows are a multiple of 32 and
+ * columns a multiple of 64.  spec_verify_init repacks every weight matrix
+ * (and the lm_head table) into a library-owned copy in the order the kernels
+ * stream it, so the library holds a second copy of the weights: for the
+ * 0.5B-class model (24 layers, hidden 896, intermediate 4864, FP8) 0.36 GB of
+ * layers plus 0.27 GB of BF16 lm_head; for the 8B-class model 7.0 GB plus
+ * 1.05 GB.  The caller's weights may be freed after init; the embedding
+ * table (read by row) and the norm gains may not. */
 
-/* Row-major -> tile-major on the device (see above).  wfmt FP8_E4M3_ROW:
- * codes uint8 [rows][cols] -> w_packed (scales unused: FP8 row scales are
- * passed as they are); MXFP4: nibbles [rows][cols/2] and e8m0 scales
- * [rows][cols/32] -> w_packed and scales_packed; BF16: [rows][cols] ->
- * w_packed.  Output buffers have the input's size, are caller-owned, must not
- * overlap the input, and are 16-byte aligned.  Asynchronous. */
-int spec_pack_weights(int32_t wfmt, int32_t rows, int32_t cols, const void *w, const void *scales,
-                      void *w_packed, void *scales_packed, hipStream_t stream);
-
-/* One decoder layer (all device pointers, caller-owned; tile-major weights).
+/* One decoder layer (all device pointers, caller-owned, row-major).
  *   w_qkv  [(Hq+2Hkv)*D][H], rows = q heads, then k heads, then v heads
  *   w_o    [H][Hq*D]
  *   w_gate_up [2I][H], rows = gate (I rows) then up (I rows)
  *   w_down [H][I]
- * s_* : fp32 [rows] for FP8_E4M3_ROW; tile-major e8m0 for MXFP4.
+ * s_* : fp32 [rows] for FP8_E4M3_ROW; e8m0 [rows][cols/32] for MXFP4.
  * attn_norm, mlp_norm: fp32 RMSNorm gains [H]. */
 typedef struct {
   const void *w_qkv, *s_qkv;
@@ -163,8 +159,8 @@ typedef struct {
 
 typedef struct {
   const spec_layer_weights *layers; /* (host) array of n_layers; copied at init */
-  const uint16_t *embed;            /* bf16 [V][H], tile-major                 */
-  const uint16_t *lm_head;          /* bf16 [V][H], tile-major; NULL when tied */
+  const uint16_t *embed;            /* bf16 [V][H]                              */
+  const uint16_t *lm_head;          /* bf16 [V][H]; NULL when tied              */
   const float *final_norm;          /* fp32 [H]                                */
 } spec_weights;
 
@@ -194,14 +190,22 @@ typedef struct {
 
 typedef struct spec_ctx spec_ctx;
 
-/* Validate the model and cache description, copy the pointer tables, and
- * allocate the library workspace (activations for max_batch*16 rows, split
- * attention partials, argmax partials, a RoPE cos/sin table for positions
- * < max_ctx, the device error word).  Supported: head_dim 64 or 128, hidden
- * and intermediate multiples of 64 with hidden <= 4096, vocab a multiple of
- * 64, Hq % Hkv == 0 with Hq / Hkv <= 8.
- * Synchronous (allocations and one table upload on `stream`).  *out is set
- * only on success. */
+/* Set up a verify context for one target model and its KV cache.  The
+ * target's weights arrive as a checkpoint holds them: FP8 (or MXFP4) linear
+ * layers with their scales and a BF16 embedding / lm_head ("The Inference
+ * Stack Behind OCRia", quantization section: the weights that are streamed
+ * on every decode step ship as FP8, mixed with other precisions per layer).
+ * Validates the model and cache description, copies the pointer tables,
+ * repacks the weights into library-owned memory (see the weight layout
+ * above), and allocates the library workspace (activations for max_batch*16
+ * rows, split attention partials, argmax partials, a RoPE cos/sin table for
+ * positions < max_ctx, the device error word).  Supported: head_dim 64 or
+ * 128, hidden and intermediate multiples of 64 with hidden <= 4096, vocab a
+ * multiple of 64, Hq % Hkv == 0 with Hq / Hkv <= 8.  Errors: SPEC_E_ARG
+ * (NULL or misaligned pointer), SPEC_E_SHAPE, SPEC_E_UNSUPPORTED (weight or
+ * activation format), SPEC_E_NOMEM, SPEC_E_HIP.  Synchronous (allocations,
+ * the repack and one table upload on `stream`).  *out is set only on
+ * success. */
 int spec_verify_init(const spec_model_desc *model /*host*/, const spec_weights *w /*host*/,
                      const spec_kv *kv /*host*/, hipStream_t stream, spec_ctx **out /*host*/);
 
@@ -232,11 +236,17 @@ int spec_verify_block(spec_ctx *ctx, int32_t batch, const int32_t *tokens, int32
 #define SPEC_MAX_LANES 4
 int spec_verify_set_lanes(spec_ctx *ctx, int32_t lanes);
 
-/* Commit: kv_len[b] += n_commit[b] for b < batch, or += the tau of the last
- * verify when n_commit is NULL (the K/V rows are already in place; this is a
- * length bump, so a rejected suffix is rolled back by not counting it).
- * Counts must lie in [0, 16] and keep kv_len <= max_ctx, else that sequence
- * is left unchanged and SPEC_DERR_COMMIT is set.  Asynchronous. */
+/* Commit the accepted rows ("HunyuanOCR-1.5 / DFlash" write-up, inference
+ * loop, steps 4-5: keep the accepted prefix and continue from the bonus;
+ * "The Inference Stack Behind OCRia", verification section: a rejected
+ * suffix is dropped by moving a pointer back, not by copying state):
+ * kv_len[b] += n_commit[b] for b < batch, or += the tau of the last verify
+ * when n_commit is NULL (int32 [batch], device).  The K/V rows are already in
+ * place, so this is a length bump and rejected rows are rolled back by not
+ * counting them.  Counts must lie in [0, 16] and keep kv_len <= max_ctx,
+ * else that sequence is left unchanged and SPEC_DERR_COMMIT is set.
+ * SPEC_E_ARG for a NULL context or batch outside [1, max_batch].
+ * Asynchronous. */
 int spec_commit_kv(spec_ctx *ctx, int32_t batch, const int32_t *n_commit, hipStream_t stream);
 
 /* Chunked prefill through the verify pass ("HunyuanOCR-1.5 / DFlash"
@@ -276,6 +286,12 @@ int spec_get_device_error(spec_ctx *ctx, int32_t *code /*host*/, hipStream_t str
 /* Static description of a spec_status value. */
 const char *spec_status_str(int status);
 
+/* The latest failure reported by a call on this thread: the call, the step
+ * or runtime function that failed and, for SPEC_E_HIP, the HIP error name and
+ * code; "" when no call has failed.  Valid until the thread's next failing
+ * call. */
+const char *spec_last_error(void);
+
 /* Test hook: when hidden/logits are non-NULL, later verify passes also write
  * the final normed hidden state (fp32 [batch*16][H], the BF16 values fed to
  * the lm_head) and the logits (fp32 [batch*16][V]).  NULL disables. */
@@ -284,9 +300,9 @@ int spec_debug_set_dump(spec_ctx *ctx, float *hidden, float *logits);
 /* Test hook: one weight-streaming linear on its own,
  *   y[m][n] = sum_k x[m][k] * w(n, k)     (fp32 out, [M][N])
  * x: FP16 bits [M][K] for FP8 / MXFP4 weights, BF16 bits for BF16 weights;
- * w tile-major in format `wfmt` with scales as in spec_layer_weights (scales
- * NULL for BF16).  K and N multiples of 64.
- * Synchronous. */
+ * w row-major in format `wfmt` with scales as in spec_layer_weights (scales
+ * NULL for BF16).  K and N multiples of 64.  Allocates a packed copy of w;
+ * synchronous. */
 int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const void *w,
                       const void *scales, int32_t wfmt, float *y, hipStream_t stream);
 
@@ -305,8 +321,9 @@ int spec_debug_rmsnorm(int32_t M, int32_t H, const float *h, const float *gain, 
                        void *x, uint8_t *xs, hipStream_t stream);
 
 /* Test hook: the gate/up projection with its SiLU-and-multiply epilogue on
- * its own: a = SiLU(x Wg^T) * (x Wu^T), w = [gate rows; up rows] [2I][H] in
- * FP8_E4M3_ROW or MXFP4 with scales as in spec_layer_weights.  Input x: FP16
+ * its own: a = SiLU(x Wg^T) * (x Wu^T), w = [gate rows; up rows] [2I][H]
+ * row-major in FP8_E4M3_ROW or MXFP4 with scales as in spec_layer_weights
+ * (a packed copy is allocated).  Input x: FP16
  * bits [M][H] (x_scales NULL) or MXFP8 codes [M][H] + e8m0 [M][H/32].  Output
  * a: FP16 bits [M][I] (out_fmt SPEC_ACT_FP16, a_scales unused) or MXFP8 codes
  * [M][I] + e8m0 [M][I/32] (SPEC_ACT_MXFP8).  H, I multiples of 64.
@@ -316,8 +333,23 @@ int spec_debug_swiglu(int32_t M, int32_t H, int32_t I, const void *x, const uint
                       hipStream_t stream);
 
 /* Test hook: spec_debug_linear with MXFP8 activations (codes [M][K], e8m0
- * [M][K/32]) and FP8_E4M3_ROW or MXFP4 weights (BF16 weights are rejected
- * with SPEC_E_UNSUPPORTED).  Synchronous. */
+ * [M][K/32]) and row-major FP8_E4M3_ROW or MXFP4 weights (BF16 weights are
+ * rejected with SPEC_E_UNSUPPORTED).  Synchronous. */
+
+/* Test hook: one residual projection with the next RMSNorm folded in, as the
+ * pass runs its O and down projections:
+ *   h_out = h_in + x W^T                      (fp32 [M][N])
+ *   xg    = h_out * gain                      (FP16 bits [M][N], or BF16 bits
+ *                                              with xg_bf16 = 1)
+ *   ssp[m][j] = sum of h_out[m][n]^2 over n in [32j, 32j+32), j < N/32
+ *                                             (fp32 [M][ld], ld = N/32
+ *                                              rounded up to a multiple of 4;
+ *                                              the last entries untouched)
+ * x FP16 bits [M][K]; w row-major FP8_E4M3_ROW or MXFP4 [N][K] with scales;
+ * gain fp32 [N]; N, K multiples of 64; all 16-byte aligned.  Synchronous. */
+int spec_debug_residual(int32_t M, int32_t N, int32_t K, const uint16_t *x, const void *w, const void *scales,
+                        int32_t wfmt, const float *h_in, const float *gain, int32_t xg_bf16, float *h_out,
+                        uint16_t *xg, float *ssp, hipStream_t stream);
 int spec_debug_linear_mx8(int32_t M, int32_t N, int32_t K, const uint8_t *x_codes, const uint8_t *x_scales,
                           const void *w, const void *scales, int32_t wfmt, float *y, hipStream_t stream);
 

@@ -85,9 +85,11 @@ def test_host_side_argument_checks():
     # debug entry points validate before launching
     assert lib.spec_debug_linear(16, 100, 64, 16, 16, 16, 1, 16, None) == -1  # N % 64
     assert lib.spec_debug_quant_mx8(4, 48, 16, 16, 16, None) == -1              # K % 32
-    assert lib.spec_pack_weights(1, 48, 64, 16, None, 16, None, None) == -1      # rows % 32
-    assert lib.spec_pack_weights(2, 64, 64, 16, None, 16, None, None) == -1      # MXFP4 without scales
-    assert lib.spec_pack_weights(4, 64, 64, 16, None, 16, None, None) == -3      # unknown format
+    assert lib.spec_debug_linear(16, 64, 64, 16, 16, None, 1, 16, None) == -1   # FP8 without scales
+    assert b"scales" in lib.spec_last_error()                                   # the failure is described
+    assert lib.spec_debug_residual(16, 96, 64, 16, 16, 16, 1, 16, 16, 0, 32, 16, 16, None) == -1  # N % 64
+    assert lib.spec_debug_residual(16, 64, 64, 16, 16, 16, 3, 16, 16, 0, 32, 16, 16, None) == -3  # BF16 weights
+    assert lib.spec_debug_residual(16, 64, 64, 16, 16, 16, 1, 16, 16, 0, 16, 16, 16, None) == -1  # h_in == h_out
     assert lib.spec_debug_quant_mx8(4, 64, 16, 24, 16, None) == -1              # codes not 16-byte aligned
     assert lib.spec_debug_linear_mx8(16, 64, 96, 16, 16, 16, 16, 1, 16, None) == -1   # K % 64
     assert lib.spec_debug_linear_mx8(16, 64, 64, 16, 16, 16, None, 2, 16, None) == -1  # MXFP4 without scales

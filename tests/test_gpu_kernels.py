@@ -9,7 +9,7 @@ import oracle
 from oracle.codecs import decode_bf16, decode_e4m3, dequant_fp8_rows, dequant_mxfp4
 import workload as W
 from block_draft_verification_amd import (WFMT_BF16, WFMT_FP8_E4M3_ROW, WFMT_MXFP4, debug_attention, debug_linear,
-                                          debug_rmsnorm, debug_swiglu, pack_weights)
+                                          debug_residual, debug_rmsnorm, debug_swiglu)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,43 +39,9 @@ def _dev(a):
 
 
 def _packed(w, s, wfmt, rows, cols):
-    """Row-major weights -> the tile-major device layout, through the library."""
-    return pack_weights(_dev(w), None if s is None else _dev(s), wfmt, rows, cols)
-
-
-def _pack_ref(w, wfmt, rows, cols):
-    """The tile-major layout of include/spec_verify.h written as an index
-    permutation: tiles (rt, kt) in row-tile-major order; inside a tile, chunk j
-    of lane 32h + c at chunk slot j*64 + 32h + c."""
-    RT, KT = rows // 32, cols // 64
-    if wfmt == WFMT_FP8_E4M3_ROW:      # row c, columns 16h + 32j + b
-        return w.reshape(RT, 32, KT, 2, 2, 16).transpose(0, 2, 3, 4, 1, 5).reshape(-1)
-    if wfmt == WFMT_BF16:              # row c, columns 32h + 8j + e
-        return w.reshape(RT, 32, KT, 2, 4, 8).transpose(0, 2, 4, 3, 1, 5).reshape(-1)
-    return w.reshape(RT, 32, KT, 2, 16).transpose(0, 2, 3, 1, 4).reshape(-1)  # MXFP4 nibble pairs
-
-
-def _pack_scales_ref(e8, rows, cols):
-    return e8.reshape(rows // 32, 32, cols // 64, 2).transpose(0, 2, 3, 1).reshape(-1)
-
-
-@pytest.mark.parametrize("wfmt,rows,cols", [(WFMT_FP8_E4M3_ROW, 96, 192), (WFMT_BF16, 64, 128),
-                                            (WFMT_MXFP4, 64, 320), (WFMT_FP8_E4M3_ROW, 1152, 896)])
-def test_pack_weights_layout(wfmt, rows, cols):
-    """spec_pack_weights against the header's definition, bit for bit."""
-    rng = np.random.default_rng(rows + cols)
-    if wfmt == WFMT_BF16:
-        w = rng.integers(0, 1 << 16, size=(rows, cols)).astype(np.uint16)
-    else:
-        w = rng.integers(0, 256, size=(rows, cols // 2 if wfmt == WFMT_MXFP4 else cols)).astype(np.uint8)
-    e8 = rng.integers(0, 256, size=(rows, cols // 32)).astype(np.uint8) if wfmt == WFMT_MXFP4 else None
-    wp, sp = _packed(w, e8, wfmt, rows, cols)
-    got = wp.cpu().numpy().reshape(-1)
-    if wfmt == WFMT_BF16:
-        got = got.view(np.uint16)
-    assert np.array_equal(got, _pack_ref(w, wfmt, rows, cols))
-    if e8 is not None:
-        assert np.array_equal(sp.cpu().numpy().reshape(-1), _pack_scales_ref(e8, rows, cols))
+    """Row-major weights on the device, as the library's hooks take them (each
+    hook packs its own copy)."""
+    return _dev(w), None if s is None else _dev(s)
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 1152, 896), (40, 896, 4864), (512, 9728, 896), (1, 64, 64)])
@@ -236,3 +202,47 @@ def test_attention(Hq, Hkv, D, lens, split, pad):
     # the same call twice gives the same bits (fixed-order split merge)
     o2 = debug_attention(_dev(q), _dev(K), _dev(V), ln, B, Hq, Hkv, D, split).cpu().numpy()
     assert np.array_equal(o, o2)
+
+
+@pytest.mark.parametrize("wfmt,M,N,K,bf16", [(WFMT_FP8_E4M3_ROW, 16, 896, 4864, False),
+                                             (WFMT_FP8_E4M3_ROW, 40, 896, 896, False),
+                                             (WFMT_MXFP4, 512, 896, 4864, False),
+                                             (WFMT_FP8_E4M3_ROW, 512, 896, 896, True),
+                                             (WFMT_FP8_E4M3_ROW, 37, 4096, 128, False)])
+def test_residual_with_folded_norm(wfmt, M, N, K, bf16):
+    """The residual projection as the pass runs O and down: h_out = h_in + x W^T
+    within the fp32 accumulation bound; xg = h_out * g rounded once (FP16 or
+    BF16) from the GPU's own h_out; ssp[m][j] = sum of h_out^2 over columns
+    32j .. 32j+31, to fp32 summation accuracy.  The shapes cover the
+    workgroup layouts a launch chooses by its row count (one to four k groups,
+    32- and 64-row activation tiles) and a ragged row count."""
+    rng = np.random.default_rng(M + N + K)
+    if wfmt == WFMT_FP8_E4M3_ROW:
+        w = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
+        w[(w & 0x7F) == 0x7F] = 0x3F
+        ws = (rng.random(N) * 2e-3 + 1e-3).astype(np.float32)
+        wd = dequant_fp8_rows(w, ws)
+    else:
+        w = rng.integers(0, 256, size=(N, K // 2)).astype(np.uint8)
+        ws = rng.integers(118, 124, size=(N, K // 32)).astype(np.uint8)
+        wd = dequant_mxfp4(w, ws)
+    xb = _x(M, K, 17)
+    h_in = rng.standard_normal((M, N)).astype(np.float32)
+    g = (1 + 0.3 * rng.standard_normal(N)).astype(np.float32)
+    h_out, xg, ssp = debug_residual(_dev(xb), _dev(w), _dev(ws), wfmt, torch.from_numpy(h_in).cuda(),
+                                    torch.from_numpy(g).cuda(), xg_bf16=bf16)
+    h_out, xg, ssp = h_out.cpu().numpy(), xg.cpu().numpy(), ssp.cpu().numpy()
+    x = _dec(xb)
+    ref = h_in.astype(np.float64) + x @ wd.T
+    bound = 3e-5 * (np.abs(x) @ np.abs(wd).T) + 2.0 ** -23 * np.abs(ref)
+    assert np.all(np.abs(h_out - ref) <= bound), f"h_out: max excess {np.max(np.abs(h_out - ref) - bound):.3g}"
+    hg = h_out.astype(np.float64) * g
+    if bf16:
+        got = decode_bf16(xg.view(np.uint16))
+        assert np.all(np.abs(got - hg) <= 2.0 ** -8 * np.abs(hg) + 1e-38), "xg (BF16: 8 significant bits)"
+    else:
+        got = xg.view(np.float16).astype(np.float64)
+        assert np.all(np.abs(got - hg) <= 2.0 ** -11 * np.abs(hg) + 2.0 ** -25), "xg (FP16)"
+    ss_ref = (h_out.astype(np.float64) ** 2).reshape(M, N // 32, 32).sum(-1)
+    assert np.allclose(ssp[:, :N // 32], ss_ref, rtol=1e-5, atol=0), "partial sums of squares"
+    assert np.all(np.isnan(ssp[:, N // 32:])), "entries past the real ones must stay untouched"

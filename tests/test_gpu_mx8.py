@@ -50,7 +50,7 @@ import oracle
 import workload as W
 from oracle.codecs import decode_e4m3, dequant_fp8_rows, dequant_mxfp4, mxfp8_quantize, round_e4m3
 from block_draft_verification_amd import (WFMT_FP8_E4M3_ROW, WFMT_MXFP4, DeviceModel, Verifier,
-                                          debug_linear_mx8, debug_quant_mx8, debug_rmsnorm, debug_swiglu, pack_weights)
+                                          debug_linear_mx8, debug_quant_mx8, debug_rmsnorm, debug_swiglu)
 from block_draft_verification_amd.decode import ar_decode, planted_drafts, spec_decode
 from gpu_cases import MARGIN, REL_TOL, build_case, gpu_verify, log, oracle_verify, row_rel
 
@@ -130,7 +130,7 @@ def test_linear_mx8_fp8_weights(M, N, K):
     s = (rng.random(N) * 1e-3 + 1e-4).astype(np.float32)
     c, e, xq = _mx_activations(M, K, seed=M + K)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    y = debug_linear_mx8(t(c), t(e), *pack_weights(t(w), t(s), WFMT_FP8_E4M3_ROW, N, K), WFMT_FP8_E4M3_ROW,
+    y = debug_linear_mx8(t(c), t(e), t(w), t(s), WFMT_FP8_E4M3_ROW,
                          N).cpu().numpy()
     _check(xq, dequant_fp8_rows(w, s), y)
 
@@ -142,7 +142,7 @@ def test_linear_mx8_mxfp4_weights(M, N, K):
     we = rng.integers(110, 135, size=(N, K // 32)).astype(np.uint8)
     c, e, xq = _mx_activations(M, K, seed=M + 2 * K)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    y = debug_linear_mx8(t(c), t(e), *pack_weights(t(w), t(we), WFMT_MXFP4, N, K), WFMT_MXFP4, N).cpu().numpy()
+    y = debug_linear_mx8(t(c), t(e), t(w), t(we), WFMT_MXFP4, N).cpu().numpy()
     _check(xq, dequant_mxfp4(w, we), y)
 
 
@@ -219,7 +219,7 @@ def test_swiglu_mx8_decisions(wfmt, M, H, I):
     bg, bu = MX_ACC_TOL * (np.abs(xq) @ np.abs(wd[:I]).T), MX_ACC_TOL * (np.abs(xq) @ np.abs(wd[I:]).T)
     window = 1.1 * np.abs(up) * bg + np.abs(oracle.silu(gate)) * bu + bg * bu + 2.0 ** -20 * np.abs(a_ref) + 1e-30
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-    codes, scales = debug_swiglu(t(c), t(e), *pack_weights(t(w), t(ws), wfmt, 2 * I, H), wfmt, I, out_fmt="mxfp8")
+    codes, scales = debug_swiglu(t(c), t(e), t(w), t(ws), wfmt, I, out_fmt="mxfp8")
     n_code, n_exp = _decisions_explained(a_ref, codes.cpu().numpy(), scales.cpu().numpy(), window)
     log(f"swiglu mx8 {M}x{H}x{I}: {n_code} codes and {n_exp} exponents at a rounding boundary")
 
