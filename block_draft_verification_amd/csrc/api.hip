@@ -68,6 +68,16 @@ struct spec_ctx {
 
 static const size_t kMaxTimedLaunches = 8192;
 
+// 1: the down projection (K = intermediate, the long one) splits K across
+// workgroups and a small step adds the partials (launch_fold); 0 (the
+// default) runs it as one residual launch like the O projection, its K split
+// between the waves of each workgroup instead: measured over whole passes at
+// 512 rows, one launch is faster than the split launch plus the fold.
+#ifndef SPEC_DOWN_SPLIT
+#define SPEC_DOWN_SPLIT 0
+#endif
+static constexpr bool kDownSplit = SPEC_DOWN_SPLIT != 0;
+
 // The latest failure of a call on this thread (spec_last_error).
 static thread_local char g_last_error[320] = "";
 
@@ -248,12 +258,12 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
     units = std::max(units, attention_grid(b, Hkv, kv->max_ctx, D, 0, c->attn_cus));
   c->part_units = units;
   size_t rfloats = 0;
-  if (m->act_fmt == SPEC_ACT_MXFP8)
-    for (int b = 1; b <= kv->max_batch; ++b) {
-      const int M = b * 16;
-      const int s = std::max(residual_nsplit(M, H, Hq * D), residual_nsplit(M, H, I));
-      rfloats = std::max(rfloats, (size_t)s * M * H);
-    }
+  for (int b = 1; b <= kv->max_batch; ++b) {
+    const int M = b * 16;
+    int s = kDownSplit ? residual_nsplit(M, H, I) : 0;
+    if (m->act_fmt == SPEC_ACT_MXFP8) s = std::max(residual_nsplit(M, H, Hq * D), residual_nsplit(M, H, I));
+    rfloats = std::max(rfloats, (size_t)s * M * H);
+  }
 
   const size_t Mm = c->Mmax;
   size_t sizes[] = {2 * Mm * H * 4,                  // h, h2
@@ -345,10 +355,11 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
 // every row-indexed one to row 16*b0, so the kernels see sequences 0..batch-1.
 //
 // FP16 activations (the default): every RMSNorm is folded into its
-// neighbours.  The step that updates the residual stream (embed, then each
-// O and down projection) writes h, the next RMSNorm's input h * g and the
-// per-32-column sums of h^2; the GEMM that follows (QKV, gate/up, lm_head)
-// normalises its outputs by 1/sqrt(mean(h^2) + eps).  Six launches per layer.
+// neighbours.  The step that updates the residual stream (embed, each O
+// projection, and the fold step after each down projection's K splits)
+// writes h, the next RMSNorm's input h * g and the per-32-column sums of h^2;
+// the GEMM that follows (QKV, gate/up, lm_head) normalises its outputs by
+// 1/sqrt(mean(h^2) + eps).  Seven launches per layer.
 // MXFP8 activations: the RMSNorm steps quantise their output, so they stay
 // kernels of their own, and the residual projections split K into partials
 // that the next RMSNorm adds (eight launches per layer).
@@ -397,7 +408,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
       CK(launch_embed(tokens, M, H, V, c->embed, h, mx ? nullptr : c->layers[0].attn_norm, mx ? nullptr : x,
                       ssp, ld, kv_len, max_ctx, kvl, c->err, plan, st));
   }
-  const int ns_o = mx ? residual_nsplit(M, H, Hq * D) : 0, ns_d = mx ? residual_nsplit(M, H, I) : 0;
+  const int ns_o = mx ? residual_nsplit(M, H, Hq * D) : 0, ns_d = mx || kDownSplit ? residual_nsplit(M, H, I) : 0;
   const ActIn xin = mx ? ActIn{x8, xs8} : ActIn{x, nullptr};
   const ActIn ain = mx ? ActIn{a8, as8} : ActIn{act, nullptr};
   // MXFP8 mode: each RMSNorm step reads the residual stream from one buffer
@@ -444,7 +455,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
       Timed t(c, SPEC_K_OPROJ, st);
       for (int r = 0; r < t.reps; ++r) {
         if (mx) CK(launch_residual_partial(ActIn{ao, nullptr}, M, H, Hq * D, L.o, rpart, st));
-        else CK(launch_residual(ActIn{ao, nullptr}, M, H, Hq * D, L.o,
+        else CK(launch_residual(kGemmOproj, ActIn{ao, nullptr}, M, H, Hq * D, L.o,
                                 ResidualOut{h, h2, L.mlp_norm, x, 0, ssp, ld, c->err}, st));
       }
     }
@@ -457,15 +468,21 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
       for (int r = 0; r < t.reps; ++r)
         CK(launch_swiglu(xin, M, H, I, L.gate_up, mx ? (void *)a8 : act, mx ? as8 : nullptr, nr, st));
     }
+    const bool last = l + 1 == m.n_layers;
+    const float *next_gain = last ? c->final_norm : c->layers[l + 1].attn_norm;
     {
       Timed t(c, SPEC_K_DOWN, st);
-      const bool last = l + 1 == m.n_layers;
       for (int r = 0; r < t.reps; ++r) {
-        if (mx) CK(launch_residual_partial(ain, M, H, I, L.down, rpart, st));
-        else CK(launch_residual(ain, M, H, I, L.down,
-                                ResidualOut{h2, h, last ? c->final_norm : c->layers[l + 1].attn_norm, x, last ? 1 : 0,
-                                            ssp, ld, c->err}, st));
+        if (mx || kDownSplit) CK(launch_residual_partial(ain, M, H, I, L.down, rpart, st));
+        else CK(launch_residual(kGemmDown, ain, M, H, I, L.down,
+                                ResidualOut{h2, h, next_gain, x, last ? 1 : 0, ssp, ld, c->err},
+                                st));
       }
+    }
+    if (!mx && kDownSplit) {  // the down projection's K splits added to h, the next RMSNorm's input prepared
+      Timed t(c, SPEC_K_RMSNORM, st);
+      for (int r = 0; r < t.reps; ++r)
+        CK(launch_fold(h2, h, rpart, ns_d, next_gain, M, H, x, last ? 1 : 0, ssp, ld, c->err, st));
     }
     pending = ns_d;
   }
@@ -476,7 +493,10 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
   }
   {
     Timed t(c, SPEC_K_LM_HEAD, st);
-    for (int r = 0; r < t.reps; ++r) CK(launch_lm_argmax(x, M, V, H, c->lm_table, amax, dump_logits, nr, st));
+    // the argmax does not need the final RMSNorm's (positive, per-row) scale;
+    // only dumped logits are normalised
+    for (int r = 0; r < t.reps; ++r)
+      CK(launch_lm_argmax(x, M, V, H, c->lm_table, amax, dump_logits, dump_logits ? nr : NormRows{}, st));
   }
   if (dump_hidden && !mx) CK(launch_final_hidden(x, ssp, ld, H, m.rms_eps, M, nullptr, dump_hidden, nullptr, st));
   {
@@ -704,7 +724,7 @@ int spec_debug_residual(int32_t M, int32_t N, int32_t K, const uint16_t *x, cons
     return fail(SPEC_E_ARG, fn, "alignment or aliasing");
   TempPacked p;
   CK(p.make(wfmt, N, K, w, scales, kRowsPlain, 0, st));
-  CK(launch_residual(ActIn{x, nullptr}, M, N, K, p.w,
+  CK(launch_residual(K > 1024 ? kGemmDown : kGemmOproj, ActIn{x, nullptr}, M, N, K, p.w,
                      ResidualOut{h_in, h_out, gain, xg, xg_bf16 ? 1 : 0, ssp, ssp_ld(N), nullptr}, st));
   CK(hipStreamSynchronize(st));
   return SPEC_OK;

@@ -76,12 +76,12 @@ template <int FMT> constexpr int w_loads() { return FMT == SPEC_WFMT_BF16 ? 4 : 
 // registers of one tile's raw weights for one step
 template <int FMT> constexpr int w_regs() { return FMT == SPEC_WFMT_BF16 ? 16 : FMT == SPEC_WFMT_MXFP4 ? 5 : 8; }
 
-// Pipeline depth in stages: the tile height's depth (two when a stage holds
-// several k steps), capped so that the register ring (depth + 1 sets of
-// weights and activation exponents) stays within 112 VGPRs.
-template <int FMT, int NT, int MT, bool A8, int KS>
+// Pipeline depth in stages: `depth` when given, else the tile height's depth
+// (two when a stage holds several k steps), capped so that the register ring
+// (depth + 1 sets of weights and activation exponents) stays within 112 VGPRs.
+template <int FMT, int NT, int MT, bool A8, int KS, int DEPTH>
 constexpr int gemm_depth() {
-  const int want = KS > 1 ? 2 : MT == 1 ? GEMM_DEPTH_MT1 : MT == 2 ? GEMM_DEPTH_MT2 : GEMM_DEPTH_MT4;
+  const int want = DEPTH > 0 ? DEPTH : KS > 1 ? 2 : MT == 1 ? GEMM_DEPTH_MT1 : MT == 2 ? GEMM_DEPTH_MT2 : GEMM_DEPTH_MT4;
   const int cap = 112 / (NT * w_regs<FMT>() + (A8 ? MT : 0)) - 1;
   const int d = want < cap ? want : cap;
   return d < 2 ? 2 : d;
@@ -228,35 +228,53 @@ template <int FMT, int NT, int MT> struct GemmOcc {
 };
 
 // Lane (c, h) of wave w reads the partial sums of squares of block row
-// m0 + 32mt + c in 16-byte chunks j = 2w + h + 2*NWV*i, i < kNormLoads.
-constexpr int kNormLoads = 4;
+// m0 + 32mt + c in 16-byte chunks j = 2w + h + 2*NWV*i, i < NRL (a kernel
+// parameter: 0 when the input rows are not h * g, 1 for rows up to 1024
+// wide with four waves, 4 for rows up to 4096).
+inline int norm_loads(const NormRows &nr, int nwv) {
+  if (!nr.ssp) return 0;
+  const int nl = (nr.ld / 4 + 2 * nwv - 1) / (2 * nwv);
+  return nl <= 1 ? 1 : nl <= 4 ? 4 : -1;
+}
 
 // A8: activations are MXFP8 (e4m3 codes + e8m0 per 32) and the MFMA is the
 // scaled 32x32x64 FP8/FP4 one: one MFMA per tile pair and k step, FP8 weights
 // enter raw (their per-row scale stays in the epilogue) and MXFP4 weights with
 // their own e8m0 scales.
-template <bool F16, int FMT, int NT, int MT, class Epi, bool A8, int NWV, int KS>
+// Compile-time shape of one gemm_kernel instantiation, shared with the host
+// (which sizes the launch's LDS from it).
+template <int FMT, int NT, int MT, class Epi, bool A8, int NWV, int KS, int DEPTH>
+struct GemmCfg {
+  static constexpr int NG = NWV / KS;              // waves side by side along N
+  static constexpr int ROWS = 32 * MT;             // activation rows per workgroup
+  static constexpr int SUB = ROWS * 64;            // 16-bit elements of one k step's activation tile
+  // LDS-DMA instructions per wave per stage: KS * ROWS * 8 (16-bit) or ROWS * 4 (FP8) chunks of 16 bytes
+  static constexpr int AJ = A8 ? (MT + 1) / 2 : 4 * MT * KS / NWV;
+  static constexpr int SE = A8 ? AJ * 2048 : SUB * KS;  // 16-bit elements per stage
+  static constexpr int DIST = gemm_depth<FMT, NT, MT, A8, KS, DEPTH>();  // stages loaded ahead of the one computed
+  static constexpr int NS = DIST + 1;              // LDS stages = weight register sets
+  // staged epilogue: per wave a [32][LD] fp32 tile of block rows x output columns
+  static constexpr int COLS = Epi::template cols<NT>(), LD = COLS + 4;
+  static constexpr int STAGE_BYTES = Epi::kStaged ? NG * 32 * LD * 4 : 0;
+  // after the main loop: the k groups' accumulators, then the lanes' partial
+  // sums of squares of the input rows
+  static constexpr int RED_BYTES = (KS - 1) * NG * NT * MT * 4096;
+  static constexpr int RSUM_BYTES = MT * 2 * NWV * 32 * 4;
+  static constexpr int A_BYTES = NS * SE * 2 > STAGE_BYTES ? NS * SE * 2 : STAGE_BYTES;
+  static constexpr int LDS_BYTES = A_BYTES > RED_BYTES + RSUM_BYTES ? A_BYTES : RED_BYTES + RSUM_BYTES;
+};
+
+template <bool F16, int FMT, int NT, int MT, class Epi, bool A8, int NWV, int KS, int DEPTH, int NRL>
 __global__ __launch_bounds__(64 * NWV) __attribute__((amdgpu_waves_per_eu(GemmOcc<FMT, NT, MT>::value, 8))) void
 gemm_kernel(GemmArgs ga, Epi epi) {
   static_assert(!A8 || FMT != SPEC_WFMT_BF16, "A8 takes FP8 or MXFP4 weights");
   static_assert(NWV % KS == 0 && (!A8 || KS == 1), "k groups divide the waves; A8 runs one k group");
-  constexpr int NG = NWV / KS;              // waves side by side along N
-  constexpr int ROWS = 32 * MT;             // activation rows per workgroup
-  constexpr int SUB = ROWS * 64;            // 16-bit elements of one k step's activation tile
-  // LDS-DMA instructions per wave per stage: KS * ROWS * 8 (16-bit) or ROWS * 4 (FP8) chunks of 16 bytes
-  constexpr int AJ = A8 ? (MT + 1) / 2 : 4 * MT * KS / NWV;
+  using C = GemmCfg<FMT, NT, MT, Epi, A8, NWV, KS, DEPTH>;
+  constexpr int NG = C::NG, ROWS = C::ROWS, SUB = C::SUB, AJ = C::AJ, SE = C::SE, DIST = C::DIST, NS = C::NS;
+  constexpr int COLS = C::COLS, LD = C::LD;
   static_assert(A8 || (AJ >= 1 && (4 * MT * KS) % NWV == 0), "a stage's activation chunks fill whole waves");
-  constexpr int SE = A8 ? AJ * 2048 : SUB * KS;  // 16-bit elements per stage
-  constexpr int DIST = gemm_depth<FMT, NT, MT, A8, KS>();  // stages loaded ahead of the one computed
-  constexpr int NS = DIST + 1;              // LDS stages = weight register sets
-  // staged epilogue: per wave a [32][LD] fp32 tile of block rows x output columns
-  constexpr int COLS = Epi::template cols<NT>(), LD = COLS + 4;
-  constexpr int STAGE_BYTES = Epi::kStaged ? NG * 32 * LD * 4 : 0;
-  constexpr int RED_BYTES = (KS - 1) * NG * NT * MT * 4096;  // k groups' accumulators
-  constexpr int LDS_A = NS * SE * 2 > STAGE_BYTES ? NS * SE * 2 : STAGE_BYTES;
-  constexpr int LDS_BYTES = LDS_A > RED_BYTES ? LDS_A : RED_BYTES;
-  __shared__ __align__(16) uint16_t As[LDS_BYTES / 2];
-  __shared__ float rsum[MT][2 * NWV][32];  // per-lane partial sums of squares of the input rows
+  extern __shared__ __align__(16) uint16_t gemm_lds[];  // C::LDS_BYTES
+  uint16_t *const As = gemm_lds;
 
   pin_args(ga, epi);
   int nblk, mblk;
@@ -320,17 +338,18 @@ gemm_kernel(GemmArgs ga, Epi epi) {
 
   // Partial sums of squares of the input rows (when the input is h * g),
   // loaded like the epilogue inputs below and added up after the main loop.
-  const bool norm = ga.nr.ssp != nullptr;
-  f32x4_t nrr[MT][kNormLoads];
-  const int nch = ga.nr.ld / 4, nnl = (nch + 2 * NWV - 1) / (2 * NWV);  // chunks per row, loads per lane
+  constexpr bool norm = NRL > 0;
+  constexpr int NRA = NRL > 0 ? NRL : 1;
+  f32x4_t nrr[MT][NRA];
+  const int nch = ga.nr.ld / 4;  // 16-byte chunks per row
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = min(m0 + 32 * mt + c, M - 1);
 #pragma unroll
-    for (int i = 0; i < kNormLoads; ++i) {
+    for (int i = 0; i < NRA; ++i) {
       const int j = 2 * wave + h + 2 * NWV * i;
       nrr[mt][i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (norm && i < nnl && j < nch) nrr[mt][i] = *reinterpret_cast<const f32x4_t *>(ga.nr.ssp + (size_t)m * ga.nr.ld + 4 * j);
+      if (norm && j < nch) nrr[mt][i] = *reinterpret_cast<const f32x4_t *>(ga.nr.ssp + (size_t)m * ga.nr.ld + 4 * j);
     }
   }
 
@@ -458,12 +477,16 @@ gemm_kernel(GemmArgs ga, Epi epi) {
       for (int mt = 0; mt < MT; ++mt) asm volatile("" ::"v"(scr[i][mt]));
     }
   }
-  if constexpr (KS > 1) {
-    // k groups 1.. hand their accumulators to group 0 through LDS, which adds
-    // them in group order (the result does not depend on timing)
+  // After the main loop the stage memory holds the k groups' accumulators
+  // (groups 1.. hand theirs to group 0, which adds them in group order, so
+  // the result does not depend on timing) and each lane's partial sum of
+  // squares of its input row (each lane's chunks summed in order).
+  float rs[MT];
+  if (KS > 1 || norm) {
     float *red = reinterpret_cast<float *>(As);
+    float *rsum = red + C::RED_BYTES / 4;  // [MT][2 NWV][32]
     lds_barrier();  // every wave is done reading the activation stages
-    if (kg > 0) {
+    if (KS > 1 && kg > 0) {
 #pragma unroll
       for (int t = 0; t < NT; ++t)
 #pragma unroll
@@ -472,8 +495,17 @@ gemm_kernel(GemmArgs ga, Epi epi) {
           for (int v = 0; v < 16; ++v)
             red[((((kg - 1) * NG + ng) * NT + t) * MT + mt) * 1024 + v * 64 + lane] = acc[t][mt][v];
     }
+    if (norm) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) {
+        float ps = 0.f;
+#pragma unroll
+        for (int i = 0; i < NRA; ++i) ps += (nrr[mt][i][0] + nrr[mt][i][1]) + (nrr[mt][i][2] + nrr[mt][i][3]);
+        rsum[(mt * 2 * NWV + 2 * wave + h) * 32 + c] = ps;
+      }
+    }
     lds_barrier();
-    if (kg == 0) {
+    if (KS > 1 && kg == 0) {
 #pragma unroll
       for (int g = 1; g < KS; ++g)
 #pragma unroll
@@ -483,29 +515,21 @@ gemm_kernel(GemmArgs ga, Epi epi) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[t][mt][v] += red[((((g - 1) * NG + ng) * NT + t) * MT + mt) * 1024 + v * 64 + lane];
     }
-  }
-  // per-row normalisation of the input: r = 1 / sqrt(sum / H + eps), each
-  // lane's chunks summed in order, then the lanes' sums in a fixed order
-  float rs[MT];
-  if (norm) {
+    // per-row normalisation of the input: r = 1 / sqrt(sum / H + eps), the
+    // lanes' sums added in a fixed order
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
-      float ps = 0.f;
+      rs[mt] = 1.f;
+      if (norm) {
+        float ss = 0.f;
 #pragma unroll
-      for (int i = 0; i < kNormLoads; ++i) ps += (nrr[mt][i][0] + nrr[mt][i][1]) + (nrr[mt][i][2] + nrr[mt][i][3]);
-      rsum[mt][2 * wave + h][c] = ps;
+        for (int q = 0; q < 2 * NWV; ++q) ss += rsum[(mt * 2 * NWV + q) * 32 + c];
+        rs[mt] = 1.0f / sqrtf(ss / (float)ga.nr.H + ga.nr.eps);
+      }
     }
-    lds_barrier();
-  }
+  } else {
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    rs[mt] = 1.f;
-    if (norm) {
-      float ss = 0.f;
-#pragma unroll
-      for (int q = 0; q < 2 * NWV; ++q) ss += rsum[mt][q][c];
-      rs[mt] = 1.0f / sqrtf(ss / (float)ga.nr.H + ga.nr.eps);
-    }
+    for (int mt = 0; mt < MT; ++mt) rs[mt] = 1.f;
   }
   const bool emit_ok = active && kg == 0;
   if constexpr (Epi::kStaged) {
@@ -581,6 +605,8 @@ __device__ __forceinline__ void prefetch_scales(const E &e, const float *scale, 
 template <int NTc>
 struct EpiF32 {  // y = acc * scale, fp32 out
   static constexpr bool kStaged = true;
+  static constexpr bool kNormInput = false;
+  static constexpr int kNT = NTc;
   int units, N;
   float *y;
   const float *scale;
@@ -612,6 +638,8 @@ struct EpiF32 {  // y = acc * scale, fp32 out
 template <int NTc>
 struct EpiPartial {
   static constexpr bool kStaged = true;
+  static constexpr bool kNormInput = false;
+  static constexpr int kNT = NTc;
   int units, N, M;
   float *part;  // [nsplit][M][N]
   const float *scale;
@@ -645,6 +673,8 @@ struct EpiPartial {
 template <int NTc>
 struct EpiResidual {
   static constexpr bool kStaged = true;
+  static constexpr bool kNormInput = false;
+  static constexpr int kNT = NTc;
   int units, N;
   const float *scale;
   ResidualOut o;
@@ -715,6 +745,8 @@ struct EpiResidual {
 template <int NTc>
 struct EpiQkv {
   static constexpr bool kStaged = true;
+  static constexpr bool kNormInput = true;
+  static constexpr int kNT = NTc;
   int units;  // units of NTc tiles
   const float *scale;  // packed per-row scales
   QkvOut o;
@@ -810,6 +842,8 @@ struct EpiQkv {
 template <int NTc, bool MX8 = false>
 struct EpiSwiglu {
   static constexpr bool kStaged = true;
+  static constexpr bool kNormInput = true;
+  static constexpr int kNT = NTc;
   static_assert(!MX8 || NTc == 2, "an MXFP8 block is the 32 outputs of one row of a unit");
   int units, I;
   const float *scale;  // packed per-row FP8 scales [2I], NULL when decoded with the scale
@@ -853,14 +887,19 @@ struct EpiSwiglu {
 };
 
 // lm_head tile -> one argmax partial per (row, workgroup), lowest index on
-// ties: each wave reduces its 32*NT vocab rows in registers (logits scaled by
-// the row's normalisation r first), the workgroup's waves meet in LDS, and
-// wave 0 folds them in wave order (increasing vocab index).  Called by every
-// wave of the workgroup (inactive ones contribute nothing), after the main
-// loop.
+// ties: each wave reduces its 32*NT vocab rows in registers, the workgroup's
+// waves meet in LDS, and wave 0 folds them in wave order (increasing vocab
+// index).  Called by every wave of the workgroup (inactive ones contribute
+// nothing), after the main loop.  The input rows are h * g of the final
+// RMSNorm; its normalisation r > 0 scales a whole row of logits and so
+// cannot move the row's argmax: the argmax is taken on the unscaled sums,
+// and r is applied only to the logits a test dump asks for (the launch then
+// passes the partial sums of squares).
 template <int NTc>
 struct EpiArgmax {
   static constexpr bool kStaged = false;
+  static constexpr bool kNormInput = true;
+  static constexpr int kNT = NTc;
   template <int NT> static constexpr int cols() { return 4; }
   template <int NT, int MT>
   struct Pre {};
@@ -887,7 +926,7 @@ struct EpiArgmax {
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int n = row(unit, t) + 8 * (v >> 2) + 4 * h + (v & 3);
-          const float lv = acc[t][mt][v] * rs[mt];
+          const float lv = acc[t][mt][v];
           const bool gt = lv > bv;
           bv = gt ? lv : bv;
           bi = gt ? n : bi;
@@ -952,33 +991,100 @@ static int pick_mt(int M, int units, int maxMT) {
   return mt;
 }
 
-// Decoder GEMMs with 16-bit activations (one 32-row tile per wave): the
-// shape of a four-wave workgroup, NG waves along N by KS along K, and its
-// activation tile height, taken in order of the bytes a workgroup moves per
-// flop (tall shared tiles first) until one gives GEMM_WG_TARGET workgroups;
-// failing that, the one with the most.
-GemmPlan decoder_plan(int M, int tiles, int ksteps) {
-  static const int kShapes[][3] = {{4, 1, 2}, {2, 2, 2}, {4, 1, 1}, {2, 2, 1}, {1, 4, 1}};  // NG, KS, MT
-  GemmPlan best{};
-  int best_wg = -1;
-  for (const auto &s : kShapes) {
-    if (s[2] > 1 && M <= 32) continue;
-    GemmPlan p = gemm_plan(M, tiles, ksteps, s[2], false, s[0]);
-    p.KS = s[1];
-    const int wg = p.nb * p.mb;
-    if (wg >= GEMM_WG_TARGET) return p;
-    if (wg > best_wg) best = p, best_wg = wg;
+// Workgroup shapes of the decoder GEMMs with 16-bit activations: NWV waves,
+// NG of them side by side along N by KS along K, NT 32-row weight tiles per
+// wave, a 32*MT-row activation tile, DEPTH stages in flight.  Short-K
+// launches at these row counts are bound by how many memory round trips they
+// wait for, so the shapes keep most of a K of 896 in flight; the one
+// MFMA-heavy launch (gate/up at hundreds of rows) takes two tiles per wave,
+// so that each activation fragment read from LDS feeds two MFMAs.
+struct Shape {
+  int nwv, ng, ks, mt, nt, depth;
+};
+enum ShapeId { kS412, kS222, kS411, kS221, kS141, kS241w8, kS812w8, kS181w8, kNumShapes };
+static constexpr Shape kShapes[kNumShapes] = {
+    {4, 4, 1, 2, 1, 4},  // 128 weight rows x 64 activation rows
+    {4, 2, 2, 2, 1, 3},  // 64 x 64, two k groups
+    {4, 4, 1, 1, 1, 6},  // 128 x 32
+    {4, 2, 2, 1, 1, 3},  // 64 x 32, two k groups
+    {4, 1, 4, 1, 1, 3},  // 32 x 32, four k groups
+    {8, 2, 4, 1, 1, 3},  // 64 x 32, four k groups
+    {8, 8, 1, 2, 2, 2},  // 512 x 64, two tiles per wave
+    {8, 1, 8, 1, 1, 2},  // 32 x 32, eight k groups
+};
+
+// Shape per GEMM and row count (the thresholds and choices measured over
+// whole passes of the 0.5B model at 16 and 512 rows).
+#ifndef GEMM_SMALL_M
+#define GEMM_SMALL_M 64
+#endif
+#ifndef GEMM_WIDE_M
+#define GEMM_WIDE_M 256
+#endif
+#ifndef GEMM_SHAPE_QKV
+#define GEMM_SHAPE_QKV kS221
+#endif
+#ifndef GEMM_SHAPE_OPROJ
+#define GEMM_SHAPE_OPROJ kS221
+#endif
+#ifndef GEMM_SHAPE_GATE_UP
+#define GEMM_SHAPE_GATE_UP kS812w8
+#endif
+#ifndef GEMM_SHAPE_GATE_UP_MID
+#define GEMM_SHAPE_GATE_UP_MID kS412
+#endif
+#ifndef GEMM_SHAPE_DOWN
+#define GEMM_SHAPE_DOWN kS241w8
+#endif
+#ifndef GEMM_SHAPE_SMALL
+#define GEMM_SHAPE_SMALL kS141
+#endif
+#ifndef GEMM_SHAPE_DOWN_SMALL
+#define GEMM_SHAPE_DOWN_SMALL kS181w8
+#endif
+static int decoder_shape(int kind, int M) {
+  if (M <= GEMM_SMALL_M) return kind == kGemmDown ? GEMM_SHAPE_DOWN_SMALL : GEMM_SHAPE_SMALL;
+  switch (kind) {
+    case kGemmQkv: return GEMM_SHAPE_QKV;
+    case kGemmOproj: return GEMM_SHAPE_OPROJ;
+    case kGemmGateUp: return M >= GEMM_WIDE_M ? GEMM_SHAPE_GATE_UP : GEMM_SHAPE_GATE_UP_MID;
+    default: return GEMM_SHAPE_DOWN;
   }
-  return best;
+}
+
+GemmPlan decoder_plan(int kind, int M, int tiles, int ksteps) {
+  const Shape &s = kShapes[decoder_shape(kind, M)];
+  GemmPlan p = gemm_plan(M, tiles / s.nt, ksteps, s.mt, false, s.ng);
+  p.KS = s.ks;
+  return p;
 }
 
 // ---------------------------------------------------------------- launchers
 
-template <bool F16, int FMT, int NT, int MT, bool A8, class Epi, int NWV = 4, int KS = 1>
-static hipError_t go(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
-  hipLaunchKernelGGL((gemm_kernel<F16, FMT, NT, MT, Epi, A8, NWV, KS>), dim3(p.grid_x, 1, p.nsplit), dim3(64 * NWV),
-                     0, st, ga, epi);
+template <bool F16, int FMT, int NT, int MT, bool A8, class Epi, int NWV, int KS, int DEPTH, int NRL>
+static hipError_t go_n(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
+  constexpr int lds = GemmCfg<FMT, NT, MT, Epi, A8, NWV, KS, DEPTH>::LDS_BYTES;
+  static_assert(lds <= 160 * 1024, "LDS of one workgroup");
+  static const hipError_t attr =  // once per instantiation: allow more than 64 KB of LDS
+      hipFuncSetAttribute((const void *)gemm_kernel<F16, FMT, NT, MT, Epi, A8, NWV, KS, DEPTH, NRL>,
+                          hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  if (attr != hipSuccess) return attr;
+  hipLaunchKernelGGL((gemm_kernel<F16, FMT, NT, MT, Epi, A8, NWV, KS, DEPTH, NRL>), dim3(p.grid_x, 1, p.nsplit),
+                     dim3(64 * NWV), lds, st, ga, epi);
   return hipGetLastError();
+}
+
+// the instantiation for the number of partial-sum loads the input rows need
+// (only epilogues that scale by the input's normalisation take them)
+template <bool F16, int FMT, int NT, int MT, bool A8, class Epi, int NWV = 4, int KS = 1, int DEPTH = 0>
+static hipError_t go(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
+  const int nrl = norm_loads(ga.nr, NWV);
+  if (nrl == 0) return go_n<F16, FMT, NT, MT, A8, Epi, NWV, KS, DEPTH, 0>(p, ga, epi, st);
+  if constexpr (Epi::kNormInput) {
+    if (nrl == 1) return go_n<F16, FMT, NT, MT, A8, Epi, NWV, KS, DEPTH, 1>(p, ga, epi, st);
+    if (nrl == 4) return go_n<F16, FMT, NT, MT, A8, Epi, NWV, KS, DEPTH, 4>(p, ga, epi, st);
+  }
+  return hipErrorInvalidValue;
 }
 
 template <bool F16, int FMT, int NT, bool A8, class Epi>
@@ -992,14 +1098,27 @@ static hipError_t go_m(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hi
   }
 }
 
-// the decoder shapes of decoder_plan, FP16 activations, NT = 1
+// one decoder shape, FP16 activations (shapes whose tiles per wave differ
+// from the epilogue's are not instantiated)
+template <int FMT, class Epi, int ID>
+static hipError_t go_shape(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
+  constexpr Shape s = kShapes[ID];
+  if constexpr (s.nt == Epi::kNT)
+    return go<true, FMT, s.nt, s.mt, false, Epi, s.nwv, s.ks, s.depth>(p, ga, epi, st);
+  return hipErrorInvalidValue;
+}
 template <int FMT, class Epi>
-static hipError_t go_decoder(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
-  if (p.MT == 2 && p.NG == 4) return go<true, FMT, 1, 2, false, Epi, 4, 1>(p, ga, epi, st);
-  if (p.MT == 2 && p.NG == 2) return go<true, FMT, 1, 2, false, Epi, 4, 2>(p, ga, epi, st);
-  if (p.MT == 1 && p.NG == 4) return go<true, FMT, 1, 1, false, Epi, 4, 1>(p, ga, epi, st);
-  if (p.MT == 1 && p.NG == 2) return go<true, FMT, 1, 1, false, Epi, 4, 2>(p, ga, epi, st);
-  if (p.MT == 1 && p.NG == 1) return go<true, FMT, 1, 1, false, Epi, 4, 4>(p, ga, epi, st);
+static hipError_t go_decoder(int id, const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hipStream_t st) {
+  switch (id) {
+    case kS412: return go_shape<FMT, Epi, kS412>(p, ga, epi, st);
+    case kS222: return go_shape<FMT, Epi, kS222>(p, ga, epi, st);
+    case kS411: return go_shape<FMT, Epi, kS411>(p, ga, epi, st);
+    case kS221: return go_shape<FMT, Epi, kS221>(p, ga, epi, st);
+    case kS141: return go_shape<FMT, Epi, kS141>(p, ga, epi, st);
+    case kS241w8: return go_shape<FMT, Epi, kS241w8>(p, ga, epi, st);
+    case kS812w8: return go_shape<FMT, Epi, kS812w8>(p, ga, epi, st);
+    case kS181w8: return go_shape<FMT, Epi, kS181w8>(p, ga, epi, st);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -1034,16 +1153,19 @@ static hipError_t run(ActIn x, int M, int K, const LinearW &w, Epi epi, bool all
   return hipErrorInvalidValue;
 }
 
-// FP16 activations, one tile per wave, the workgroup shape of decoder_plan
+// FP16 activations, the workgroup shape decoder_shape() picks for the GEMM
 template <unsigned FMTS, class Epi>
-static hipError_t run_decoder(ActIn x, int M, int K, const LinearW &w, Epi epi, NormRows nr, hipStream_t st) {
+static hipError_t run_decoder(int kind, ActIn x, int M, int K, const LinearW &w, Epi epi, NormRows nr,
+                              hipStream_t st) {
   if (x.xs) return hipErrorInvalidValue;
-  const GemmPlan p = decoder_plan(M, epi.units, K / 64);
+  const int id = decoder_shape(kind, M);
+  if (kShapes[id].nt != Epi::kNT) return hipErrorInvalidValue;
+  const GemmPlan p = decoder_plan(kind, M, epi.units * Epi::kNT, K / 64);
   const GemmArgs ga = gemm_args(x, M, K, w, p, nr);
   if constexpr ((FMTS & kFp8) != 0)
-    if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW) return go_decoder<SPEC_WFMT_FP8_E4M3_ROW>(p, ga, epi, st);
+    if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW) return go_decoder<SPEC_WFMT_FP8_E4M3_ROW>(id, p, ga, epi, st);
   if constexpr ((FMTS & kMx4) != 0)
-    if (w.wfmt == SPEC_WFMT_MXFP4) return go_decoder<SPEC_WFMT_MXFP4>(p, ga, epi, st);
+    if (w.wfmt == SPEC_WFMT_MXFP4) return go_decoder<SPEC_WFMT_MXFP4>(id, p, ga, epi, st);
   return hipErrorInvalidValue;
 }
 
@@ -1064,15 +1186,17 @@ int residual_nsplit(int M, int N, int K) {
   return gemm_plan(M, units, K / 64, pick_mt(M, units, 4), true, 4).nsplit;
 }
 
-hipError_t launch_residual(ActIn x, int M, int N, int K, LinearW w, const ResidualOut &o, hipStream_t st) {
-  return run_decoder<kFp8 | kMx4>(x, M, K, w, EpiResidual<1>{N / 32, N, fp8_scale(w), o}, NormRows{}, st);
+hipError_t launch_residual(int kind, ActIn x, int M, int N, int K, LinearW w, const ResidualOut &o, hipStream_t st) {
+  return run_decoder<kFp8 | kMx4>(kind, x, M, K, w, EpiResidual<1>{N / 32, N, fp8_scale(w), o}, NormRows{}, st);
 }
 
 hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8_t *a_scales, NormRows nr,
                          hipStream_t st) {
   if (a_scales)  // MXFP8 output: a unit of two tiles gives one 32-wide block per row
     return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2, true>{I / 32, I, fp8_scale(w), a, a_scales}, false, nr, st);
-  return run_decoder<kFp8 | kMx4>(x, M, H, w, EpiSwiglu<1>{I / 16, I, fp8_scale(w), a, nullptr}, nr, st);
+  if (kShapes[decoder_shape(kGemmGateUp, M)].nt == 2)
+    return run_decoder<kFp8 | kMx4>(kGemmGateUp, x, M, H, w, EpiSwiglu<2>{I / 32, I, fp8_scale(w), a, nullptr}, nr, st);
+  return run_decoder<kFp8 | kMx4>(kGemmGateUp, x, M, H, w, EpiSwiglu<1>{I / 16, I, fp8_scale(w), a, nullptr}, nr, st);
 }
 
 hipError_t launch_qkv(ActIn x, int M, int H, LinearW w, QkvOut o, NormRows nr, hipStream_t st) {
@@ -1080,7 +1204,7 @@ hipError_t launch_qkv(ActIn x, int M, int H, LinearW w, QkvOut o, NormRows nr, h
   const float *s = reinterpret_cast<const float *>(w.s);
   const int tiles = (o.Hq + 2 * o.Hkv) * o.D / 32;
   if (x.xs) return run<1, kFp8>(x, M, H, w, EpiQkv<1>{tiles, s, o}, false, nr, st);
-  return run_decoder<kFp8>(x, M, H, w, EpiQkv<1>{tiles, s, o}, nr, st);
+  return run_decoder<kFp8>(kGemmQkv, x, M, H, w, EpiQkv<1>{tiles, s, o}, nr, st);
 }
 
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,

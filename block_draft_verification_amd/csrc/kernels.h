@@ -61,8 +61,10 @@ struct GemmPlan {
   int MT, NG, KS, nb, mb, spl, nsplit, grid_x;
 };
 GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split, int ng = 4);  // ng waves along N
-// the workgroup shape of a decoder GEMM with 16-bit activations, one tile per wave
-GemmPlan decoder_plan(int M, int tiles, int ksteps);
+// the decoder GEMMs, whose workgroup shapes are chosen per GEMM and row count
+enum GemmKind { kGemmQkv = 0, kGemmOproj = 1, kGemmGateUp = 2, kGemmDown = 3 };
+// the plan of a decoder GEMM with 16-bit activations over `tiles` 32-row weight tiles
+GemmPlan decoder_plan(int kind, int M, int tiles, int ksteps);
 // splits the MXFP8 mode's residual projection [M][K] x [N][K]^T uses (partials to reduce)
 int residual_nsplit(int M, int N, int K);
 
@@ -91,7 +93,8 @@ struct ResidualOut {
   int ssp_ld;
   int32_t *err;
 };
-hipError_t launch_residual(ActIn x, int M, int N, int K, LinearW w, const ResidualOut &o, hipStream_t st);
+// kind: kGemmOproj or kGemmDown (the workgroup shape)
+hipError_t launch_residual(int kind, ActIn x, int M, int N, int K, LinearW w, const ResidualOut &o, hipStream_t st);
 
 // y fp32 [M][N] (test hook)
 hipError_t launch_linear_f32(ActIn x, int M, int N, int K, LinearW w, float *y, hipStream_t st);
@@ -206,7 +209,14 @@ hipError_t launch_final_hidden(const uint16_t *xg, const float *ssp, int ld, int
 // x = RMSNorm(h_out) * gain, written as FP16 (out_bf16 = 0) or BF16 (out_bf16 = 1)
 hipError_t launch_norm(const float *h, float *h_out, const float *part, int nsplit, const float *gain, int M, int H,
                        float eps, uint16_t *x, int out_bf16, float *dump, hipStream_t st);
-// the same, x written as MXFP8: e4m3 codes [M][H] in x8, e8m0 [M][H/32] in xs
+// h_out = h + part[0] + ... + part[nsplit-1] (in that order; h_out is never
+// h), xg = h_out * gain (FP16, or BF16 with xg_bf16) and ssp[m][j] = sum of
+// h_out^2 over columns 32j .. 32j+31 (entries past H/32 up to ld zeroed): the
+// residual step after a split-K projection, with the next RMSNorm left to the
+// GEMM that reads xg (NormRows).
+hipError_t launch_fold(const float *h, float *h_out, const float *part, int nsplit, const float *gain, int M, int H,
+                       uint16_t *xg, int xg_bf16, float *ssp, int ld, int32_t *err, hipStream_t st);
+// the same as launch_norm, x written as MXFP8: e4m3 codes [M][H] in x8, e8m0 [M][H/32] in xs
 // (dump, when non-NULL, gets the decoded values code * 2^(e - 127))
 hipError_t launch_norm_mx8(const float *h, float *h_out, const float *part, int nsplit, const float *gain, int M,
                            int H, float eps, uint8_t *x8, uint8_t *xs, float *dump, hipStream_t st);

@@ -264,6 +264,83 @@ __global__ __launch_bounds__(256) void norm_kernel(const float *__restrict__ h, 
   }
 }
 
+// The split-K partials of a residual projection added to the residual
+// stream with the next RMSNorm's input prepared for its GEMM:
+// h_out = h + part[0] + ... + part[ns-1] (in that order), xg = h_out * gain
+// (FP16, or BF16 before the lm_head) and ssp[m][j] = sum of h_out^2 over
+// columns 32j .. 32j+31 (the row's remaining entries zeroed); the
+// normalisation itself is applied by the GEMM that reads xg.  One 256-thread
+// workgroup per row as in norm_kernel; the 8 threads of a 32-column group
+// are consecutive lanes.  An FP16 xg beyond the format's range sets
+// SPEC_DERR_RANGE.
+template <bool BF16>
+__global__ __launch_bounds__(256) void fold_kernel(const float *__restrict__ h, float *__restrict__ h_out,
+                                                   const float *__restrict__ part, int ns,
+                                                   const float *__restrict__ gain, int M, int H,
+                                                   uint16_t *__restrict__ xg, float *__restrict__ ssp, int ld,
+                                                   int32_t *err) {
+  pin_args(h, h_out, part, ns, gain, M, H, xg, ssp, ld, err);
+  constexpr int MAXC = 4;
+  const int m = blockIdx.x, tid = threadIdx.x;
+  const float *hr = h + (size_t)m * H;
+  const float *pr = part + (size_t)m * H;
+  const size_t pstride = (size_t)M * H;
+  f32x4_t t[MAXC], gv[MAXC];
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = 4 * tid + 1024 * i;
+    t[i] = c < H ? *reinterpret_cast<const f32x4_t *>(hr + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    gv[i] = c < H ? *reinterpret_cast<const f32x4_t *>(gain + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  int s = 0;
+  for (; s + 4 <= ns; s += 4) {  // four splits' loads issued together
+    f32x4_t p[4][MAXC];
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) {
+        const int c = 4 * tid + 1024 * i;
+        p[q][i] = c < H ? *reinterpret_cast<const f32x4_t *>(pr + (s + q) * pstride + c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int i = 0; i < MAXC; ++i) t[i] += p[q][i];
+  }
+  for (; s < ns; ++s) {
+#pragma unroll
+    for (int i = 0; i < MAXC; ++i) {
+      const int c = 4 * tid + 1024 * i;
+      if (c < H) t[i] += *reinterpret_cast<const f32x4_t *>(pr + s * pstride + c);
+    }
+  }
+  bool range_ok = true;
+#pragma unroll
+  for (int i = 0; i < MAXC; ++i) {
+    const int c = 4 * tid + 1024 * i;
+    float ss = (t[i][0] * t[i][0] + t[i][1] * t[i][1]) + (t[i][2] * t[i][2] + t[i][3] * t[i][3]);
+    ss += __shfl_xor(ss, 1);
+    ss += __shfl_xor(ss, 2);
+    ss += __shfl_xor(ss, 4);
+    if (c >= H) continue;
+    *reinterpret_cast<f32x4_t *>(h_out + (size_t)m * H + c) = t[i];
+    const f32x4_t x = t[i] * gv[i];
+    uint32_t lo, hi;
+    if constexpr (BF16) {
+      lo = pack_bf16x2(x[0], x[1]);
+      hi = pack_bf16x2(x[2], x[3]);
+    } else {
+      lo = pack_f16x2(x[0], x[1]);
+      hi = pack_f16x2(x[2], x[3]);
+      range_ok &= fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))) <= 65504.f;
+    }
+    *reinterpret_cast<u32x2_t *>(xg + (size_t)m * H + c) = u32x2_t{lo, hi};
+    if ((c & 31) == 0) ssp[(size_t)m * ld + c / 32] = ss;
+  }
+  if (!range_ok) set_error(err, SPEC_DERR_RANGE);
+  if (tid < ld - H / 32) ssp[(size_t)m * ld + H / 32 + tid] = 0.f;
+}
+
 // One workgroup of 16 waves per sequence, wave j = block row b*16+j:
 // g[j] = argmax over the vocab partials of the row (lowest id on ties; lanes
 // read the partials with independent loads, then a shuffle tree), then
@@ -426,6 +503,18 @@ hipError_t launch_norm(const float *h, float *h_out, const float *part, int nspl
   else
     hipLaunchKernelGGL(norm_kernel<kOutF16>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, eps,
                        (void *)x, (uint8_t *)nullptr, dump);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold(const float *h, float *h_out, const float *part, int nsplit, const float *gain, int M, int H,
+                       uint16_t *xg, int xg_bf16, float *ssp, int ld, int32_t *err, hipStream_t st) {
+  if (H > 4096 || H % 32 || h == h_out || ld - H / 32 > 256) return hipErrorInvalidValue;
+  if (xg_bf16)
+    hipLaunchKernelGGL(fold_kernel<true>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, xg, ssp, ld,
+                       err);
+  else
+    hipLaunchKernelGGL(fold_kernel<false>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, xg, ssp, ld,
+                       err);
   return hipGetLastError();
 }
 
