@@ -67,6 +67,7 @@ EXPORTS = {
     "spec_debug_rmsnorm": (_I, [_I, _I, _P, _P, ctypes.c_float, _I, _P, _P, _P]),
     "spec_debug_swiglu": (_I, [_I, _I, _I, _P, _P, _P, _P, _I, _I, _P, _P, _P]),
     "spec_debug_attention": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P]),
+    "spec_debug_attention_noalloc": (_I, [_I, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _P]),
     "spec_debug_time_kernel": (_I, [_P, _I]),
     "spec_debug_set_repeat": (_I, [_P, _I]),
     "spec_debug_kernel_time": (_I, [_P, ctypes.POINTER(ctypes.c_float), ctypes.POINTER(_I)]),
@@ -358,11 +359,14 @@ def debug_swiglu(x: torch.Tensor, x_scales, w: torch.Tensor, wscales, wfmt: int,
     return a if as_ is None else (a, as_)
 
 
-def debug_attention(q, k_cache, v_cache, kv_len, batch, n_q_heads, n_kv_heads, head_dim, split_len=0):
-    """One layer's block-causal attention through the library's kernel."""
+def debug_attention(q, k_cache, v_cache, kv_len, batch, n_q_heads, n_kv_heads, head_dim, split_len=0,
+                    noalloc=False, out=None):
+    """One layer's block-causal attention through the library's kernel;
+    noalloc=True goes through spec_debug_attention_noalloc (no device
+    allocation, asynchronous) with `out` as the caller's output buffer."""
     max_batch, _, max_ctx, _ = k_cache.shape
-    o = torch.empty_like(q)
-    _check(load_library().spec_debug_attention(batch, n_q_heads, n_kv_heads, head_dim, max_batch, max_ctx,
-                                               _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(o),
-                                               split_len, _stream()), "spec_debug_attention")
+    o = torch.empty_like(q) if out is None else out
+    fn = "spec_debug_attention_noalloc" if noalloc else "spec_debug_attention"
+    _check(getattr(load_library(), fn)(batch, n_q_heads, n_kv_heads, head_dim, max_batch, max_ctx, _ptr(q),
+                                       _ptr(k_cache), _ptr(v_cache), _ptr(kv_len), _ptr(o), split_len, _stream()), fn)
     return o

@@ -4,6 +4,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -827,3 +828,68 @@ int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int3
 }
 
 }  // extern "C"
+
+// ---- block-causal attention without allocation ----
+// For callers that cannot allocate device memory: the split partials and the
+// split plan live in this static device buffer.  Host code never names it
+// directly (its name is a host-side stand-in); each device's address of it is
+// looked up once, with that device current, and kept.
+static __device__ __align__(256) uint8_t scratch[SPEC_ATTN_SCRATCH_BYTES];
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[64] = {};
+
+static int scratch_ptr(const char *fn, void **out) {
+  int dev = -1;
+  const hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(SPEC_E_HIP, fn, "hipGetDevice", e);
+  if (dev < 0 || dev >= 64) return fail(SPEC_E_ARG, fn, "device index beyond 63");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t es = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (es != hipSuccess || !p) return fail(SPEC_E_HIP, fn, "hipGetSymbolAddress(scratch)", es);
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return SPEC_OK;
+}
+
+extern "C" int spec_debug_attention_noalloc(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_batch,
+                                            int32_t max_ctx, const uint16_t *q, const uint16_t *k_cache,
+                                            const uint16_t *v_cache, const int32_t *kv_len, uint16_t *o,
+                                            int32_t split_len, hipStream_t st) {
+  static const char *fn = "spec_debug_attention_noalloc";
+  if (!q || !k_cache || !v_cache || !kv_len || !o) return fail(SPEC_E_ARG, fn, "NULL argument");
+  if (batch < 1 || batch > max_batch || Hkv < 1 || Hq % Hkv || Hq / Hkv > 8 || max_ctx < 16)
+    return fail(SPEC_E_ARG, fn, "shape");
+  if (D != 64 && D != 128) return fail(SPEC_E_SHAPE, fn, "head_dim");
+  if (split_len < 0 || split_len % 64) return fail(SPEC_E_ARG, fn, "split_len");
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return fail(SPEC_E_ARG, fn, "alignment");
+  if (split_len && (max_ctx + split_len - 1) / split_len > 64) return fail(SPEC_E_ARG, fn, "more than 64 splits");
+  AttnPlanArgs p = attention_plan_args(nullptr, batch, Hkv, max_ctx, D, split_len, attention_device_cus());
+  const size_t units = (size_t)p.grid, R = (size_t)(Hq / Hkv) * 16;
+  const size_t o_bytes = round256(units * R * D * 2), ml_bytes = round256(units * R * 8);
+  const size_t plan_bytes = round256((1 + (size_t)batch) * 16);
+  if (o_bytes + ml_bytes + plan_bytes > SPEC_ATTN_SCRATCH_BYTES)
+    return fail(SPEC_E_ARG, fn, "split partials exceed SPEC_ATTN_SCRATCH_BYTES");
+  void *buf = nullptr;
+  const int rc = scratch_ptr(fn, &buf);
+  if (rc != SPEC_OK) return rc;
+  AttnArgs a{};
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.o = o;
+  a.batch = batch;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.max_ctx = max_ctx;
+  a.grid = p.grid;
+  a.part_o = (uint16_t *)buf;
+  a.part_ml = (float2 *)((char *)buf + o_bytes);
+  p.plan = (int4 *)((char *)buf + o_bytes + ml_bytes);
+  a.plan = p.plan;
+  CK(launch_attention_plan(kv_len, p, st));  // writes the whole plan: nothing in the buffer needs clearing
+  CK(launch_attention(a, D, st));
+  return SPEC_OK;
+}

@@ -364,6 +364,24 @@ int spec_debug_attention(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, i
                          const uint16_t *k_cache, const uint16_t *v_cache, const int32_t *kv_len,
                          uint16_t *o, int32_t split_len, hipStream_t stream);
 
+/* spec_debug_attention for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc).  Same arguments and results as spec_debug_attention, but the
+ * split partials and the split plan live in a library-owned static device
+ * buffer of SPEC_ATTN_SCRATCH_BYTES, which every GPU the library runs on holds
+ * until the process ends; nothing is allocated or freed, and the call is
+ * asynchronous (no host synchronisation; the caller orders or synchronises
+ * `stream`).  A launch whose partials would exceed the buffer is rejected with
+ * SPEC_E_ARG (e.g. 1 sequence x 8 KV heads of head_dim 128 and 8 query heads
+ * each fits; see spec_last_error for the reason of a rejection).  Every call on
+ * a GPU shares that GPU's buffer, so calls that overlap on one GPU (other
+ * streams, other threads) race; the buffer keeps the last call's contents. */
+#define SPEC_ATTN_SCRATCH_BYTES (32u << 20)
+int spec_debug_attention_noalloc(int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, int32_t head_dim,
+                                 int32_t max_batch, int32_t max_ctx, const uint16_t *q, const uint16_t *k_cache,
+                                 const uint16_t *v_cache, const int32_t *kv_len, uint16_t *o, int32_t split_len,
+                                 hipStream_t stream);
+
 /* Kernel classes for spec_debug_time_kernel.  SPEC_K_ATTENTION is the split
  * attention kernel alone; SPEC_K_ATTN_MERGE the kernel that merges its splits. */
 typedef enum {
