@@ -10,10 +10,18 @@ planted from the pass's own greedy continuation with acceptance lengths
 min(Geometric(0.1), 16).  The timed region replays a captured graph of
 {restore kv_len, verify, commit} K times between two events.
 
-Prints one JSON line (see the keys below).  --gpus N > 1 is refused: this
-build measures one GPU.
+Also measured, as keys of the same JSON line: per-step percentiles with the
+caches warm and after a 512 MB eviction write (outside the timed events),
+every kernel class's duration inside a pass (the kernel's own dispatch
+events), the roofline of the dominant kernel and of the whole pass, the other
+single-GPU workloads (the batch-1 and MXFP4 shapes; the 8B shape with
+--with-8b), batch-1 decoding loops, the FP8-activation mode, and the CPU
+oracle on a bounded sample.
+
+Prints one JSON line.  --gpus N > 1 is refused: this build measures one GPU.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -30,27 +38,28 @@ MFMA_FP8_PEAK = 5.0e15     # flop/s, dense FP8 MFMA
 RIDGE = MFMA_BF16_PEAK / HBM_PEAK
 METRIC = "verify passes/s & accepted tok/s, 0.5B FP8 target, K=16 block; % of HBM peak"
 WORKLOAD = "0.5b-fp8-b32-ctx512to4096"
-REPEAT = 20  # back-to-back launches per event pair in the per-kernel timing
+OTHER_WORKLOADS = ["0.5b-fp8-b1-ctx2048", "0.5b-mxfp4mlp-b16-ctx3072"]
+EVICT_BYTES = 512 << 20
 
-# HBM bytes per launch of a kernel class from two rocprofv3 --pmc runs
-# (FETCH_SIZE x 2.0 and WRITE_SIZE x 1.0: the factors that make a plain 1 GiB
-# device copy read back as 1 GiB), valid for the kernel sources whose digest
-# is recorded; any other source reports null.
-TRAFFIC_PROFILE = "profiles/verify_pass_0.5b-fp8-b32-ctx512to4096_hbm_traffic.md"
-TRAFFIC = {
-    "attention": {"bytes": (38.47 + 3.69) * 2 ** 20, "sources": ("attention.hip", "attn_plan.h", "common.h", "kernels.h"),
-                  "sha256_16": "8b31cfa2fb105611,796e17fcecfb030f,57d79c5d9e2360c0,14ecfd7a951d813f"},
-    "gate_up": {"bytes": (18.53 + 4.75) * 2 ** 20, "sources": ("gemm.hip", "common.h", "kernels.h"),
-                "sha256_16": "bbbb721a1e0d3202,57d79c5d9e2360c0,14ecfd7a951d813f"},
-    "rmsnorm": {"bytes": (7.10 + 2.62) * 2 ** 20, "sources": ("misc.hip", "attn_plan.h", "common.h", "kernels.h"),
-                "sha256_16": "491bcc3d50dea8d2,796e17fcecfb030f,57d79c5d9e2360c0,14ecfd7a951d813f"},
-}
+# Hardware-counter figures of the dominant kernel classes, from rocprofv3 --pmc
+# runs of `bench.py --no-extras` (profiles/ holds the summaries):
+#   traffic = FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 per launch (the factors that
+#             make a plain 1 GiB device copy read back as 1 GiB), bytes
+#   mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs)
+# valid for the kernel sources whose digest is recorded; any other source
+# reports null.
+COUNTERS_PROFILE = "profiles/verify_pass_0.5b-fp8-b32-ctx512to4096_counters.md"
+SOURCES = ("gemm.hip", "attention.hip", "attn_plan.h", "misc.hip", "common.h", "kernels.h")
+COUNTERS = {}
+COUNTERS_DIGEST = None
 
 
-def _sources_digest(files):
-    import hashlib
+def _sources_digest():
     d = os.path.join(ROOT, "block_draft_verification_amd", "csrc")
-    return ",".join(hashlib.sha256(open(os.path.join(d, f), "rb").read()).hexdigest()[:16] for f in files)
+    h = hashlib.sha256()
+    for f in SOURCES:
+        h.update(open(os.path.join(d, f), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def log(msg):
@@ -69,27 +78,34 @@ def weight_bytes_per_layer(m):
 
 
 def kernel_work(kind, m, lens):
-    """Algorithmic (bytes, flops) of ONE launch of a kernel class."""
+    """Algorithmic (bytes, flops) of ONE launch of a kernel class: the bytes it
+    must read and write (weights, its activation inputs and outputs, KV rows)
+    and the multiply-add flops of its products."""
     B = len(lens)
     M, H, D, I, V = B * 16, m.hidden, m.head_dim, m.intermediate, m.vocab
     wb = weight_bytes_per_layer(m)
     HqD = m.n_q_heads * D
+    kvd = m.n_kv_heads * D
     if kind == "attention":
-        kv = int(np.sum(lens + 16)) * m.n_kv_heads * D * 2 * 2
+        kv = int(np.sum(lens + 16)) * kvd * 2 * 2
         flops = sum(int(np.sum(n + 1 + np.arange(16))) for n in lens) * m.n_q_heads * D * 4
         return kv + 2 * M * HqD * 2, flops
-    if kind == "qkv":
-        return wb["qkv"] + M * H * 2 + M * (HqD + 2 * m.n_kv_heads * D) * 2, 2 * M * m.qkv_rows * H
-    if kind == "o_proj":
-        return wb["o_proj"] + M * HqD * 2 + 2 * M * H * 4, 2 * M * H * HqD
+    if kind == "attn_merge":
+        return 2 * M * HqD * 2, 0
+    if kind == "qkv":  # h*g in, per-row partial sums in, q out, block K/V rows out
+        return wb["qkv"] + M * H * 2 + M * (HqD + 2 * kvd) * 2, 2 * M * m.qkv_rows * H
+    if kind == "o_proj":  # attention out and h in; h, h*g and partial sums out
+        return wb["o_proj"] + M * HqD * 2 + M * H * (4 + 4 + 2), 2 * M * H * HqD
     if kind == "gate_up":
         return wb["gate_up"] + M * H * 2 + M * I * 2, 2 * M * 2 * I * H
     if kind == "down":
-        return wb["down"] + M * I * 2 + 2 * M * H * 4, 2 * M * H * I
+        return wb["down"] + M * I * 2 + M * H * (4 + 4 + 2), 2 * M * H * I
     if kind == "lm_head":
-        return V * H * 2 + M * H * 2 + (V // 64) * M * 8, 2 * M * V * H
+        return V * H * 2 + M * H * 2 + (V // 128) * M * 8, 2 * M * V * H
+    if kind == "embed":
+        return M * H * (2 + 4 + 2), 0
     if kind == "rmsnorm":
-        return M * H * 4 + M * H * 2 + H * 4, 4 * M * H
+        return M * H * 4 * 3 + M * H * 2, 4 * M * H
     return 0, 0
 
 
@@ -104,6 +120,22 @@ def pass_bytes(m, lens):
     kv_read = int(np.sum(lens + 16)) * per_tok
     kv_write = B * 16 * per_tok
     return w + kv_read + kv_write + B * 16 * m.hidden * 2
+
+
+def roofline_time(kind, m, lens):
+    """The roofline time of one launch: max(bytes / HBM peak, flops / MFMA peak)."""
+    by, fl = kernel_work(kind, m, lens)
+    return max(by / HBM_PEAK, fl / MFMA_BF16_PEAK)
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(wl, weights, kv_layers, lens, n_seq, min_seconds=10.0):
@@ -130,7 +162,8 @@ def cpu_baseline(wl, weights, kv_layers, lens, n_seq, min_seconds=10.0):
     return {"value": (n_seq / len(lens)) / dt, "unit": "verify passes/s", "cores": int(threads),
             "kind": "oracle",
             "sample": f"float64 numpy oracle, {reps} verify passes of {n_seq} of {len(lens)} sequences "
-                      f"({dt:.2f} s each), scaled by {n_seq}/{len(lens)}; weight decoding untimed"}
+                      f"({dt:.2f} s each), scaled by {n_seq}/{len(lens)}; weight decoding untimed",
+            "cpu_model": cpu_model()}
 
 
 def e2e_batch1(ver, dev, m, lens, seed, n_rounds=32):
@@ -172,13 +205,15 @@ def e2e_batch1(ver, dev, m, lens, seed, n_rounds=32):
     return {"batch": 1, "context": int(lens[b]), "ar_tokens": n_ref, "ar_ms_per_token": ms_pass_ar,
             "ar_tok_per_s": ar_tps, "spec_rounds": n_rounds, "spec_tokens": n, "spec_ms_per_round": ms_round,
             "spec_tok_per_s": spec_tps, "speedup": spec_tps / ar_tps, "mean_tau": n / n_rounds,
-            "lossless": lossless, "drafts": "planted from the AR stream, acceptance min(Geometric(0.1), 16)"}
+            "lossless": lossless, "drafts": "planted from the AR stream, acceptance min(Geometric(0.1), 16)",
+            "ar_rows_per_pass": 16,
+            "ar_note": "the autoregressive arm runs the library's 16-row pass with one committed row per token; "
+                       "at batch 1 both arms stream the same weight bytes per pass, so this is an upper bound "
+                       "on a one-row pass's time by the attention and MFMA work of 15 extra rows"}
 
 
-def time_graph(ver, dev, tok, kv0, steps, warmup):
-    """Capture one step (restore kv_len, verify, commit) in a graph; replay
-    `warmup` times, then time `steps` replays with events on the stream.
-    Returns (ms per step, accept_len of the last step)."""
+def make_graph(ver, dev, tok, kv0):
+    """Capture one step (restore kv_len, verify, commit) in a graph."""
     import torch
     B = tok.shape[0]
     acc = torch.empty(B, dtype=torch.int32, device="cuda")
@@ -197,6 +232,13 @@ def time_graph(ver, dev, tok, kv0, steps, warmup):
         dev.kv_len.copy_(kv0)
         ver.verify(tok, acc, bon, amx)
         ver.commit(B)
+    return graph, acc
+
+
+def time_graph(graph, steps, warmup):
+    """`warmup` replays, then `steps` replays timed between two events on the
+    stream, bracketed by synchronisations.  Returns ms per step."""
+    import torch
     for _ in range(warmup):
         graph.replay()
     torch.cuda.synchronize()
@@ -206,20 +248,37 @@ def time_graph(ver, dev, tok, kv0, steps, warmup):
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, acc.cpu().numpy()
+    return e0.elapsed_time(e1) / steps
 
 
-def kernel_times(ver, dev, tok, kv0, kinds, reps, repeat=REPEAT):
-    """Per kernel class: launch durations over `reps` eager passes, events on
-    the stream; every launch of the timed class is issued `repeat` times back
-    to back between its two events (commit, which updates kv_len in place,
-    once), so the events' own cost is shared."""
+def step_percentiles(graph, n, evict=None):
+    """Each of n replays timed on its own (an event pair around it); with
+    `evict` (a device buffer), a full write of that buffer before each replay,
+    outside the events, so the replay starts with the caches holding none of
+    the pass's data.  Returns (p10, p50, p90) in ms."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for e0, e1 in evs:
+        if evict is not None:
+            evict.fill_(1)
+        e0.record()
+        graph.replay()
+        e1.record()
+    torch.cuda.synchronize()
+    t = np.array([e0.elapsed_time(e1) for e0, e1 in evs])
+    return [float(np.percentile(t, q)) for q in (10, 50, 90)]
+
+
+def kernel_times(ver, dev, tok, kv0, kinds, reps):
+    """Per kernel class: the duration of each of its launches inside eager
+    passes, recorded by events bound to that launch's dispatch (its own
+    start and end); the mean over `reps` passes."""
     import torch
     B = tok.shape[0]
     acc = torch.empty(B, dtype=torch.int32, device="cuda")
     bon = torch.empty(B, dtype=torch.int32, device="cuda")
     per_kind = {}
-    ver.set_repeat(repeat)
+    ver.set_repeat(1)
     for k in kinds:
         ver.time_kernel(k)
         for _ in range(reps):
@@ -228,12 +287,83 @@ def kernel_times(ver, dev, tok, kv0, kinds, reps, repeat=REPEAT):
             ver.commit(B)
         ver.time_kernel(None)
         tot, n = ver.kernel_time()
-        r = 1 if k == "commit" else repeat
-        per_kind[k] = {"ms_per_pass": tot / reps / r, "us_per_launch": 1000 * tot / max(n, 1),
-                       "launches_per_pass": n // (reps * r), "back_to_back": r}
-    ver.set_repeat(1)
+        if n:
+            per_kind[k] = {"ms_per_pass": tot / reps, "us_per_launch": 1000 * tot / n, "launches_per_pass": n // reps}
     dev.kv_len.copy_(kv0)
     return per_kind
+
+
+def plant(ver, wl, m, tok_np):
+    """Drafts from the pass's own greedy continuation: row j-1's argmax depends
+    only on tokens 0..j-1, so 15 uncommitted passes fill the block."""
+    import torch
+    import workload as W
+    B = wl.batch
+    L = W.accept_lengths(wl)
+    blocks = tok_np
+    tok = torch.from_numpy(blocks).cuda()
+    for j in range(1, 16):
+        g = ver.verify(tok)["argmax"].cpu().numpy()
+        for b in range(B):
+            if j < L[b]:
+                blocks[b, j] = g[b, j - 1]
+            elif j == L[b]:
+                redraw = W.draft_rng(wl, b, 2)
+                while blocks[b, j] == g[b, j - 1]:
+                    blocks[b, j] = redraw.integers(0, m.vocab)
+        tok.copy_(torch.from_numpy(blocks))
+    tau = ver.verify(tok)["accept_len"].cpu().numpy()
+    return tok, tau, L
+
+
+def setup(wl, weights=None):
+    import workload as W
+    from block_draft_verification_amd import DeviceModel, Verifier
+    m = wl.model
+    if weights is None:
+        log(f"workload {wl.name}: generating weights")
+        weights = W.model_weights(m, wl.seed)
+    lens = W.context_lengths(wl)
+    log(f"{wl.name}: synthetic KV")
+    kv_layers = [W.synthetic_kv_layer(m, wl.seed, l, lens, wl.max_ctx) for l in range(m.n_layers)]
+    log(f"{wl.name}: upload")
+    dev = DeviceModel(m, weights, max_batch=wl.batch, max_ctx=wl.max_ctx, kv_layers=kv_layers, kv_len=lens)
+    return weights, lens, kv_layers, dev
+
+
+def config_line(wl, weights, steps, warmup):
+    """Throughput of one more workload, timed like the headline one."""
+    import torch
+    import workload as W
+    from block_draft_verification_amd import Verifier
+    m = wl.model
+    weights, lens, kv_layers, dev = setup(wl, weights)
+    ver = Verifier(dev)
+    blocks = np.stack([W.draft_rng(wl, b).integers(0, m.vocab, size=16) for b in range(wl.batch)]).astype(np.int32)
+    blocks[:, 0] = W.pending_tokens(wl)
+    log(f"{wl.name}: planting drafts")
+    tok, tau, L = plant(ver, wl, m, blocks)
+    kv0 = dev.kv_len.clone()
+    graph, acc = make_graph(ver, dev, tok, kv0)
+    ms = time_graph(graph, steps, warmup)
+    assert np.array_equal(acc.cpu().numpy(), tau)
+    assert ver.device_error() == 0
+    nb = pass_bytes(m, lens)
+    kinds = ["embed", "qkv", "attention", "attn_merge", "o_proj", "gate_up", "down", "lm_head", "accept", "commit"]
+    roof = sum(roofline_time(k, m, lens) * (1 if k in ("embed", "lm_head", "accept", "commit") else m.n_layers)
+               for k in kinds)
+    ver.close()
+    del graph
+    out = {"value": 1000.0 / ms, "unit": "verify passes/s", "ms_per_step": ms, "batch": wl.batch,
+           "rows": wl.batch * 16, "sum_tau": int(tau.sum()), "planted_L_equals_tau": bool(np.array_equal(tau, L)),
+           "emitted_tok_per_s": 1000.0 / ms * float(tau.sum()),
+           "accepted_draft_tok_per_s": 1000.0 / ms * float((tau - 1).sum()),
+           "hbm_frac_of_peak": nb / (ms * 1e-3) / HBM_PEAK, "algorithmic_bytes_per_pass": nb,
+           "pass_roofline_frac": roof / (ms * 1e-3),
+           "kv_fill": "synthetic BF16 draws (the KV values do not change the work)"}
+    del dev
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -246,12 +376,15 @@ def main():
     ap.add_argument("--lanes", type=int, default=1, help="concurrent sequence ranges per pass (spec_verify_set_lanes)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the batch-1 decoding loops and the FP8-activation figure (for counter runs)")
+                    help="only the headline workload (no other workloads, decoding loops, FP8 mode; for counter runs)")
+    ap.add_argument("--no-kernel-times", action="store_true", help="skip the per-kernel-class timing passes")
+    ap.add_argument("--with-8b", action="store_true", help="also time the 8B workload (several minutes of set-up)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB three times (reference for HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a single device)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the path runs on a single device)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -265,71 +398,38 @@ def main():
         print(json.dumps({"copy_probe_bytes": n, "launches": 3}), flush=True)
         return
     import workload as W
-    from block_draft_verification_amd import DeviceModel, Verifier
+    from block_draft_verification_amd import Verifier
 
     wl = W.WORKLOADS[args.workload]
     m = wl.model
     B = wl.batch
-    log(f"workload {wl.name}: generating weights")
-    weights = W.model_weights(m, wl.seed)
-    lens = W.context_lengths(wl)
-    log("synthetic KV")
-    kv_layers = [W.synthetic_kv_layer(m, wl.seed, l, lens, wl.max_ctx) for l in range(m.n_layers)]
-    log("upload")
-    dev = DeviceModel(m, weights, max_batch=B, max_ctx=wl.max_ctx, kv_layers=kv_layers, kv_len=lens)
+    weights, lens, kv_layers, dev = setup(wl)
     ver = Verifier(dev, lanes=args.lanes)
     torch.cuda.synchronize()
-
-    # plant drafts from the pass's own greedy continuation: row j-1's argmax
-    # depends only on tokens 0..j-1, so 15 uncommitted passes fill the block
-    L = W.accept_lengths(wl)
     blocks = np.stack([W.draft_rng(wl, b).integers(0, m.vocab, size=16) for b in range(B)]).astype(np.int32)
     blocks[:, 0] = W.pending_tokens(wl)
-    tok = torch.from_numpy(blocks).cuda()
     log("planting drafts (15 passes)")
-    for j in range(1, 16):
-        g = ver.verify(tok)["argmax"].cpu().numpy()
-        for b in range(B):
-            if j < L[b]:
-                blocks[b, j] = g[b, j - 1]
-            elif j == L[b]:
-                redraw = W.draft_rng(wl, b, 2)
-                while blocks[b, j] == g[b, j - 1]:
-                    blocks[b, j] = redraw.integers(0, m.vocab)
-        tok.copy_(torch.from_numpy(blocks))
-    out = ver.verify(tok)
-    tau = out["accept_len"].cpu().numpy()
+    tok, tau, L = plant(ver, wl, m, blocks)
     log(f"planted L == tau: {np.array_equal(tau, L)}; sum tau = {tau.sum()}")
 
-    # graph of one step: restore kv_len, verify, commit
     kv0 = dev.kv_len.clone()
+    graph, acc = make_graph(ver, dev, tok, kv0)
     log(f"timing {args.steps} steps")
-    ms, acc = time_graph(ver, dev, tok, kv0, args.steps, args.warmup)
-    assert np.array_equal(acc, tau)
+    ms = time_graph(graph, args.steps, args.warmup)
+    assert np.array_equal(acc.cpu().numpy(), tau)
     assert ver.device_error() == 0
-
-    # per-kernel-class launch durations (eager passes, events on the stream)
-    kinds = ["qkv", "attention", "attn_merge", "o_proj", "gate_up", "down", "lm_head", "rmsnorm", "accept", "embed",
-             "commit"]
-    reps = max(3, min(20, args.steps // 5))
-    per_kind = kernel_times(ver, dev, tok, kv0, kinds, reps)
-    dom = max(per_kind, key=lambda k: per_kind[k]["ms_per_pass"])
-    by, fl = kernel_work(dom, m, lens)
-    t_launch = per_kind[dom]["us_per_launch"] * 1e-6
-    if fl / max(by, 1) > RIDGE:
-        roof = {"bound": "mfma", "achieved": fl / t_launch / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": by / t_launch / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    tr = TRAFFIC.get(dom)
-    roof["traffic"] = tr["bytes"] if tr and tr["sha256_16"] == _sources_digest(tr["sources"]) else None
-    roof["kernel"] = dom
-    roof["us_per_launch"] = per_kind[dom]["us_per_launch"]
-    roof["algorithmic_bytes_per_launch"] = by
-    roof["algorithmic_flops_per_launch"] = fl
+    n_pct = max(20, min(100, args.steps))
+    warm = step_percentiles(graph, n_pct)
+    evict = torch.empty(EVICT_BYTES, dtype=torch.uint8, device="cuda")
+    cold = step_percentiles(graph, n_pct, evict)
+    del evict
 
     passes = 1000.0 / ms
     nbytes = pass_bytes(m, lens)
+    kinds = ["embed", "qkv", "attention", "attn_merge", "o_proj", "rmsnorm", "gate_up", "down", "lm_head", "accept",
+             "commit"]
+    counts = {k: (1 if k in ("embed", "lm_head", "accept", "commit") else m.n_layers) for k in kinds}
+    roof_pass = sum(roofline_time(k, m, lens) * counts[k] for k in kinds if k != "rmsnorm")
     res = {
         "metric": METRIC, "value": passes, "unit": "verify passes/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -342,9 +442,36 @@ def main():
         "sum_tau": int(tau.sum()),
         "hbm_frac_of_peak": nbytes / (ms * 1e-3) / HBM_PEAK,
         "algorithmic_bytes_per_pass": nbytes,
-        "roofline": roof,
-        "kernels": per_kind,
+        "pass_roofline_frac": roof_pass / (ms * 1e-3),
+        "pass_roofline_us": roof_pass * 1e6,
+        "step_ms_warm_p10_p50_p90": warm,
+        "step_ms_cold_p10_p50_p90": cold,
     }
+    if not args.no_kernel_times:
+        reps = max(3, min(10, args.steps // 10))
+        per_kind = kernel_times(ver, dev, tok, kv0, kinds, reps)
+        dom = max(per_kind, key=lambda k: per_kind[k]["ms_per_pass"])
+        by, fl = kernel_work(dom, m, lens)
+        t_launch = per_kind[dom]["us_per_launch"] * 1e-6
+        if fl / max(by, 1) > RIDGE:
+            roof = {"bound": "mfma", "achieved": fl / t_launch / 1e12, "peak": MFMA_BF16_PEAK / 1e12, "unit": "TFLOP/s"}
+        else:
+            roof = {"bound": "hbm", "achieved": by / t_launch / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        cnt = COUNTERS.get(dom) if COUNTERS_DIGEST == _sources_digest() else None
+        roof["traffic"] = cnt["traffic"] if cnt else None
+        roof["mfma_util"] = cnt.get("mfma_util") if cnt else None
+        roof["kernel"] = dom
+        roof["us_per_launch"] = per_kind[dom]["us_per_launch"]
+        roof["algorithmic_bytes_per_launch"] = by
+        roof["algorithmic_flops_per_launch"] = fl
+        roof["timing"] = "the kernel's own dispatch events inside eager passes (every layer's weights from HBM)"
+        for k, v in per_kind.items():
+            v["roofline_us"] = roofline_time(k, m, lens) * 1e6
+            v["roofline_frac"] = v["roofline_us"] / v["us_per_launch"] if v["us_per_launch"] else None
+        res["roofline"] = roof
+        res["kernels"] = per_kind
+        res["kernel_sum_ms_per_pass"] = sum(v["ms_per_pass"] for v in per_kind.values())
     if args.no_extras:
         ver.close()
         print(json.dumps(res), flush=True)
@@ -357,24 +484,30 @@ def main():
     log("FP8-activation mode")
     dev.kv_len.copy_(kv0)
     ver8 = Verifier(dev, act_fmt="mxfp8")
-    ms8, acc8 = time_graph(ver8, dev, tok, kv0, args.steps, args.warmup)
-    k8 = kernel_times(ver8, dev, tok, kv0, ["qkv", "gate_up", "down", "rmsnorm"], reps)
+    g8, acc8 = make_graph(ver8, dev, tok, kv0)
+    ms8 = time_graph(g8, args.steps, args.warmup)
     assert ver8.device_error() == 0
     ver8.close()
+    acc8 = acc8.cpu().numpy()
     res["fp8_activations"] = {
         "value": 1000.0 / ms8, "unit": "verify passes/s", "ms_per_step": ms8,
         "activations": "MXFP8 (e4m3 + e8m0 per 32) into QKV, gate/up and down on the scaled FP8 MFMA; "
                        "FP16 into O-proj and attention",
         "sum_tau": int(acc8.sum()), "tau_rows_equal_fp16_mode": int((acc8 == tau).sum()),
-        "mean_tau_fp16_mode": float(tau.mean()), "mean_tau": float(acc8.mean()),
-        "kernels": k8}
-    _, fl8 = kernel_work("gate_up", m, lens)
-    a8 = fl8 / (k8["gate_up"]["us_per_launch"] * 1e-6)
-    res["fp8_activations"]["roofline_gate_up"] = {"bound": "mfma", "achieved": a8 / 1e12, "peak": MFMA_FP8_PEAK / 1e12,
-                                                  "unit": "TFLOP/s", "frac": a8 / MFMA_FP8_PEAK}
+        "mean_tau_fp16_mode": float(tau.mean()), "mean_tau": float(acc8.mean())}
+    del g8, graph
+    cpu = None
     if not args.no_cpu:
         log(f"cpu baseline: oracle on {args.cpu_seqs} sequences")
-        res["cpu_baseline"] = cpu_baseline(wl, weights, kv_layers, lens, args.cpu_seqs)
+        cpu = cpu_baseline(wl, weights, kv_layers, lens, args.cpu_seqs)
+    del dev, kv_layers
+    torch.cuda.empty_cache()
+    res["configs"] = {}
+    for name in OTHER_WORKLOADS + (["8b-fp8-b8-ctx4096"] if args.with_8b else []):
+        w2 = W.WORKLOADS[name]
+        res["configs"][name] = config_line(w2, weights if w2.model == m else None, args.steps, args.warmup)
+    if cpu is not None:
+        res["cpu_baseline"] = cpu
     print(json.dumps(res), flush=True)
 
 

@@ -90,23 +90,40 @@ static int fail(int rc, const char *call, const char *what, hipError_t e = hipSu
   return rc;
 }
 
-// Brackets one launch with events when its class is being timed; `reps` is
-// how many times the call site issues it (the class's repeat count while it
-// is timed, else 1).  Commit, which updates its own input in place, is never
-// repeated.
+thread_local LaunchTimer g_launch_timer;
+
+// Times one launch of a kernel class while that class is being timed.  With
+// a repeat count of 1 the launch itself records a pair of events at its
+// dispatch boundaries (launch_k), so the recorded time is the kernel's
+// execution alone, as a kernel trace measures it.  With repeat r > 1 the call
+// site issues the launch r times back to back between one pair of events on
+// the stream (`reps` = r); commit, which updates its own input in place, is
+// never repeated.
 struct Timed {
   spec_ctx *c;
   hipStream_t st;
-  bool on;
+  bool on, ext;
   int reps;
-  Timed(spec_ctx *c_, int kind, hipStream_t s) : c(c_), st(s), on(false), reps(1) {
+  Timed(spec_ctx *c_, int kind, hipStream_t s) : c(c_), st(s), on(false), ext(false), reps(1) {
     if (c->prof_kind != kind || c->ev_used + 2 > c->ev.size()) return;
-    on = hipEventRecord(c->ev[c->ev_used], st) == hipSuccess;
-    if (on && kind != SPEC_K_COMMIT) reps = c->prof_repeat;
+    if (kind != SPEC_K_COMMIT) reps = c->prof_repeat;
+    ext = reps == 1;
+    if (ext) {
+      g_launch_timer = LaunchTimer{c->ev[c->ev_used], c->ev[c->ev_used + 1], false};
+      on = true;
+    } else {
+      on = hipEventRecord(c->ev[c->ev_used], st) == hipSuccess;
+    }
   }
   ~Timed() {
     if (!on) return;
-    if (hipEventRecord(c->ev[c->ev_used + 1], st) == hipSuccess) {
+    if (ext) {
+      const bool used = g_launch_timer.used;
+      g_launch_timer = LaunchTimer{};
+      if (!used) return;  // the class launched nothing here
+      c->ev_used += 2;
+      c->ev_launches += 1;
+    } else if (hipEventRecord(c->ev[c->ev_used + 1], st) == hipSuccess) {
       c->ev_used += 2;
       c->ev_launches += reps;
     }

@@ -491,7 +491,7 @@ static hipError_t go_attn(const AttnArgs &a, dim3 grid, float sc, hipStream_t st
   static const hipError_t attr =  // once per instantiation: allow more than 64 KB of LDS
       hipFuncSetAttribute((const void *)attn_kernel<D, NW, NTEAM, NR>, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((attn_kernel<D, NW, NTEAM, NR>), grid, dim3(64 * NW * NTEAM), lds, st, a, sc);
+  launch_k((attn_kernel<D, NW, NTEAM, NR>), grid, dim3(64 * NW * NTEAM), lds, st, a, sc);
   return hipGetLastError();
 }
 
@@ -524,9 +524,9 @@ hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st) {
 
 hipError_t launch_attention_merge(const AttnArgs &a, int D, hipStream_t st) {
   if (D == 64)
-    hipLaunchKernelGGL(attn_merge_kernel<64>, dim3(a.Hq, a.batch), dim3(256), 0, st, a);
+    launch_k(attn_merge_kernel<64>, dim3(a.Hq, a.batch), dim3(256), 0, st, a);
   else if (D == 128)
-    hipLaunchKernelGGL(attn_merge_kernel<128>, dim3(a.Hq, a.batch), dim3(256), 0, st, a);
+    launch_k(attn_merge_kernel<128>, dim3(a.Hq, a.batch), dim3(256), 0, st, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

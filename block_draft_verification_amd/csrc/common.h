@@ -1,5 +1,6 @@
 // Shared device helpers for the verify-pass kernels (gfx950, wave64).
 #pragma once
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -191,4 +192,26 @@ __device__ __forceinline__ float halves_sum(float x) {
 // argmax pair ordering: larger value wins, lower index on equal values.
 __device__ __forceinline__ bool better(float v, int32_t i, float bv, int32_t bi) {
   return (v > bv) | ((v == bv) & (i < bi));  // bitwise: no short-circuit branches
+}
+
+// Measurement hook: while `start` is set (a context timing one kernel class,
+// spec_debug_time_kernel), the next launch through launch_k records these two
+// events at its own dispatch boundaries, so their difference is that kernel's
+// execution time alone.  One per host thread; set and cleared by the host code
+// of the C ABI around a single launch.
+struct LaunchTimer {
+  hipEvent_t start = nullptr, stop = nullptr;
+  bool used = false;
+};
+extern thread_local LaunchTimer g_launch_timer;
+
+// (callers read hipGetLastError() after it, as after hipLaunchKernelGGL)
+template <class K, class... A>
+inline void launch_k(K kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t st, A... args) {
+  if (g_launch_timer.start && !g_launch_timer.used) {
+    g_launch_timer.used = true;
+    hipExtLaunchKernelGGL(kernel, grid, block, lds, st, g_launch_timer.start, g_launch_timer.stop, 0, args...);
+  } else {
+    hipLaunchKernelGGL(kernel, grid, block, lds, st, args...);
+  }
 }

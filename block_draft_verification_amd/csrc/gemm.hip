@@ -1002,15 +1002,24 @@ struct Shape {
   int nwv, ng, ks, mt, nt, depth;
 };
 enum ShapeId { kS412, kS222, kS411, kS221, kS141, kS241w8, kS812w8, kS181w8, kNumShapes };
+#ifndef GEMM_DEPTH_S221
+#define GEMM_DEPTH_S221 3
+#endif
+#ifndef GEMM_DEPTH_S241W8
+#define GEMM_DEPTH_S241W8 3
+#endif
+#ifndef GEMM_DEPTH_S812W8
+#define GEMM_DEPTH_S812W8 2
+#endif
 static constexpr Shape kShapes[kNumShapes] = {
-    {4, 4, 1, 2, 1, 4},  // 128 weight rows x 64 activation rows
-    {4, 2, 2, 2, 1, 3},  // 64 x 64, two k groups
-    {4, 4, 1, 1, 1, 6},  // 128 x 32
-    {4, 2, 2, 1, 1, 3},  // 64 x 32, two k groups
-    {4, 1, 4, 1, 1, 3},  // 32 x 32, four k groups
-    {8, 2, 4, 1, 1, 3},  // 64 x 32, four k groups
-    {8, 8, 1, 2, 2, 2},  // 512 x 64, two tiles per wave
-    {8, 1, 8, 1, 1, 2},  // 32 x 32, eight k groups
+    {4, 4, 1, 2, 1, 4},                  // 128 weight rows x 64 activation rows
+    {4, 2, 2, 2, 1, 3},                  // 64 x 64, two k groups
+    {4, 4, 1, 1, 1, 6},                  // 128 x 32
+    {4, 2, 2, 1, 1, GEMM_DEPTH_S221},    // 64 x 32, two k groups
+    {4, 1, 4, 1, 1, 3},                  // 32 x 32, four k groups
+    {8, 2, 4, 1, 1, GEMM_DEPTH_S241W8},  // 64 x 32, four k groups
+    {8, 8, 1, 2, 2, GEMM_DEPTH_S812W8},  // 512 x 64, two tiles per wave
+    {8, 1, 8, 1, 1, 2},                  // 32 x 32, eight k groups
 };
 
 // Shape per GEMM and row count (the thresholds and choices measured over
@@ -1069,7 +1078,7 @@ static hipError_t go_n(const GemmPlan &p, const GemmArgs &ga, const Epi &epi, hi
       hipFuncSetAttribute((const void *)gemm_kernel<F16, FMT, NT, MT, Epi, A8, NWV, KS, DEPTH, NRL>,
                           hipFuncAttributeMaxDynamicSharedMemorySize, lds);
   if (attr != hipSuccess) return attr;
-  hipLaunchKernelGGL((gemm_kernel<F16, FMT, NT, MT, Epi, A8, NWV, KS, DEPTH, NRL>), dim3(p.grid_x, 1, p.nsplit),
+  launch_k((gemm_kernel<F16, FMT, NT, MT, Epi, A8, NWV, KS, DEPTH, NRL>), dim3(p.grid_x, 1, p.nsplit),
                      dim3(64 * NWV), lds, st, ga, epi);
   return hipGetLastError();
 }

@@ -450,7 +450,7 @@ hipError_t launch_embed(const int32_t *tokens, int M, int H, int V, const uint16
                         const float *gain, uint16_t *xg, float *ssp, int ld, const int32_t *kv_len, int max_ctx,
                         KvLayout kvl, int32_t *err, const AttnPlanArgs &plan, hipStream_t st) {
   if (H % 32 || (xg && ld - H / 32 > 256)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(embed_kernel, dim3(M), dim3(256), 0, st, tokens, H, V, table, h, gain, xg, ssp, ld, kv_len,
+  launch_k(embed_kernel, dim3(M), dim3(256), 0, st, tokens, H, V, table, h, gain, xg, ssp, ld, kv_len,
                      max_ctx, kvl, err, plan);
   return hipGetLastError();
 }
@@ -498,10 +498,10 @@ hipError_t launch_norm(const float *h, float *h_out, const float *part, int nspl
                        float eps, uint16_t *x, int out_bf16, float *dump, hipStream_t st) {
   if (H > 4096 || H % 4 || h == h_out) return hipErrorInvalidValue;
   if (out_bf16)
-    hipLaunchKernelGGL(norm_kernel<kOutBF16>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, eps,
+    launch_k(norm_kernel<kOutBF16>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, eps,
                        (void *)x, (uint8_t *)nullptr, dump);
   else
-    hipLaunchKernelGGL(norm_kernel<kOutF16>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, eps,
+    launch_k(norm_kernel<kOutF16>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, eps,
                        (void *)x, (uint8_t *)nullptr, dump);
   return hipGetLastError();
 }
@@ -510,10 +510,10 @@ hipError_t launch_fold(const float *h, float *h_out, const float *part, int nspl
                        uint16_t *xg, int xg_bf16, float *ssp, int ld, int32_t *err, hipStream_t st) {
   if (H > 4096 || H % 32 || h == h_out || ld - H / 32 > 256) return hipErrorInvalidValue;
   if (xg_bf16)
-    hipLaunchKernelGGL(fold_kernel<true>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, xg, ssp, ld,
+    launch_k(fold_kernel<true>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, xg, ssp, ld,
                        err);
   else
-    hipLaunchKernelGGL(fold_kernel<false>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, xg, ssp, ld,
+    launch_k(fold_kernel<false>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, xg, ssp, ld,
                        err);
   return hipGetLastError();
 }
@@ -521,7 +521,7 @@ hipError_t launch_fold(const float *h, float *h_out, const float *part, int nspl
 hipError_t launch_norm_mx8(const float *h, float *h_out, const float *part, int nsplit, const float *gain, int M,
                            int H, float eps, uint8_t *x8, uint8_t *xs, float *dump, hipStream_t st) {
   if (H > 4096 || H % 32 || h == h_out) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(norm_kernel<kOutMX8>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, eps,
+  launch_k(norm_kernel<kOutMX8>, dim3(M), dim3(256), 0, st, h, h_out, part, nsplit, gain, M, H, eps,
                      (void *)x8, xs, dump);
   return hipGetLastError();
 }
@@ -551,14 +551,14 @@ hipError_t launch_quant_mx8(const float *x, int M, int K, uint8_t *codes, uint8_
 hipError_t launch_accept(const ArgmaxPart *part, int nparts, int M, const int32_t *tokens, int batch,
                          int32_t *accept_len, int32_t *bonus, int32_t *argmax, int32_t *last_tau,
                          hipStream_t st) {
-  hipLaunchKernelGGL(accept_kernel, dim3(batch), dim3(1024), 0, st, part, nparts, M, tokens, accept_len,
+  launch_k(accept_kernel, dim3(batch), dim3(1024), 0, st, part, nparts, M, tokens, accept_len,
                      bonus, argmax, last_tau);
   return hipGetLastError();
 }
 
 hipError_t launch_commit(int batch, const int32_t *n_commit, const int32_t *last_tau, int32_t *kv_len,
                          int max_ctx, int32_t *err, hipStream_t st) {
-  hipLaunchKernelGGL(commit_kernel, dim3((batch + 255) / 256), dim3(256), 0, st, batch, n_commit, last_tau,
+  launch_k(commit_kernel, dim3((batch + 255) / 256), dim3(256), 0, st, batch, n_commit, last_tau,
                      kv_len, max_ctx, err);
   return hipGetLastError();
 }
