@@ -273,7 +273,7 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   int units = 0;
   c->attn_cus = attention_device_cus();
   for (int b = 1; b <= kv->max_batch; ++b)
-    units = std::max(units, attention_grid(b, Hkv, kv->max_ctx, D, 0, c->attn_cus));
+    units = std::max(units, attention_grid(b, Hq, Hkv, kv->max_ctx, D, 0, c->attn_cus));
   c->part_units = units;
   size_t rfloats = 0;
   for (int b = 1; b <= kv->max_batch; ++b) {
@@ -406,7 +406,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
   const bool mx = m.act_fmt == SPEC_ACT_MXFP8;
   const NormRows nr = mx ? NormRows{} : NormRows{ssp, ld, H, m.rms_eps};
 
-  const AttnPlanArgs plan = attention_plan_args(c->lane_buf[lane].plan, batch, Hkv, max_ctx, D, 0, c->attn_cus);
+  const AttnPlanArgs plan = attention_plan_args(c->lane_buf[lane].plan, batch, Hq, Hkv, max_ctx, D, 0, c->attn_cus);
   AttnArgs aa{};
   aa.q = q;
   aa.plan = plan.plan;
@@ -818,7 +818,7 @@ int spec_debug_attention(int32_t batch, int32_t Hq, int32_t Hkv, int32_t D, int3
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return fail(SPEC_E_ARG, fn, "alignment");
   // the merge step holds at most 64 splits per sequence
   if (split_len && (max_ctx + split_len - 1) / split_len > 64) return fail(SPEC_E_ARG, fn, "more than 64 splits");
-  AttnPlanArgs p = attention_plan_args(nullptr, batch, Hkv, max_ctx, D, split_len, attention_device_cus());
+  AttnPlanArgs p = attention_plan_args(nullptr, batch, Hq, Hkv, max_ctx, D, split_len, attention_device_cus());
   AttnArgs a{};
   a.q = q;
   a.k_cache = k_cache;
@@ -883,7 +883,7 @@ extern "C" int spec_debug_attention_noalloc(int32_t batch, int32_t Hq, int32_t H
   if (split_len < 0 || split_len % 64) return fail(SPEC_E_ARG, fn, "split_len");
   if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(o)) return fail(SPEC_E_ARG, fn, "alignment");
   if (split_len && (max_ctx + split_len - 1) / split_len > 64) return fail(SPEC_E_ARG, fn, "more than 64 splits");
-  AttnPlanArgs p = attention_plan_args(nullptr, batch, Hkv, max_ctx, D, split_len, attention_device_cus());
+  AttnPlanArgs p = attention_plan_args(nullptr, batch, Hq, Hkv, max_ctx, D, split_len, attention_device_cus());
   const size_t units = (size_t)p.grid, R = (size_t)(Hq / Hkv) * 16;
   const size_t o_bytes = round256(units * R * D * 2), ml_bytes = round256(units * R * 8);
   const size_t plan_bytes = round256((1 + (size_t)batch) * 16);

@@ -52,7 +52,10 @@ __device__ __forceinline__ int wi_x() { return __builtin_amdgcn_workitem_id_x();
 #define ATTN_TEAMS 2  // wave groups per workgroup splitting a split's key tiles
 #endif
 #ifndef ATTN_NR
-#define ATTN_NR 2  // K/V tiles in flight in registers
+#define ATTN_NR 2  // K/V tiles in flight in registers (head_dim 64)
+#endif
+#ifndef ATTN_NR128
+#define ATTN_NR128 2  // the same for head_dim 128 with two or more waves per team
 #endif
 
 // V^T tile in LDS: key k of row d sits at column k ^ vsw(d).  The XOR moves
@@ -458,21 +461,55 @@ int attention_device_cus() {
   return cached[dev];
 }
 
-int attention_grid(int batch, int Hkv, int max_ctx, int D, int split_len, int cus) {
+// Workgroups of one attention instantiation that fit on a CU at once
+// (registers, LDS including the dynamic part, waves), from the runtime's
+// occupancy query; once per instantiation.
+template <int D, int NW, int NTEAM, int NR = ATTN_NR>
+static int attn_resident_of() {
+  static const int n = [] {
+    const int lds = NTEAM * attn_team_halfs<D>() * 2;
+    const void *f = (const void *)attn_kernel<D, NW, NTEAM, NR>;
+    int r = 0;
+    if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&r, f, 64 * NW * NTEAM, lds) != hipSuccess || r < 1)
+      r = 1;
+    return r;
+  }();
+  return n;
+}
+
+// the instantiation launch_attention_splits runs for (D, G)
+static int attn_resident(int D, int G) {
+  const int nw = (G + 1) / 2;
+  if (D == 64) {
+    switch (nw) {
+      case 1: return attn_resident_of<64, 1, ATTN_TEAMS>();
+      case 2: return attn_resident_of<64, 2, ATTN_TEAMS>();
+      case 3: return attn_resident_of<64, 3, ATTN_TEAMS>();
+      default: return attn_resident_of<64, 4, ATTN_TEAMS>();
+    }
+  }
+  switch (nw) {
+    case 1: return attn_resident_of<128, 1, 1, 1>();
+    case 2: return attn_resident_of<128, 2, 1, ATTN_NR128>();
+    case 3: return attn_resident_of<128, 3, 1, ATTN_NR128>();
+    default: return attn_resident_of<128, 4, 1, ATTN_NR128>();
+  }
+}
+
+int attention_grid(int batch, int Hq, int Hkv, int max_ctx, int D, int split_len, int cus) {
   const int units = batch * Hkv;
   if (split_len > 0) {  // at most ceil(ceil(max_ctx / 64) / t) splits per unit
     const int t = split_len / KT, tiles = (max_ctx + KT - 1) / KT;
     return units * ((tiles + t - 1) / t);
   }
-  // One resident round: a two-team workgroup (8 waves, ~200 VGPRs each)
-  // takes a whole CU; one-team workgroups of head_dim 128, three per CU.
-  // Every unit needs at least one workgroup.
-  const int resident = (cus > 0 ? cus : 256) * (attn_teams(D) > 1 ? 1 : 3);
+  // One resident round of workgroups; every unit needs at least one.
+  const int resident = (cus > 0 ? cus : 256) * attn_resident(D, Hq / Hkv);
   return units > resident ? units : resident;
 }
 
-AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hkv, int max_ctx, int D, int split_len, int cus) {
-  return AttnPlanArgs{plan, batch, Hkv, max_ctx, attention_grid(batch, Hkv, max_ctx, D, split_len, cus), attn_teams(D),
+AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hq, int Hkv, int max_ctx, int D, int split_len, int cus) {
+  return AttnPlanArgs{plan, batch, Hkv, max_ctx, attention_grid(batch, Hq, Hkv, max_ctx, D, split_len, cus), attn_teams(D),
                       split_len > 0 ? split_len / KT : 0};
 }
 
@@ -514,9 +551,9 @@ hipError_t launch_attention_splits(const AttnArgs &a, int D, hipStream_t st) {
       // one wave holds a whole 64 x 128 K and V tile per register set: one set
       // in flight, as two would spill
       case 1: return go_attn<128, 1, 1, 1>(a, grid, sc, st);
-      case 2: return go_attn<128, 2, 1>(a, grid, sc, st);
-      case 3: return go_attn<128, 3, 1>(a, grid, sc, st);
-      default: return go_attn<128, 4, 1>(a, grid, sc, st);
+      case 2: return go_attn<128, 2, 1, ATTN_NR128>(a, grid, sc, st);
+      case 3: return go_attn<128, 3, 1, ATTN_NR128>(a, grid, sc, st);
+      default: return go_attn<128, 4, 1, ATTN_NR128>(a, grid, sc, st);
     }
   }
   return hipErrorInvalidValue;

@@ -183,9 +183,9 @@ int attention_device_cus();
 // compute units: split_len > 0 fixes the split length (keys, a multiple of
 // 64), 0 lets the plan choose.  A context fixes `cus` when it sizes its
 // buffers, so its launches never outgrow them.
-int attention_grid(int batch, int Hkv, int max_ctx, int D, int split_len, int cus);
+int attention_grid(int batch, int Hq, int Hkv, int max_ctx, int D, int split_len, int cus);
 // the plan's arguments for a launch of attention_grid(...) workgroups
-AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hkv, int max_ctx, int D, int split_len, int cus);
+AttnPlanArgs attention_plan_args(int4 *plan, int batch, int Hq, int Hkv, int max_ctx, int D, int split_len, int cus);
 // the plan on its own (one wave); the pass computes it inside launch_embed
 hipError_t launch_attention_plan(const int32_t *kv_len, const AttnPlanArgs &p, hipStream_t st);
 
