@@ -41,17 +41,33 @@ WORKLOAD = "0.5b-fp8-b32-ctx512to4096"
 OTHER_WORKLOADS = ["0.5b-fp8-b1-ctx2048", "0.5b-mxfp4mlp-b16-ctx3072"]
 EVICT_BYTES = 512 << 20
 
-# Hardware-counter figures of the dominant kernel classes, from rocprofv3 --pmc
-# runs of `bench.py --no-extras` (profiles/ holds the summaries):
+# Hardware-counter figures per kernel class, from rocprofv3 --pmc runs of
+# `bench.py --no-cpu --no-extras --no-kernel-times` (profiles/ holds the summary):
 #   traffic = FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0 per launch (the factors that
 #             make a plain 1 GiB device copy read back as 1 GiB), bytes
-#   mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE x 1024 SIMDs)
+#   mfma_util = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x 2.4 GHz x the launch's
+#             measured duration): the busy cycles are the MFMA instructions'
+#             own cycles (32 per 32x32x16 MFMA), so this is the share of the
+#             chip's MFMA time the launch keeps busy
 # valid for the kernel sources whose digest is recorded; any other source
 # reports null.
+SIMD_CLOCK = 2.4e9
+N_SIMD = 1024
 COUNTERS_PROFILE = "profiles/verify_pass_0.5b-fp8-b32-ctx512to4096_counters.md"
 SOURCES = ("gemm.hip", "attention.hip", "attn_plan.h", "misc.hip", "common.h", "kernels.h")
-COUNTERS = {}
-COUNTERS_DIGEST = None
+COUNTERS = {  # per launch at the batch-32 grid: FETCH_SIZE / WRITE_SIZE (KiB, medians over dispatches), traffic (bytes), MFMA busy (SIMD cycles)
+    "embed": {"fetch_kib": 509.4, "write_kib": 2752.5, "traffic": 3861920, "mfma_busy_cycles": 0},
+    "qkv": {"fetch_kib": 4981.4, "write_kib": 1152.0, "traffic": 11381504, "mfma_busy_cycles": 1032192},
+    "attention": {"fetch_kib": 19696.6, "write_kib": 3778.2, "traffic": 44207488, "mfma_busy_cycles": 4616192},
+    "attn_merge": {"fetch_kib": 1924.6, "write_kib": 896.0, "traffic": 4859136, "mfma_busy_cycles": 0},
+    "o_proj": {"fetch_kib": 5099.5, "write_kib": 2840.0, "traffic": 13351936, "mfma_busy_cycles": 802816},
+    "gate_up": {"fetch_kib": 9720.0, "write_kib": 4864.0, "traffic": 24887296, "mfma_busy_cycles": 8716288},
+    "down": {"fetch_kib": 23454.0, "write_kib": 2840.0, "traffic": 50941952, "mfma_busy_cycles": 4358144},
+    "lm_head": {"fetch_kib": 137415.8, "write_kib": 9057.9, "traffic": 290702848, "mfma_busy_cycles": 136134656},
+    "accept": {"fetch_kib": 2399.3, "write_kib": 5.0, "traffic": 4918912, "mfma_busy_cycles": 0},
+    "commit": {"fetch_kib": 1.5, "write_kib": 0.1, "traffic": 3200, "mfma_busy_cycles": 0},
+}
+COUNTERS_DIGEST = "c9803aa9ff6cef47"
 
 
 def _sources_digest():
@@ -459,9 +475,10 @@ def main():
         else:
             roof = {"bound": "hbm", "achieved": by / t_launch / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s"}
         roof["frac"] = roof["achieved"] / roof["peak"]
-        cnt = COUNTERS.get(dom) if COUNTERS_DIGEST == _sources_digest() else None
+        counters_ok = COUNTERS_DIGEST == _sources_digest()
+        cnt = COUNTERS.get(dom) if counters_ok else None
         roof["traffic"] = cnt["traffic"] if cnt else None
-        roof["mfma_util"] = cnt.get("mfma_util") if cnt else None
+        roof["mfma_util"] = cnt["mfma_busy_cycles"] / (N_SIMD * SIMD_CLOCK * t_launch) if cnt else None
         roof["kernel"] = dom
         roof["us_per_launch"] = per_kind[dom]["us_per_launch"]
         roof["algorithmic_bytes_per_launch"] = by
@@ -470,6 +487,11 @@ def main():
         for k, v in per_kind.items():
             v["roofline_us"] = roofline_time(k, m, lens) * 1e6
             v["roofline_frac"] = v["roofline_us"] / v["us_per_launch"] if v["us_per_launch"] else None
+            c = COUNTERS.get(k) if counters_ok else None
+            v["algorithmic_bytes"] = kernel_work(k, m, lens)[0]
+            v["traffic"] = c["traffic"] if c else None
+            if c and c["mfma_busy_cycles"] and v["us_per_launch"]:
+                v["mfma_util"] = c["mfma_busy_cycles"] / (N_SIMD * SIMD_CLOCK * v["us_per_launch"] * 1e-6)
         res["roofline"] = roof
         res["kernels"] = per_kind
         res["kernel_sum_ms_per_pass"] = sum(v["ms_per_pass"] for v in per_kind.values())
