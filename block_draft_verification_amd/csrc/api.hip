@@ -54,10 +54,11 @@ struct spec_ctx {
     float *rpart;
     float2 *part_ml;
     int4 *plan;  // attention split plan of the lane's pass
+    SplitWs fx;  // the GEMMs' K splits reduced inside their launches
   };
   LaneBufs lane_buf[SPEC_MAX_LANES] = {};
   void *lane_ws = nullptr;                      // lanes 1.. (one allocation)
-  size_t lane_bytes[4] = {0, 0, 0, 0};          // part_o, part_ml, rpart, plan sizes of one lane
+  size_t lane_bytes[6] = {0, 0, 0, 0, 0, 0};    // part_o, part_ml, rpart, plan, split partials, counters of one lane
   hipStream_t lane_st[SPEC_MAX_LANES] = {};     // [0] unused (the caller's stream)
   hipEvent_t lane_ev[SPEC_MAX_LANES] = {};      // [0] fork, [i] join of lane i
   // launch timing of one kernel class (measurement hook)
@@ -283,6 +284,22 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
     rfloats = std::max(rfloats, (size_t)s * M * H);
   }
 
+  // the in-launch split partials and counters of the decoder GEMMs, for every
+  // row count a lane may run
+  size_t fx_floats = 0;
+  int fx_cnt = 0;
+  for (int M = 16; M <= c->Mmax; M += 16) {
+    const int shape[4][2] = {{(Hq + 2 * Hkv) * D / 32, H / 64}, {H / 32, Hq * D / 64}, {2 * I / 32, H / 64},
+                             {H / 32, I / 64}};  // tiles, k steps of kGemmQkv .. kGemmDown
+    for (int k = 0; k < 4; ++k) {
+      size_t f;
+      int n;
+      split_ws_need(k, M, shape[k][0], shape[k][1], &f, &n);
+      fx_floats = std::max(fx_floats, f);
+      fx_cnt = std::max(fx_cnt, n);
+    }
+  }
+
   const size_t Mm = c->Mmax;
   size_t sizes[] = {2 * Mm * H * 4,                  // h, h2
                     Mm * H * 2,                      // x
@@ -300,7 +317,9 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
                     m->act_fmt == SPEC_ACT_MXFP8 ? Mm * H + Mm * (H / 32) : 16,   // x8, xs8
                     m->act_fmt == SPEC_ACT_MXFP8 ? Mm * I + Mm * (I / 32) : 16,   // a8, as8
                     (1 + (size_t)kv->max_batch) * 16,  // attention split plan
-                    Mm * c->ld * 4};                 // ssp
+                    Mm * c->ld * 4,                  // ssp
+                    fx_floats * 4 + 16,              // in-launch split partials
+                    (size_t)fx_cnt * 4 + 16};        // their counters
   const int NS = sizeof(sizes) / sizeof(sizes[0]);
   size_t off[NS], total = 0;
   for (int i = 0; i < NS; ++i) {
@@ -338,11 +357,20 @@ int spec_verify_init(const spec_model_desc *m, const spec_weights *w, const spec
   c->as8 = c->a8 + Mm * I;
   c->ssp = (float *)(base + off[16]);
   c->dump_hidden = c->dump_logits = nullptr;
-  c->lane_buf[0] = spec_ctx::LaneBufs{c->part_o, c->rpart, c->part_ml, (int4 *)(base + off[15])};
+  c->lane_buf[0] = spec_ctx::LaneBufs{c->part_o, c->rpart, c->part_ml, (int4 *)(base + off[15]),
+                                      SplitWs{(float *)(base + off[17]), (int *)(base + off[18]), fx_floats, fx_cnt}};
   c->lane_bytes[0] = sizes[5];
   c->lane_bytes[1] = sizes[6];
   c->lane_bytes[2] = sizes[12];
   c->lane_bytes[3] = sizes[15];
+  c->lane_bytes[4] = sizes[17];
+  c->lane_bytes[5] = sizes[18];
+  if (hipMemset(base + off[18], 0, sizes[18]) != hipSuccess) {  // the counters start at zero
+    (void)hipFree(c->ws);
+    (void)hipFree(c->wbuf);
+    delete c;
+    return fail(SPEC_E_HIP, fn, "split counter clear");
+  }
 
   // RoPE table: angle = p * theta^(-2i/D), in double, stored as fp32 (cos, sin)
   std::vector<float2> rope((size_t)kv->max_ctx * (D / 2));
@@ -405,6 +433,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
   int32_t *last_tau = c->last_tau + b0;
   const bool mx = m.act_fmt == SPEC_ACT_MXFP8;
   const NormRows nr = mx ? NormRows{} : NormRows{ssp, ld, H, m.rms_eps};
+  const SplitWs *fx = &c->lane_buf[lane].fx;
 
   const AttnPlanArgs plan = attention_plan_args(c->lane_buf[lane].plan, batch, Hq, Hkv, max_ctx, D, 0, c->attn_cus);
   AttnArgs aa{};
@@ -457,7 +486,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
     QkvOut qo{q, kc, vc, kv_len, c->rope, Hq, Hkv, D, max_ctx, kvl, c->err};
     {
       Timed t(c, SPEC_K_QKV, st);
-      for (int r = 0; r < t.reps; ++r) CK(launch_qkv(xin, M, H, L.qkv, qo, nr, st));
+      for (int r = 0; r < t.reps; ++r) CK(launch_qkv(xin, M, H, L.qkv, qo, nr, fx, st));
     }
     aa.k_cache = kc;
     aa.v_cache = vc;
@@ -474,7 +503,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
       for (int r = 0; r < t.reps; ++r) {
         if (mx) CK(launch_residual_partial(ActIn{ao, nullptr}, M, H, Hq * D, L.o, rpart, st));
         else CK(launch_residual(kGemmOproj, ActIn{ao, nullptr}, M, H, Hq * D, L.o,
-                                ResidualOut{h, h2, L.mlp_norm, x, 0, ssp, ld, c->err}, st));
+                                ResidualOut{h, h2, L.mlp_norm, x, 0, ssp, ld, c->err}, fx, st));
       }
     }
     if (mx) {
@@ -484,7 +513,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
     {
       Timed t(c, SPEC_K_GATE_UP, st);
       for (int r = 0; r < t.reps; ++r)
-        CK(launch_swiglu(xin, M, H, I, L.gate_up, mx ? (void *)a8 : act, mx ? as8 : nullptr, nr, st));
+        CK(launch_swiglu(xin, M, H, I, L.gate_up, mx ? (void *)a8 : act, mx ? as8 : nullptr, nr, fx, st));
     }
     const bool last = l + 1 == m.n_layers;
     const float *next_gain = last ? c->final_norm : c->layers[l + 1].attn_norm;
@@ -493,8 +522,7 @@ static int run_pass(spec_ctx *c, int lane, int b0, int batch, const int32_t *tok
       for (int r = 0; r < t.reps; ++r) {
         if (mx || kDownSplit) CK(launch_residual_partial(ain, M, H, I, L.down, rpart, st));
         else CK(launch_residual(kGemmDown, ain, M, H, I, L.down,
-                                ResidualOut{h2, h, next_gain, x, last ? 1 : 0, ssp, ld, c->err},
-                                st));
+                                ResidualOut{h2, h, next_gain, x, last ? 1 : 0, ssp, ld, c->err}, fx, st));
       }
     }
     if (!mx && kDownSplit) {  // the down projection's K splits added to h, the next RMSNorm's input prepared
@@ -577,7 +605,13 @@ int spec_verify_set_lanes(spec_ctx *c, int32_t lanes) {
       p += round256(c->lane_bytes[2]);
       lb.plan = (int4 *)p;
       p += round256(c->lane_bytes[3]);
+      lb.fx = c->lane_buf[0].fx;
+      lb.fx.part = (float *)p;
+      p += round256(c->lane_bytes[4]);
+      lb.fx.cnt = (int *)p;
+      p += round256(c->lane_bytes[5]);
     }
+    CK(hipMemset(ws, 0, per * (SPEC_MAX_LANES - 1)));  // the split counters start at zero
     for (int i = 1; i < SPEC_MAX_LANES; ++i) CK(hipStreamCreateWithFlags(&c->lane_st[i], hipStreamNonBlocking));
     for (hipEvent_t &e : c->lane_ev) CK(hipEventCreateWithFlags(&e, hipEventDisableTiming));
   }
@@ -729,6 +763,28 @@ int spec_debug_linear(int32_t M, int32_t N, int32_t K, const uint16_t *x, const 
   return SPEC_OK;
 }
 
+// the in-launch split workspace of one decoder GEMM (freed at scope exit), so
+// that the debug hooks run the launch shapes the pass runs
+struct TempSplit {
+  void *buf = nullptr;
+  SplitWs ws{};
+  hipError_t make(int kind, int M, int tiles, int ksteps) {
+    size_t f = 0;
+    int n = 0;
+    split_ws_need(kind, M, tiles, ksteps, &f, &n);
+    if (!f) return hipSuccess;
+    const size_t pb = round256(f * 4);
+    hipError_t e = hipMalloc(&buf, pb + (size_t)n * 4);
+    if (e == hipSuccess) e = hipMemset((char *)buf + pb, 0, (size_t)n * 4);
+    ws = SplitWs{(float *)buf, (int *)((char *)buf + pb), f, n};
+    return e;
+  }
+  const SplitWs *get() const { return buf ? &ws : nullptr; }
+  ~TempSplit() {
+    if (buf) (void)hipFree(buf);
+  }
+};
+
 int spec_debug_residual(int32_t M, int32_t N, int32_t K, const uint16_t *x, const void *w, const void *scales,
                         int32_t wfmt, const float *h_in, const float *gain, int32_t xg_bf16, float *h_out,
                         uint16_t *xg, float *ssp, hipStream_t st) {
@@ -742,8 +798,11 @@ int spec_debug_residual(int32_t M, int32_t N, int32_t K, const uint16_t *x, cons
     return fail(SPEC_E_ARG, fn, "alignment or aliasing");
   TempPacked p;
   CK(p.make(wfmt, N, K, w, scales, kRowsPlain, 0, st));
-  CK(launch_residual(K > 1024 ? kGemmDown : kGemmOproj, ActIn{x, nullptr}, M, N, K, p.w,
-                     ResidualOut{h_in, h_out, gain, xg, xg_bf16 ? 1 : 0, ssp, ssp_ld(N), nullptr}, st));
+  const int kind = K > 1024 ? kGemmDown : kGemmOproj;
+  TempSplit fx;
+  CK(fx.make(kind, M, N / 32, K / 64));
+  CK(launch_residual(kind, ActIn{x, nullptr}, M, N, K, p.w,
+                     ResidualOut{h_in, h_out, gain, xg, xg_bf16 ? 1 : 0, ssp, ssp_ld(N), nullptr}, fx.get(), st));
   CK(hipStreamSynchronize(st));
   return SPEC_OK;
 }
@@ -785,8 +844,10 @@ int spec_debug_swiglu(int32_t M, int32_t H, int32_t I, const void *x, const uint
     return fail(SPEC_E_ARG, fn, "alignment");
   TempPacked p;
   CK(p.make(wfmt, 2 * I, H, w, scales, kRowsSwiglu, I, st));
+  TempSplit fx;
+  CK(fx.make(kGemmGateUp, M, 2 * I / 32, H / 64));
   CK(launch_swiglu(ActIn{x, x_scales}, M, H, I, p.w, a, out_fmt == SPEC_ACT_MXFP8 ? a_scales : nullptr, NormRows{},
-                   st));
+                   fx.get(), st));
   CK(hipStreamSynchronize(st));
   return SPEC_OK;
 }

@@ -183,6 +183,8 @@ struct GemmArgs {
   int per_xcd;        // tiles per XCD (gridDim.x = 8 * per_xcd)
   int spl;            // k steps (of 64) per split; gridDim.z splits
   NormRows nr;        // per-row normalisation of the input rows (nr.ssp NULL: none)
+  float *fx_part;     // splits reduced inside the launch (fx_cnt non-NULL): fp32 partial tiles
+  int *fx_cnt;        // arrival counter per tile, zero between launches
 };
 
 // Linear workgroup id -> (N block, M block).  Workgroup L runs on XCD L % 8;
@@ -531,6 +533,69 @@ gemm_kernel(GemmArgs ga, Epi epi) {
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) rs[mt] = 1.f;
   }
+  // Splits reduced inside the launch: every split's k group 0 writes its
+  // partial tile (fp32, accumulator v of all 64 lanes contiguous) with
+  // device-coherent stores, waits until they have completed, and counts its
+  // arrival on the tile's counter; the last split to arrive (whichever it
+  // is) reads the others' partials with device-coherent loads, adds all of
+  // them in split order, sets the counter back to zero and runs the
+  // epilogue; the others are done.  Only the partials and the counter cross
+  // workgroups, each access coherent at device scope on its own, so no
+  // fence (which would write back or invalidate the whole L2 of an XCD) is
+  // needed.
+  const bool fix = ga.fx_cnt != nullptr && gridDim.z > 1;
+  if (fix) {
+    const int S = gridDim.z, z = blockIdx.z, blk = mblk * ga.nb + nblk;
+    auto tile_part = [&](int zz, int t, int mt) {
+      return ga.fx_part + ((((size_t)blk * S + zz) * NG + ng) * (NT * MT) + t * MT + mt) * 1024 + lane;
+    };
+    if (kg == 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          float *q = tile_part(z, t, mt);
+#pragma unroll
+          for (int v = 0; v < 16; ++v) __hip_atomic_store(q + 64 * v, acc[t][mt][v], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+    WAIT_VMCNT(0);    // this wave's partials have reached the device's coherence point
+    __syncthreads();  // every wave's (also: no wave still reads the reduction scratch below)
+    volatile int *flag = reinterpret_cast<volatile int *>(As);
+    if (tid == 0) *flag = __hip_atomic_fetch_add(ga.fx_cnt + blk, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == S - 1;
+    __syncthreads();
+    const bool last = *flag != 0;
+    if (!last) return;  // whole workgroup
+    if (tid == 0) __hip_atomic_store(ga.fx_cnt + blk, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (kg == 0) {
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          f32x16_t tot = acc[t][mt];
+          for (int z0 = 0; z0 < S; z0 += 4) {
+            float b[4][16];  // four splits' partials in flight at once (past the last: the last again)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const float *q = tile_part(min(z0 + u, S - 1), t, mt);
+#pragma unroll
+              for (int v = 0; v < 16; ++v) b[u][v] = __hip_atomic_load(q + 64 * v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int zz = z0 + u;
+              if (zz >= S) break;
+#pragma unroll
+              for (int v = 0; v < 16; ++v) {
+                const float x = zz == z ? acc[t][mt][v] : b[u][v];
+                tot[v] = zz == 0 ? x : tot[v] + x;
+              }
+            }
+          }
+          acc[t][mt] = tot;
+        }
+    }
+  }
   const bool emit_ok = active && kg == 0;
   if constexpr (Epi::kStaged) {
     // Each wave of k group 0 writes its finished outputs (scaled, RoPE /
@@ -551,7 +616,7 @@ gemm_kernel(GemmArgs ga, Epi epi) {
         for (int r0 = 0; r0 < 32; r0 += RPP) {
           const int row = r0 + lane / LPR, col = 4 * (lane % LPR), m = m0 + 32 * mt + row;
           const f32x4_t v = *reinterpret_cast<const f32x4_t *>(st + row * LD + col);
-          epi.template put<NT, MT>(unit, m, M, col, v, blockIdx.z, mt, r0 / RPP, pre);
+          epi.template put<NT, MT>(unit, m, M, col, v, fix ? 0 : (int)blockIdx.z, mt, r0 / RPP, pre);
         }
       }
     }
@@ -1061,10 +1126,38 @@ static int decoder_shape(int kind, int M) {
   }
 }
 
-GemmPlan decoder_plan(int kind, int M, int tiles, int ksteps) {
+// Split K, reduced inside the launch, for the GEMMs in GEMM_FIX_KINDS (bit
+// per GemmKind) whose tiles give fewer than GEMM_FIX_TARGET workgroups: up to
+// that many, at most 8 splits, each k group of a split at least
+// GEMM_FIX_MIN_STEPS k steps, and only while the partials fit the workspace.
+// Measured over whole passes of the 0.5B model: the down projection at 16
+// rows (28 workgroups, 76 k steps) runs 12.1 -> 9.5 us with 4 splits; at
+// 512 rows splitting any of the four GEMMs makes it slower (the partials'
+// round trip and the arrival sit on every workgroup's path), so only down,
+// and only launches that leave most CUs idle, split.
+#ifndef GEMM_FIX_KINDS
+#define GEMM_FIX_KINDS (1 << kGemmDown)
+#endif
+#ifndef GEMM_FIX_TARGET
+#define GEMM_FIX_TARGET 128
+#endif
+#ifndef GEMM_FIX_MIN_STEPS
+#define GEMM_FIX_MIN_STEPS 2
+#endif
+GemmPlan decoder_plan(int kind, int M, int tiles, int ksteps, const SplitWs *ws) {
   const Shape &s = kShapes[decoder_shape(kind, M)];
   GemmPlan p = gemm_plan(M, tiles / s.nt, ksteps, s.mt, false, s.ng);
   p.KS = s.ks;
+  if (!ws || !ws->cnt || !((GEMM_FIX_KINDS >> kind) & 1)) return p;
+  const int wgs = p.nb * p.mb;
+  int S = (GEMM_FIX_TARGET + wgs - 1) / wgs;
+  S = std::min(S, std::min(8, ksteps / (s.ks * GEMM_FIX_MIN_STEPS)));
+  const size_t tile_floats = (size_t)s.ng * s.nt * s.mt * 1024;
+  while (S > 1 && (size_t)S * wgs * tile_floats > ws->part_floats) --S;
+  if (S <= 1 || wgs > ws->cnt_n) return p;
+  p.spl = (ksteps + S - 1) / S;
+  p.nsplit = (ksteps + p.spl - 1) / p.spl;  // every split non-empty
+  p.fix = p.nsplit > 1;
   return p;
 }
 
@@ -1135,9 +1228,11 @@ static hipError_t go_decoder(int id, const GemmPlan &p, const GemmArgs &ga, cons
 // only those kernels are instantiated.
 constexpr unsigned kFp8 = 1u << SPEC_WFMT_FP8_E4M3_ROW, kMx4 = 1u << SPEC_WFMT_MXFP4, kBf16 = 1u << SPEC_WFMT_BF16;
 
-static GemmArgs gemm_args(ActIn x, int M, int K, const LinearW &w, const GemmPlan &p, NormRows nr) {
+static GemmArgs gemm_args(ActIn x, int M, int K, const LinearW &w, const GemmPlan &p, NormRows nr,
+                          const SplitWs *ws = nullptr) {
+  const bool fix = p.fix && ws;
   return GemmArgs{x.x, x.xs, M, K, reinterpret_cast<const uint8_t *>(w.w), reinterpret_cast<const uint8_t *>(w.s),
-                  p.nb, p.mb, p.grid_x / 8, p.spl, nr};
+                  p.nb, p.mb, p.grid_x / 8, p.spl, nr, fix ? ws->part : nullptr, fix ? ws->cnt : nullptr};
 }
 
 // x.xs == NULL: FP16 (BF16 for BF16 weights) activations on the 32x32x16 MFMA;
@@ -1165,12 +1260,12 @@ static hipError_t run(ActIn x, int M, int K, const LinearW &w, Epi epi, bool all
 // FP16 activations, the workgroup shape decoder_shape() picks for the GEMM
 template <unsigned FMTS, class Epi>
 static hipError_t run_decoder(int kind, ActIn x, int M, int K, const LinearW &w, Epi epi, NormRows nr,
-                              hipStream_t st) {
+                              const SplitWs *ws, hipStream_t st) {
   if (x.xs) return hipErrorInvalidValue;
   const int id = decoder_shape(kind, M);
   if (kShapes[id].nt != Epi::kNT) return hipErrorInvalidValue;
-  const GemmPlan p = decoder_plan(kind, M, epi.units * Epi::kNT, K / 64);
-  const GemmArgs ga = gemm_args(x, M, K, w, p, nr);
+  const GemmPlan p = decoder_plan(kind, M, epi.units * Epi::kNT, K / 64, ws);
+  const GemmArgs ga = gemm_args(x, M, K, w, p, nr, ws);
   if constexpr ((FMTS & kFp8) != 0)
     if (w.wfmt == SPEC_WFMT_FP8_E4M3_ROW) return go_decoder<SPEC_WFMT_FP8_E4M3_ROW>(id, p, ga, epi, st);
   if constexpr ((FMTS & kMx4) != 0)
@@ -1195,25 +1290,36 @@ int residual_nsplit(int M, int N, int K) {
   return gemm_plan(M, units, K / 64, pick_mt(M, units, 4), true, 4).nsplit;
 }
 
-hipError_t launch_residual(int kind, ActIn x, int M, int N, int K, LinearW w, const ResidualOut &o, hipStream_t st) {
-  return run_decoder<kFp8 | kMx4>(kind, x, M, K, w, EpiResidual<1>{N / 32, N, fp8_scale(w), o}, NormRows{}, st);
+hipError_t launch_residual(int kind, ActIn x, int M, int N, int K, LinearW w, const ResidualOut &o,
+                           const SplitWs *ws, hipStream_t st) {
+  return run_decoder<kFp8 | kMx4>(kind, x, M, K, w, EpiResidual<1>{N / 32, N, fp8_scale(w), o}, NormRows{}, ws, st);
 }
 
 hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8_t *a_scales, NormRows nr,
-                         hipStream_t st) {
+                         const SplitWs *ws, hipStream_t st) {
   if (a_scales)  // MXFP8 output: a unit of two tiles gives one 32-wide block per row
     return run<2, kFp8 | kMx4>(x, M, H, w, EpiSwiglu<2, true>{I / 32, I, fp8_scale(w), a, a_scales}, false, nr, st);
   if (kShapes[decoder_shape(kGemmGateUp, M)].nt == 2)
-    return run_decoder<kFp8 | kMx4>(kGemmGateUp, x, M, H, w, EpiSwiglu<2>{I / 32, I, fp8_scale(w), a, nullptr}, nr, st);
-  return run_decoder<kFp8 | kMx4>(kGemmGateUp, x, M, H, w, EpiSwiglu<1>{I / 16, I, fp8_scale(w), a, nullptr}, nr, st);
+    return run_decoder<kFp8 | kMx4>(kGemmGateUp, x, M, H, w, EpiSwiglu<2>{I / 32, I, fp8_scale(w), a, nullptr}, nr,
+                                    ws, st);
+  return run_decoder<kFp8 | kMx4>(kGemmGateUp, x, M, H, w, EpiSwiglu<1>{I / 16, I, fp8_scale(w), a, nullptr}, nr,
+                                  ws, st);
 }
 
-hipError_t launch_qkv(ActIn x, int M, int H, LinearW w, QkvOut o, NormRows nr, hipStream_t st) {
+hipError_t launch_qkv(ActIn x, int M, int H, LinearW w, QkvOut o, NormRows nr, const SplitWs *ws, hipStream_t st) {
   if (w.wfmt != SPEC_WFMT_FP8_E4M3_ROW || (o.D != 64 && o.D != 128)) return hipErrorInvalidValue;
   const float *s = reinterpret_cast<const float *>(w.s);
   const int tiles = (o.Hq + 2 * o.Hkv) * o.D / 32;
   if (x.xs) return run<1, kFp8>(x, M, H, w, EpiQkv<1>{tiles, s, o}, false, nr, st);
-  return run_decoder<kFp8>(kGemmQkv, x, M, H, w, EpiQkv<1>{tiles, s, o}, nr, st);
+  return run_decoder<kFp8>(kGemmQkv, x, M, H, w, EpiQkv<1>{tiles, s, o}, nr, ws, st);
+}
+
+void split_ws_need(int kind, int M, int tiles, int ksteps, size_t *floats, int *counters) {
+  SplitWs any{nullptr, reinterpret_cast<int *>(1), ~(size_t)0, 1 << 30};  // sizes only, never dereferenced
+  const GemmPlan p = decoder_plan(kind, M, tiles, ksteps, &any);
+  const Shape &s = kShapes[decoder_shape(kind, M)];
+  *floats = p.fix ? (size_t)p.nsplit * p.nb * p.mb * s.ng * s.nt * s.mt * 1024 : 0;
+  *counters = p.fix ? p.nb * p.mb : 0;
 }
 
 hipError_t launch_lm_argmax(const uint16_t *x, int M, int V, int H, const uint16_t *table, ArgmaxPart *part,

@@ -59,12 +59,27 @@ hipError_t launch_pack_weights(int wfmt, int rows, int cols, const void *w, cons
 // across workgroups into nsplit pieces of spl steps.
 struct GemmPlan {
   int MT, NG, KS, nb, mb, spl, nsplit, grid_x;
+  bool fix = false;  // the nsplit splits are reduced inside the launch
 };
+// Workspace of the GEMMs whose K splits are reduced inside the launch: each
+// split writes an fp32 partial tile, the last split of a tile to finish adds
+// them in split order and runs the epilogue.  The counters are zero between
+// launches (zeroed once when allocated; each tile's last split resets its
+// own), so one workspace serves the launches of one stream in turn.
+struct SplitWs {
+  float *part;
+  int *cnt;
+  size_t part_floats;
+  int cnt_n;
+};
+// the workspace a decoder GEMM at M rows needs (0, 0: it does not split)
+void split_ws_need(int kind, int M, int tiles, int ksteps, size_t *floats, int *counters);
 GemmPlan gemm_plan(int M, int units, int ksteps, int MT, bool allow_split, int ng = 4);  // ng waves along N
 // the decoder GEMMs, whose workgroup shapes are chosen per GEMM and row count
 enum GemmKind { kGemmQkv = 0, kGemmOproj = 1, kGemmGateUp = 2, kGemmDown = 3 };
 // the plan of a decoder GEMM with 16-bit activations over `tiles` 32-row weight tiles
-GemmPlan decoder_plan(int kind, int M, int tiles, int ksteps);
+// (ws non-NULL: K may be split, reduced inside the launch, within ws's sizes)
+GemmPlan decoder_plan(int kind, int M, int tiles, int ksteps, const SplitWs *ws = nullptr);
 // splits the MXFP8 mode's residual projection [M][K] x [N][K]^T uses (partials to reduce)
 int residual_nsplit(int M, int N, int K);
 
@@ -94,7 +109,8 @@ struct ResidualOut {
   int32_t *err;
 };
 // kind: kGemmOproj or kGemmDown (the workgroup shape)
-hipError_t launch_residual(int kind, ActIn x, int M, int N, int K, LinearW w, const ResidualOut &o, hipStream_t st);
+hipError_t launch_residual(int kind, ActIn x, int M, int N, int K, LinearW w, const ResidualOut &o,
+                           const SplitWs *ws, hipStream_t st);
 
 // y fp32 [M][N] (test hook)
 hipError_t launch_linear_f32(ActIn x, int M, int N, int K, LinearW w, float *y, hipStream_t st);
@@ -130,13 +146,13 @@ struct QkvOut {
   int32_t *err;                 // SPEC_DERR_RANGE: a q, k or v value beyond FP16's range
 };
 // q (FP16) and k, v (BF16 cache) from x; w packed with kRowsRope
-hipError_t launch_qkv(ActIn x, int M, int H, LinearW w, QkvOut o, NormRows nr, hipStream_t st);
+hipError_t launch_qkv(ActIn x, int M, int H, LinearW w, QkvOut o, NormRows nr, const SplitWs *ws, hipStream_t st);
 
 // a[m][n] = SiLU(x Wg^T) * (x Wu^T), W = [gate; up] with I rows each, packed
 // with kRowsSwiglu: FP16 (a_scales NULL) or MXFP8 codes in a and e8m0
 // [M][I/32] in a_scales
 hipError_t launch_swiglu(ActIn x, int M, int H, int I, LinearW w, void *a, uint8_t *a_scales, NormRows nr,
-                         hipStream_t st);
+                         const SplitWs *ws, hipStream_t st);
 
 // part[z][m][n] = split z of (x W^T)[m][n] (fp32); residual_nsplit() splits.
 // The following launch_norm adds them to h (the MXFP8-activation mode).

@@ -2,6 +2,9 @@
 (spec_verify_init / spec_verify_block / spec_commit_kv), on the synthetic
 workloads; plus the data-movement, error-path, determinism and graph-replay
 properties of the boundary.  The parity rule is documented in gpu_cases."""
+import dataclasses
+import types
+
 import numpy as np
 import pytest
 import torch
@@ -135,6 +138,55 @@ def test_multi_round_tiny_with_explicit_commits():
         pend = ref.bonus
         torch.cuda.synchronize()
         assert dev.kv_len[0].item() == okv.n[0]
+    assert ver.device_error() == 0
+    ver.close()
+
+
+def test_split_down_matches_oracle_and_repeats():
+    """At batch 1 the down projection (K = 4864 over 28 workgroups) splits K
+    four ways inside its launch: each split's partial goes out with
+    device-coherent stores, and the last split of a tile to arrive adds the
+    partials in split order, resets the tile's arrival counter and runs the
+    epilogue.  Two layers of the 0.5B shape: the pass matches the oracle,
+    two eager passes give identical bits, and graph replays (the counters
+    reused launch after launch) give the eager results."""
+    m = dataclasses.replace(W.M05B, name="0.5b-L2", n_layers=2)
+    seed, cap = 13, 1024
+    wts = W.model_weights(m, seed)
+    lens = np.array([700], np.int32)
+    kvs = [W.synthetic_kv_layer(m, seed, l, lens, cap) for l in range(m.n_layers)]
+    blocks = W.child_rng(seed, 996).integers(0, m.vocab, size=(1, 16)).astype(np.int32)
+    om = oracle.OracleModel(m, wts)
+    okv = oracle.OracleKV.from_bf16(m, [k for k, _ in kvs], [v for _, v in kvs], lens)
+    ref = oracle.verify_block(om, okv, blocks)
+    dev = DeviceModel(m, wts, max_batch=1, max_ctx=cap, kv_layers=kvs, kv_len=lens)
+    ver = Verifier(dev)
+    case = types.SimpleNamespace(wl=types.SimpleNamespace(model=m), lens=lens, blocks=blocks)
+    a = gpu_verify(ver, case)
+    log(f"split down: {compare(ref, a, blocks)}")
+    b = gpu_verify(ver, case)
+    for k in ("hidden", "logits", "argmax", "accept_len", "bonus"):
+        assert np.array_equal(a[k], b[k], equal_nan=True), k
+    tokens = torch.from_numpy(blocks).cuda()
+    tau = torch.empty(1, dtype=torch.int32, device="cuda")
+    bonus = torch.empty(1, dtype=torch.int32, device="cuda")
+    amax = torch.empty(1, 16, dtype=torch.int32, device="cuda")
+    kv0 = dev.kv_len.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        ver.verify(tokens, tau, bonus, amax)
+    torch.cuda.current_stream().wait_stream(s)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        ver.verify(tokens, tau, bonus, amax)
+    for rep in range(3):
+        dev.kv_len.copy_(kv0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert tau.item() == a["accept_len"][0] and bonus.item() == a["bonus"][0], rep
+        assert np.array_equal(amax.cpu().numpy().reshape(-1), a["argmax"].reshape(-1)), rep
     assert ver.device_error() == 0
     ver.close()
 
