@@ -112,7 +112,9 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dev(a: np.ndarray, device):
+def _dev(a, device):
+    if isinstance(a, torch.Tensor):  # already a tensor (drawn on the device): used as it is
+        return a.contiguous().to(device)
     a = np.ascontiguousarray(a)
     if a.dtype == np.uint16:
         a = a.view(np.int16)
