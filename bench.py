@@ -471,7 +471,10 @@ def main():
     wl = W.WORKLOADS[args.workload]
     m = wl.model
     B = wl.batch
-    weights, lens, kv_layers, dev = setup(wl)
+    on_device = args.workload == WORKLOAD_8B
+    if on_device and not (args.no_cpu and args.no_extras):
+        sys.exit("the 8B workload as the main line needs --no-cpu --no-extras (its model is drawn on the device)")
+    weights, lens, kv_layers, dev = device_setup(wl) if on_device else setup(wl)
     ver = Verifier(dev, lanes=args.lanes)
     torch.cuda.synchronize()
     blocks = np.stack([W.draft_rng(wl, b).integers(0, m.vocab, size=16) for b in range(B)]).astype(np.int32)

@@ -1066,7 +1066,7 @@ static int pick_mt(int M, int units, int maxMT) {
 struct Shape {
   int nwv, ng, ks, mt, nt, depth;
 };
-enum ShapeId { kS412, kS222, kS411, kS221, kS141, kS241w8, kS812w8, kS181w8, kNumShapes };
+enum ShapeId { kS412, kS222, kS411, kS221, kS141, kS241w8, kS812w8, kS181w8, kS4112, kNumShapes };
 #ifndef GEMM_DEPTH_S221
 #define GEMM_DEPTH_S221 3
 #endif
@@ -1085,15 +1085,23 @@ static constexpr Shape kShapes[kNumShapes] = {
     {8, 2, 4, 1, 1, GEMM_DEPTH_S241W8},  // 64 x 32, four k groups
     {8, 8, 1, 2, 2, GEMM_DEPTH_S812W8},  // 512 x 64, two tiles per wave
     {8, 1, 8, 1, 1, 2},                  // 32 x 32, eight k groups
+    {4, 4, 1, 1, 2, 3},                  // 256 x 32, two tiles per wave
 };
 
 // Shape per GEMM and row count (the thresholds and choices measured over
-// whole passes of the 0.5B model at 16 and 512 rows).
+// whole passes of the 0.5B model at 16, 256 and 512 rows and of the 8B model
+// at 128 rows).  Gate/up: from 512 rows the 8-wave 512 x 64 tiles (152
+// workgroups at 512 rows); from 256, 256 x 32 tiles with two per wave (304
+// workgroups at 256 rows, where the wide tiles leave 180 CUs idle: 16.3 ->
+// 12.4 us); below, 128 x 64.
 #ifndef GEMM_SMALL_M
 #define GEMM_SMALL_M 64
 #endif
 #ifndef GEMM_WIDE_M
-#define GEMM_WIDE_M 256
+#define GEMM_WIDE_M 512
+#endif
+#ifndef GEMM_MID_M
+#define GEMM_MID_M 256
 #endif
 #ifndef GEMM_SHAPE_QKV
 #define GEMM_SHAPE_QKV kS221
@@ -1105,7 +1113,10 @@ static constexpr Shape kShapes[kNumShapes] = {
 #define GEMM_SHAPE_GATE_UP kS812w8
 #endif
 #ifndef GEMM_SHAPE_GATE_UP_MID
-#define GEMM_SHAPE_GATE_UP_MID kS412
+#define GEMM_SHAPE_GATE_UP_MID kS4112
+#endif
+#ifndef GEMM_SHAPE_GATE_UP_NARROW
+#define GEMM_SHAPE_GATE_UP_NARROW kS412
 #endif
 #ifndef GEMM_SHAPE_DOWN
 #define GEMM_SHAPE_DOWN kS241w8
@@ -1121,7 +1132,8 @@ static int decoder_shape(int kind, int M) {
   switch (kind) {
     case kGemmQkv: return GEMM_SHAPE_QKV;
     case kGemmOproj: return GEMM_SHAPE_OPROJ;
-    case kGemmGateUp: return M >= GEMM_WIDE_M ? GEMM_SHAPE_GATE_UP : GEMM_SHAPE_GATE_UP_MID;
+    case kGemmGateUp:
+      return M >= GEMM_WIDE_M ? GEMM_SHAPE_GATE_UP : M >= GEMM_MID_M ? GEMM_SHAPE_GATE_UP_MID : GEMM_SHAPE_GATE_UP_NARROW;
     default: return GEMM_SHAPE_DOWN;
   }
 }
@@ -1220,6 +1232,7 @@ static hipError_t go_decoder(int id, const GemmPlan &p, const GemmArgs &ga, cons
     case kS241w8: return go_shape<FMT, Epi, kS241w8>(p, ga, epi, st);
     case kS812w8: return go_shape<FMT, Epi, kS812w8>(p, ga, epi, st);
     case kS181w8: return go_shape<FMT, Epi, kS181w8>(p, ga, epi, st);
+    case kS4112: return go_shape<FMT, Epi, kS4112>(p, ga, epi, st);
   }
   return hipErrorInvalidValue;
 }

@@ -102,7 +102,8 @@ def test_rmsnorm_fp16(M, H):
 
 
 @pytest.mark.parametrize("wfmt,M,H,I", [(WFMT_FP8_E4M3_ROW, 16, 896, 4864), (WFMT_MXFP4, 40, 896, 4864),
-                                        (WFMT_FP8_E4M3_ROW, 512, 896, 4864)])
+                                        (WFMT_FP8_E4M3_ROW, 128, 896, 4864), (WFMT_MXFP4, 256, 896, 4864),
+                                        (WFMT_FP8_E4M3_ROW, 300, 896, 4864), (WFMT_FP8_E4M3_ROW, 512, 896, 4864)])
 def test_swiglu_fp16(wfmt, M, H, I):
     """a = SiLU(x Wg^T) * (x Wu^T) rounded to FP16: the gate and up sums carry
     the fp32 accumulation bound (3e-5 of sum |x||w|, as for the plain
