@@ -14,11 +14,11 @@ Also measured, as keys of the same JSON line: per-step percentiles with the
 caches warm and after a 512 MB eviction write (outside the timed events),
 every kernel class's duration inside a pass (the kernel's own dispatch
 events), the roofline of the dominant kernel and of the whole pass, the other
-single-GPU workloads (the batch-1 and MXFP4 shapes; the 8B shape with
---with-8b), batch-1 decoding loops, the FP8-activation mode, and the CPU
+single-GPU workloads (the batch-1 and MXFP4 shapes, and the 8B shape unless
+--no-8b), batch-1 decoding loops, the FP8-activation mode, and the CPU
 oracle on a bounded sample.
 
-Prints one JSON line.  --gpus N > 1 is refused: this build measures one GPU.
+Prints one JSON line.  --gpus N > 1 is refused: the path runs on one GPU.
 """
 import argparse
 import hashlib
