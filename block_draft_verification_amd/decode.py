@@ -97,7 +97,7 @@ def spec_decode(ver: Verifier, pending: torch.Tensor, n_rounds: int, draft_fn, c
         ver.verify(block, acc, bon, None)
         ver.commit(B)  # tau rows of each sequence
         tau = acc.long()
-        # emitted this round, at pos .. pos+tau-1: block[1 .. tau-1], then the bonus
+        # emitted this iteration, at pos .. pos+tau-1: block[1 .. tau-1], then the bonus
         nxt = torch.cat([block[:, 1:], bon[:, None]], dim=1)
         emit = torch.where(j[None, :] < tau[:, None] - 1, nxt, bon[:, None])
         idx = torch.clamp(pos[:, None] + j[None, :], max=capacity + BLOCK - 1)
