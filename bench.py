@@ -58,17 +58,17 @@ COUNTERS_PROFILE = "profiles/verify_pass_0.5b-fp8-b32-ctx512to4096_counters.md"
 SOURCES = ("gemm.hip", "attention.hip", "attn_plan.h", "misc.hip", "common.h", "kernels.h")
 COUNTERS = {  # per launch at the batch-32 grid: FETCH_SIZE / WRITE_SIZE (KiB, medians over dispatches), traffic (bytes), MFMA busy (SIMD cycles)
     "embed": {"fetch_kib": 509.4, "write_kib": 2752.5, "traffic": 3861920, "mfma_busy_cycles": 0},
-    "qkv": {"fetch_kib": 4999.8, "write_kib": 1152.0, "traffic": 11419264, "mfma_busy_cycles": 1032192},
+    "qkv": {"fetch_kib": 5002.9, "write_kib": 1152.0, "traffic": 11425664, "mfma_busy_cycles": 1032192},
     "attention": {"fetch_kib": 19696.6, "write_kib": 3778.2, "traffic": 44207488, "mfma_busy_cycles": 4616192},
     "attn_merge": {"fetch_kib": 1924.6, "write_kib": 896.0, "traffic": 4859136, "mfma_busy_cycles": 0},
-    "o_proj": {"fetch_kib": 5116.5, "write_kib": 2840.0, "traffic": 13386752, "mfma_busy_cycles": 802816},
-    "gate_up": {"fetch_kib": 9730.5, "write_kib": 4864.0, "traffic": 24908800, "mfma_busy_cycles": 8716288},
-    "down": {"fetch_kib": 23470.5, "write_kib": 2840.0, "traffic": 50975744, "mfma_busy_cycles": 4358144},
-    "lm_head": {"fetch_kib": 137384.2, "write_kib": 9003.6, "traffic": 290582560, "mfma_busy_cycles": 136134656},
+    "o_proj": {"fetch_kib": 5112.5, "write_kib": 2840.0, "traffic": 13378560, "mfma_busy_cycles": 802816},
+    "gate_up": {"fetch_kib": 9735.0, "write_kib": 4864.0, "traffic": 24918016, "mfma_busy_cycles": 8716288},
+    "down": {"fetch_kib": 23644.5, "write_kib": 2840.0, "traffic": 51332160, "mfma_busy_cycles": 4358144},
+    "lm_head": {"fetch_kib": 137932.5, "write_kib": 8684.0, "traffic": 291378208, "mfma_busy_cycles": 136134656},
     "accept": {"fetch_kib": 2399.3, "write_kib": 5.0, "traffic": 4918912, "mfma_busy_cycles": 0},
     "commit": {"fetch_kib": 1.5, "write_kib": 0.1, "traffic": 3200, "mfma_busy_cycles": 0},
 }
-COUNTERS_DIGEST = "c28a36bcd2866bcc"
+COUNTERS_DIGEST = "280fa4b0b2f0d8bd"
 
 
 def _sources_digest():

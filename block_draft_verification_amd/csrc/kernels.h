@@ -59,7 +59,8 @@ hipError_t launch_pack_weights(int wfmt, int rows, int cols, const void *w, cons
 // across workgroups into nsplit pieces of spl steps.
 struct GemmPlan {
   int MT, NG, KS, nb, mb, spl, nsplit, grid_x;
-  bool fix = false;  // the nsplit splits are reduced inside the launch
+  bool fix = false;   // the nsplit splits are reduced inside the launch
+  bool krot = false;  // the M blocks start their k loops at staggered steps
 };
 // Workspace of the GEMMs whose K splits are reduced inside the launch: each
 // split writes an fp32 partial tile, the last split of a tile to finish adds
