@@ -63,12 +63,12 @@ COUNTERS = {  # per launch at the batch-32 grid: FETCH_SIZE / WRITE_SIZE (KiB, m
     "attn_merge": {"fetch_kib": 1924.6, "write_kib": 896.0, "traffic": 4859136, "mfma_busy_cycles": 0},
     "o_proj": {"fetch_kib": 5112.5, "write_kib": 2840.0, "traffic": 13378560, "mfma_busy_cycles": 802816},
     "gate_up": {"fetch_kib": 9735.0, "write_kib": 4864.0, "traffic": 24918016, "mfma_busy_cycles": 8716288},
-    "down": {"fetch_kib": 23644.5, "write_kib": 2840.0, "traffic": 51332160, "mfma_busy_cycles": 4358144},
-    "lm_head": {"fetch_kib": 137932.5, "write_kib": 8684.0, "traffic": 291378208, "mfma_busy_cycles": 136134656},
+    "down": {"fetch_kib": 23642.5, "write_kib": 2840.0, "traffic": 51328000, "mfma_busy_cycles": 4358144},
+    "lm_head": {"fetch_kib": 137936.0, "write_kib": 8684.6, "traffic": 291386048, "mfma_busy_cycles": 136134656},
     "accept": {"fetch_kib": 2399.3, "write_kib": 5.0, "traffic": 4918912, "mfma_busy_cycles": 0},
     "commit": {"fetch_kib": 1.5, "write_kib": 0.1, "traffic": 3200, "mfma_busy_cycles": 0},
 }
-COUNTERS_DIGEST = "280fa4b0b2f0d8bd"
+COUNTERS_DIGEST = "d91ef063ce46a412"
 
 
 def _sources_digest():

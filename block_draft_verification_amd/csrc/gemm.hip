@@ -1160,20 +1160,25 @@ static int decoder_shape(int kind, int M) {
 #ifndef GEMM_FIX_MIN_STEPS
 #define GEMM_FIX_MIN_STEPS 2
 #endif
-// The GEMMs whose M blocks walk K from staggered starting steps (bit 1 << kind):
-// the M blocks that share a weight tile, on one XCD, then read different k
-// steps of it at any one time instead of the same lines together.  Measured
-// over whole passes of the 0.5B model at 512 rows: down 16.4 -> 15.4 us per
-// launch (K = 4864, 16 M blocks per tile), while QKV, O, gate/up and the
-// lm_head ran slower staggered.
+// The GEMMs whose M blocks walk K from staggered starting steps (bit 1 << kind),
+// from GEMM_KROT_MIN_M rows: the M blocks that share a weight tile, on one
+// XCD, then read different k steps of it at any one time instead of the same
+// lines together.  Measured over whole passes, alternated on one box: down at
+// 512 rows of the 0.5B model 16.6 -> 15.4 us per launch (K = 4864, 16 M
+// blocks per tile), at 256 rows (MXFP4) unchanged, at 128 rows of the 8B
+// model (K = 14336, 4 M blocks) 36 -> 42 us; QKV, O, gate/up and the lm_head
+// at 512 rows ran slower staggered.
 #ifndef GEMM_KROT_KINDS
 #define GEMM_KROT_KINDS (1 << kGemmDown)
+#endif
+#ifndef GEMM_KROT_MIN_M
+#define GEMM_KROT_MIN_M 512
 #endif
 GemmPlan decoder_plan(int kind, int M, int tiles, int ksteps, const SplitWs *ws) {
   const Shape &s = kShapes[decoder_shape(kind, M)];
   GemmPlan p = gemm_plan(M, tiles / s.nt, ksteps, s.mt, false, s.ng);
   p.KS = s.ks;
-  p.krot = (GEMM_KROT_KINDS >> kind) & 1;
+  p.krot = ((GEMM_KROT_KINDS >> kind) & 1) && M >= GEMM_KROT_MIN_M;
   if (!ws || !ws->cnt || !((GEMM_FIX_KINDS >> kind) & 1)) return p;
   const int wgs = p.nb * p.mb;
   int S = (GEMM_FIX_TARGET + wgs - 1) / wgs;
