@@ -208,6 +208,7 @@ def test_attention(Hq, Hkv, D, lens, split, pad):
 @pytest.mark.parametrize("wfmt,M,N,K,bf16", [(WFMT_FP8_E4M3_ROW, 16, 896, 4864, False),
                                              (WFMT_FP8_E4M3_ROW, 40, 896, 896, False),
                                              (WFMT_MXFP4, 512, 896, 4864, False),
+                                             (WFMT_FP8_E4M3_ROW, 600, 896, 4864, False),
                                              (WFMT_FP8_E4M3_ROW, 512, 896, 896, True),
                                              (WFMT_FP8_E4M3_ROW, 37, 4096, 128, False)])
 def test_residual_with_folded_norm(wfmt, M, N, K, bf16):
@@ -216,7 +217,8 @@ def test_residual_with_folded_norm(wfmt, M, N, K, bf16):
     BF16) from the GPU's own h_out; ssp[m][j] = sum of h_out^2 over columns
     32j .. 32j+31, to fp32 summation accuracy.  The shapes cover the
     workgroup layouts a launch chooses by its row count (one to four k groups,
-    32- and 64-row activation tiles) and a ragged row count."""
+    32- and 64-row activation tiles), ragged row counts, and down's staggered
+    k order from 512 rows (each M block starting at its own k step)."""
     rng = np.random.default_rng(M + N + K)
     if wfmt == WFMT_FP8_E4M3_ROW:
         w = rng.integers(0, 256, size=(N, K)).astype(np.uint8)
